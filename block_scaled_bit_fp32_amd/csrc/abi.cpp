@@ -1,0 +1,429 @@
+// C ABI of libmoe_mi355x.so: argument checks, launch planning, workspace layout and
+// dispatch to the gfx950 kernels. Declarations and contracts: include/moe.h.
+#include "../../include/moe.h"
+
+#include <algorithm>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "plan.hpp"
+
+namespace moe {
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
+hipError_t launch_quantize_nvfp4(const uint16_t* x, int rows, int cols, uint8_t* codes,
+                                 uint8_t* scales, float* g, uint8_t* choice, hipStream_t s);
+hipError_t launch_route(const RouteArgs& a, int n_quant, hipStream_t s);
+#define MOE_DECL_EXPERTS(NAME)                                                              \
+  hipError_t NAME(const ExpertArgs& gu, int gu_grid, size_t gu_lds, const ExpertArgs& dn,  \
+                  int dn_grid, size_t dn_lds, int sf, hipStream_t s);
+MOE_DECL_EXPERTS(launch_experts_bf16)
+MOE_DECL_EXPERTS(launch_experts_nvfp4)
+MOE_DECL_EXPERTS(launch_experts_mxfp4)
+MOE_DECL_EXPERTS(launch_experts_mxfp8)
+#undef MOE_DECL_EXPERTS
+
+// Both expert kernels for the layer's (routed, shared) weight formats.
+static hipError_t launch_experts(const ExpertArgs& gu, int gu_grid, size_t gu_lds,
+                                 const ExpertArgs& dn, int dn_grid, size_t dn_lds, hipStream_t s) {
+  const int sf = gu.has_shared ? gu.sw.fmt : gu.rw.fmt;
+  switch (gu.rw.fmt) {
+    case W_BF16: return launch_experts_bf16(gu, gu_grid, gu_lds, dn, dn_grid, dn_lds, sf, s);
+    case W_NVFP4: return launch_experts_nvfp4(gu, gu_grid, gu_lds, dn, dn_grid, dn_lds, sf, s);
+    case W_MXFP4: return launch_experts_mxfp4(gu, gu_grid, gu_lds, dn, dn_grid, dn_lds, sf, s);
+    case W_MXFP8: return launch_experts_mxfp8(gu, gu_grid, gu_lds, dn, dn_grid, dn_lds, sf, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+}  // namespace moe
+
+using namespace moe;
+
+namespace {
+
+thread_local std::string g_err;
+
+constexpr int kMaxTokens = 64;     // token masks are 64-bit
+constexpr int kMaxE = 1024;
+constexpr int kMaxK = 16;
+constexpr int kRouteTT = 8;
+constexpr int kLdsActBudget = 32768;
+constexpr size_t kAlign = 256;
+
+moe_status_t set_err(moe_status_t st, const std::string& msg) {
+  g_err = msg;
+  return st;
+}
+
+size_t align_up(size_t v, size_t a = kAlign) { return (v + a - 1) / a * a; }
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool valid_wfmt(int f) { return f >= MOE_W_BF16 && f <= MOE_W_MXFP8; }
+
+// weight bytes per row of K elements
+int64_t code_row_bytes(int fmt, int K) {
+  return fmt == W_BF16 ? 2 * (int64_t)K : (fmt == W_MXFP8 ? (int64_t)K : (int64_t)K / 2);
+}
+int64_t scale_row_bytes(int fmt, int K) {
+  return fmt == W_NVFP4 ? K / 16 : (fmt == W_BF16 ? 0 : K / 32);
+}
+
+// Workgroup row mapping for a weight of row length K (see GemvMap). R_force = 0 picks
+// the smallest R >= R_min the mapping allows; at most max_rpl rows per lane.
+bool plan_gemv(int fmt, int K, int ntok, int esize, int R_force, GemvMap& m, int R_min = 16,
+               int max_rpl = 4) {
+  const int EPL = elems_per_piece(fmt);
+  if (K <= 0 || K % EPL) return false;
+  int LPR = 64;
+  while (LPR > 1 && K % (LPR * EPL)) LPR >>= 1;
+  const int G = 64 / LPR;
+  const int R = R_force ? R_force : std::max(R_min, 4 * G);
+  if (R % (4 * G)) return false;
+  const int RPL = R / (4 * G);
+  if (RPL < 1 || RPL > max_rpl || (RPL & (RPL - 1))) return false;
+  const int unit = LPR * EPL, nunits = K / unit;
+  // tokens per pass: 1, 2 or 4 -- a power of two, because a group of 3 runs the 4-token
+  // code path, which reads (and discards) a 4th LDS slot
+  int NG = ntok <= 1 ? 1 : (ntok == 2 ? 2 : 4);
+  while (NG > 1 && NG * unit * esize > kLdsActBudget) NG /= 2;
+  if (NG * unit * esize > kLdsActBudget) return false;
+  int NP = 1;
+  for (int np = RPL >= 4 ? 2 : 4; np >= 1; --np)
+    if (nunits % np == 0 && NG * np * unit * esize <= kLdsActBudget) { NP = np; break; }
+  m.LPR = LPR; m.G = G; m.RPL = RPL; m.R = R; m.KC = NP * unit; m.NP = NP; m.NG = NG;
+  m.esize = esize; m.nchunks = 0;
+  return true;
+}
+
+struct Plan {
+  GemvMap gu_r, gu_s, dn_r, dn_s;
+  int gu_grid, dn_grid, max_slots;
+  size_t gu_lds, dn_lds, list_bytes, gu_tile, dn_tile;
+};
+
+bool make_plan(const moe_layer_t& L, int T, Plan& p) {
+  const int Ish = L.has_shared ? L.I_shared : L.I;
+  const int sfmt = L.has_shared ? L.shared_wfmt : L.wfmt;
+  const int nt = std::max(1, T);
+  if (!plan_gemv(L.wfmt, L.H, nt, 2, 0, p.gu_r)) return false;
+  if (!plan_gemv(sfmt, L.H, nt, 2, 0, p.gu_s)) return false;
+  if (L.I % (p.gu_r.R / 2) || Ish % (p.gu_s.R / 2)) return false;
+  p.gu_r.nchunks = L.I / (p.gu_r.R / 2);
+  p.gu_s.nchunks = Ish / (p.gu_s.R / 2);
+  const int r_es = L.afmt == A_BF16 ? 4 : 2;
+  GemvMap a, b;
+  // down: routed and shared share the hidden-row chunking (the combine is per chunk)
+  if (!plan_gemv(L.wfmt, L.I, nt, r_es, 0, a, 8, 2) || !plan_gemv(sfmt, Ish, nt, 4, 0, b, 8, 2))
+    return false;
+  const int R = std::max(a.R, b.R);
+  if (!plan_gemv(L.wfmt, L.I, nt, r_es, R, p.dn_r, 8, 2) ||
+      !plan_gemv(sfmt, Ish, nt, 4, R, p.dn_s, 8, 2))
+    return false;
+  if (L.H % R) return false;
+  p.dn_r.nchunks = p.dn_s.nchunks = L.H / R;
+  p.max_slots = std::min(L.E, nt * L.k);
+  p.gu_grid = p.max_slots * p.gu_r.nchunks + (L.has_shared ? p.gu_s.nchunks : 0);
+  p.dn_grid = p.max_slots * p.dn_r.nchunks + (L.has_shared ? p.dn_s.nchunks : 0);
+  p.list_bytes = align_up((size_t)L.E * 12 + (size_t)nt * L.k * 4 + 8 * 4 + 64 * 12 + 16, 16);
+  auto tile = [](const GemvMap& m) { return (size_t)m.NG * m.KC * m.esize; };
+  p.gu_tile = align_up(std::max(tile(p.gu_r), tile(p.gu_s)), 16);
+  p.dn_tile = align_up(std::max(tile(p.dn_r), tile(p.dn_s)), 16);
+  const size_t gu_out = (size_t)std::max(p.gu_r.NG * p.gu_r.R, p.gu_s.NG * p.gu_s.R) * 4;
+  p.gu_lds = p.list_bytes + p.gu_tile + gu_out;
+  p.dn_lds = p.list_bytes + p.dn_tile;
+  return true;
+}
+
+struct WsLayout {
+  size_t c_route, c_gu, c_dn, logits, h, hq_codes, hq_scales, hq_scale, o, total;
+  int hs;
+};
+
+WsLayout ws_layout(const moe_layer_t& L, int maxT) {
+  WsLayout w{};
+  const int Ish = L.has_shared ? L.I_shared : 0;
+  const size_t Pr = (size_t)maxT * L.k, Pt = Pr + (L.has_shared ? maxT : 0);
+  w.hs = std::max(L.I, Ish);
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t at = off; off = align_up(off + bytes); return at; };
+  // counters first, at offsets that do not depend on the token count: they must stay
+  // zero between calls, whatever T each call uses
+  w.c_route = take(4 * (size_t)((kMaxTokens + kRouteTT - 1) / kRouteTT));
+  w.c_gu = take(4 * (size_t)L.E);
+  w.c_dn = take(4 * (size_t)(L.H / 8 + 1));   // one per hidden chunk; chunks have >= 8 rows
+  w.logits = take(4 * (size_t)maxT * L.E);
+  w.h = take(4 * Pt * w.hs);
+  const size_t qrow = L.afmt == A_NVFP4_4O6 ? L.I / 2 : (L.afmt == A_FP8_TOKEN ? L.I : 0);
+  w.hq_codes = take(Pr * qrow);
+  w.hq_scales = take(L.afmt == A_NVFP4_4O6 ? Pr * (L.I / 16) : 0);
+  w.hq_scale = take(4 * Pr);
+  w.o = take(4 * Pt * L.H);
+  w.total = off;
+  return w;
+}
+
+// Every violated constraint, or "" if none.
+std::string check_layer(const moe_layer_t* L, int max_tokens) {
+  if (!L) return "layer pointer is NULL";
+  std::string why;
+  auto add = [&](const std::string& s) { why += (why.empty() ? "" : "; ") + s; };
+  char b[256];
+  if (L->H < 32 || L->H % 32) { snprintf(b, sizeof b, "H=%d must be a positive multiple of 32", L->H); add(b); }
+  if (L->I < 32 || L->I % 32) { snprintf(b, sizeof b, "I=%d must be a positive multiple of 32", L->I); add(b); }
+  if (L->E < 1 || L->E > kMaxE) { snprintf(b, sizeof b, "E=%d must be in [1, %d]", L->E, kMaxE); add(b); }
+  if (L->k < 1 || L->k > std::min(std::max(L->E, 1), kMaxK)) {
+    snprintf(b, sizeof b, "k=%d must be in [1, min(E, %d)]", L->k, kMaxK); add(b);
+  }
+  if (L->has_shared != 0 && L->has_shared != 1) add("has_shared must be 0 or 1");
+  if (L->has_shared == 1 && (L->I_shared < 32 || L->I_shared % 32)) {
+    snprintf(b, sizeof b, "I_shared=%d must be a positive multiple of 32", L->I_shared); add(b);
+  }
+  if (max_tokens < 1 || max_tokens > kMaxTokens) {
+    snprintf(b, sizeof b, "max_tokens=%d must be in [1, %d]", max_tokens, kMaxTokens); add(b);
+  }
+  const bool wf_ok = valid_wfmt(L->wfmt), sf_ok = valid_wfmt(L->shared_wfmt);
+  if (!wf_ok) { snprintf(b, sizeof b, "unknown wfmt %d", L->wfmt); add(b); }
+  if (L->has_shared == 1 && !sf_ok) { snprintf(b, sizeof b, "unknown shared_wfmt %d", L->shared_wfmt); add(b); }
+  if (L->afmt < MOE_A_BF16 || L->afmt > MOE_A_FP8_TOKEN) { snprintf(b, sizeof b, "unknown afmt %d", L->afmt); add(b); }
+  if (L->afmt == MOE_A_NVFP4_4O6 && L->wfmt != MOE_W_NVFP4) add("afmt NVFP4_4O6 needs NVFP4 routed weights");
+  if (L->afmt == MOE_A_FP8_TOKEN && L->wfmt != MOE_W_MXFP4 && L->wfmt != MOE_W_MXFP8)
+    add("afmt FP8_TOKEN needs MXFP4 or MXFP8 routed weights");
+  if (L->has_shared == 1 && wf_ok && sf_ok && L->shared_wfmt != L->wfmt && L->shared_wfmt != MOE_W_BF16)
+    add("the shared expert must use the routed format or BF16");
+  if (!L->router_w) add("router_w is NULL");
+  else if (!aligned(L->router_w, 16)) add("router_w must be 16-byte aligned");
+  auto check_w = [&](const moe_weights_t& w, int fmt, const char* name) {
+    if (!w.codes) { snprintf(b, sizeof b, "%s.codes is NULL", name); add(b); }
+    else if (!aligned(w.codes, 16)) { snprintf(b, sizeof b, "%s.codes must be 16-byte aligned", name); add(b); }
+    if (fmt != MOE_W_BF16 && !w.scales) { snprintf(b, sizeof b, "%s.scales is NULL", name); add(b); }
+    if (fmt == MOE_W_NVFP4 && w.scales && !aligned(w.scales, 2)) {
+      snprintf(b, sizeof b, "%s.scales must be 2-byte aligned", name); add(b);
+    }
+    if (fmt == MOE_W_NVFP4 && !w.gscale) { snprintf(b, sizeof b, "%s.gscale is NULL", name); add(b); }
+  };
+  if (wf_ok) { check_w(L->w13, L->wfmt, "w13"); check_w(L->w2, L->wfmt, "w2"); }
+  if (L->has_shared == 1 && sf_ok) { check_w(L->sh13, L->shared_wfmt, "sh13"); check_w(L->sh2, L->shared_wfmt, "sh2"); }
+  if (why.empty()) {
+    Plan p;
+    if (!make_plan(*L, std::max(1, max_tokens), p))
+      add("no workgroup row mapping fits these sizes (H, I, I_shared) and formats");
+  }
+  return why;
+}
+
+moe_status_t check_or_fail(const moe_layer_t* L, int max_tokens) {
+  std::string why = check_layer(L, max_tokens);
+  if (!why.empty()) return set_err(L ? MOE_EUNSUPPORTED : MOE_EINVAL, why);
+  return MOE_OK;
+}
+
+WTensor wtensor(const moe_weights_t& w, int fmt, int rows, int K, int gs_per_expert) {
+  WTensor t;
+  t.codes = static_cast<const uint8_t*>(w.codes);
+  t.scales = fmt == W_BF16 ? nullptr : w.scales;
+  t.gscale = fmt == W_NVFP4 ? w.gscale : nullptr;
+  t.code_row_bytes = code_row_bytes(fmt, K);
+  t.scale_row_bytes = scale_row_bytes(fmt, K);
+  t.rows = rows;
+  t.K = K;
+  t.gs_per_expert = gs_per_expert;
+  t.fmt = fmt;
+  return t;
+}
+
+// Token count the workspace was sized for, recovered from its byte size is not
+// possible; callers pass T <= the max_tokens they sized it for, and the check below
+// compares against the layout for T itself.
+moe_status_t check_ws(const moe_layer_t& L, int T, void* ws, size_t ws_bytes, WsLayout& w) {
+  w = ws_layout(L, std::max(1, T));
+  if (!ws) return set_err(MOE_EWORKSPACE, "workspace is NULL");
+  if (!aligned(ws, kAlign)) return set_err(MOE_EWORKSPACE, "workspace must be 256-byte aligned");
+  if (ws_bytes < w.total) {
+    char b[160];
+    snprintf(b, sizeof b, "workspace has %zu bytes, this call needs %zu", ws_bytes, w.total);
+    return set_err(MOE_EWORKSPACE, b);
+  }
+  return MOE_OK;
+}
+
+size_t xq_part(size_t bytes) { return align_up(bytes); }
+
+}  // namespace
+
+extern "C" {
+
+int32_t moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char* moe_last_error(void) { return g_err.c_str(); }
+
+moe_status_t moe_layer_check(const moe_layer_t* L, int32_t max_tokens, char* why, size_t why_len) {
+  std::string w = check_layer(L, max_tokens);
+  if (why && why_len) {
+    const size_t n = std::min(w.size(), why_len - 1);
+    memcpy(why, w.data(), n);
+    why[n] = '\0';
+  }
+  if (w.empty()) return MOE_OK;
+  g_err = w;
+  return L ? MOE_EUNSUPPORTED : MOE_EINVAL;
+}
+
+size_t moe_workspace_bytes(const moe_layer_t* L, int32_t max_tokens) {
+  if (!check_layer(L, max_tokens).empty()) return 0;
+  return ws_layout(*L, max_tokens).total;
+}
+
+size_t moe_xq_bytes(const moe_layer_t* L, int32_t T) {
+  if (!L || T <= 0) return 0;
+  if (L->afmt == MOE_A_NVFP4_4O6)
+    return xq_part((size_t)T * L->H / 2) + xq_part((size_t)T * L->H / 16) + xq_part(4 * (size_t)T);
+  if (L->afmt == MOE_A_FP8_TOKEN) return xq_part((size_t)T * L->H) + xq_part(4 * (size_t)T);
+  return 0;
+}
+
+moe_status_t moe_workspace_init(void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!ws) return set_err(MOE_EINVAL, "workspace is NULL");
+  if (!aligned(ws, 16) || ws_bytes % 16) return set_err(MOE_EINVAL, "workspace must be 16-byte aligned and sized");
+  if (launch_fill_zero(ws, ws_bytes, stream) != hipSuccess) return set_err(MOE_ELAUNCH, "fill kernel launch failed");
+  return MOE_OK;
+}
+
+moe_status_t moe_route(const moe_layer_t* L, const uint16_t* x_bf16, int32_t T, int32_t* topk_ids,
+                       float* topk_w, void* xq, void* ws, size_t ws_bytes, hipStream_t stream) {
+  moe_status_t st = check_or_fail(L, std::max(1, T));
+  if (st != MOE_OK) return st;
+  if (T < 0) return set_err(MOE_EINVAL, "T must be >= 0");
+  if (T == 0) return MOE_OK;
+  std::string bad;
+  if (!x_bf16 || !aligned(x_bf16, 16)) bad += "x_bf16 must be non-NULL and 16-byte aligned; ";
+  if (!topk_ids) bad += "topk_ids is NULL; ";
+  if (!topk_w) bad += "topk_w is NULL; ";
+  if (L->afmt != MOE_A_BF16 && (!xq || !aligned(xq, kAlign))) bad += "xq must be non-NULL and 256-byte aligned; ";
+  if (!bad.empty()) return set_err(MOE_EINVAL, bad);
+  WsLayout w;
+  if ((st = check_ws(*L, T, ws, ws_bytes, w)) != MOE_OK) return st;
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  RouteArgs a{};
+  a.x = x_bf16;
+  a.wr = L->router_w;
+  a.bias = L->router_bias;
+  a.T = T; a.H = L->H; a.E = L->E; a.k = L->k; a.afmt = L->afmt;
+  a.TT = kRouteTT;
+  a.ET = T <= kRouteTT ? 1 : 4;
+  a.n_tt = (T + kRouteTT - 1) / kRouteTT;
+  a.n_et = (L->E + a.ET - 1) / a.ET;
+  a.logits = reinterpret_cast<float*>(base + w.logits);
+  a.counters = reinterpret_cast<uint32_t*>(base + w.c_route);
+  a.ids = topk_ids;
+  a.w = topk_w;
+  int n_quant = 0;
+  if (L->afmt != MOE_A_BF16) {
+    uint8_t* q = static_cast<uint8_t*>(xq);
+    a.xq_codes = q;
+    if (L->afmt == MOE_A_NVFP4_4O6) {
+      a.xq_scales = q + xq_part((size_t)T * L->H / 2);
+      a.xq_scale = reinterpret_cast<float*>(a.xq_scales + xq_part((size_t)T * L->H / 16));
+    } else {
+      a.xq_scale = reinterpret_cast<float*>(q + xq_part((size_t)T * L->H));
+    }
+    n_quant = T;
+  }
+  if (launch_route(a, n_quant, stream) != hipSuccess) return set_err(MOE_ELAUNCH, "route kernel launch failed");
+  return MOE_OK;
+}
+
+moe_status_t moe_expert_forward(const moe_layer_t* L, const uint16_t* x_bf16, const void* xq, int32_t T,
+                                const int32_t* topk_ids, const float* topk_w, uint16_t* y_bf16,
+                                void* ws, size_t ws_bytes, const moe_debug_t* dbg, hipStream_t stream) {
+  moe_status_t st = check_or_fail(L, std::max(1, T));
+  if (st != MOE_OK) return st;
+  if (T < 0) return set_err(MOE_EINVAL, "T must be >= 0");
+  if (T == 0) return MOE_OK;
+  std::string bad;
+  if (!x_bf16 || !aligned(x_bf16, 16)) bad += "x_bf16 must be non-NULL and 16-byte aligned; ";
+  if (!topk_ids) bad += "topk_ids is NULL; ";
+  if (!topk_w) bad += "topk_w is NULL; ";
+  if (!y_bf16) bad += "y_bf16 is NULL; ";
+  if (L->afmt != MOE_A_BF16 && (!xq || !aligned(xq, kAlign))) bad += "xq must be non-NULL and 256-byte aligned; ";
+  if (dbg && dbg->hq_codes && L->afmt == MOE_A_BF16) bad += "dbg->hq_codes needs a quantized afmt; ";
+  if (dbg && dbg->hq_codes && (!dbg->hq_scale || (L->afmt == MOE_A_NVFP4_4O6 && !dbg->hq_scales)))
+    bad += "dbg->hq_codes needs hq_scale (and hq_scales for NVFP4); ";
+  if (dbg && dbg->hq_codes && !aligned(dbg->hq_codes, 16)) bad += "dbg->hq_codes must be 16-byte aligned; ";
+  if (!bad.empty()) return set_err(MOE_EINVAL, bad);
+  WsLayout w;
+  if ((st = check_ws(*L, T, ws, ws_bytes, w)) != MOE_OK) return st;
+  Plan p;
+  if (!make_plan(*L, T, p)) return set_err(MOE_EUNSUPPORTED, "no launch plan");
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  const int Ish = L->has_shared ? L->I_shared : L->I;
+  const int sfmt = L->has_shared ? L->shared_wfmt : L->wfmt;
+  ExpertArgs a{};
+  a.x = x_bf16;
+  if (L->afmt != MOE_A_BF16) {
+    const uint8_t* q = static_cast<const uint8_t*>(xq);
+    a.xq_codes = q;
+    if (L->afmt == MOE_A_NVFP4_4O6) {
+      a.xq_scales = q + xq_part((size_t)T * L->H / 2);
+      a.xq_scale = reinterpret_cast<const float*>(a.xq_scales + xq_part((size_t)T * L->H / 16));
+    } else {
+      a.xq_scale = reinterpret_cast<const float*>(q + xq_part((size_t)T * L->H));
+    }
+  }
+  a.ids = topk_ids;
+  a.topk_w = topk_w;
+  a.T = T; a.H = L->H; a.I = L->I; a.Ish = Ish; a.E = L->E; a.k = L->k;
+  a.has_shared = L->has_shared; a.afmt = L->afmt;
+  a.max_slots = p.max_slots;
+  a.h = reinterpret_cast<float*>(base + w.h);
+  a.hs = w.hs;
+  a.hq_codes = base + w.hq_codes;
+  a.hq_scales = base + w.hq_scales;
+  a.hq_scale = reinterpret_cast<float*>(base + w.hq_scale);
+  a.o = reinterpret_cast<float*>(base + w.o);
+  a.y = y_bf16;
+  if (dbg) {
+    a.dbg_h = dbg->h;
+    a.dbg_codes = dbg->hq_codes;
+    a.dbg_scales = dbg->hq_scales;
+    a.dbg_scale = dbg->hq_scale;
+  }
+  a.lds_list_bytes = (int)p.list_bytes;
+
+  ExpertArgs gu = a, dn = a;
+  gu.rw = wtensor(L->w13, L->wfmt, 2 * L->I, L->H, 2);
+  gu.sw = wtensor(L->has_shared ? L->sh13 : L->w13, sfmt, 2 * Ish, L->H, 2);
+  gu.rmap = p.gu_r;
+  gu.smap = p.gu_s;
+  gu.counters = reinterpret_cast<uint32_t*>(base + w.c_gu);
+  gu.lds_act_bytes = (int)p.gu_tile;
+  dn.rw = wtensor(L->w2, L->wfmt, L->H, L->I, 1);
+  dn.sw = wtensor(L->has_shared ? L->sh2 : L->w2, sfmt, L->H, Ish, 1);
+  dn.rmap = p.dn_r;
+  dn.smap = p.dn_s;
+  dn.counters = reinterpret_cast<uint32_t*>(base + w.c_dn);
+  dn.lds_act_bytes = (int)p.dn_tile;
+  if (launch_experts(gu, p.gu_grid, p.gu_lds, dn, p.dn_grid, p.dn_lds, stream) != hipSuccess)
+    return set_err(MOE_ELAUNCH, "expert kernel launch failed");
+  return MOE_OK;
+}
+
+moe_status_t quantize_nvfp4_4o6(const uint16_t* x_bf16, int32_t rows, int32_t cols, uint8_t* codes,
+                                uint8_t* scales, float* gscale, uint8_t* choice, hipStream_t stream) {
+  std::string bad;
+  if (rows < 0) bad += "rows must be >= 0; ";
+  if (cols <= 0 || cols % 16) bad += "cols must be a positive multiple of 16; ";
+  if (rows > 0) {
+    if (!x_bf16 || !aligned(x_bf16, 16) || (cols % 8)) bad += "x_bf16 must be non-NULL with 16-byte aligned rows; ";
+    if (!codes || !aligned(codes, 8)) bad += "codes must be non-NULL and 8-byte aligned; ";
+    if (!scales) bad += "scales is NULL; ";
+    if (!gscale) bad += "gscale is NULL; ";
+  }
+  if (!bad.empty()) return set_err(MOE_EINVAL, bad);
+  if (rows == 0) return MOE_OK;
+  if (launch_quantize_nvfp4(x_bf16, rows, cols, codes, scales, gscale, choice, stream) != hipSuccess)
+    return set_err(MOE_ELAUNCH, "quantize kernel launch failed");
+  return MOE_OK;
+}
+
+}  // extern "C"

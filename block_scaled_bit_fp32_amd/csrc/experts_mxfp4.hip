@@ -1,0 +1,14 @@
+// Expert kernels for MXFP4 routed weights (shared expert: MXFP4, BF16).
+#include "experts.hpp"
+
+namespace moe {
+
+hipError_t launch_experts_mxfp4(const ExpertArgs& gu, int gu_grid, size_t gu_lds,
+                             const ExpertArgs& dn, int dn_grid, size_t dn_lds, int sf,
+                             hipStream_t s) {
+  if (sf == W_MXFP4) return launch_experts_t<W_MXFP4, W_MXFP4>(gu, gu_grid, gu_lds, dn, dn_grid, dn_lds, s);
+  if (sf == W_BF16) return launch_experts_t<W_MXFP4, W_BF16>(gu, gu_grid, gu_lds, dn, dn_grid, dn_lds, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace moe

@@ -1,0 +1,14 @@
+// Expert kernels for MXFP8 routed weights (shared expert: MXFP8, BF16).
+#include "experts.hpp"
+
+namespace moe {
+
+hipError_t launch_experts_mxfp8(const ExpertArgs& gu, int gu_grid, size_t gu_lds,
+                             const ExpertArgs& dn, int dn_grid, size_t dn_lds, int sf,
+                             hipStream_t s) {
+  if (sf == W_MXFP8) return launch_experts_t<W_MXFP8, W_MXFP8>(gu, gu_grid, gu_lds, dn, dn_grid, dn_lds, s);
+  if (sf == W_BF16) return launch_experts_t<W_MXFP8, W_BF16>(gu, gu_grid, gu_lds, dn, dn_grid, dn_lds, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace moe

@@ -1,0 +1,79 @@
+// Host/device shared plain structs: launch plans and kernel arguments.
+#pragma once
+#include <stdint.h>
+
+namespace moe {
+
+enum WFmt : int { W_BF16 = 0, W_NVFP4 = 1, W_MXFP4 = 2, W_MXFP8 = 3 };
+enum AFmt : int { A_BF16 = 0, A_NVFP4_4O6 = 1, A_FP8_TOKEN = 2 };
+
+// Elements one lane reads per 16-byte weight load.
+inline constexpr int elems_per_piece(int fmt) {
+  return fmt == W_BF16 ? 8 : (fmt == W_MXFP8 ? 16 : 32);
+}
+
+// How a workgroup (4 waves) covers R weight rows of length K:
+//   LPR lanes per row (power of two), G = 64 / LPR rows per wave in parallel,
+//   RPL rows per lane, R = 4 * G * RPL rows per workgroup. A lane reads 16-byte pieces
+//   at element offsets (s * LPR + lane_in_row) * EPL of each K-chunk of KC elements,
+//   NP = KC / (LPR * EPL) pieces per row per chunk (NP <= 4).
+//   NG tokens are staged in LDS at a time.
+struct GemvMap {
+  int LPR, G, RPL, R, KC, NP, NG, nchunks, esize;
+};
+
+struct WTensor {
+  const uint8_t* codes;
+  const uint8_t* scales;
+  const float* gscale;
+  int64_t code_row_bytes;
+  int64_t scale_row_bytes;
+  int rows;   // rows per expert
+  int K;
+  int gs_per_expert;
+  int fmt;
+};
+
+struct RouteArgs {
+  const uint16_t* x;
+  const float* wr;
+  const float* bias;
+  int T, H, E, k, afmt;
+  int TT, ET, n_tt, n_et;   // token tile, experts per workgroup, tile counts
+  float* logits;            // [T][E]
+  uint32_t* counters;       // [n_tt]
+  int32_t* ids;
+  float* w;
+  uint8_t* xq_codes;
+  uint8_t* xq_scales;
+  float* xq_scale;
+};
+
+struct ExpertArgs {
+  const uint16_t* x;
+  const uint8_t* xq_codes;
+  const uint8_t* xq_scales;
+  const float* xq_scale;
+  const int32_t* ids;
+  const float* topk_w;
+  WTensor rw, sw;        // routed / shared weights of this stage
+  GemvMap rmap, smap;
+  int T, H, I, Ish, E, k, has_shared, afmt;
+  int max_slots;         // routed expert slots launched: min(E, T * k)
+  float* h;              // [T*k + T][hs]
+  int hs;
+  uint8_t* hq_codes;     // [T*k][I/2 | I]
+  uint8_t* hq_scales;    // [T*k][I/16]
+  float* hq_scale;       // [T*k]
+  float* o;              // [T*k + T][H]
+  uint32_t* counters;
+  uint16_t* y;
+  float* dbg_h;
+  uint8_t* dbg_codes;
+  uint8_t* dbg_scales;
+  float* dbg_scale;
+  int lds_list_bytes;    // offset of the activation tile in dynamic LDS
+  int lds_act_bytes;     // size of the activation tile
+};
+
+}  // namespace moe

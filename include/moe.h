@@ -1,0 +1,181 @@
+/*
+ * moe.h -- C ABI of libmoe_mi355x.so: one small-batch decode Mixture-of-Experts layer
+ * on one AMD Instinct MI355X (gfx950).
+ *
+ * The layer (what every page describes for its model):
+ *   - an FP32 router GEMV with sigmoid top-k selection ("Inkling 2 Small on vLLM:
+ *     Day-0 Support", accuracy evaluation: FP32 router; "Day 0 support for Mistral
+ *     Large 4 on vLLM", breakable CUDA graphs and fusions: FP32 router GEMM;
+ *     "vLLM Day-0 support for Recursive's Flint", architecture: sigmoid top-6 of 256
+ *     experts plus one shared expert);
+ *   - gate/up and down projections that read only the selected experts' weights
+ *     (Flint page, optimization strategy: small-batch MoE kernels), with SwiGLU;
+ *   - block-scaled weights: NVFP4 (Inkling page, mixed-precision MoE), OCP MXFP4 and
+ *     MXFP8 (Mistral Large 4 page, AMD section and ROCm implementation details);
+ *   - optional in-kernel activation quantization: NVFP4 "Four Over Six" (Inkling page,
+ *     Four-Over-Six NVFP4; MoE with fused activation quantization) or FP8-E4M3 with
+ *     one scale per token (Mistral Large 4 page, MXFP4 experts, a8w4);
+ *   - a weighted combine of the routed outputs plus the shared expert (Flint page,
+ *     low-latency decode path: routing and expert combine fused into the GEMVs).
+ *
+ * Conventions for every entry point:
+ *   - Tensor pointers are DEVICE pointers owned by the caller (e.g. a torch tensor's
+ *     data_ptr()). The library never allocates, frees or synchronizes inside
+ *     moe_route, moe_expert_forward or quantize_nvfp4_4o6; they enqueue kernels on
+ *     `stream` and return.
+ *   - Every entry returns a moe_status_t and never throws. Arguments are validated
+ *     before anything is launched; on error nothing is enqueued and moe_last_error()
+ *     returns a message (thread-local) naming every problem found.
+ *   - A launch failure reported by the HIP runtime maps to MOE_ELAUNCH.
+ *   - BF16 values are passed as uint16_t bit patterns; FP8 / E8M0 bytes as uint8_t.
+ *   - Results are deterministic: repeated calls on the same inputs give identical bits.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_EINVAL = -1,        /* bad argument: null pointer, size, alignment            */
+  MOE_EUNSUPPORTED = -2,  /* valid request this library does not implement          */
+  MOE_EWORKSPACE = -3,    /* workspace missing or smaller than moe_workspace_bytes  */
+  MOE_ELAUNCH = -4        /* the HIP runtime refused or failed a kernel launch      */
+} moe_status_t;
+
+/* Storage format of a weight tensor [rows][K], K contiguous. */
+typedef enum {
+  MOE_W_BF16 = 0,   /* codes: uint16 BF16 [rows][K]; no scales                         */
+  MOE_W_NVFP4 = 1,  /* codes: E2M1 nibbles [rows][K/2], element 2i in the low nibble;
+                       scales: E4M3 bytes [rows][K/16]; gscale: one FP32 per tensor    */
+  MOE_W_MXFP4 = 2,  /* codes as NVFP4; scales: E8M0 bytes [rows][K/32]; no gscale       */
+  MOE_W_MXFP8 = 3   /* codes: E4M3 bytes [rows][K]; scales: E8M0 bytes [rows][K/32]     */
+} moe_wfmt_t;
+
+/* Format the routed experts' activations (x before gate/up, h before down) take. */
+typedef enum {
+  MOE_A_BF16 = 0,        /* x used as given (BF16); h kept in FP32                      */
+  MOE_A_NVFP4_4O6 = 1,   /* NVFP4 with a per-row FP32 global scale amax/2688 and a
+                            Four-Over-Six E4M3 scale per 16 elements (NVFP4 weights only) */
+  MOE_A_FP8_TOKEN = 2    /* FP8-E4M3 with one FP32 scale amax/448 per row (MX weights)  */
+} moe_afmt_t;
+
+/* One stacked weight set: n experts x [rows][K]. Expert e's codes start at
+ * codes + e * rows * (bytes per row); scales and gscale likewise. */
+typedef struct {
+  const void *codes;       /* see moe_wfmt_t; 16-byte aligned                           */
+  const uint8_t *scales;   /* NVFP4 / MX: see moe_wfmt_t (2-byte aligned); BF16: NULL   */
+  const float *gscale;     /* NVFP4 only: FP32 [n][2] for w13 (gate, up), [n][1] for w2 */
+} moe_weights_t;
+
+typedef struct {
+  int32_t H;            /* hidden size (K of gate/up, rows of down); multiple of 32      */
+  int32_t I;            /* routed expert intermediate size; multiple of 32               */
+  int32_t E;            /* routed experts, 1..1024                                       */
+  int32_t k;            /* experts per token, 1..min(E, 16)                              */
+  int32_t has_shared;   /* 1: one shared expert added with weight 1 to every token        */
+  int32_t I_shared;     /* shared expert intermediate size; multiple of 32                */
+  int32_t wfmt;         /* moe_wfmt_t of the routed experts                               */
+  int32_t shared_wfmt;  /* moe_wfmt_t of the shared expert                                */
+  int32_t afmt;         /* moe_afmt_t of the routed experts (the shared expert: BF16 x,
+                           FP32 h)                                                        */
+  const float *router_w;     /* FP32 [E][H]                                              */
+  const float *router_bias;  /* FP32 [E], added to the logits before selection and
+                                weighting, or NULL                                        */
+  moe_weights_t w13;    /* routed gate/up: [E][2I][H], gate rows 0..I-1 then up rows      */
+  moe_weights_t w2;     /* routed down: [E][H][I]                                         */
+  moe_weights_t sh13;   /* shared gate/up: [1][2*I_shared][H] (ignored if !has_shared)    */
+  moe_weights_t sh2;    /* shared down: [1][H][I_shared]                                  */
+} moe_layer_t;
+
+/* Layout of the quantized-token buffer `xq` for T tokens (see moe_xq_bytes):
+ *   MOE_A_NVFP4_4O6: codes [T][H/2] | scales E4M3 [T][H/16] | g FP32 [T]
+ *   MOE_A_FP8_TOKEN: codes E4M3 [T][H] | s FP32 [T]
+ * Each part starts at a 256-byte boundary from the start of xq. */
+
+/* Optional per-call debug outputs of moe_expert_forward (any field may be NULL).
+ * Pair p = t*k + j is token t's j-th selected expert; rows T*k + t hold token t's
+ * shared expert. */
+typedef struct {
+  float *h;             /* FP32 [T*k + T*has_shared][max(I, I_shared)]: SwiGLU outputs   */
+  uint8_t *hq_codes;    /* quantized routed h: NVFP4 [T*k][I/2] or FP8 [T*k][I]           */
+  uint8_t *hq_scales;   /* NVFP4: E4M3 [T*k][I/16]                                        */
+  float *hq_scale;      /* NVFP4: g [T*k]; FP8: s [T*k]                                   */
+} moe_debug_t;
+
+/* Host only; no device access. Checks every constraint the kernels rely on for a
+ * layer run with up to max_tokens tokens (default-deny: anything not known to work
+ * is refused) and writes every violated one, ';'-separated, into why (if non-NULL).
+ * This follows the refuse-at-startup-with-every-reason rule of the Mistral Large 4
+ * page's ROCm implementation details (specialized decode, default deny). */
+moe_status_t moe_layer_check(const moe_layer_t *L, int32_t max_tokens, char *why,
+                             size_t why_len);
+
+/* Bytes of device workspace a layer needs for calls with up to max_tokens tokens;
+ * 0 if moe_layer_check fails. */
+size_t moe_workspace_bytes(const moe_layer_t *L, int32_t max_tokens);
+
+/* Bytes of the xq buffer for T tokens (0 for MOE_A_BF16). */
+size_t moe_xq_bytes(const moe_layer_t *L, int32_t T);
+
+/* Enqueues a fill kernel that zeroes ws. Call once after allocating a workspace
+ * (and after any call that returned an error mid-way). Every successful call leaves
+ * the workspace's counters at zero again. One workspace must not be used by calls
+ * that may overlap (different streams). */
+moe_status_t moe_workspace_init(void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Router: logits = x * router_w^T (+ bias) in FP32; per token the k largest logits,
+ * largest first, ties to the lower expert index; topk_w = sigmoid of the selected
+ * logits, renormalized to sum to 1 (FP32). With afmt != MOE_A_BF16 also quantizes
+ * every token into xq (layout above) in the same launch.
+ *   x_bf16   [T][H] BF16, device.      topk_ids [T][k] int32, device (output).
+ *   topk_w   [T][k] FP32 (output).     xq: NULL for MOE_A_BF16, else moe_xq_bytes.
+ *   0 <= T <= the max_tokens ws was sized for; T = 0 enqueues nothing. */
+moe_status_t moe_route(const moe_layer_t *L, const uint16_t *x_bf16, int32_t T,
+                       int32_t *topk_ids, float *topk_w, void *xq, void *ws,
+                       size_t ws_bytes, hipStream_t stream);
+
+/* Experts and combine: for every selected (token, expert) pair, and for the shared
+ * expert, h = silu(Wg x) * (Wu x) (x quantized per afmt for routed experts; the
+ * shared expert takes x_bf16), h re-quantized per afmt for routed experts, o = Wd h;
+ * y[t] = sum_j topk_w[t][j] * o[t, j] + o_shared[t], FP32 accumulation, BF16 output
+ * (round to nearest even). Reads only the experts named in topk_ids.
+ *   x_bf16 [T][H]; xq as written by moe_route (ignored for MOE_A_BF16);
+ *   topk_ids [T][k] with entries in [0, E); topk_w [T][k]; y_bf16 [T][H] (output).
+ *   dbg: NULL or debug outputs. */
+moe_status_t moe_expert_forward(const moe_layer_t *L, const uint16_t *x_bf16,
+                                const void *xq, int32_t T, const int32_t *topk_ids,
+                                const float *topk_w, uint16_t *y_bf16, void *ws,
+                                size_t ws_bytes, const moe_debug_t *dbg,
+                                hipStream_t stream);
+
+/* Four-Over-Six NVFP4 quantization of rows x[rows][cols] (BF16), cols % 16 == 0
+ * ("Inkling 2 Small on vLLM: Day-0 Support", mixed-precision MoE and Four-Over-Six
+ * NVFP4): per row g = amax/2688 (FP32); per 16-block with max m and c in {6, 4}:
+ * S_c = E4M3((m/g)/c), codes E2M1(x/(S_c*g)); keep c = 4 only if its FP32 sum of
+ * |x - decoded| (pairwise tree 8,4,2,1) is strictly lower. An all-zero row gives
+ * g = 0, zero scales and sign-only codes. Outputs: codes [rows][cols/2] (element 2i
+ * in the low nibble), scales [rows][cols/16], gscale [rows], choice [rows][cols/16]
+ * in {4, 6} (NULL to skip). Bit-exact with the stated FP32 operation order. */
+moe_status_t quantize_nvfp4_4o6(const uint16_t *x_bf16, int32_t rows, int32_t cols,
+                                uint8_t *codes, uint8_t *scales, float *gscale,
+                                uint8_t *choice, hipStream_t stream);
+
+/* Message for the last non-OK status returned on this thread ("" if none). */
+const char *moe_last_error(void);
+
+/* MOE_ABI_VERSION of the loaded library. */
+int32_t moe_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_MI355X_H */

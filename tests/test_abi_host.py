@@ -1,0 +1,114 @@
+"""Host-side checks of the C ABI (no GPU): the library loads, exports every function
+include/moe.h declares, and validates layers and arguments before any launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    src = open(os.path.join(ROOT, "include", "moe.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^[A-Za-z_][\w\s\*]*?\b(\w+)\s*\(", src, flags=re.M)) - {"if"})
+
+
+def test_header_declares_the_boundary():
+    names = _declared_functions()
+    for n in ("moe_route", "moe_expert_forward", "quantize_nvfp4_4o6", "moe_layer_check",
+              "moe_workspace_bytes", "moe_workspace_init", "moe_xq_bytes", "moe_last_error",
+              "moe_abi_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    so = ctypes.CDLL(lib.LIB_PATH)
+    for n in _declared_functions():
+        assert hasattr(so, n), n
+    assert so.moe_abi_version() == 1
+
+
+def _fake_layer(lib, name, **over):
+    """A moe_layer_t with non-NULL aligned dummy pointers: only host checks read it."""
+    cfg = synth.CONFIGS[name]
+    s = lib.LayerT()
+    s.H, s.I, s.E, s.k = cfg.H, cfg.I, cfg.E, cfg.k
+    s.has_shared, s.I_shared = int(cfg.has_shared), cfg.Ish if cfg.has_shared else 0
+    s.wfmt, s.shared_wfmt, s.afmt = lib.WFMT[cfg.wfmt], lib.WFMT[cfg.shared_wfmt], lib.AFMT[cfg.afmt]
+    p = 1 << 20
+    s.router_w = p
+    for f in ("w13", "w2", "sh13", "sh2"):
+        setattr(s, f, lib.WeightsT(p, p, p))
+    for k, v in over.items():
+        setattr(s, k, v)
+    return s
+
+
+def _check(lib, s, max_tokens):
+    buf = ctypes.create_string_buffer(2048)
+    st = lib.lib().moe_layer_check(ctypes.byref(s), max_tokens, buf, len(buf))
+    return st, buf.value.decode()
+
+
+@pytest.mark.parametrize("name", list(synth.CONFIGS))
+def test_every_config_is_accepted_and_sized(lib, name):
+    s = _fake_layer(lib, name)
+    for T in (1, 8, 64):
+        st, why = _check(lib, s, T)
+        assert st == 0, why
+        assert lib.lib().moe_workspace_bytes(ctypes.byref(s), T) > 0
+    assert lib.lib().moe_workspace_bytes(ctypes.byref(s), 8) <= lib.lib().moe_workspace_bytes(ctypes.byref(s), 64)
+
+
+def test_default_deny_lists_every_reason(lib):
+    s = _fake_layer(lib, "flint_w4a16", H=100, k=0, afmt=1, router_w=None)
+    st, why = _check(lib, s, 65)
+    assert st == lib.MOE_EUNSUPPORTED
+    assert "H=100" in why and "k=0" in why and "max_tokens=65" in why
+    assert "router_w is NULL" in why
+    s = _fake_layer(lib, "mistral_mxfp4", afmt=1)
+    st, why = _check(lib, s, 8)
+    assert "NVFP4_4O6 needs NVFP4" in why
+    s = _fake_layer(lib, "flint_w4a16", shared_wfmt=2)
+    st, why = _check(lib, s, 8)
+    assert "shared expert must use" in why
+    assert lib.lib().moe_workspace_bytes(ctypes.byref(s), 8) == 0
+
+
+def test_misaligned_and_null_weights_are_refused(lib):
+    s = _fake_layer(lib, "flint_w4a16")
+    s.w13 = lib.WeightsT((1 << 20) + 4, 0, 0)
+    st, why = _check(lib, s, 8)
+    assert st != 0 and "w13.codes must be 16-byte aligned" in why
+    assert "w13.scales is NULL" in why and "w13.gscale is NULL" in why
+
+
+def test_calls_validate_before_launching(lib):
+    so = lib.lib()
+    s = _fake_layer(lib, "flint_w4a16")
+    # NULL x, ids, w: rejected without touching the device
+    st = so.moe_route(ctypes.byref(s), None, 1, None, None, None, None, 0, None)
+    assert st == lib.MOE_EINVAL
+    msg = so.moe_last_error().decode()
+    assert "x_bf16" in msg and "topk_ids" in msg
+    # workspace too small
+    st = so.moe_route(ctypes.byref(s), 1 << 20, 1, 1 << 20, 1 << 20, None, 1 << 20, 16, None)
+    assert st == lib.MOE_EWORKSPACE
+    assert so.quantize_nvfp4_4o6(1 << 20, 4, 24, 1 << 20, 1 << 20, 1 << 20, None, None) == lib.MOE_EINVAL
+    assert so.moe_route(None, None, 1, None, None, None, None, 0, None) == lib.MOE_EINVAL
+    # zero rows / zero tokens enqueue nothing and succeed
+    assert so.quantize_nvfp4_4o6(None, 0, 32, None, None, None, None, None) == 0
+
+
+def test_xq_bytes_layout(lib):
+    s = _fake_layer(lib, "inkling_w4a4")
+    n = lib.lib().moe_xq_bytes(ctypes.byref(s), 3)
+    assert n == 3 * 4096 // 2 + 768 + 256      # codes | scales (padded to 256) | g (padded)
+    s = _fake_layer(lib, "mistral_mxfp4_a8")
+    assert lib.lib().moe_xq_bytes(ctypes.byref(s), 2) == 2 * 6144 + 256
+    s = _fake_layer(lib, "flint_w4a16")
+    assert lib.lib().moe_xq_bytes(ctypes.byref(s), 2) == 0

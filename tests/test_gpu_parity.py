@@ -1,0 +1,197 @@
+"""GPU parity: every entry point of include/moe.h against the CPU oracle.
+
+Bars: top-k ids, quantized token codes/scales and quantized h codes bit-exact (h codes
+are compared with the oracle's quantizer applied to the GPU's own FP32 h, since FP32 and
+FP64 h legitimately differ in the last bits); combine weights within 2e-6 absolute; the
+layer output within the bar stated in parity_util.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import quant as OQ
+from parity_util import (bf16_bits_to_f64, check_ids, device_layer, host_layer, oracle_layer,
+                         say, y_close)
+
+pytestmark = pytest.mark.gpu
+
+W_ATOL = 2e-6
+
+
+def _x_dev(x_np):
+    return torch.from_numpy(x_np.view(np.int16)).cuda()
+
+
+# ------------------------------------------------------------ quantize_nvfp4_4o6
+def _quant_rows_case():
+    rng = np.random.default_rng(21)
+    rows = []
+    x = rng.normal(size=(37, 4096))
+    x = np.where(rng.random(x.shape) < 0.01, 20 * x, x)
+    rows.append(x)
+    z = np.zeros((3, 4096))
+    z[1, 5] = -0.0
+    z[2, :16] = 1e-30          # tiny blocks: scale underflow paths
+    z[2, 100] = 3.0
+    rows.append(z)
+    return synth.to_bf16_bits(np.concatenate(rows))
+
+
+@pytest.mark.parametrize("cols", [16, 48, 1536, 4096])
+def test_quantize_nvfp4_4o6_bit_exact(lib, cols):
+    xb = _quant_rows_case()[:, :cols].copy()
+    say(f"[parity] quantize_nvfp4_4o6 rows={xb.shape[0]} cols={cols}")
+    codes, scales, g, choice = lib.quantize_nvfp4_4o6(_x_dev(xb))
+    torch.cuda.synchronize()
+    x32 = bf16_bits_to_f64(torch.from_numpy(xb.view(np.int16))).astype(np.float32)
+    rc, rs, rg, rch = OQ.quantize_nvfp4_4o6(x32)
+    assert np.array_equal(g.cpu().numpy().view(np.uint32), rg.view(np.uint32))
+    assert np.array_equal(scales.cpu().numpy(), rs)
+    assert np.array_equal(choice.cpu().numpy(), rch)
+    assert np.array_equal(codes.cpu().numpy(), rc)
+
+
+def test_quantize_nvfp4_4o6_all_bf16_values(lib):
+    """Every finite BF16 value, laid out 4096 per row (row maxima vary by row)."""
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    v = (bits.astype(np.uint32) << 16).view(np.float32)
+    bits = bits[np.isfinite(v)]
+    n = len(bits) // 4096 * 4096
+    xb = bits[:n].reshape(-1, 4096)
+    say(f"[parity] quantize_nvfp4_4o6 all BF16 rows={xb.shape[0]}")
+    codes, scales, g, choice = lib.quantize_nvfp4_4o6(_x_dev(xb))
+    torch.cuda.synchronize()
+    rc, rs, rg, rch = OQ.quantize_nvfp4_4o6((xb.astype(np.uint32) << 16).view(np.float32))
+    assert np.array_equal(g.cpu().numpy().view(np.uint32), rg.view(np.uint32))
+    assert np.array_equal(scales.cpu().numpy(), rs)
+    assert np.array_equal(codes.cpu().numpy(), rc)
+
+
+def test_quantize_zero_rows(lib):
+    xb = np.zeros((0, 64), np.uint16)
+    out = lib.quantize_nvfp4_4o6(_x_dev(np.zeros((1, 64), np.uint16)))
+    torch.cuda.synchronize()
+    assert float(out[2].cpu()[0]) == 0.0
+    assert xb.shape[0] == 0
+
+
+# ------------------------------------------------------------------- full layer
+LAYER_CASES = [
+    ("tiny_bf16", [1, 3]),
+    ("flint_w4a16", [1, 2, 4, 8]),
+    ("flint_bf16", [1, 8]),
+    ("inkling_w4a4", [1, 5, 8]),
+    ("inkling_mxfp8", [1, 8]),
+    ("mistral_mxfp4", [1, 8]),
+    ("mistral_mxfp4_a8", [1, 8]),
+]
+
+
+def _run_layer(lib, name, T, debug=True):
+    dl = device_layer(name)
+    ws = lib.Workspace(dl, max(T, 8))
+    x_np, ref = oracle_layer(name, T)
+    x = _x_dev(x_np)
+    ids, w, xq = lib.route(dl, x, ws)
+    y, dbg = lib.expert_forward(dl, x, xq, ids, w, ws, debug=True)
+    torch.cuda.synchronize()
+    return dl, x_np, ref, ids, w, xq, y, dbg
+
+
+@pytest.mark.parametrize("name,T", [(n, t) for n, ts in LAYER_CASES for t in ts])
+def test_layer_parity(lib, name, T):
+    say(f"[parity] layer {name} T={T}")
+    dl, x_np, ref, ids, w, xq, y, dbg = _run_layer(lib, name, T)
+    cfg = dl.cfg
+    ids_g = ids.cpu().numpy()
+    bad = check_ids(ids_g, ref, cfg.k)
+    assert not bad, f"top-k mismatch on tokens {bad}"
+    same = np.all(ids_g == ref["ids"], axis=1)
+    assert np.max(np.abs(w.cpu().numpy()[same] - ref["w"][same]), initial=0) <= W_ATOL
+    # quantized tokens: bit-exact
+    if cfg.afmt != "bf16":
+        parts = lib.split_xq(dl, xq, T)
+        if cfg.afmt == "nvfp4_4o6":
+            assert np.array_equal(parts["codes"].cpu().numpy(), ref["xq"]["codes"])
+            assert np.array_equal(parts["scales"].cpu().numpy(), ref["xq"]["scales"])
+            assert np.array_equal(parts["g"].cpu().numpy().view(np.uint32), ref["xq"]["g"].view(np.uint32))
+        else:
+            assert np.array_equal(parts["codes"].cpu().numpy(), ref["xq"]["codes"])
+            assert np.array_equal(parts["s"].cpu().numpy().view(np.uint32), ref["xq"]["s"].view(np.uint32))
+    # SwiGLU outputs: FP32 vs FP64, same routing
+    h_g = dbg["h"].cpu().numpy().astype(np.float64)
+    if np.array_equal(ids_g, ref["ids"]):
+        h_r = ref["h"].reshape(T * cfg.k, cfg.I)
+        scale = max(1.0, float(np.sqrt(np.mean(h_r ** 2))))
+        assert np.max(np.abs(h_g[:T * cfg.k, :cfg.I] - h_r)) / scale < 5e-3
+    # quantized h: bit-exact when the oracle quantizes the GPU's own h
+    if cfg.afmt != "bf16":
+        h32 = dbg["h"].cpu().numpy()[:T * cfg.k, :cfg.I]
+        if cfg.afmt == "nvfp4_4o6":
+            rc, rs, rg, _ = OQ.quantize_nvfp4_4o6(h32)
+            assert np.array_equal(dbg["hq_codes"].cpu().numpy(), rc)
+            assert np.array_equal(dbg["hq_scales"].cpu().numpy(), rs)
+            assert np.array_equal(dbg["hq_scale"].cpu().numpy().view(np.uint32), rg.view(np.uint32))
+        else:
+            rc, rs = OQ.quantize_fp8_token(h32)
+            assert np.array_equal(dbg["hq_codes"].cpu().numpy(), rc)
+            assert np.array_equal(dbg["hq_scale"].cpu().numpy().view(np.uint32), rs.view(np.uint32))
+    # layer output
+    if np.array_equal(ids_g, ref["ids"]):
+        ok, max_abs, rel = y_close(bf16_bits_to_f64(y), ref["y"])
+        say(f"[parity]   y max_abs/r={max_abs:.3g} rel_l2={rel:.3g}")
+        assert ok, (max_abs, rel)
+
+
+def test_repeat_calls_are_bit_identical_and_workspace_is_reusable(lib):
+    name = "flint_w4a16"
+    dl = device_layer(name)
+    ws = lib.Workspace(dl, 8)
+    outs = []
+    for T in (8, 1, 3, 8):
+        x = _x_dev(synth.make_x(name, T))
+        ids, w, xq = lib.route(dl, x, ws)
+        outs.append((T, lib.expert_forward(dl, x, xq, ids, w, ws).clone(), ids.clone()))
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0][1].view(torch.int16), outs[3][1].view(torch.int16))
+    assert torch.equal(outs[0][2], outs[3][2])
+    _, ref = oracle_layer(name, 3)
+    ok, _, _ = y_close(bf16_bits_to_f64(outs[2][1]), ref["y"])
+    assert ok
+
+
+def test_zero_tokens_is_a_no_op(lib):
+    dl = device_layer("flint_w4a16")
+    ws = lib.Workspace(dl, 8)
+    x = torch.zeros((0, dl.cfg.H), dtype=torch.int16, device="cuda")
+    ids, w, xq = lib.route(dl, x, ws)
+    y = lib.expert_forward(dl, x, xq, ids, w, ws)
+    torch.cuda.synchronize()
+    assert ids.shape == (0, dl.cfg.k) and y.shape == (0, dl.cfg.H)
+
+
+def test_route_ties_go_to_lower_index(lib):
+    """Duplicate router rows give bit-identical logits; the lower expert index wins."""
+    name = "tiny_bf16"
+    L = dict(host_layer(name))
+    rw = L["router_w"].copy()
+    rw[5] = rw[1]
+    rw[3] = rw[1]
+    L["router_w"] = rw
+    import block_scaled_bit_fp32_amd as moe
+    dl = moe.DeviceLayer.from_host(L)
+    ws = lib.Workspace(dl, 64)
+    x_np = synth.to_bf16_bits(np.random.default_rng(4).normal(size=(64, 256)))
+    ids, w, _ = lib.route(dl, _x_dev(x_np), ws)
+    torch.cuda.synchronize()
+    from oracle import router as OR
+    r_ids, r_w, lg = OR.route(x_np, rw, None, 2)
+    ids_g = ids.cpu().numpy()
+    # ambiguity from near-equal *distinct* logits only: the duplicate rows tie exactly
+    # on both sides and must resolve to the lower index
+    amb = np.array([OR.ambiguous_tokens(np.unique(lg[t])[::-1][None, :4], 2)[0]
+                    for t in range(lg.shape[0])])
+    hit = np.isin(r_ids, [1, 3, 5]).any(axis=1) & ~amb
+    assert hit.sum() > 5
+    assert np.array_equal(ids_g[hit], r_ids[hit])
