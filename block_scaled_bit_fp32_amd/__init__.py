@@ -51,6 +51,10 @@ class DebugT(ctypes.Structure):
                 ("hq_scales", ctypes.c_void_p), ("hq_scale", ctypes.c_void_p)]
 
 
+class KernelTimeT(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char_p), ("launches", ctypes.c_int32), ("total_ms", ctypes.c_double)]
+
+
 # Every symbol include/moe.h declares, with its ctypes signature.
 _P, _I32, _SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
 _SIGNATURES = {
@@ -62,6 +66,8 @@ _SIGNATURES = {
     "moe_expert_forward": (_I32, [ctypes.POINTER(LayerT), _P, _P, _I32, _P, _P, _P, _P, _SZ,
                                   ctypes.POINTER(DebugT), _P]),
     "quantize_nvfp4_4o6": (_I32, [_P, _I32, _I32, _P, _P, _P, _P, _P]),
+    "moe_profile_begin": (_I32, []),
+    "moe_profile_end": (_I32, [ctypes.POINTER(KernelTimeT), _I32]),
     "moe_last_error": (ctypes.c_char_p, []),
     "moe_abi_version": (_I32, []),
 }
@@ -292,6 +298,18 @@ def quantize_nvfp4_4o6(x: torch.Tensor, want_choice: bool = True):
     _check(_lib.quantize_nvfp4_4o6(x.data_ptr(), rows, cols, codes.data_ptr(), scales.data_ptr(),
                                    g.data_ptr(), _ptr(choice), _stream()))
     return codes, scales, g, choice
+
+
+def profile_begin() -> None:
+    """Start timing every kernel the library launches (see moe_profile_begin)."""
+    _check(_lib.moe_profile_begin())
+
+
+def profile_end() -> dict:
+    """End the timing session: {kernel kind: (launches, total ms)}."""
+    arr = (KernelTimeT * 8)()
+    n = _lib.moe_profile_end(arr, 8)
+    return {arr[i].name.decode(): (arr[i].launches, arr[i].total_ms) for i in range(n)}
 
 
 def routed_bytes(layer: DeviceLayer, ids: np.ndarray, T: int) -> int:

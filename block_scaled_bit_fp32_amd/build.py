@@ -19,7 +19,7 @@ BUILD = os.path.join(ROOT, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["route.hip", "experts_bf16.hip", "experts_nvfp4.hip", "experts_mxfp4.hip",
-           "experts_mxfp8.hip", "abi.cpp"]
+           "experts_mxfp8.hip", "abi.cpp", "profile.cpp"]
 COMMON = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
           "-I" + os.path.join(ROOT, "include")]
 DEVICE_ONLY = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

@@ -47,7 +47,7 @@ constexpr int kMaxTokens = 64;     // token masks are 64-bit
 constexpr int kMaxE = 1024;
 constexpr int kMaxK = 16;
 constexpr int kRouteTT = 8;
-constexpr int kLdsActBudget = 32768;
+constexpr int kLdsActBudget = 48 * 1024;   // activation tile per workgroup
 constexpr size_t kAlign = 256;
 
 moe_status_t set_err(moe_status_t st, const std::string& msg) {
@@ -69,30 +69,36 @@ int64_t scale_row_bytes(int fmt, int K) {
   return fmt == W_NVFP4 ? K / 16 : (fmt == W_BF16 ? 0 : K / 32);
 }
 
-// Workgroup row mapping for a weight of row length K (see GemvMap). R_force = 0 picks
-// the smallest R >= R_min the mapping allows; at most max_rpl rows per lane.
-bool plan_gemv(int fmt, int K, int ntok, int esize, int R_force, GemvMap& m, int R_min = 16,
-               int max_rpl = 4) {
+// Row mapping of one weight class (see GemvMap) for rows of length K, activations of
+// `esize` bytes per element, up to ntok tokens per expert; paired = gate/up.
+bool plan_class(int fmt, int K, int ntok, int esize, bool paired, GemvMap& m) {
   const int EPL = elems_per_piece(fmt);
   if (K <= 0 || K % EPL) return false;
-  int LPR = 64;
-  while (LPR > 1 && K % (LPR * EPL)) LPR >>= 1;
-  const int G = 64 / LPR;
-  const int R = R_force ? R_force : std::max(R_min, 4 * G);
-  if (R % (4 * G)) return false;
-  const int RPL = R / (4 * G);
-  if (RPL < 1 || RPL > max_rpl || (RPL & (RPL - 1))) return false;
-  const int unit = LPR * EPL, nunits = K / unit;
-  // tokens per pass: 1, 2 or 4 -- a power of two, because a group of 3 runs the 4-token
-  // code path, which reads (and discards) a 4th LDS slot
-  int NG = ntok <= 1 ? 1 : (ntok == 2 ? 2 : 4);
-  while (NG > 1 && NG * unit * esize > kLdsActBudget) NG /= 2;
-  if (NG * unit * esize > kLdsActBudget) return false;
-  int NP = 1;
-  for (int np = RPL >= 4 ? 2 : 4; np >= 1; --np)
-    if (nunits % np == 0 && NG * np * unit * esize <= kLdsActBudget) { NP = np; break; }
-  m.LPR = LPR; m.G = G; m.RPL = RPL; m.R = R; m.KC = NP * unit; m.NP = NP; m.NG = NG;
-  m.esize = esize; m.nchunks = 0;
+  const int units = K / EPL;
+  // lanes per row: the largest power of two giving every lane >= 3 pieces of the row
+  int LPR = 1;
+  for (int l = 64; l >= 1; l >>= 1)
+    if (units % l == 0 && units / l >= 3) { LPR = l; break; }
+  const int NP = units / LPR;
+  int NPB = 1;
+  for (int d = 4; d >= 1; --d)
+    if (NP % d == 0) { NPB = d; break; }
+  m.LPR = LPR;
+  m.G = 64 / LPR;
+  m.NP = NP;
+  m.NPB = NPB;
+  m.NB = NP / NPB;
+  m.RPL = paired ? 2 : (m.G >= 2 ? 1 : 2);
+  m.RS = 4 * m.G * m.RPL;
+  // tokens per LDS pass: 1, 2 or 4 (a group of 3 runs the 4-token code, which reads and
+  // discards a 4th slot, so groups are powers of two); FP32 tiles 2 at most
+  int NG = ntok <= 1 ? 1 : (ntok == 2 || esize == 4 ? 2 : 4);
+  while (NG > 1 && NG * K * esize > kLdsActBudget) NG /= 2;
+  if (NG * K * esize > kLdsActBudget) return false;
+  m.NG = NG;
+  m.esize = esize;
+  m.NSTEP = 1;
+  m.nchunks = 0;
   return true;
 }
 
@@ -102,35 +108,44 @@ struct Plan {
   size_t gu_lds, dn_lds, list_bytes, gu_tile, dn_tile;
 };
 
-bool make_plan(const moe_layer_t& L, int T, Plan& p) {
+// `resident`: workgroups the expert kernels keep resident (a larger item count than
+// twice that buys nothing, a smaller one leaves CUs idle).
+bool make_plan(const moe_layer_t& L, int T, int resident, Plan& p) {
   const int Ish = L.has_shared ? L.I_shared : L.I;
   const int sfmt = L.has_shared ? L.shared_wfmt : L.wfmt;
   const int nt = std::max(1, T);
-  if (!plan_gemv(L.wfmt, L.H, nt, 2, 0, p.gu_r)) return false;
-  if (!plan_gemv(sfmt, L.H, nt, 2, 0, p.gu_s)) return false;
-  if (L.I % (p.gu_r.R / 2) || Ish % (p.gu_s.R / 2)) return false;
-  p.gu_r.nchunks = L.I / (p.gu_r.R / 2);
-  p.gu_s.nchunks = Ish / (p.gu_s.R / 2);
-  const int r_es = L.afmt == A_BF16 ? 4 : 2;
-  GemvMap a, b;
+  const int u_exp = std::min(L.E, nt * L.k) + (L.has_shared ? 1 : 0);
+  const int target = 2 * resident;
+  // gate/up: chunks of RU = 4 * G * NSTEP intermediate rows (gate + up)
+  if (!plan_class(L.wfmt, L.H, nt, 2, true, p.gu_r) || !plan_class(sfmt, L.H, nt, 2, true, p.gu_s))
+    return false;
+  for (GemvMap* m : {&p.gu_r, &p.gu_s}) {
+    const int Iexp = m == &p.gu_r ? L.I : Ish;
+    const int ps = m->RS / 2;
+    if (Iexp % ps) return false;
+    int ns = 1;
+    while ((Iexp / ps) % (2 * ns) == 0 && u_exp * (Iexp / ps) / (2 * ns) >= target) ns *= 2;
+    m->NSTEP = ns;
+    m->nchunks = Iexp / (ps * ns);
+  }
   // down: routed and shared share the hidden-row chunking (the combine is per chunk)
-  if (!plan_gemv(L.wfmt, L.I, nt, r_es, 0, a, 8, 2) || !plan_gemv(sfmt, Ish, nt, 4, 0, b, 8, 2))
+  const int r_es = L.afmt == A_BF16 ? 4 : 2;
+  if (!plan_class(L.wfmt, L.I, nt, r_es, false, p.dn_r) || !plan_class(sfmt, Ish, nt, 4, false, p.dn_s))
     return false;
-  const int R = std::max(a.R, b.R);
-  if (!plan_gemv(L.wfmt, L.I, nt, r_es, R, p.dn_r, 8, 2) ||
-      !plan_gemv(sfmt, Ish, nt, 4, R, p.dn_s, 8, 2))
-    return false;
-  if (L.H % R) return false;
-  p.dn_r.nchunks = p.dn_s.nchunks = L.H / R;
+  int CH = std::max(p.dn_r.RS, p.dn_s.RS);
+  if (L.H % CH) return false;
+  while (L.H % (2 * CH) == 0 && u_exp * (L.H / (2 * CH)) >= target) CH *= 2;
+  p.dn_r.NSTEP = CH / p.dn_r.RS;
+  p.dn_s.NSTEP = CH / p.dn_s.RS;
+  p.dn_r.nchunks = p.dn_s.nchunks = L.H / CH;
   p.max_slots = std::min(L.E, nt * L.k);
   p.gu_grid = p.max_slots * p.gu_r.nchunks + (L.has_shared ? p.gu_s.nchunks : 0);
   p.dn_grid = p.max_slots * p.dn_r.nchunks + (L.has_shared ? p.dn_s.nchunks : 0);
   p.list_bytes = align_up((size_t)L.E * 12 + (size_t)nt * L.k * 4 + 8 * 4 + 64 * 12 + 16, 16);
-  auto tile = [](const GemvMap& m) { return (size_t)m.NG * m.KC * m.esize; };
-  p.gu_tile = align_up(std::max(tile(p.gu_r), tile(p.gu_s)), 16);
-  p.dn_tile = align_up(std::max(tile(p.dn_r), tile(p.dn_s)), 16);
-  const size_t gu_out = (size_t)std::max(p.gu_r.NG * p.gu_r.R, p.gu_s.NG * p.gu_s.R) * 4;
-  p.gu_lds = p.list_bytes + p.gu_tile + gu_out;
+  auto tile = [](const GemvMap& m, int K) { return (size_t)m.NG * K * m.esize; };
+  p.gu_tile = align_up(std::max(tile(p.gu_r, L.H), tile(p.gu_s, L.H)), 16);
+  p.dn_tile = align_up(std::max(tile(p.dn_r, L.I), tile(p.dn_s, Ish)), 16);
+  p.gu_lds = p.list_bytes + p.gu_tile;
   p.dn_lds = p.list_bytes + p.dn_tile;
   return true;
 }
@@ -206,7 +221,7 @@ std::string check_layer(const moe_layer_t* L, int max_tokens) {
   if (L->has_shared == 1 && sf_ok) { check_w(L->sh13, L->shared_wfmt, "sh13"); check_w(L->sh2, L->shared_wfmt, "sh2"); }
   if (why.empty()) {
     Plan p;
-    if (!make_plan(*L, std::max(1, max_tokens), p))
+    if (!make_plan(*L, std::max(1, max_tokens), 512, p))
       add("no workgroup row mapping fits these sizes (H, I, I_shared) and formats");
   }
   return why;
@@ -248,6 +263,24 @@ moe_status_t check_ws(const moe_layer_t& L, int T, void* ws, size_t ws_bytes, Ws
 }
 
 size_t xq_part(size_t bytes) { return align_up(bytes); }
+
+// Compute units of the current device (cached per device id).
+int device_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cached[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+// The expert kernels are persistent: at most kWgPerCu resident workgroups per CU walk
+// the item list (their launch bounds allow 2 per CU).
+constexpr int kWgPerCu = 2;
 
 }  // namespace
 
@@ -353,8 +386,9 @@ moe_status_t moe_expert_forward(const moe_layer_t* L, const uint16_t* x_bf16, co
   if (!bad.empty()) return set_err(MOE_EINVAL, bad);
   WsLayout w;
   if ((st = check_ws(*L, T, ws, ws_bytes, w)) != MOE_OK) return st;
+  const int resident = kWgPerCu * device_cus();
   Plan p;
-  if (!make_plan(*L, T, p)) return set_err(MOE_EUNSUPPORTED, "no launch plan");
+  if (!make_plan(*L, T, resident, p)) return set_err(MOE_EUNSUPPORTED, "no launch plan");
   uint8_t* base = static_cast<uint8_t*>(ws);
   const int Ish = L->has_shared ? L->I_shared : L->I;
   const int sfmt = L->has_shared ? L->shared_wfmt : L->wfmt;
@@ -403,7 +437,8 @@ moe_status_t moe_expert_forward(const moe_layer_t* L, const uint16_t* x_bf16, co
   dn.smap = p.dn_s;
   dn.counters = reinterpret_cast<uint32_t*>(base + w.c_dn);
   dn.lds_act_bytes = (int)p.dn_tile;
-  if (launch_experts(gu, p.gu_grid, p.gu_lds, dn, p.dn_grid, p.dn_lds, stream) != hipSuccess)
+  const int gu_grid = std::min(p.gu_grid, resident), dn_grid = std::min(p.dn_grid, resident);
+  if (launch_experts(gu, gu_grid, p.gu_lds, dn, dn_grid, p.dn_lds, stream) != hipSuccess)
     return set_err(MOE_ELAUNCH, "expert kernel launch failed");
   return MOE_OK;
 }

@@ -73,6 +73,37 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(a), as_bf16x2(b), c, false);
 }
 
+// ---------------------------------------------------------------- hand-offs
+// Data one workgroup hands to another inside the same launch is written and read with
+// agent-scope relaxed atomics: on gfx950 these are global_store/global_load with the
+// sc1 bit, coherent across the XCDs' separate L2 caches, so no L2 writeback
+// (buffer_wbl2, what a device-scope release fence costs) is ever needed. The writer
+// waits for its stores to complete (s_waitcnt vmcnt(0)) and for the whole workgroup
+// (barrier) before it increments the hand-off counter.
+__device__ __forceinline__ void store_coherent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_coherent(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Called by every thread of a workgroup after its coherent stores: returns (to every
+// thread) whether this workgroup is the `total`-th and last to arrive at *ctr, in which
+// case it also resets the counter for the next launch. `flag` is one int of LDS.
+__device__ __forceinline__ bool arrive_last(uint32_t* ctr, uint32_t total, int* flag) {
+  wait_stores();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t old = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const bool last = old == total - 1u;
+    if (last) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *flag = last ? 1 : 0;
+  }
+  __syncthreads();
+  return *flag != 0;
+}
+
 // ---------------------------------------------------------------- reductions
 template <int WIDTH>
 __device__ __forceinline__ float group_sum(float v) {

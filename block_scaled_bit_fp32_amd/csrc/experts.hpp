@@ -1,19 +1,24 @@
 // Dequant-fused expert GEMVs for gfx950: gate/up with SwiGLU, down with the combine.
 //
-//   gateup_kernel  one workgroup per (selected expert, chunk of intermediate rows) plus
-//                  (shared expert, chunk); gate and up rows of the same chunk, SwiGLU in
-//                  the epilogue; the last workgroup of each routed expert re-quantizes
-//                  that expert's h rows when the layer quantizes h.
-//   down_kernel    one workgroup per (selected expert, chunk of hidden rows); the last
-//                  workgroup of each hidden chunk combines every expert's partial output
-//                  in a fixed order and writes BF16 y.
-// Each workgroup streams its weight rows once with 16-byte loads, decodes them in
-// registers (gfx950 FP4/FP8 converts) and takes activations from an LDS tile.
-// "Last workgroup" hand-offs use a device-scope counter after a release fence; nothing
-// ever waits on another workgroup.
+//   gateup_kernel  items = (shared expert, chunk of intermediate rows), then (selected
+//                  expert, chunk); each lane holds a gate row and the matching up row,
+//                  so SwiGLU is applied in registers; the last workgroup to finish a
+//                  routed expert re-quantizes that expert's h rows when the layer
+//                  quantizes h.
+//   down_kernel    items = (shared or selected expert, chunk of hidden rows); the last
+//                  workgroup to finish a hidden chunk combines every expert's partial
+//                  output for it in a fixed order and writes BF16 y.
+// Both kernels are persistent: a few resident workgroups per CU walk the item list
+// (item = blockIdx.x, + gridDim.x, ...). An item stages the activations of its tokens
+// (full K) in LDS once, then streams its weight rows in row-steps; the 16-byte weight
+// pieces of the next step (possibly of the next item) are loaded while the current
+// step computes. Weights are decoded in registers with the gfx950 FP4/FP8 converts.
+// Hand-offs between workgroups use coherent stores/loads and a counter (device.hpp);
+// nothing ever waits on another workgroup.
 #pragma once
 #include <algorithm>
 
+#include "launch.hpp"
 #include "rows.hpp"
 
 namespace moe {
@@ -21,14 +26,16 @@ namespace moe {
 // =================================================================== expert list
 // Builds, in LDS, the set of selected experts in increasing id order and a token mask
 // per expert. Entries outside [0, E) are ignored. Returns the number of experts.
-__device__ __forceinline__ int build_list(const ExpertArgs& a, uint64_t* tmask, int* act, int* ids_l, int* scan) {
+__device__ __forceinline__ int build_list(const ExpertArgs& a, uint64_t* tmask, int* act,
+                                          int* ids_l, int* scan) {
   const int P = a.T * a.k;
   for (int i = threadIdx.x; i < a.E; i += kBlock) tmask[i] = 0ull;
   for (int i = threadIdx.x; i < P; i += kBlock) ids_l[i] = a.ids[i];
   __syncthreads();
   for (int i = threadIdx.x; i < P; i += kBlock) {
     const int e = ids_l[i];
-    if ((unsigned)e < (unsigned)a.E) atomicOr(reinterpret_cast<unsigned long long*>(&tmask[e]), 1ull << (i / a.k));
+    if ((unsigned)e < (unsigned)a.E)
+      atomicOr(reinterpret_cast<unsigned long long*>(&tmask[e]), 1ull << (i / a.k));
   }
   __syncthreads();
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
@@ -54,9 +61,9 @@ __device__ __forceinline__ int build_list(const ExpertArgs& a, uint64_t* tmask, 
   return nact;
 }
 
-// Tokens of expert e (increasing) and their pair index t*k + j.
-__device__ __forceinline__ int expert_tokens(const ExpertArgs& a, int e, const uint64_t* tmask, const int* ids_l,
-                             int* tok, int* pair) {
+// Tokens of expert e (increasing) and their pair index t*k + j, into LDS.
+__device__ __forceinline__ int expert_tokens(const ExpertArgs& a, int e, const uint64_t* tmask,
+                                             const int* ids_l, int* tok, int* pair) {
   const uint64_t m = tmask[e];
   const int t = threadIdx.x;
   if (t < a.T && ((m >> t) & 1ull)) {
@@ -66,50 +73,74 @@ __device__ __forceinline__ int expert_tokens(const ExpertArgs& a, int e, const u
     tok[pos] = t;
     pair[pos] = t * a.k + j;
   }
-  __syncthreads();
   return __popcll(m);
 }
 
+struct ExpertLds {
+  uint64_t* tmask;
+  int* act;
+  int* ids;
+  int* scan;   // [4] + a flag at [4]
+  int* tok;    // [64]
+  int* pair;   // [64]
+  float* tsc;  // [64]
+  float* red;  // [4]
+  uint8_t* tile;
+};
+
+__device__ __forceinline__ ExpertLds carve(const ExpertArgs& a, uint8_t* smem) {
+  ExpertLds L;
+  L.tmask = reinterpret_cast<uint64_t*>(smem);
+  L.act = reinterpret_cast<int*>(L.tmask + a.E);
+  L.ids = L.act + a.E;
+  L.scan = L.ids + a.T * a.k;
+  L.tok = L.scan + 8;
+  L.pair = L.tok + 64;
+  L.tsc = reinterpret_cast<float*>(L.pair + 64);
+  L.red = L.tsc + 64;
+  L.tile = smem + a.lds_list_bytes;
+  return L;
+}
+
 // ===================================================================== GEMV core
-// Byte address of element `el` of a weight row.
 template <int FMT>
 __device__ __forceinline__ int64_t elem_byte(int el) {
   return FMT == W_BF16 ? 2 * (int64_t)el : (FMT == W_MXFP8 ? (int64_t)el : (int64_t)(el >> 1));
 }
 
-// LDS byte offset of the 16-byte sub-piece `sub` of piece `pc` (chunk-relative) for
-// lane-in-row jl: consecutive lanes read consecutive 16-byte slots.
+// LDS byte offset of 16-byte sub-piece `sub` of piece `pc` (pc = s * LPR + jl): the
+// sub-pieces of all lanes of a row are consecutive, so a wave's reads are conflict-free
+// and the G rows of a wave read the same addresses (broadcast).
 __device__ __forceinline__ int act_slot(int pc, int sub, int nsub, int LPR) {
   const int jl = pc % LPR, pass = pc / LPR;
   return ((pass * nsub + sub) * LPR + jl) * 16;
 }
 
-// Stage the activation chunk [kc0, kc0 + KC) of nt tokens into LDS.
+// Stage all K elements of nt tokens into the LDS tile.
 //   AK = 0: BF16 values (exact), 8 per slot;  AK = 1: FP32 values, 4 per slot.
-// src(t, el) returns the 16-byte slot content for token t and absolute element el.
+// src(t, el) returns the 16-byte slot for token t at element el.
 template <int AK, int EPL, class Src>
-__device__ __forceinline__ void stage_chunk(uint8_t* tile, const GemvMap& m, int kc0, int nt, Src src) {
+__device__ __forceinline__ void stage_tile(uint8_t* tile, const GemvMap& m, int K, int nt, Src src) {
   constexpr int PER = AK == 0 ? 8 : 4;
   constexpr int NSUB = EPL / PER;
-  const int units = m.KC / PER;
+  const int units = K / PER;
+  const int tstride = K * m.esize;
   for (int u = threadIdx.x; u < nt * units; u += kBlock) {
     const int t = u / units, el = (u % units) * PER;
     const int pc = el / EPL, sub = (el % EPL) / PER;
-    *reinterpret_cast<uint4*>(tile + t * m.KC * m.esize + act_slot(pc, sub, NSUB, m.LPR)) =
-        src(t, kc0 + el);
+    *reinterpret_cast<uint4*>(tile + t * tstride + act_slot(pc, sub, NSUB, m.LPR)) = src(t, el);
   }
 }
 
 // acc[q][t] += row_q(piece) . act(t, piece) for one 16-byte weight piece per row.
 template <int FMT, int AK, int NT, int RPL>
 __device__ __forceinline__ void accumulate_piece(const uint4 (&wv)[RPL], const uint32_t (&sv)[RPL],
-                                                 const uint8_t* tile, const GemvMap& m, int s,
-                                                 int jl, float (&acc)[RPL][NT]) {
+                                                 const uint8_t* tile, int tstride, int LPR, int s,
+                                                 int jl, float (&acc)[RPL][4]) {
   constexpr int EPL = elems_per_piece(FMT);
   constexpr int NSUB = AK == 0 ? EPL / 8 : EPL / 4;
-  const int tstride = m.KC * m.esize;
-  const uint8_t* base = tile + ((s * NSUB) * m.LPR + jl) * 16;
-  const int sstride = m.LPR * 16;  // next sub-piece of the same piece
+  const uint8_t* base = tile + ((s * NSUB) * LPR + jl) * 16;
+  const int sstride = LPR * 16;  // next sub-piece of the same piece
 #pragma unroll
   for (int q = 0; q < RPL; ++q) {
     const uint32_t w[4] = {wv[q].x, wv[q].y, wv[q].z, wv[q].w};
@@ -249,91 +280,121 @@ __device__ __forceinline__ void accumulate_piece(const uint4 (&wv)[RPL], const u
   }
 }
 
-// One workgroup computes R rows x nt tokens of  out = W[rows] . act  for expert e.
-// row_of(r) maps a local row (0..R-1) to the weight row. Results (FP32, unscaled) go to
-// sink(t, r, value) from the lane that owns the row.
-template <int FMT, int AK, int NT, int RPL, class RowOf, class Stage, class Sink>
-__device__ __forceinline__ void gemv_tile(const WTensor& W, const GemvMap& m, int e, uint8_t* tile,
-                                          RowOf row_of, Stage stage, Sink sink) {
+// Raw weight pieces of one pipeline step for this lane: NPB pieces x RPL rows.
+template <int RPL>
+struct WeightRegs {
+  static constexpr int NPB = 4;
+  uint4 w[NPB][RPL];
+  uint32_t s[NPB][RPL];
+};
+
+// Loads batch b (pieces b*NPB .. b*NPB + NPB - 1) of the lane's rows.
+template <int FMT, int RPL>
+__device__ __forceinline__ void fetch_batch(const WTensor& W, const GemvMap& m, const int64_t (&rows)[RPL],
+                                            int b, int jl, WeightRegs<RPL>& R) {
   constexpr int EPL = elems_per_piece(FMT);
-  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-  const int grp = lane / m.LPR, jl = lane % m.LPR;
-  const uint8_t* rp[RPL];
-  const uint8_t* sp[RPL];
-  int rloc[RPL];
 #pragma unroll
   for (int q = 0; q < RPL; ++q) {
-    rloc[q] = (wave * m.G + grp) * RPL + q;
-    const int64_t row = (int64_t)e * W.rows + row_of(rloc[q]);
-    rp[q] = W.codes + row * W.code_row_bytes;
-    sp[q] = W.scales ? W.scales + row * W.scale_row_bytes : nullptr;
-  }
-  float acc[RPL][NT];
+    const uint8_t* rp = W.codes + rows[q] * W.code_row_bytes;
+    const uint8_t* sp = W.scales ? W.scales + rows[q] * W.scale_row_bytes : nullptr;
 #pragma unroll
-  for (int q = 0; q < RPL; ++q)
-#pragma unroll
-    for (int t = 0; t < NT; ++t) acc[q][t] = 0.0f;
-
-  for (int kc0 = 0; kc0 < W.K; kc0 += m.KC) {
-    constexpr int NPMAX = RPL >= 4 ? 2 : 4;   // at most 8 weight pieces in flight per lane
-    uint4 wv[NPMAX][RPL];
-    uint32_t sv[NPMAX][RPL];
-#pragma unroll
-    for (int s = 0; s < NPMAX; ++s) {
-      if (s < m.NP) {
-        const int el = kc0 + (s * m.LPR + jl) * EPL;
-#pragma unroll
-        for (int q = 0; q < RPL; ++q) {
-          wv[s][q] = load_stream16(rp[q] + elem_byte<FMT>(el));
-          if constexpr (FMT == W_NVFP4)
-            sv[s][q] = *reinterpret_cast<const uint16_t*>(sp[q] + (el >> 4));
-          else if constexpr (FMT == W_MXFP4 || FMT == W_MXFP8)
-            sv[s][q] = sp[q][el >> 5];
-          else
-            sv[s][q] = 0u;
-        }
+    for (int i = 0; i < WeightRegs<RPL>::NPB; ++i) {
+      if (i < m.NPB) {
+        const int el = ((b * m.NPB + i) * m.LPR + jl) * EPL;
+        R.w[i][q] = load_stream16(rp + elem_byte<FMT>(el));
+        if constexpr (FMT == W_NVFP4)
+          R.s[i][q] = *reinterpret_cast<const uint16_t*>(sp + (el >> 4));
+        else if constexpr (FMT == W_MXFP4 || FMT == W_MXFP8)
+          R.s[i][q] = sp[el >> 5];
+        else
+          R.s[i][q] = 0u;
       }
     }
-    stage(kc0);
-    __syncthreads();
-#pragma unroll
-    for (int s = 0; s < NPMAX; ++s)
-      if (s < m.NP) accumulate_piece<FMT, AK, NT, RPL>(wv[s], sv[s], tile, m, s, jl, acc);
-    __syncthreads();
   }
-#pragma unroll
-  for (int q = 0; q < RPL; ++q)
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      float v = acc[q][t];
-      for (int o = m.LPR / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-      if (jl == 0) sink(t, rloc[q], v);
-    }
 }
 
-// Runs gemv_tile over all token groups of an item, dispatching the compile-time token
-// count and rows-per-lane. group(tg, nt) sets up the group; done(tg, nt) is the epilogue.
-template <int FMT, int AK, int MAXRPL, class RowOf, class StageF, class Sink, class Done>
-__device__ __forceinline__ void gemv_item(const WTensor& W, const GemvMap& m, int e, uint8_t* tile,
-                                          int n, RowOf row_of, StageF stage_for, Sink sink_for,
-                                          Done done) {
-  for (int tg = 0; tg < n; tg += m.NG) {
-    const int nt = min(m.NG, n - tg);
-    auto stage = [&](int kc0) { stage_for(kc0, tg, nt); };
-    auto sink = [&](int t, int r, float v) { if (t < nt) sink_for(tg + t, r, v); };
-#define MOE_RUN(NT_, RPL_) gemv_tile<FMT, AK, NT_, RPL_>(W, m, e, tile, row_of, stage, sink)
-#define MOE_RUN_NT(RPL_)                    \
-    if (nt == 1) MOE_RUN(1, RPL_);          \
-    else if (nt == 2) MOE_RUN(2, RPL_);     \
-    else MOE_RUN(4, RPL_);
-    if (MAXRPL >= 4 && m.RPL == 4) { MOE_RUN_NT(4) }
-    else if (MAXRPL >= 2 && m.RPL == 2) { MOE_RUN_NT(2) }
-    else { MOE_RUN_NT(1) }
-#undef MOE_RUN_NT
-#undef MOE_RUN
-    __syncthreads();
-    done(tg, nt);
-    __syncthreads();
+// Walks items first, first + gridDim.x, ... < n_items of one weight class. Call-backs
+// (workgroup-uniform):
+//   rows(item, step, lrow, out[RPL])  global weight rows (expert * rows + row) of this
+//                                     lane's RPL rows at row-step `step`
+//   setup(item) -> token count        fills the LDS token tables (synchronizes)
+//   stage(item, tg, nt)               fills the LDS activation tile (no sync needed)
+//   sink(item, tg, step, lrow, nt, acc)  results of the lanes with jl == 0
+//   finish(item)                      item epilogue (hand-offs)
+template <int FMT, int AK, int RPL, class Rows, class Setup, class Stage, class Sink, class Finish>
+__device__ __forceinline__ void gemv_loop(const WTensor& W, const GemvMap& m, uint8_t* tile,
+                                          int first, int n_items, Rows rows, Setup setup,
+                                          Stage stage, Sink sink, Finish finish) {
+  if (first >= n_items) return;
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int grp = lane / m.LPR, jl = lane % m.LPR;
+  const int lrow = wave * m.G + grp;   // row slot of this lane within a row-step
+  const int tstride = W.K * m.esize;
+  WeightRegs<RPL> cur;
+  int64_t rr[RPL];
+  int item = first;
+  rows(item, 0, lrow, rr);
+  fetch_batch<FMT, RPL>(W, m, rr, 0, jl, cur);
+  while (true) {
+    const int n = setup(item);
+    for (int tg = 0; tg < n; tg += m.NG) {
+      const int nt = min(m.NG, n - tg);
+      stage(item, tg, nt);
+      __syncthreads();
+      for (int step = 0; step < m.NSTEP; ++step) {
+        float acc[RPL][4];
+#pragma unroll
+        for (int q = 0; q < RPL; ++q)
+#pragma unroll
+          for (int t = 0; t < 4; ++t) acc[q][t] = 0.0f;
+        for (int b = 0; b < m.NB; ++b) {
+          // the next pipeline step: next batch, next row-step, next token group or next item
+          int nitem = item, nstep = step, nb = b + 1;
+          bool more = true;
+          if (nb == m.NB) {
+            nb = 0;
+            if (++nstep == m.NSTEP) {
+              nstep = 0;
+              if (tg + m.NG >= n) {
+                nitem = item + (int)gridDim.x;
+                more = nitem < n_items;
+              }
+            }
+          }
+          WeightRegs<RPL> nxt;
+          if (more) {
+            int64_t nr[RPL];
+            rows(nitem, nstep, lrow, nr);
+            fetch_batch<FMT, RPL>(W, m, nr, nb, jl, nxt);
+          }
+#pragma unroll
+          for (int i = 0; i < WeightRegs<RPL>::NPB; ++i) {
+            if (i < m.NPB) {
+              const int s = b * m.NPB + i;
+              if (nt == 1) accumulate_piece<FMT, AK, 1, RPL>(cur.w[i], cur.s[i], tile, tstride, m.LPR, s, jl, acc);
+              else if (AK == 1 || nt == 2) accumulate_piece<FMT, AK, 2, RPL>(cur.w[i], cur.s[i], tile, tstride, m.LPR, s, jl, acc);
+              else accumulate_piece<FMT, AK, 4, RPL>(cur.w[i], cur.s[i], tile, tstride, m.LPR, s, jl, acc);
+            }
+          }
+          if (more) cur = nxt;
+        }
+#pragma unroll
+        for (int q = 0; q < RPL; ++q)
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            if (t < nt) {
+              float v = acc[q][t];
+              for (int o = m.LPR / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+              acc[q][t] = v;
+            }
+          }
+        if (jl == 0) sink(item, tg, step, lrow, nt, acc);
+      }
+      __syncthreads();   // the tile is restaged by the next group or item
+    }
+    finish(item);
+    item += gridDim.x;
+    if (item >= n_items) break;
   }
 }
 
@@ -364,82 +425,38 @@ __device__ __forceinline__ uint4 f32_slot(const float* row, int el) {
   return *reinterpret_cast<const uint4*>(row + el);
 }
 
-struct ExpertLds {
-  uint64_t* tmask;
-  int* act;
-  int* ids;
-  int* scan;   // [4] + flag at [4]
-  int* tok;    // [64]
-  int* pair;   // [64]
-  float* tsc;  // [64]
-  float* red;  // [4]
-  uint8_t* tile;
-  float* out;
-};
+// Items are numbered shared chunks first, then (routed expert, chunk); workgroup b takes
+// items b, b + gridDim.x, ... of that numbering.
+__device__ __forceinline__ int first_of_class(int class_base) {
+  const int G = gridDim.x;
+  return (((int)blockIdx.x - class_base) % G + G) % G;
+}
 
-__device__ __forceinline__ ExpertLds carve(const ExpertArgs& a, uint8_t* smem) {
-  ExpertLds L;
-  L.tmask = reinterpret_cast<uint64_t*>(smem);
-  L.act = reinterpret_cast<int*>(L.tmask + a.E);
-  L.ids = L.act + a.E;
-  L.scan = L.ids + a.T * a.k;
-  L.tok = L.scan + 8;
-  L.pair = L.tok + 64;
-  L.tsc = reinterpret_cast<float*>(L.pair + 64);
-  L.red = L.tsc + 64;
-  L.tile = smem + a.lds_list_bytes;
-  L.out = reinterpret_cast<float*>(L.tile + a.lds_act_bytes);
-  return L;
+// Token tables for the item's expert: routed experts from the list, the shared expert
+// takes every token (pairs T*k + t).
+__device__ __forceinline__ int setup_tokens(const ExpertArgs& a, const ExpertLds& L, bool routed,
+                                            int e) {
+  int n;
+  if (routed) {
+    n = expert_tokens(a, e, L.tmask, L.ids, L.tok, L.pair);
+  } else {
+    n = a.T;
+    for (int t = threadIdx.x; t < n; t += kBlock) {
+      L.tok[t] = t;
+      L.pair[t] = a.T * a.k + t;
+    }
+  }
+  __syncthreads();
+  return n;
 }
 
 // ================================================================ gate/up kernel
-template <int FMT>
-__device__ __forceinline__ void gateup_item(const ExpertArgs& a, const ExpertLds& L, const WTensor& W,
-                            const GemvMap& m, int e, int c, int n, int Iexp, bool routed) {
-  const int RU = m.R / 2;
-  const int i0 = c * RU;
-  const float gsg = W.gscale ? W.gscale[(int64_t)e * W.gs_per_expert + 0] : 1.0f;
-  const float gsu = W.gscale ? W.gscale[(int64_t)e * W.gs_per_expert + 1] : 1.0f;
-  auto row_of = [&](int r) { return r < RU ? i0 + r : Iexp + i0 + r - RU; };
-  const int afmt = routed ? a.afmt : A_BF16;
-  auto stage_for = [&](int kc0, int tg, int nt) {
-    const int* tok = L.tok + tg;
-    if (afmt == A_NVFP4_4O6) {
-      stage_chunk<0, elems_per_piece(FMT)>(L.tile, m, kc0, nt, [&](int t, int el) {
-        const int tk = tok[t];
-        return nvfp4_slot(a.xq_codes + (int64_t)tk * (a.H / 2), a.xq_scales + (int64_t)tk * (a.H / 16), el);
-      });
-    } else if (afmt == A_FP8_TOKEN) {
-      stage_chunk<0, elems_per_piece(FMT)>(L.tile, m, kc0, nt, [&](int t, int el) {
-        return fp8_slot(a.xq_codes + (int64_t)tok[t] * a.H, el);
-      });
-    } else {
-      stage_chunk<0, elems_per_piece(FMT)>(L.tile, m, kc0, nt, [&](int t, int el) {
-        return bf16_slot(a.x + (int64_t)tok[t] * a.H, el);
-      });
-    }
-  };
-  auto sink_for = [&](int t, int r, float v) { L.out[(t % m.NG) * m.R + r] = v; };
-  auto done = [&](int tg, int nt) {
-    for (int idx = threadIdx.x; idx < nt * RU; idx += kBlock) {
-      const int tl = idx / RU, i = idx % RU, t = tg + tl;
-      const float ts = L.tsc[t];
-      const float gv = L.out[tl * m.R + i] * gsg * ts;
-      const float uv = L.out[tl * m.R + RU + i] * gsu * ts;
-      const float hv = gv / (1.0f + expf(-gv)) * uv;
-      const int64_t off = (int64_t)L.pair[t] * a.hs + i0 + i;
-      a.h[off] = hv;
-      if (a.dbg_h) a.dbg_h[off] = hv;
-    }
-  };
-  gemv_item<FMT, 0, 4>(W, m, e, L.tile, n, row_of, stage_for, sink_for, done);
-}
-
 // Re-quantize the h rows of one routed expert (all its pairs) per the layer's afmt.
+// The rows were written by other workgroups of this launch (coherent loads).
 __device__ __forceinline__ void quantize_expert_h(const ExpertArgs& a, const ExpertLds& L, int n) {
   for (int ti = 0; ti < n; ++ti) {
     const int p = L.pair[ti];
-    const F32Row row{a.h + (int64_t)p * a.hs};
+    const F32RowCoherent row{a.h + (int64_t)p * a.hs};
     if (a.afmt == A_NVFP4_4O6) {
       uint8_t* codes = a.hq_codes + (int64_t)p * (a.I / 2);
       uint8_t* scales = a.hq_scales + (int64_t)p * (a.I / 16);
@@ -455,139 +472,198 @@ __device__ __forceinline__ void quantize_expert_h(const ExpertArgs& a, const Exp
   }
 }
 
+// Gate/up rows: lane row slot lrow at step `step` of chunk c is intermediate index
+// i = c * RU + step * PS + lrow (PS = 4 * G pairs per step, RU = PS * NSTEP); the lane
+// holds gate row i (q = 0) and up row I + i (q = 1).
+template <int FMT>
+__device__ __forceinline__ void gateup_class(const ExpertArgs& a, const ExpertLds& L, bool routed,
+                                             int first, int n_items) {
+  const WTensor& W = routed ? a.rw : a.sw;
+  const GemvMap& m = routed ? a.rmap : a.smap;
+  const int nch = m.nchunks, PS = 4 * m.G, RU = PS * m.NSTEP;
+  const int Iexp = routed ? a.I : a.Ish;
+  const int afmt = routed ? a.afmt : A_BF16;
+  const bool coherent_h = routed && a.afmt != A_BF16;   // h is handed to the quantizer
+  auto expert_of = [&](int item) { return routed ? L.act[item / nch] : 0; };
+  auto rows = [&](int item, int step, int lrow, int64_t (&out)[2]) {
+    const int64_t base = (int64_t)expert_of(item) * W.rows;
+    const int i = (item % nch) * RU + step * PS + lrow;
+    out[0] = base + i;
+    out[1] = base + Iexp + i;
+  };
+  auto setup = [&](int item) {
+    const int n = setup_tokens(a, L, routed, expert_of(item));
+    for (int t = threadIdx.x; t < n; t += kBlock)
+      L.tsc[t] = afmt == A_BF16 ? 1.0f : a.xq_scale[L.tok[t]];
+    __syncthreads();
+    return n;
+  };
+  auto stage = [&](int, int tg, int nt) {
+    const int* tok = L.tok + tg;
+    if (afmt == A_NVFP4_4O6) {
+      stage_tile<0, elems_per_piece(FMT)>(L.tile, m, a.H, nt, [&](int t, int el) {
+        const int tk = tok[t];
+        return nvfp4_slot(a.xq_codes + (int64_t)tk * (a.H / 2), a.xq_scales + (int64_t)tk * (a.H / 16), el);
+      });
+    } else if (afmt == A_FP8_TOKEN) {
+      stage_tile<0, elems_per_piece(FMT)>(L.tile, m, a.H, nt, [&](int t, int el) {
+        return fp8_slot(a.xq_codes + (int64_t)tok[t] * a.H, el);
+      });
+    } else {
+      stage_tile<0, elems_per_piece(FMT)>(L.tile, m, a.H, nt, [&](int t, int el) {
+        return bf16_slot(a.x + (int64_t)tok[t] * a.H, el);
+      });
+    }
+  };
+  auto sink = [&](int item, int tg, int step, int lrow, int nt, const float (&acc)[2][4]) {
+    const int e = expert_of(item);
+    const int i = (item % nch) * RU + step * PS + lrow;
+    const float gsg = W.gscale ? W.gscale[(int64_t)e * W.gs_per_expert + 0] : 1.0f;
+    const float gsu = W.gscale ? W.gscale[(int64_t)e * W.gs_per_expert + 1] : 1.0f;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      if (t < nt) {
+        const float ts = L.tsc[tg + t];
+        const float gv = acc[0][t] * gsg * ts;
+        const float uv = acc[1][t] * gsu * ts;
+        const float hv = gv / (1.0f + expf(-gv)) * uv;
+        const int64_t off = (int64_t)L.pair[tg + t] * a.hs + i;
+        if (coherent_h) store_coherent(a.h + off, hv);
+        else a.h[off] = hv;
+        if (a.dbg_h) a.dbg_h[off] = hv;
+      }
+    }
+  };
+  auto finish = [&](int item) {
+    if (!coherent_h) return;
+    const int e = expert_of(item);
+    if (arrive_last(&a.counters[e], (uint32_t)nch, &L.scan[4])) {
+      const int n = setup_tokens(a, L, true, e);
+      quantize_expert_h(a, L, n);
+    }
+  };
+  gemv_loop<FMT, 0, 2>(W, m, L.tile, first, n_items, rows, setup, stage, sink, finish);
+}
+
 template <int RF, int SF>
 __global__ void __launch_bounds__(kBlock, 2) gateup_kernel(ExpertArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
   const ExpertLds L = carve(a, smem);
-  const int routed_items = a.max_slots * a.rmap.nchunks;
-  if ((int)blockIdx.x >= routed_items) {  // shared expert: independent of routing
-    const int c = blockIdx.x - routed_items;
-    for (int t = threadIdx.x; t < a.T; t += kBlock) {
-      L.tok[t] = t;
-      L.pair[t] = a.T * a.k + t;
-      L.tsc[t] = 1.0f;
-    }
-    __syncthreads();
-    gateup_item<SF>(a, L, a.sw, a.smap, 0, c, a.T, a.Ish, false);
-    return;
-  }
-  const int u = blockIdx.x / a.rmap.nchunks, c = blockIdx.x % a.rmap.nchunks;
   const int nact = build_list(a, L.tmask, L.act, L.ids, L.scan);
-  if (u >= nact) return;
-  const int e = L.act[u];
-  const int n = expert_tokens(a, e, L.tmask, L.ids, L.tok, L.pair);
-  for (int t = threadIdx.x; t < n; t += kBlock)
-    L.tsc[t] = a.afmt == A_BF16 ? 1.0f : a.xq_scale[L.tok[t]];
-  __syncthreads();
-  gateup_item<RF>(a, L, a.rw, a.rmap, e, c, n, a.I, true);
-  if (a.afmt == A_BF16) return;
-  // the last workgroup of this expert re-quantizes its h rows
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0)
-    L.scan[4] = atomicAdd(&a.counters[e], 1u) == (uint32_t)(a.rmap.nchunks - 1);
-  __syncthreads();
-  if (!L.scan[4]) return;
-  __threadfence();
-  quantize_expert_h(a, L, n);
-  if (threadIdx.x == 0) a.counters[e] = 0u;
+  const int ns = a.has_shared ? a.smap.nchunks : 0;
+  if (a.has_shared) gateup_class<SF>(a, L, false, blockIdx.x, ns);
+  gateup_class<RF>(a, L, true, first_of_class(ns), nact * a.rmap.nchunks);
 }
 
 // =================================================================== down kernel
-template <int FMT, int AK>
-__device__ __forceinline__ void down_item(const ExpertArgs& a, const ExpertLds& L, const WTensor& W,
-                          const GemvMap& m, int e, int c, int n, int Kexp, bool routed) {
-  const int r0 = c * m.R;
-  const float gs = W.gscale ? W.gscale[(int64_t)e * W.gs_per_expert] : 1.0f;
-  auto row_of = [&](int r) { return r0 + r; };
+// Combine of one hidden chunk: y[t][row] = sum_j w[t][j] * o[t*k+j][row] + o_shared[t][row]
+// in that order, FP32, rounded to BF16. The o rows come from every workgroup of this
+// launch (coherent loads).
+__device__ __forceinline__ void combine_chunk(const ExpertArgs& a, int c, int CH) {
+  const int r0 = c * CH;
+  for (int idx = threadIdx.x; idx < a.T * CH; idx += kBlock) {
+    const int t = idx / CH, row = r0 + idx % CH;
+    float s = 0.0f;
+    for (int j = 0; j < a.k; ++j) {
+      const int p = t * a.k + j;
+      s = fmaf(a.topk_w[p], load_coherent(a.o + (int64_t)p * a.H + row), s);
+    }
+    if (a.has_shared) s += load_coherent(a.o + (int64_t)(a.T * a.k + t) * a.H + row);
+    a.y[(int64_t)t * a.H + row] = (uint16_t)f32_to_bf16_rne(s);
+  }
+}
+
+// Down rows: lane row slot lrow, row q, at step `step` of hidden chunk c is hidden row
+// c * CH + step * RS + lrow * RPL + q (CH = RS * NSTEP, equal for routed and shared).
+template <int FMT, int AK, int RPL>
+__device__ __forceinline__ void down_loop(const ExpertArgs& a, const ExpertLds& L, bool routed,
+                                          int nact, int first, int n_items) {
+  const WTensor& W = routed ? a.rw : a.sw;
+  const GemvMap& m = routed ? a.rmap : a.smap;
+  const int nch = m.nchunks, RS = m.RS, CH = RS * m.NSTEP;
+  const int Kexp = routed ? a.I : a.Ish;
   const int afmt = routed ? a.afmt : A_BF16;
-  auto stage_for = [&](int kc0, int tg, int nt) {
+  auto expert_of = [&](int item) { return routed ? L.act[item / nch] : 0; };
+  auto rows = [&](int item, int step, int lrow, int64_t (&out)[RPL]) {
+    const int64_t base = (int64_t)expert_of(item) * W.rows + (item % nch) * CH + step * RS + lrow * RPL;
+#pragma unroll
+    for (int q = 0; q < RPL; ++q) out[q] = base + q;
+  };
+  auto setup = [&](int item) {
+    const int n = setup_tokens(a, L, routed, expert_of(item));
+    for (int t = threadIdx.x; t < n; t += kBlock)
+      L.tsc[t] = afmt == A_BF16 ? 1.0f : a.hq_scale[L.pair[t]];
+    __syncthreads();
+    return n;
+  };
+  auto stage = [&](int, int tg, int nt) {
     const int* pair = L.pair + tg;
     if constexpr (AK == 1) {
-      stage_chunk<1, elems_per_piece(FMT)>(L.tile, m, kc0, nt, [&](int t, int el) {
+      stage_tile<1, elems_per_piece(FMT)>(L.tile, m, Kexp, nt, [&](int t, int el) {
         return f32_slot(a.h + (int64_t)pair[t] * a.hs, el);
       });
     } else {
       if (afmt == A_NVFP4_4O6) {
-        stage_chunk<0, elems_per_piece(FMT)>(L.tile, m, kc0, nt, [&](int t, int el) {
+        stage_tile<0, elems_per_piece(FMT)>(L.tile, m, Kexp, nt, [&](int t, int el) {
           const int p = pair[t];
           return nvfp4_slot(a.hq_codes + (int64_t)p * (Kexp / 2), a.hq_scales + (int64_t)p * (Kexp / 16), el);
         });
       } else {
-        stage_chunk<0, elems_per_piece(FMT)>(L.tile, m, kc0, nt, [&](int t, int el) {
+        stage_tile<0, elems_per_piece(FMT)>(L.tile, m, Kexp, nt, [&](int t, int el) {
           return fp8_slot(a.hq_codes + (int64_t)pair[t] * Kexp, el);
         });
       }
     }
   };
-  auto sink_for = [&](int t, int r, float v) {
-    a.o[(int64_t)L.pair[t] * a.H + r0 + r] = v * gs * L.tsc[t];
+  auto sink = [&](int item, int tg, int step, int lrow, int nt, const float (&acc)[RPL][4]) {
+    const int e = expert_of(item);
+    const float gs = W.gscale ? W.gscale[(int64_t)e * W.gs_per_expert] : 1.0f;
+    const int row0 = (item % nch) * CH + step * RS + lrow * RPL;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      if (t < nt) {
+        const float sc = gs * L.tsc[tg + t];
+        float* o = a.o + (int64_t)L.pair[tg + t] * a.H + row0;
+#pragma unroll
+        for (int q = 0; q < RPL; ++q) store_coherent(o + q, acc[q][t] * sc);
+      }
+    }
   };
-  auto done = [](int, int) {};
-  gemv_item<FMT, AK, 2>(W, m, e, L.tile, n, row_of, stage_for, sink_for, done);
+  auto finish = [&](int item) {
+    const int c = item % nch;
+    if (arrive_last(&a.counters[c], (uint32_t)(nact + a.has_shared), &L.scan[4])) combine_chunk(a, c, CH);
+  };
+  gemv_loop<FMT, AK, RPL>(W, m, L.tile, first, n_items, rows, setup, stage, sink, finish);
+}
+
+template <int FMT, int AK>
+__device__ __forceinline__ void down_class(const ExpertArgs& a, const ExpertLds& L, bool routed,
+                                           int nact, int first, int n_items) {
+  const int rpl = routed ? a.rmap.RPL : a.smap.RPL;
+  if (rpl == 2) down_loop<FMT, AK, 2>(a, L, routed, nact, first, n_items);
+  else down_loop<FMT, AK, 1>(a, L, routed, nact, first, n_items);
 }
 
 template <int RF, int SF, int RAK>
 __global__ void __launch_bounds__(kBlock, 2) down_kernel(ExpertArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
   const ExpertLds L = carve(a, smem);
-  const int nch = a.rmap.nchunks;  // equal for routed and shared (same R)
-  const int routed_items = a.max_slots * nch;
   const int nact = build_list(a, L.tmask, L.act, L.ids, L.scan);
-  int c;
-  if ((int)blockIdx.x >= routed_items) {
-    c = blockIdx.x - routed_items;
-    for (int t = threadIdx.x; t < a.T; t += kBlock) {
-      L.tok[t] = t;
-      L.pair[t] = a.T * a.k + t;
-      L.tsc[t] = 1.0f;
-    }
-    __syncthreads();
-    down_item<SF, 1>(a, L, a.sw, a.smap, 0, c, a.T, a.Ish, false);
-  } else {
-    const int u = blockIdx.x / nch;
-    c = blockIdx.x % nch;
-    if (u >= nact) return;
-    const int e = L.act[u];
-    const int n = expert_tokens(a, e, L.tmask, L.ids, L.tok, L.pair);
-    for (int t = threadIdx.x; t < n; t += kBlock)
-      L.tsc[t] = a.afmt == A_BF16 ? 1.0f : a.hq_scale[L.pair[t]];
-    __syncthreads();
-    down_item<RF, RAK>(a, L, a.rw, a.rmap, e, c, n, a.I, true);
-  }
-  // the last workgroup of this hidden chunk combines every expert's output
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0)
-    L.scan[4] = atomicAdd(&a.counters[c], 1u) == (uint32_t)(nact + a.has_shared - 1);
-  __syncthreads();
-  if (!L.scan[4]) return;
-  __threadfence();
-  const int R = a.rmap.R, r0 = c * R;
-  for (int idx = threadIdx.x; idx < a.T * R; idx += kBlock) {
-    const int t = idx / R, row = r0 + idx % R;
-    float s = 0.0f;
-    for (int j = 0; j < a.k; ++j) {
-      const int p = t * a.k + j;
-      s = fmaf(a.topk_w[p], __builtin_nontemporal_load(a.o + (int64_t)p * a.H + row), s);
-    }
-    if (a.has_shared) s += __builtin_nontemporal_load(a.o + (int64_t)(a.T * a.k + t) * a.H + row);
-    a.y[(int64_t)t * a.H + row] = (uint16_t)f32_to_bf16_rne(s);
-  }
-  if (threadIdx.x == 0) a.counters[c] = 0u;
+  const int nch = a.rmap.nchunks;  // equal for routed and shared (same chunk rows)
+  const int ns = a.has_shared ? nch : 0;
+  if (a.has_shared) down_class<SF, 1>(a, L, false, nact, blockIdx.x, ns);
+  down_class<RF, RAK>(a, L, true, nact, first_of_class(ns), nact * nch);
 }
 
+// ================================================================ host launchers
 template <int RF, int SF>
 hipError_t launch_experts_t(const ExpertArgs& gu, int gu_grid, size_t gu_lds,
-                                   const ExpertArgs& dn, int dn_grid, size_t dn_lds, hipStream_t s) {
-  hipLaunchKernelGGL((gateup_kernel<RF, SF>), dim3(gu_grid), dim3(kBlock), gu_lds, s, gu);
-  hipError_t err = hipGetLastError();
+                            const ExpertArgs& dn, int dn_grid, size_t dn_lds, hipStream_t s) {
+  hipError_t err = launch_kernel(K_GATEUP, gateup_kernel<RF, SF>, dim3(gu_grid), dim3(kBlock), gu_lds, s, gu);
   if (err != hipSuccess) return err;
   if (dn.afmt == A_BF16)
-    hipLaunchKernelGGL((down_kernel<RF, SF, 1>), dim3(dn_grid), dim3(kBlock), dn_lds, s, dn);
-  else
-    hipLaunchKernelGGL((down_kernel<RF, SF, 0>), dim3(dn_grid), dim3(kBlock), dn_lds, s, dn);
-  return hipGetLastError();
+    return launch_kernel(K_DOWN, down_kernel<RF, SF, 1>, dim3(dn_grid), dim3(kBlock), dn_lds, s, dn);
+  return launch_kernel(K_DOWN, down_kernel<RF, SF, 0>, dim3(dn_grid), dim3(kBlock), dn_lds, s, dn);
 }
 
 }  // namespace moe

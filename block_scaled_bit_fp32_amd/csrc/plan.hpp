@@ -12,14 +12,16 @@ inline constexpr int elems_per_piece(int fmt) {
   return fmt == W_BF16 ? 8 : (fmt == W_MXFP8 ? 16 : 32);
 }
 
-// How a workgroup (4 waves) covers R weight rows of length K:
-//   LPR lanes per row (power of two), G = 64 / LPR rows per wave in parallel,
-//   RPL rows per lane, R = 4 * G * RPL rows per workgroup. A lane reads 16-byte pieces
-//   at element offsets (s * LPR + lane_in_row) * EPL of each K-chunk of KC elements,
-//   NP = KC / (LPR * EPL) pieces per row per chunk (NP <= 4).
-//   NG tokens are staged in LDS at a time.
+// How a workgroup (4 waves) walks the rows of one weight class (routed or shared).
+//   LPR lanes share a row (power of two); G = 64 / LPR rows per wave at a time; each
+//   lane holds RPL rows (for gate/up: RPL = 2, the gate row and the up row of the same
+//   intermediate index, so SwiGLU happens in registers). A row-step covers
+//   RS = 4 * G * RPL rows. Lane jl of a row reads the 16-byte pieces at element
+//   offsets (s * LPR + jl) * EPL, s < NP = K / (LPR * EPL), in NB batches of NPB.
+//   An item is NSTEP row-steps of one expert; the activations of NG tokens (full K)
+//   sit in LDS for the whole item. nchunks = items per expert.
 struct GemvMap {
-  int LPR, G, RPL, R, KC, NP, NG, nchunks, esize;
+  int LPR, G, RPL, RS, NP, NPB, NB, NSTEP, NG, esize, nchunks;
 };
 
 struct WTensor {

@@ -7,6 +7,7 @@
 // workgroups quantize the tokens in the same launch when the layer quantizes x.
 #include <algorithm>
 
+#include "launch.hpp"
 #include "rows.hpp"
 
 namespace moe {
@@ -84,15 +85,10 @@ __global__ void __launch_bounds__(kBlock) route_kernel(RouteArgs a) {
 #pragma unroll
       for (int w = 1; w < kBlock / kWave; ++w) v += red[(w * ET + e) * TT + t];
       if (a.bias) v += a.bias[e0 + e];
-      a.logits[(int64_t)(t0 + t) * a.E + e0 + e] = v;
+      store_coherent(a.logits + (int64_t)(t0 + t) * a.E + e0 + e, v);
     }
   }
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) last = atomicAdd(&a.counters[tt], 1u) == (uint32_t)(a.n_et - 1);
-  __syncthreads();
-  if (!last) return;
-  __threadfence();
+  if (!arrive_last(&a.counters[tt], (uint32_t)a.n_et, &last)) return;
   // ---- top-k for the tile's tokens: one wave per token, k rounds of a wave argmax
   for (int ti = wave; ti < nt; ti += kBlock / kWave) {
     const int t = t0 + ti;
@@ -101,7 +97,7 @@ __global__ void __launch_bounds__(kBlock) route_kernel(RouteArgs a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int e = lane + kWave * i;
-      v[i] = e < a.E ? __builtin_nontemporal_load(lg + e) : -INFINITY;
+      v[i] = e < a.E ? load_coherent(lg + e) : -INFINITY;
     }
     uint32_t taken = 0;
     float myv = 0.0f;
@@ -140,7 +136,6 @@ __global__ void __launch_bounds__(kBlock) route_kernel(RouteArgs a) {
       a.w[(int64_t)t * a.k + lane] = s / tot;
     }
   }
-  if (threadIdx.x == 0) a.counters[tt] = 0u;
 }
 
 // ================================================================ host launchers
@@ -152,23 +147,20 @@ __global__ void fill_zero_kernel(uint4* p, int64_t n16) {
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s) {
   const int64_t n16 = (int64_t)(bytes / 16);
   const int grid = (int)std::min<int64_t>(1024, (n16 + kBlock - 1) / kBlock);
-  if (grid > 0) hipLaunchKernelGGL(fill_zero_kernel, dim3(grid), dim3(kBlock), 0, s, (uint4*)p, n16);
-  return hipGetLastError();
+  if (grid <= 0) return hipSuccess;
+  return launch_kernel(K_FILL, fill_zero_kernel, dim3(grid), dim3(kBlock), 0, s, (uint4*)p, n16);
 }
 
 hipError_t launch_quantize_nvfp4(const uint16_t* x, int rows, int cols, uint8_t* codes, uint8_t* scales,
                                  float* g, uint8_t* choice, hipStream_t s) {
-  hipLaunchKernelGGL(quantize_nvfp4_kernel, dim3(rows), dim3(kBlock), 0, s, x, cols, codes, scales, g, choice);
-  return hipGetLastError();
+  return launch_kernel(K_QUANT, quantize_nvfp4_kernel, dim3(rows), dim3(kBlock), 0, s, x, cols, codes,
+                       scales, g, choice);
 }
 
 hipError_t launch_route(const RouteArgs& a, int n_quant, hipStream_t s) {
   const int grid = a.n_tt * a.n_et + n_quant;
-  if (a.ET == 1)
-    hipLaunchKernelGGL((route_kernel<1, 8>), dim3(grid), dim3(kBlock), 0, s, a);
-  else
-    hipLaunchKernelGGL((route_kernel<4, 8>), dim3(grid), dim3(kBlock), 0, s, a);
-  return hipGetLastError();
+  if (a.ET == 1) return launch_kernel(K_ROUTE, route_kernel<1, 8>, dim3(grid), dim3(kBlock), 0, s, a);
+  return launch_kernel(K_ROUTE, route_kernel<4, 8>, dim3(grid), dim3(kBlock), 0, s, a);
 }
 
 }  // namespace moe

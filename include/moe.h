@@ -169,6 +169,22 @@ moe_status_t quantize_nvfp4_4o6(const uint16_t *x_bf16, int32_t rows, int32_t co
                                 uint8_t *codes, uint8_t *scales, float *gscale,
                                 uint8_t *choice, hipStream_t stream);
 
+/* Diagnostics: per-kernel device time.
+ * Between moe_profile_begin() and moe_profile_end(), every kernel the library launches
+ * is bracketed by a start/stop event pair taken by the dispatch itself
+ * (hipExtLaunchKernel), on the stream it runs on. moe_profile_end() waits for those
+ * events, fills up to max_entries records (one per kernel kind: route, gateup, down,
+ * quantize_nvfp4, fill) with the launch count and summed milliseconds, ends the session
+ * and returns the number of records written. Meant for measurement runs; do not use
+ * while capturing a stream into a graph. One process-wide session. */
+typedef struct {
+  const char *name;
+  int32_t launches;
+  double total_ms;
+} moe_kernel_time_t;
+moe_status_t moe_profile_begin(void);
+int32_t moe_profile_end(moe_kernel_time_t *out, int32_t max_entries);
+
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char *moe_last_error(void);
 
