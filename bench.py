@@ -128,8 +128,15 @@ def main() -> int:
     def bytes_of(kind: str, U: int, T: int) -> int:
         """Algorithmic HBM bytes one launch of a kernel moves."""
         xb = T * cfg.H * 2
+        P = T * cfg.k + (T if cfg.has_shared else 0)
         if kind == "route":
             return cfg.E * cfg.H * 4 + (cfg.E * 4 if cfg.router_bias else 0) + xb
+        if kind == "topk":
+            return T * cfg.E * 4 + T * cfg.k * 8
+        if kind == "combine":
+            return P * cfg.H * 4 + T * cfg.k * 4 + xb
+        if kind == "hquant":
+            return T * cfg.k * cfg.I * 4
         w13 = dl0.t["w13"]
         per13 = sum(v[0].numel() * v.element_size() for v in w13.values() if v is not None)
         sh13 = sum(v[0].numel() * v.element_size() for v in dl0.t["sh13"].values()
@@ -179,7 +186,7 @@ def main() -> int:
             one_pass()
         prof = moe.profile_end()
         kern = {}
-        for kind in ("route", "gateup", "down"):
+        for kind in ("route", "topk", "gateup", "hquant", "down", "combine"):
             n, tot = prof.get(kind, (0, 0.0))
             if n:
                 us = tot * 1e3 / n

@@ -18,7 +18,7 @@ OUT = os.path.join(HERE, "libmoe_mi355x.so")
 BUILD = os.path.join(ROOT, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["route.hip", "experts_bf16.hip", "experts_nvfp4.hip", "experts_mxfp4.hip",
+SOURCES = ["route.hip", "combine.hip", "experts_bf16.hip", "experts_nvfp4.hip", "experts_mxfp4.hip",
            "experts_mxfp8.hip", "abi.cpp", "profile.cpp"]
 COMMON = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
           "-I" + os.path.join(ROOT, "include")]
@@ -27,9 +27,8 @@ DEVICE_ONLY = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *COMMON]
-    if src.endswith(".hip"):
-        cmd += DEVICE_ONLY
+    # hipcc compiles .cpp sources as HIP too: every unit gets the device flags
+    cmd = [HIPCC, *COMMON, *DEVICE_ONLY]
     cmd += ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:

@@ -1,6 +1,6 @@
 // C ABI of libmoe_mi355x.so: argument checks, launch planning, workspace layout and
 // dispatch to the gfx950 kernels. Declarations and contracts: include/moe.h.
-#include "../../include/moe.h"
+#include "moe.h"
 
 #include <algorithm>
 #include <cstdio>
@@ -88,7 +88,7 @@ bool plan_class(int fmt, int K, int ntok, int esize, bool paired, GemvMap& m) {
   m.NP = NP;
   m.NPB = NPB;
   m.NB = NP / NPB;
-  m.RPL = paired ? 2 : (m.G >= 2 ? 1 : 2);
+  m.RPL = paired ? 2 : 1;
   m.RS = 4 * m.G * m.RPL;
   // tokens per LDS pass: 1, 2 or 4 (a group of 3 runs the 4-token code, which reads and
   // discards a 4th slot, so groups are powers of two); FP32 tiles 2 at most
@@ -97,61 +97,73 @@ bool plan_class(int fmt, int K, int ntok, int esize, bool paired, GemvMap& m) {
   if (NG * K * esize > kLdsActBudget) return false;
   m.NG = NG;
   m.esize = esize;
-  m.NSTEP = 1;
-  m.nchunks = 0;
   return true;
 }
 
 struct Plan {
   GemvMap gu_r, gu_s, dn_r, dn_s;
-  int gu_grid, dn_grid, max_slots;
+  int max_slots;
   size_t gu_lds, dn_lds, list_bytes, gu_tile, dn_tile;
 };
 
-// `resident`: workgroups the expert kernels keep resident (a larger item count than
-// twice that buys nothing, a smaller one leaves CUs idle).
-bool make_plan(const moe_layer_t& L, int T, int resident, Plan& p) {
+// Weight bytes per element, times 2 (FP4 1, MXFP8 2, BF16 4; block scales ignored).
+int wbytes_x2(int fmt) { return fmt == W_BF16 ? 4 : (fmt == W_MXFP8 ? 2 : 1); }
+
+// Cost weights of one row-step (see GemvMap) over rows of K elements: weight bytes
+// against activation work (a token costs half a step's weight bytes for FP4 weights and
+// BF16 activations).
+void set_costs(GemvMap& m, int fmt, int K) {
+  const int64_t elems = (int64_t)m.RS * K;
+  m.cw = (int)std::max<int64_t>(1, elems * wbytes_x2(fmt) / 256);
+  m.ct = (int)std::max<int64_t>(1, elems * m.esize / 1024);
+}
+
+// Row maps of both expert kernels and their LDS needs. Gate/up row-steps cover RS / 2
+// intermediate indices (gate and up rows), down row-steps RS hidden rows.
+bool make_plan(const moe_layer_t& L, int T, Plan& p) {
   const int Ish = L.has_shared ? L.I_shared : L.I;
   const int sfmt = L.has_shared ? L.shared_wfmt : L.wfmt;
   const int nt = std::max(1, T);
-  const int u_exp = std::min(L.E, nt * L.k) + (L.has_shared ? 1 : 0);
-  const int target = 2 * resident;
-  // gate/up: chunks of RU = 4 * G * NSTEP intermediate rows (gate + up)
   if (!plan_class(L.wfmt, L.H, nt, 2, true, p.gu_r) || !plan_class(sfmt, L.H, nt, 2, true, p.gu_s))
     return false;
-  for (GemvMap* m : {&p.gu_r, &p.gu_s}) {
-    const int Iexp = m == &p.gu_r ? L.I : Ish;
-    const int ps = m->RS / 2;
-    if (Iexp % ps) return false;
-    int ns = 1;
-    while ((Iexp / ps) % (2 * ns) == 0 && u_exp * (Iexp / ps) / (2 * ns) >= target) ns *= 2;
-    m->NSTEP = ns;
-    m->nchunks = Iexp / (ps * ns);
-  }
-  // down: routed and shared share the hidden-row chunking (the combine is per chunk)
+  if (L.I % (p.gu_r.RS / 2) || Ish % (p.gu_s.RS / 2)) return false;
   const int r_es = L.afmt == A_BF16 ? 4 : 2;
   if (!plan_class(L.wfmt, L.I, nt, r_es, false, p.dn_r) || !plan_class(sfmt, Ish, nt, 4, false, p.dn_s))
     return false;
-  int CH = std::max(p.dn_r.RS, p.dn_s.RS);
-  if (L.H % CH) return false;
-  while (L.H % (2 * CH) == 0 && u_exp * (L.H / (2 * CH)) >= target) CH *= 2;
-  p.dn_r.NSTEP = CH / p.dn_r.RS;
-  p.dn_s.NSTEP = CH / p.dn_s.RS;
-  p.dn_r.nchunks = p.dn_s.nchunks = L.H / CH;
+  if (L.H % p.dn_r.RS || L.H % p.dn_s.RS) return false;
+  set_costs(p.gu_r, L.wfmt, L.H);
+  set_costs(p.gu_s, sfmt, L.H);
+  set_costs(p.dn_r, L.wfmt, L.I);
+  set_costs(p.dn_s, sfmt, Ish);
+  // summed costs must fit an int: bound every unit by NG tokens
+  auto bound = [&](const GemvMap& m, int steps, int units) {
+    return (int64_t)units * steps * (m.cw + (int64_t)m.ct * m.NG);
+  };
+  const int ur = nt * L.k, us = L.has_shared ? nt : 0;
+  if (bound(p.gu_r, L.I / (p.gu_r.RS / 2), ur) + bound(p.gu_s, Ish / (p.gu_s.RS / 2), us) > (1ll << 30) ||
+      bound(p.dn_r, L.H / p.dn_r.RS, ur) + bound(p.dn_s, L.H / p.dn_s.RS, us) > (1ll << 30))
+    return false;
   p.max_slots = std::min(L.E, nt * L.k);
-  p.gu_grid = p.max_slots * p.gu_r.nchunks + (L.has_shared ? p.gu_s.nchunks : 0);
-  p.dn_grid = p.max_slots * p.dn_r.nchunks + (L.has_shared ? p.dn_s.nchunks : 0);
-  p.list_bytes = align_up((size_t)L.E * 12 + (size_t)nt * L.k * 4 + 8 * 4 + 64 * 12 + 16, 16);
-  auto tile = [](const GemvMap& m, int K) { return (size_t)m.NG * K * m.esize; };
-  p.gu_tile = align_up(std::max(tile(p.gu_r, L.H), tile(p.gu_s, L.H)), 16);
-  p.dn_tile = align_up(std::max(tile(p.dn_r, L.I), tile(p.dn_s, Ish)), 16);
+  p.list_bytes = (size_t)expert_lds_list_bytes(L.E, nt, L.k);
+  // activation tile: the rows of up to kWinRows tokens of a class, within 64 KB of LDS
+  // per workgroup, but never less than one unit's NG rows
+  auto tile = [&](const GemvMap& r, int Kr, const GemvMap& s, int Ks) {
+    const size_t sr = (size_t)Kr * r.esize, ss = (size_t)Ks * s.esize;
+    const size_t want = std::max(std::min<size_t>(ur, kWinRows) * sr,
+                                 L.has_shared ? std::min<size_t>(us, kWinRows) * ss : 0);
+    const size_t need = std::max(r.NG * sr, L.has_shared ? s.NG * ss : 0);
+    const size_t room = 64 * 1024 > p.list_bytes ? 64 * 1024 - p.list_bytes : 0;
+    return align_up(std::max(need, std::min(want, room)), 16);
+  };
+  p.gu_tile = tile(p.gu_r, L.H, p.gu_s, L.H);
+  p.dn_tile = tile(p.dn_r, L.I, p.dn_s, Ish);
   p.gu_lds = p.list_bytes + p.gu_tile;
   p.dn_lds = p.list_bytes + p.dn_tile;
   return true;
 }
 
 struct WsLayout {
-  size_t c_route, c_gu, c_dn, logits, h, hq_codes, hq_scales, hq_scale, o, total;
+  size_t logits, h, hq_codes, hq_scales, hq_scale, o, total;
   int hs;
 };
 
@@ -162,11 +174,6 @@ WsLayout ws_layout(const moe_layer_t& L, int maxT) {
   w.hs = std::max(L.I, Ish);
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t at = off; off = align_up(off + bytes); return at; };
-  // counters first, at offsets that do not depend on the token count: they must stay
-  // zero between calls, whatever T each call uses
-  w.c_route = take(4 * (size_t)((kMaxTokens + kRouteTT - 1) / kRouteTT));
-  w.c_gu = take(4 * (size_t)L.E);
-  w.c_dn = take(4 * (size_t)(L.H / 8 + 1));   // one per hidden chunk; chunks have >= 8 rows
   w.logits = take(4 * (size_t)maxT * L.E);
   w.h = take(4 * Pt * w.hs);
   const size_t qrow = L.afmt == A_NVFP4_4O6 ? L.I / 2 : (L.afmt == A_FP8_TOKEN ? L.I : 0);
@@ -221,7 +228,7 @@ std::string check_layer(const moe_layer_t* L, int max_tokens) {
   if (L->has_shared == 1 && sf_ok) { check_w(L->sh13, L->shared_wfmt, "sh13"); check_w(L->sh2, L->shared_wfmt, "sh2"); }
   if (why.empty()) {
     Plan p;
-    if (!make_plan(*L, std::max(1, max_tokens), 512, p))
+    if (!make_plan(*L, std::max(1, max_tokens), p))
       add("no workgroup row mapping fits these sizes (H, I, I_shared) and formats");
   }
   return why;
@@ -278,8 +285,8 @@ int device_cus() {
   return cached[dev];
 }
 
-// The expert kernels are persistent: at most kWgPerCu resident workgroups per CU walk
-// the item list (their launch bounds allow 2 per CU).
+// The expert kernels are persistent: kWgPerCu resident workgroups per CU (their launch
+// bounds allow 2 per CU) split the work units' row-steps between them.
 constexpr int kWgPerCu = 2;
 
 }  // namespace
@@ -347,7 +354,6 @@ moe_status_t moe_route(const moe_layer_t* L, const uint16_t* x_bf16, int32_t T, 
   a.n_tt = (T + kRouteTT - 1) / kRouteTT;
   a.n_et = (L->E + a.ET - 1) / a.ET;
   a.logits = reinterpret_cast<float*>(base + w.logits);
-  a.counters = reinterpret_cast<uint32_t*>(base + w.c_route);
   a.ids = topk_ids;
   a.w = topk_w;
   int n_quant = 0;
@@ -388,7 +394,7 @@ moe_status_t moe_expert_forward(const moe_layer_t* L, const uint16_t* x_bf16, co
   if ((st = check_ws(*L, T, ws, ws_bytes, w)) != MOE_OK) return st;
   const int resident = kWgPerCu * device_cus();
   Plan p;
-  if (!make_plan(*L, T, resident, p)) return set_err(MOE_EUNSUPPORTED, "no launch plan");
+  if (!make_plan(*L, T, p)) return set_err(MOE_EUNSUPPORTED, "no launch plan");
   uint8_t* base = static_cast<uint8_t*>(ws);
   const int Ish = L->has_shared ? L->I_shared : L->I;
   const int sfmt = L->has_shared ? L->shared_wfmt : L->wfmt;
@@ -429,15 +435,15 @@ moe_status_t moe_expert_forward(const moe_layer_t* L, const uint16_t* x_bf16, co
   gu.sw = wtensor(L->has_shared ? L->sh13 : L->w13, sfmt, 2 * Ish, L->H, 2);
   gu.rmap = p.gu_r;
   gu.smap = p.gu_s;
-  gu.counters = reinterpret_cast<uint32_t*>(base + w.c_gu);
   gu.lds_act_bytes = (int)p.gu_tile;
   dn.rw = wtensor(L->w2, L->wfmt, L->H, L->I, 1);
   dn.sw = wtensor(L->has_shared ? L->sh2 : L->w2, sfmt, L->H, Ish, 1);
   dn.rmap = p.dn_r;
   dn.smap = p.dn_s;
-  dn.counters = reinterpret_cast<uint32_t*>(base + w.c_dn);
   dn.lds_act_bytes = (int)p.dn_tile;
-  const int gu_grid = std::min(p.gu_grid, resident), dn_grid = std::min(p.dn_grid, resident);
+  // every workgroup takes an equal share of the row-steps (workgroups past the work
+  // exit at once); a step is at least one row per wave
+  const int gu_grid = resident, dn_grid = resident;
   if (launch_experts(gu, gu_grid, p.gu_lds, dn, dn_grid, p.dn_lds, stream) != hipSuccess)
     return set_err(MOE_ELAUNCH, "expert kernel launch failed");
   return MOE_OK;

@@ -73,38 +73,54 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(a), as_bf16x2(b), c, false);
 }
 
-// ---------------------------------------------------------------- hand-offs
-// Data one workgroup hands to another inside the same launch is written and read with
-// agent-scope relaxed atomics: on gfx950 these are global_store/global_load with the
-// sc1 bit, coherent across the XCDs' separate L2 caches, so no L2 writeback
-// (buffer_wbl2, what a device-scope release fence costs) is ever needed. The writer
-// waits for its stores to complete (s_waitcnt vmcnt(0)) and for the whole workgroup
-// (barrier) before it increments the hand-off counter.
-__device__ __forceinline__ void store_coherent(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float load_coherent(const float* p) {
-  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Marks a value that is the same on every lane (read from LDS, say) as wave-uniform,
+// so that branches on it are scalar branches instead of exec-masked code.
+__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
-// Called by every thread of a workgroup after its coherent stores: returns (to every
-// thread) whether this workgroup is the `total`-th and last to arrive at *ctr, in which
-// case it also resets the counter for the next launch. `flag` is one int of LDS.
-__device__ __forceinline__ bool arrive_last(uint32_t* ctr, uint32_t total, int* flag) {
-  wait_stores();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const uint32_t old = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const bool last = old == total - 1u;
-    if (last) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    *flag = last ? 1 : 0;
-  }
-  __syncthreads();
-  return *flag != 0;
+// ---------------------------------------------------------------- barriers
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS operations, then
+// for every wave. Unlike __syncthreads it does not wait for outstanding global loads,
+// so weight loads already in flight keep streaming across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 // ---------------------------------------------------------------- reductions
+// Wave-wide maximum of a 64-bit key, returned to every lane. Within each row of 16
+// lanes DPP moves (xor 1, xor 2, rotate 4, rotate 8) spread the row maximum to all its
+// lanes; the four row maxima are then read out (readlane) and combined in scalars.
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t k) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)k, CTRL, 0xF, 0xF, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(k >> 32), CTRL, 0xF, 0xF, false);
+  return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t k, int lane) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)k, lane);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(k >> 32), lane);
+  return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t k) {
+  uint64_t p;
+  p = dpp_u64<0xB1>(k); k = p > k ? p : k;    // quad_perm [1,0,3,2]
+  p = dpp_u64<0x4E>(k); k = p > k ? p : k;    // quad_perm [2,3,0,1]
+  p = dpp_u64<0x124>(k); k = p > k ? p : k;   // row_ror:4
+  p = dpp_u64<0x128>(k); k = p > k ? p : k;   // row_ror:8
+  uint64_t r = readlane_u64(k, 0);
+  p = readlane_u64(k, 16); r = p > r ? p : r;
+  p = readlane_u64(k, 32); r = p > r ? p : r;
+  p = readlane_u64(k, 48); r = p > r ? p : r;
+  return r;
+}
+
+// Order-preserving map of a finite float to uint32 (larger float -> larger key).
+__device__ __forceinline__ uint32_t float_order_key(float v) {
+  const uint32_t b = __float_as_uint(v);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+__device__ __forceinline__ float float_from_order_key(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
 template <int WIDTH>
 __device__ __forceinline__ float group_sum(float v) {
 #pragma unroll

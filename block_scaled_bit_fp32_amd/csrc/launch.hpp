@@ -9,7 +9,10 @@
 
 namespace moe {
 
-enum KernelKind : int { K_ROUTE = 0, K_GATEUP = 1, K_DOWN = 2, K_QUANT = 3, K_FILL = 4, K_KINDS = 5 };
+enum KernelKind : int {
+  K_ROUTE = 0, K_GATEUP = 1, K_DOWN = 2, K_QUANT = 3, K_FILL = 4, K_TOPK = 5, K_HQUANT = 6,
+  K_COMBINE = 7, K_KINDS = 8
+};
 
 bool profiling_enabled();
 // A start/stop event pair registered under `kind`; false if none could be created.

@@ -14,15 +14,26 @@ inline constexpr int elems_per_piece(int fmt) {
 
 // How a workgroup (4 waves) walks the rows of one weight class (routed or shared).
 //   LPR lanes share a row (power of two); G = 64 / LPR rows per wave at a time; each
-//   lane holds RPL rows (for gate/up: RPL = 2, the gate row and the up row of the same
-//   intermediate index, so SwiGLU happens in registers). A row-step covers
+//   lane holds RPL rows (gate/up: RPL = 2, the gate row and the up row of the same
+//   intermediate index, so SwiGLU happens in registers; down: RPL = 1). A row-step covers
 //   RS = 4 * G * RPL rows. Lane jl of a row reads the 16-byte pieces at element
 //   offsets (s * LPR + jl) * EPL, s < NP = K / (LPR * EPL), in NB batches of NPB.
-//   An item is NSTEP row-steps of one expert; the activations of NG tokens (full K)
-//   sit in LDS for the whole item. nchunks = items per expert.
+//   A work unit is one expert with a group of at most NG of its tokens, whose
+//   activations (full K, esize bytes per element) sit in LDS while the unit streams.
+//   A step of a unit with n tokens costs cw + ct * n (workgroups split the summed
+//   cost evenly).
 struct GemvMap {
-  int LPR, G, RPL, RS, NP, NPB, NB, NSTEP, NG, esize, nchunks;
+  int LPR, G, RPL, RS, NP, NPB, NB, NG, esize, cw, ct;
 };
+
+constexpr int kWinRows = 64;   // most token rows one staged window of units holds
+
+// Bytes of the expert kernels' LDS tables, before the activation tile: token masks,
+// row bases, ids, the routed and shared class tables, and the staged rows' scales.
+inline constexpr int expert_lds_list_bytes(int E, int T, int k) {
+  return (E * 12 + T * k * 4 + 16 + 4 * (5 * (E < T * k ? E : T * k) + 3) + 12 * T * k +
+          4 * (5 * 1 + 3) + 12 * T + 3 * kWinRows * 4 + 15) / 16 * 16;
+}
 
 struct WTensor {
   const uint8_t* codes;
@@ -43,7 +54,6 @@ struct RouteArgs {
   int T, H, E, k, afmt;
   int TT, ET, n_tt, n_et;   // token tile, experts per workgroup, tile counts
   float* logits;            // [T][E]
-  uint32_t* counters;       // [n_tt]
   int32_t* ids;
   float* w;
   uint8_t* xq_codes;
@@ -68,7 +78,6 @@ struct ExpertArgs {
   uint8_t* hq_scales;    // [T*k][I/16]
   float* hq_scale;       // [T*k]
   float* o;              // [T*k + T][H]
-  uint32_t* counters;
   uint16_t* y;
   float* dbg_h;
   uint8_t* dbg_codes;

@@ -7,7 +7,7 @@
 #include <mutex>
 #include <vector>
 
-#include "../../include/moe.h"
+#include "moe.h"
 
 namespace moe {
 
@@ -21,8 +21,9 @@ std::atomic<bool> g_on{false};
 std::vector<hipEvent_t> g_pool;   // all events ever created
 size_t g_next = 0;                // next unused pool slot in this session
 std::vector<Rec> g_recs;
-const char* const kNames[] = {"route", "gateup", "down", "quantize_nvfp4", "fill"};
-constexpr int kKinds = 5;
+const char* const kNames[] = {"route", "gateup", "down", "quantize_nvfp4", "fill", "topk", "hquant",
+                              "combine"};
+constexpr int kKinds = 8;
 }  // namespace
 
 bool profiling_enabled() { return g_on.load(std::memory_order_relaxed); }

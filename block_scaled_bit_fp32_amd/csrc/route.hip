@@ -1,10 +1,6 @@
-// Router GEMV + sigmoid top-k, token quantization, the standalone Four-Over-Six
-// quantizer and the workspace fill kernel.
-//
-// route_kernel: workgroups tile (tokens x experts); each of the 4 waves reduces a quarter
-// of H. The last workgroup to finish a token tile (device-scope counter after a release
-// fence) selects that tile's top-k; nothing waits on another workgroup. Extra
-// workgroups quantize the tokens in the same launch when the layer quantizes x.
+// Router GEMV and sigmoid top-k (two launches: the top-k needs every logit of a token),
+// token quantization, the standalone Four-Over-Six quantizer and the workspace fill
+// kernel.
 #include <algorithm>
 
 #include "launch.hpp"
@@ -24,10 +20,12 @@ quantize_nvfp4_kernel(const uint16_t* x, int cols, uint8_t* codes, uint8_t* scal
 }
 
 // ======================================================================== route
+// Router GEMV: workgroups tile (tokens x experts); each of the 4 waves reduces a quarter
+// of H, the partial sums meet in LDS in a fixed order. Extra workgroups (one per token)
+// quantize the tokens in the same launch when the layer quantizes x.
 template <int ET, int TT>
-__global__ void __launch_bounds__(kBlock) route_kernel(RouteArgs a) {
+__global__ void __launch_bounds__(kBlock) route_gemv_kernel(RouteArgs a) {
   __shared__ float red[(kBlock / kWave) * ET * TT];
-  __shared__ int last;
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int n_router = a.n_tt * a.n_et;
   if ((int)blockIdx.x >= n_router) {  // token quantization workgroups
@@ -74,8 +72,10 @@ __global__ void __launch_bounds__(kBlock) route_kernel(RouteArgs a) {
   for (int e = 0; e < ET; ++e)
 #pragma unroll
     for (int t = 0; t < TT; ++t) {
-      const float v = group_sum<kWave>(acc[e][t]);
-      if (lane == 0) red[(wave * ET + e) * TT + t] = v;
+      if (t < nt) {
+        const float v = group_sum<kWave>(acc[e][t]);
+        if (lane == 0) red[(wave * ET + e) * TT + t] = v;
+      }
     }
   __syncthreads();
   if ((int)threadIdx.x < ET * TT) {
@@ -85,56 +85,48 @@ __global__ void __launch_bounds__(kBlock) route_kernel(RouteArgs a) {
 #pragma unroll
       for (int w = 1; w < kBlock / kWave; ++w) v += red[(w * ET + e) * TT + t];
       if (a.bias) v += a.bias[e0 + e];
-      store_coherent(a.logits + (int64_t)(t0 + t) * a.E + e0 + e, v);
+      a.logits[(int64_t)(t0 + t) * a.E + e0 + e] = v;
     }
   }
-  if (!arrive_last(&a.counters[tt], (uint32_t)a.n_et, &last)) return;
-  // ---- top-k for the tile's tokens: one wave per token, k rounds of a wave argmax
-  for (int ti = wave; ti < nt; ti += kBlock / kWave) {
-    const int t = t0 + ti;
-    const float* lg = a.logits + (int64_t)t * a.E;
-    float v[16];
+}
+
+// Top-k: one wave per token, k rounds of a wave argmax. The key (order-preserving bits
+// of the logit, then the complement of the expert index) makes "larger logit, then
+// lower index" a plain unsigned maximum. Weights = sigmoid of the selected logits,
+// renormalized in selection order.
+__global__ void __launch_bounds__(kBlock) topk_kernel(RouteArgs a) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int t = blockIdx.x * (kBlock / kWave) + threadIdx.x / kWave;
+  if (t >= a.T) return;
+  const float* lg = a.logits + (int64_t)t * a.E;
+  uint64_t key[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int e = lane + kWave * i;
-      v[i] = e < a.E ? load_coherent(lg + e) : -INFINITY;
-    }
-    uint32_t taken = 0;
-    float myv = 0.0f;
-    int mye = 0;
-    for (int j = 0; j < a.k; ++j) {
-      float bv = -INFINITY;
-      int be = 0x7FFFFFFF;
+  for (int i = 0; i < 16; ++i) {
+    const int e = lane + kWave * i;
+    key[i] = e < a.E ? ((uint64_t)float_order_key(lg[e]) << 32) | (0xFFFFFFFFu - (uint32_t)e) : 0ull;
+  }
+  float myv = 0.0f;
+  int mye = 0;
+  for (int j = 0; j < a.k; ++j) {
+    uint64_t best = 0ull;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int e = lane + kWave * i;
-        if (e < a.E && !((taken >> i) & 1u) && (v[i] > bv || (v[i] == bv && e < be))) {
-          bv = v[i];
-          be = e;
-        }
-      }
+    for (int i = 0; i < 16; ++i) best = key[i] > best ? key[i] : best;
+    best = wave_max_u64(best);
+    const int be = (int)(0xFFFFFFFFu - (uint32_t)best);
 #pragma unroll
-      for (int o = kWave / 2; o > 0; o >>= 1) {
-        const float ov = __shfl_xor(bv, o, kWave);
-        const int oe = __shfl_xor(be, o, kWave);
-        if (ov > bv || (ov == bv && oe < be)) {
-          bv = ov;
-          be = oe;
-        }
-      }
-      if ((be & (kWave - 1)) == lane) taken |= 1u << (be / kWave);
-      if (lane == j) {
-        myv = bv;
-        mye = be;
-      }
+    for (int i = 0; i < 16; ++i)
+      if (lane + kWave * i == be) key[i] = 0ull;      // taken
+    if (lane == j) {
+      myv = float_from_order_key((uint32_t)(best >> 32));
+      mye = be;
     }
-    const float s = lane < a.k ? 1.0f / (1.0f + expf(-myv)) : 0.0f;
-    float tot = 0.0f;
-    for (int j = 0; j < a.k; ++j) tot += __shfl(s, j, kWave);
-    if (lane < a.k) {
-      a.ids[(int64_t)t * a.k + lane] = mye;
-      a.w[(int64_t)t * a.k + lane] = s / tot;
-    }
+  }
+  const float s = lane < a.k ? 1.0f / (1.0f + expf(-myv)) : 0.0f;
+  float tot = 0.0f;
+  for (int j = 0; j < a.k; ++j) tot += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s), j));
+  if (lane < a.k) {
+    a.ids[(int64_t)t * a.k + lane] = mye;
+    a.w[(int64_t)t * a.k + lane] = s / tot;
   }
 }
 
@@ -159,8 +151,12 @@ hipError_t launch_quantize_nvfp4(const uint16_t* x, int rows, int cols, uint8_t*
 
 hipError_t launch_route(const RouteArgs& a, int n_quant, hipStream_t s) {
   const int grid = a.n_tt * a.n_et + n_quant;
-  if (a.ET == 1) return launch_kernel(K_ROUTE, route_kernel<1, 8>, dim3(grid), dim3(kBlock), 0, s, a);
-  return launch_kernel(K_ROUTE, route_kernel<4, 8>, dim3(grid), dim3(kBlock), 0, s, a);
+  hipError_t err = a.ET == 1
+      ? launch_kernel(K_ROUTE, route_gemv_kernel<1, 8>, dim3(grid), dim3(kBlock), 0, s, a)
+      : launch_kernel(K_ROUTE, route_gemv_kernel<4, 8>, dim3(grid), dim3(kBlock), 0, s, a);
+  if (err != hipSuccess) return err;
+  const int waves = kBlock / kWave;
+  return launch_kernel(K_TOPK, topk_kernel, dim3((a.T + waves - 1) / waves), dim3(kBlock), 0, s, a);
 }
 
 }  // namespace moe

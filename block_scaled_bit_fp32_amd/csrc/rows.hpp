@@ -32,15 +32,6 @@ struct F32Row {
   }
 };
 
-// FP32 row written by other workgroups of the same launch (coherent loads).
-struct F32RowCoherent {
-  const float* p;
-  __device__ __forceinline__ void load(int b, float (&v)[16]) const {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) v[i] = load_coherent(p + 16 * b + i);
-  }
-};
-
 // Four-Over-Six NVFP4 of one row of n elements (n % 16 == 0), whole workgroup.
 template <class Row>
 __device__ __forceinline__ void quant_row_nvfp4(const Row& row, int n, uint8_t* codes, uint8_t* scales,
