@@ -307,8 +307,8 @@ def profile_begin() -> None:
 
 def profile_end() -> dict:
     """End the timing session: {kernel kind: (launches, total ms)}."""
-    arr = (KernelTimeT * 8)()
-    n = _lib.moe_profile_end(arr, 8)
+    arr = (KernelTimeT * 32)()
+    n = _lib.moe_profile_end(arr, 32)
     return {arr[i].name.decode(): (arr[i].launches, arr[i].total_ms) for i in range(n)}
 
 

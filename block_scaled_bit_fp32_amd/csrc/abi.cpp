@@ -162,6 +162,19 @@ bool make_plan(const moe_layer_t& L, int T, Plan& p) {
   return true;
 }
 
+// Workgroups of a G-workgroup expert launch that walk the shared expert: its share of
+// the summed cost, with the routed cost bounded by min(E, T*k) one-group experts (the
+// routing is not known on the host). At least one workgroup each.
+int shared_wgs(const moe_layer_t& L, int T, const GemvMap& s, int steps_s, const GemvMap& r, int steps_r,
+               int G) {
+  if (!L.has_shared || G < 2) return 0;
+  const int64_t cs = (int64_t)steps_s * (s.cw * (int64_t)((T + s.NG - 1) / s.NG) + (int64_t)s.ct * T);
+  const int64_t pairs = (int64_t)T * L.k, ur = std::min<int64_t>(L.E, pairs);
+  const int64_t cr = (int64_t)steps_r * (r.cw * ur + r.ct * pairs);
+  const int64_t g = (G * cs + (cs + cr) / 2) / (cs + cr);
+  return (int)std::min<int64_t>(std::max<int64_t>(g, 1), G - 1);
+}
+
 struct WsLayout {
   size_t logits, h, hq_codes, hq_scales, hq_scale, o, total;
   int hs;
@@ -441,9 +454,11 @@ moe_status_t moe_expert_forward(const moe_layer_t* L, const uint16_t* x_bf16, co
   dn.rmap = p.dn_r;
   dn.smap = p.dn_s;
   dn.lds_act_bytes = (int)p.dn_tile;
-  // every workgroup takes an equal share of the row-steps (workgroups past the work
-  // exit at once); a step is at least one row per wave
+  // persistent launches: every workgroup takes an equal share of its class's cost
   const int gu_grid = resident, dn_grid = resident;
+  const int Ish_ = L->has_shared ? L->I_shared : L->I;
+  gu.sh_wgs = shared_wgs(*L, T, p.gu_s, Ish_ / (p.gu_s.RS / 2), p.gu_r, L->I / (p.gu_r.RS / 2), gu_grid);
+  dn.sh_wgs = shared_wgs(*L, T, p.dn_s, L->H / p.dn_s.RS, p.dn_r, L->H / p.dn_r.RS, dn_grid);
   if (launch_experts(gu, gu_grid, p.gu_lds, dn, dn_grid, p.dn_lds, stream) != hipSuccess)
     return set_err(MOE_ELAUNCH, "expert kernel launch failed");
   return MOE_OK;

@@ -113,6 +113,24 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t k) {
   return r;
 }
 
+// Wave-wide inclusive prefix sum (lane i gets the sum over lanes 0..i). Within each row
+// of 16 lanes, DPP row shifts by 1, 2, 4, 8 (lanes shifted in from outside the row add
+// 0); then row_bcast:15 adds row 0's and row 2's totals to rows 1 and 3, and
+// row_bcast:31 adds the total of rows 0-1 to rows 2 and 3.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ int dpp_add_src(int x) {
+  return __builtin_amdgcn_update_dpp(0, x, CTRL, ROWS, 0xF, false);
+}
+__device__ __forceinline__ int wave_incl_sum(int x) {
+  x += dpp_add_src<0x111, 0xF>(x);   // row_shr:1
+  x += dpp_add_src<0x112, 0xF>(x);   // row_shr:2
+  x += dpp_add_src<0x114, 0xF>(x);   // row_shr:4
+  x += dpp_add_src<0x118, 0xF>(x);   // row_shr:8
+  x += dpp_add_src<0x142, 0xA>(x);   // row_bcast:15 into rows 1, 3
+  x += dpp_add_src<0x143, 0xC>(x);   // row_bcast:31 into rows 2, 3
+  return x;
+}
+
 // Order-preserving map of a finite float to uint32 (larger float -> larger key).
 __device__ __forceinline__ uint32_t float_order_key(float v) {
   const uint32_t b = __float_as_uint(v);

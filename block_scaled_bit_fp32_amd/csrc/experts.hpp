@@ -21,6 +21,7 @@
 
 #include "launch.hpp"
 #include "rows.hpp"
+#include "span.hpp"
 
 namespace moe {
 
@@ -42,9 +43,11 @@ struct ClassTab {
 
 struct ExpertLds {
   uint64_t* tmask;  // [E] token mask of each expert
+  int* first;       // [E] first pair (t*k + j) naming each expert
   int* ebase;       // [E] first routed class row of each selected expert
   int* ids;         // [T*k] topk_ids
   int* nA;          // [4] selected expert count
+  int* span;        // [8] this workgroup's Span (routed workgroups)
   ClassTab rt, sh;
   float* w_gs;      // [2 * kWinRows] global weight scales of the staged rows' experts
   float* w_tsc;     // [kWinRows] activation scales of the staged rows
@@ -55,10 +58,12 @@ __device__ __forceinline__ ExpertLds carve(const ExpertArgs& a, uint8_t* smem) {
   ExpertLds L;
   const int P = a.T * a.k, Am = min(a.E, P);
   L.tmask = reinterpret_cast<uint64_t*>(smem);
-  L.ebase = reinterpret_cast<int*>(L.tmask + a.E);
+  L.first = reinterpret_cast<int*>(L.tmask + a.E);
+  L.ebase = L.first + a.E;
   L.ids = L.ebase + a.E;
   L.nA = L.ids + P;
-  int* q = L.nA + 4;
+  L.span = L.nA + 4;
+  int* q = L.span + 8;
   auto tab = [&](ClassTab& C, int A, int rows) {
     C.ex_id = q; q += A;
     C.ex_n = q; q += A;
@@ -78,108 +83,6 @@ __device__ __forceinline__ ExpertLds carve(const ExpertArgs& a, uint8_t* smem) {
   return L;
 }
 
-// The shared expert's class: one expert with all T tokens (no synchronization; the
-// routed build that follows synchronizes).
-__device__ __forceinline__ void build_shared(const ExpertArgs& a, ClassTab& C, int NG, int steps, int cw,
-                                             int ct) {
-  const int units = (a.T + NG - 1) / NG;
-  if (threadIdx.x == 0) {
-    C.ex_id[0] = 0;
-    C.ex_n[0] = a.T;
-    C.ex_row[0] = 0; C.ex_row[1] = a.T;
-    C.ex_unit[0] = 0; C.ex_unit[1] = units;
-    C.ex_cost[0] = 0; C.ex_cost[1] = steps * (cw * units + ct * a.T);
-  }
-  for (int t = threadIdx.x; t < a.T; t += kBlock) {
-    C.r_tok[t] = t;
-    C.r_pair[t] = a.T * a.k + t;
-    C.r_exp[t] = 0;
-  }
-  C.A = 1;
-}
-
-// The routed class from topk_ids (synchronizes): token masks, then wave 0 compacts the
-// selected experts in id order (ballots) and scans their tokens, units and costs.
-// Entries outside [0, E) are ignored. Class rows are filled later by build_rows.
-__device__ __forceinline__ void build_routed(const ExpertArgs& a, const ExpertLds& L, ClassTab& C, int NG,
-                                             int steps, int cw, int ct) {
-  const int P = a.T * a.k;
-  for (int i = threadIdx.x; i < a.E; i += kBlock) L.tmask[i] = 0ull;
-  __syncthreads();
-  for (int p = threadIdx.x; p < P; p += kBlock) {
-    const int e = a.ids[p];
-    L.ids[p] = e;
-    if ((unsigned)e < (unsigned)a.E)
-      atomicOr(reinterpret_cast<unsigned long long*>(&L.tmask[e]), 1ull << (p / a.k));
-  }
-  __syncthreads();
-  if (threadIdx.x < kWave) {
-    const int lane = threadIdx.x;
-    const uint64_t below = (1ull << lane) - 1ull;
-    int A = 0;
-    for (int c0 = 0; c0 < a.E; c0 += kWave) {
-      const int e = c0 + lane;
-      const int n = e < a.E ? __popcll(L.tmask[e]) : 0;
-      const uint64_t bal = __ballot(n > 0);
-      if (n > 0) {
-        const int i = A + __popcll(bal & below);
-        C.ex_id[i] = e;
-        C.ex_n[i] = n;
-      }
-      A += __popcll(bal);
-    }
-    int rr = 0, ru = 0, rc = 0;
-    for (int c0 = 0; c0 < A; c0 += kWave) {
-      const int i = c0 + lane;
-      const int n = i < A ? C.ex_n[i] : 0;
-      const int u = (n + NG - 1) / NG;
-      const int c = steps * (cw * u + ct * n);
-      int xn = n, xu = u, xc = c;
-#pragma unroll
-      for (int off = 1; off < kWave; off <<= 1) {
-        const int yn = __shfl_up(xn, off, kWave), yu = __shfl_up(xu, off, kWave);
-        const int yc = __shfl_up(xc, off, kWave);
-        if (lane >= off) { xn += yn; xu += yu; xc += yc; }
-      }
-      if (i < A) {
-        C.ex_row[i] = rr + xn - n;
-        C.ex_unit[i] = ru + xu - u;
-        C.ex_cost[i] = rc + xc - c;
-        L.ebase[C.ex_id[i]] = rr + xn - n;
-      }
-      rr += __shfl(xn, kWave - 1, kWave);
-      ru += __shfl(xu, kWave - 1, kWave);
-      rc += __shfl(xc, kWave - 1, kWave);
-    }
-    if (lane == 0) {
-      C.ex_row[A] = rr;
-      C.ex_unit[A] = ru;
-      C.ex_cost[A] = rc;
-      L.nA[0] = A;
-    }
-  }
-  __syncthreads();
-  C.A = uni(L.nA[0]);
-}
-
-// Routed class rows: each pair's token goes to its expert's rows at the rank of the
-// token among the expert's tokens (a token naming one expert twice keeps one row).
-// Ends with an LDS barrier.
-__device__ __forceinline__ void build_rows(const ExpertArgs& a, const ExpertLds& L, const ClassTab& C) {
-  const int P = a.T * a.k;
-  for (int p = threadIdx.x; p < P; p += kBlock) {
-    const int e = L.ids[p];
-    if ((unsigned)e < (unsigned)a.E) {
-      const int t = p / a.k;
-      const int r = L.ebase[e] + __popcll(L.tmask[e] & ((1ull << t) - 1ull));
-      C.r_tok[r] = t;
-      C.r_pair[r] = p;
-      C.r_exp[r] = e;
-    }
-  }
-  lds_barrier();
-}
-
 // ===================================================================== GEMV core
 template <int FMT>
 __device__ __forceinline__ int64_t elem_byte(int el) {
@@ -194,19 +97,65 @@ __device__ __forceinline__ int act_slot(int pc, int sub, int nsub, int LPR) {
   return ((pass * nsub + sub) * LPR + jl) * 16;
 }
 
-// Stage all K elements of nt tokens into the LDS tile.
-//   AK = 0: BF16 values (exact), 8 per slot;  AK = 1: FP32 values, 4 per slot.
-// src(t, el) returns the 16-byte slot for token t at element el.
-template <int AK, int EPL, class Src>
-__device__ __forceinline__ void stage_tile(uint8_t* tile, const GemvMap& m, int K, int nt, Src src) {
-  constexpr int PER = AK == 0 ? 8 : 4;
-  constexpr int NSUB = EPL / PER;
-  const int units = K / PER;
-  const int tstride = K * m.esize;
-  for (int u = threadIdx.x; u < nt * units; u += kBlock) {
-    const int t = u / units, el = (u % units) * PER;
+// Staging of nt activation rows (all K elements each) into the LDS tile.
+//   AK = 0: BF16 values (exact), 8 per 16-byte slot;  AK = 1: FP32 values, 4 per slot.
+// Slot u of the rows is row u / units, element (u % units) * PER. The quotient is
+// taken in FP32 from (u + 1/2) / units, exact here: u < 2^16 and the fraction is at
+// least 1/(2 units) away from an integer.
+template <int AK>
+struct SlotMap {
+  static constexpr int PER = AK == 0 ? 8 : 4;
+  int units, lg, tstride;
+  float inv;
+  __device__ __forceinline__ SlotMap(const GemvMap& m, int K)
+      : units(K / PER), lg(__builtin_ctz(m.LPR)), tstride(K * m.esize), inv(1.0f / (float)(K / PER)) {}
+  __device__ __forceinline__ int row(int u) const { return (int)(((float)u + 0.5f) * inv); }
+  __device__ __forceinline__ int elem(int u, int t) const { return (u - t * units) * PER; }
+  // LDS byte offset (see act_slot) of slot u in row t
+  template <int EPL>
+  __device__ __forceinline__ int offset(int t, int el) const {
+    constexpr int NSUB = EPL / PER;
     const int pc = el / EPL, sub = (el % EPL) / PER;
-    *reinterpret_cast<uint4*>(tile + t * tstride + act_slot(pc, sub, NSUB, m.LPR)) = src(t, el);
+    return t * tstride + ((((pc >> lg) * NSUB + sub) << lg) + (pc & ((1 << lg) - 1))) * 16;
+  }
+};
+
+template <int AK, int EPL, class Ld, class Cv>
+__device__ __forceinline__ void stage_tile(uint8_t* tile, const GemvMap& m, int K, int nt, Ld ld, Cv cv) {
+  const SlotMap<AK> sm(m, K);
+  for (int u = threadIdx.x; u < nt * sm.units; u += kBlock) {
+    const int t = sm.row(u), el = sm.elem(u, t);
+    *reinterpret_cast<uint4*>(tile + sm.template offset<EPL>(t, el)) = cv(ld(t, el));
+  }
+}
+
+// The same in two phases with the raw slots parked in registers (at most kPreSlots per
+// thread): the loads are issued before the first weight loads and stored afterwards, so
+// waiting for them never waits for weight bytes (vector-memory counters retire in order).
+constexpr int kPreSlots = 12;
+template <int AK, class Ld>
+__device__ __forceinline__ void park_rows(const SlotMap<AK>& sm, int nt, Ld ld, uint4 (&raw)[kPreSlots]) {
+  const int n = nt * sm.units;
+#pragma unroll
+  for (int i = 0; i < kPreSlots; ++i) {
+    const int u = i * kBlock + threadIdx.x;
+    if (u < n) {
+      const int t = sm.row(u);
+      raw[i] = ld(t, sm.elem(u, t));
+    }
+  }
+}
+template <int AK, int EPL, class Cv>
+__device__ __forceinline__ void unpark_rows(const SlotMap<AK>& sm, uint8_t* tile, int nt, Cv cv,
+                                            const uint4 (&raw)[kPreSlots]) {
+  const int n = nt * sm.units;
+#pragma unroll
+  for (int i = 0; i < kPreSlots; ++i) {
+    const int u = i * kBlock + threadIdx.x;
+    if (u < n) {
+      const int t = sm.row(u);
+      *reinterpret_cast<uint4*>(tile + sm.template offset<EPL>(t, sm.elem(u, t))) = cv(raw[i]);
+    }
   }
 }
 
@@ -402,34 +351,155 @@ struct Cursor {
   int e, n, rb;
 };
 
-// Cost parameters of one class in one kernel.
-struct ClassCost {
-  int NG, steps, cw, ct;
-};
+// The shared expert's class: one expert with all T tokens (no synchronization; the
+// routed build that follows synchronizes).
+__device__ __forceinline__ void build_shared(const ExpertArgs& a, ClassTab& C, int NG, int steps, int cw,
+                                             int ct) {
+  const int units = (a.T + NG - 1) / NG;
+  if (threadIdx.x == 0) {
+    C.ex_id[0] = 0;
+    C.ex_n[0] = a.T;
+    C.ex_row[0] = 0; C.ex_row[1] = a.T;
+    C.ex_unit[0] = 0; C.ex_unit[1] = units;
+    C.ex_cost[0] = 0; C.ex_cost[1] = steps * (cw * units + ct * a.T);
+  }
+  for (int t = threadIdx.x; t < a.T; t += kBlock) {
+    C.r_tok[t] = t;
+    C.r_pair[t] = a.T * a.k + t;
+    C.r_exp[t] = 0;
+  }
+  C.A = 1;
+}
 
-// First position (b = 0) whose start cost is >= c; a == A when c >= the class total.
-// Workgroup-uniform.
-__device__ __forceinline__ void pos_at(const ClassTab& C, const ClassCost& k, int c, int& a, int& g, int& s) {
-  const int lane = threadIdx.x & (kWave - 1);
-  int cnt = 0;
-  for (int c0 = 0; c0 < C.A; c0 += kWave) {
-    const int i = c0 + lane;
-    cnt += __popcll(__ballot(i < C.A && C.ex_cost[i] <= c));
+// The routed class from topk_ids (synchronizes). The selected experts are taken in the
+// order of their first pair (t*k + j): an expert's first pair is its leader, so wave 0
+// scans the T*k pairs (64 per chunk, from registers) rather than all E experts. From
+// per-chunk DPP prefix sums of tokens, units and costs it writes the compacted tables
+// and locates the span of routed workgroup b of G, which it leaves in L.span. Entries
+// outside [0, E) are ignored. Class rows are filled by build_rows.
+constexpr int kMaxPChunks = 16;   // T*k <= 1024
+__device__ __forceinline__ void build_routed(const ExpertArgs& a, const ExpertLds& L, ClassTab& C,
+                                             const ClassCost& k, int NB, int b, int G) {
+  const int P = a.T * a.k;
+  for (int i = threadIdx.x; i < a.E; i += kBlock) {
+    L.tmask[i] = 0ull;
+    L.first[i] = 0x7FFFFFFF;
   }
-  g = 0; s = 0;
-  if (c >= uni(C.ex_cost[C.A])) { a = C.A; return; }
-  a = cnt - 1;
-  const int n = uni(C.ex_n[a]);
-  const int G = (n + k.NG - 1) / k.NG;
-  const int rem = c - uni(C.ex_cost[a]);
-  const int F = k.steps * (k.cw + k.ct * k.NG);
-  g = min(rem / F, G - 1);
-  const int cs = k.cw + k.ct * min(k.NG, n - g * k.NG);
-  s = (rem - g * F + cs - 1) / cs;
-  if (s >= k.steps) {
-    s = 0;
-    if (++g >= G) { g = 0; ++a; }
+  __syncthreads();
+  for (int p = threadIdx.x; p < P; p += kBlock) {
+    const int e = a.ids[p];
+    L.ids[p] = e;
+    if ((unsigned)e < (unsigned)a.E) {
+      atomicOr(reinterpret_cast<unsigned long long*>(&L.tmask[e]), 1ull << (p / a.k));
+      atomicMin(&L.first[e], p);
+    }
   }
+  __syncthreads();
+  if (threadIdx.x < kWave) {
+    const int lane = threadIdx.x;
+    const uint64_t below = (1ull << lane) - 1ull;
+    const int nch = (P + kWave - 1) / kWave;
+    int cnt[kMaxPChunks], cst[kMaxPChunks], eid[kMaxPChunks];
+    uint64_t lead[kMaxPChunks];
+    int tnu = 0, tc = 0, A = 0;
+#pragma unroll
+    for (int c = 0; c < kMaxPChunks; ++c) {
+      cnt[c] = 0; cst[c] = 0; eid[c] = -1; lead[c] = 0ull;
+      if (c < nch) {
+        const int p = c * kWave + lane;
+        const int e = p < P ? L.ids[p] : -1;
+        const bool ld = (unsigned)e < (unsigned)a.E && L.first[e] == p;
+        const int n = ld ? __popcll(L.tmask[e]) : 0;
+        const int u = (n + k.NG - 1) / k.NG;
+        eid[c] = e;
+        cnt[c] = n | (u << 16);
+        cst[c] = k.steps * (k.cw * u + k.ct * n);
+        lead[c] = __ballot(ld);
+        tnu += __builtin_amdgcn_readlane(wave_incl_sum(cnt[c]), kWave - 1);
+        tc += __builtin_amdgcn_readlane(wave_incl_sum(cst[c]), kWave - 1);
+        A += __popcll(lead[c]);
+      }
+    }
+    int c_lo, c_hi;
+    wg_share(tc, b, G, c_lo, c_hi);
+    const Located end{A, 0, tc, tnu >> 16, tnu & 0xFFFF, -1};
+    Located lo = end, hi = end;
+    int bnu = 0, bc = 0, ba = 0;
+#pragma unroll
+    for (int c = 0; c < kMaxPChunks; ++c) {
+      if (c < nch) {
+        const int inu = wave_incl_sum(cnt[c]), ic = wave_incl_sum(cst[c]);
+        const int xnu = bnu + inu - cnt[c], xc = bc + ic - cst[c];   // exclusive
+        const int n = cnt[c] & 0xFFFF, e = eid[c];
+        const bool ld = (lead[c] >> lane) & 1ull;
+        const int i = ba + __popcll(lead[c] & below);
+        if (ld) {
+          C.ex_id[i] = e;
+          C.ex_n[i] = n;
+          C.ex_row[i] = xnu & 0xFFFF;
+          C.ex_unit[i] = xnu >> 16;
+          C.ex_cost[i] = xc;
+          L.ebase[e] = xnu & 0xFFFF;
+        }
+        const uint64_t blo = __ballot(ld && xc <= c_lo), bhi = __ballot(ld && xc <= c_hi);
+        if (blo && c_lo < tc) {
+          const int j = 63 - __clzll(blo);
+          lo = Located{__builtin_amdgcn_readlane(i, j), __builtin_amdgcn_readlane(n, j),
+                       __builtin_amdgcn_readlane(xc, j), __builtin_amdgcn_readlane(xnu >> 16, j),
+                       __builtin_amdgcn_readlane(xnu & 0xFFFF, j), __builtin_amdgcn_readlane(e, j)};
+        }
+        if (bhi && c_hi < tc) {
+          const int j = 63 - __clzll(bhi);
+          hi = Located{__builtin_amdgcn_readlane(i, j), __builtin_amdgcn_readlane(n, j),
+                       __builtin_amdgcn_readlane(xc, j), __builtin_amdgcn_readlane(xnu >> 16, j),
+                       __builtin_amdgcn_readlane(xnu & 0xFFFF, j), __builtin_amdgcn_readlane(e, j)};
+        }
+        bnu += __builtin_amdgcn_readlane(inu, kWave - 1);
+        bc += __builtin_amdgcn_readlane(ic, kWave - 1);
+        ba += __popcll(lead[c]);
+      }
+    }
+    Span sp = make_span(lo, hi, A, k, c_lo, c_hi, NB);
+    if (sp.e0 < 0 && sp.a0 < A) {   // the start rolled over to the next expert
+      sp.e0 = C.ex_id[sp.a0];
+      sp.n0 = C.ex_n[sp.a0];
+    }
+    if (lane == 0) {
+      C.ex_row[A] = tnu & 0xFFFF;
+      C.ex_unit[A] = tnu >> 16;
+      C.ex_cost[A] = tc;
+      L.nA[0] = A;
+      L.span[0] = sp.a0; L.span[1] = sp.g0; L.span[2] = sp.s0; L.span[3] = sp.e0;
+      L.span[4] = sp.n0; L.span[5] = sp.rb0; L.span[6] = sp.left; L.span[7] = sp.row_limit;
+    }
+  }
+  __syncthreads();
+  C.A = uni(L.nA[0]);
+}
+
+__device__ __forceinline__ Span read_span(const ExpertLds& L) {
+  Span sp;
+  sp.a0 = uni(L.span[0]); sp.g0 = uni(L.span[1]); sp.s0 = uni(L.span[2]); sp.e0 = uni(L.span[3]);
+  sp.n0 = uni(L.span[4]); sp.rb0 = uni(L.span[5]); sp.left = uni(L.span[6]); sp.row_limit = uni(L.span[7]);
+  return sp;
+}
+
+// Routed class rows: each pair's token goes to its expert's rows at the rank of the
+// token among the expert's tokens (a token naming one expert twice keeps one row).
+// Ends with an LDS barrier.
+__device__ __forceinline__ void build_rows(const ExpertArgs& a, const ExpertLds& L, const ClassTab& C) {
+  const int P = a.T * a.k;
+  for (int p = threadIdx.x; p < P; p += kBlock) {
+    const int e = L.ids[p];
+    if ((unsigned)e < (unsigned)a.E) {
+      const int t = p / a.k;
+      const int r = L.ebase[e] + __popcll(L.tmask[e] & ((1ull << t) - 1ull));
+      C.r_tok[r] = t;
+      C.r_pair[r] = p;
+      C.r_exp[r] = e;
+    }
+  }
+  lds_barrier();
 }
 
 // Where the current unit's data sits: its first class row, its first staged row, and
@@ -438,37 +508,30 @@ struct UnitCtx {
   int crow, wrow, n;
 };
 
-// Walks the positions of one class whose start cost lies in [c_lo, c_hi).
-// Call-backs (workgroup-uniform):
-//   rows(e, s, lrow, out[RPL])     global weight rows of this lane at step s of expert e
-//   prep()                         runs once after the first weight loads are issued,
-//                                  before the first staging (ends with a barrier)
-//   src(tok, pair, el) -> uint4    16 bytes of a row's activations at element el
-//   tsc(tok, pair) -> float        a row's activation scale
-//   gs(e, q) -> float              global weight scale q of expert e
-//   sink(ctx, s, lrow, acc)        results, on the lanes with jl == 0
-// Two register sets alternate (no loop-carried copy); every step but the last issues
-// the same number of weight loads for the next one, so the compiler waits for one
-// step's loads while the next step's are in flight (vector-memory counters retire in
-// issue order). Staged rows are a window of consecutive class rows, restaged only when
-// a unit does not fit; only LDS barriers are used, so weight loads stream across it.
-template <int FMT, int AK, int RPL, class Rows, class Prep, class Src, class Tsc, class Gs, class Sink>
+// Walks one workgroup's span of a class. The class's operations (workgroup-uniform):
+//   op.rows(e, s, lrow, out[RPL])  global weight rows of this lane at step s of expert e
+//   op.ld(tok, pair, el) -> uint4  raw bytes behind 16 staged bytes of a row at element el
+//   op.cv(uint4) -> uint4          those 16 staged bytes
+//   op.tsc(tok, pair) -> float     a row's activation scale
+//   op.gs(e, q) -> float           global weight scale q of expert e
+//   op.sink(ctx, s, lrow, acc)     results, on the lanes with jl == 0
+// Ops is a plain struct per (projection, activation format), so the shared and routed
+// classes run the same code whenever their formats agree (the kernels stay small
+// enough for the instruction cache).
+// The first staged window (rows of the first units) is loaded into registers before
+// the first weight loads are issued and stored to LDS after them. Two register sets
+// alternate (no loop-carried copy); every step but the last issues the same number of
+// weight loads for the next one, so the compiler waits for one step's loads while the
+// next step's are in flight. Later windows are staged when a unit does not fit; only
+// LDS barriers are used, so weight loads stream across them.
+template <int FMT, int AK, int RPL, class Ops>
 __device__ __forceinline__ void walk_class(const WTensor& W, const GemvMap& m, const ExpertLds& L,
                                            int lds_tile_bytes, const ClassTab& C, const ClassCost& k,
-                                           int c_lo, int c_hi, Rows rows, Prep prep, Src src, Tsc tsc,
-                                           Gs gs, Sink sink) {
+                                           const Span& sp, const Ops& op) {
   constexpr int EPL = elems_per_piece(FMT);
-  int a0, g0, s0, a1, g1, s1;
-  pos_at(C, k, c_lo, a0, g0, s0);
-  pos_at(C, k, c_hi, a1, g1, s1);
-  const int l0 = (uni(C.ex_unit[a0]) + g0) * k.steps + s0;
-  const int l1 = (uni(C.ex_unit[a1]) + g1) * k.steps + s1;
-  if (l1 <= l0) return;
-  int left = (l1 - l0) * m.NB;   // positions to walk
-  // one past the last class row walked
-  int row_limit = uni(C.ex_row[a1]) + g1 * k.NG;
-  if (s1 > 0) row_limit += min(k.NG, uni(C.ex_n[a1]) - g1 * k.NG);
-
+  constexpr int PER = AK == 0 ? 8 : 4;
+  if (sp.left <= 0) return;
+  int left = sp.left;
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int jl = lane % m.LPR, lrow = wave * m.G + lane / m.LPR;
   const int tstride = W.K * m.esize;
@@ -486,26 +549,28 @@ __device__ __forceinline__ void walk_class(const WTensor& W, const GemvMap& m, c
       p.rb = uni(C.ex_row[p.a]);
     }
   };
-  int r0 = 0, r1 = 0;            // staged class rows [r0, r1)
-  int cur_a = -1, cur_g = -1;
-  UnitCtx cx{0, 0, 0};
+  auto row_ld = [&](int r0) {
+    return [&, r0](int t, int el) { return op.ld(C.r_tok[r0 + t], C.r_pair[r0 + t], el); };
+  };
+  int r0 = sp.rb0 + sp.g0 * k.NG;   // staged class rows [r0, r1)
+  int r1 = min(min(r0 + cap, sp.row_limit), r0 + kPreSlots * kBlock / (W.K / PER));
   auto stage = [&](int ra) {
-    lds_barrier();               // everyone is done with the previous rows
+    lds_barrier();                  // everyone is done with the previous rows
     r0 = ra;
-    r1 = min(ra + cap, row_limit);
+    r1 = min(ra + cap, sp.row_limit);
     const int nrows = r1 - r0;
-    stage_tile<AK, EPL>(L.tile, m, W.K, nrows, [&](int r, int el) {
-      return src(C.r_tok[r0 + r], C.r_pair[r0 + r], el);
-    });
+    stage_tile<AK, EPL>(L.tile, m, W.K, nrows, row_ld(r0), [&](uint4 r) { return op.cv(r); });
     for (int i = threadIdx.x; i < nrows; i += kBlock) {
       const int tk = C.r_tok[r0 + i], pr = C.r_pair[r0 + i], e = C.r_exp[r0 + i];
-      L.w_tsc[i] = tsc(tk, pr);
-      L.w_gs[2 * i] = gs(e, 0);
-      L.w_gs[2 * i + 1] = gs(e, 1);
+      L.w_tsc[i] = op.tsc(tk, pr);
+      L.w_gs[2 * i] = op.gs(e, 0);
+      L.w_gs[2 * i + 1] = op.gs(e, 1);
     }
     lds_barrier();
   };
   float acc[RPL][4];
+  int cur_a = -1, cur_g = -1;
+  UnitCtx cx{0, 0, 0};
   auto do_step = [&](auto pf, const Cursor& p, WeightRegs<RPL>& cur, WeightRegs<RPL>& nxt, Cursor& np) {
     if (p.a != cur_a || p.g != cur_g) {   // next unit
       cur_a = p.a;
@@ -527,7 +592,7 @@ __device__ __forceinline__ void walk_class(const WTensor& W, const GemvMap& m, c
       np = p;
       advance(np);
       int64_t nr[RPL];
-      rows(np.e, np.s, lrow, nr);
+      op.rows(np.e, np.s, lrow, nr);
       fetch_batch<FMT, RPL>(W, m, nr, np.b, jl, nxt);
     }
     const uint8_t* tile = L.tile + cx.wrow * tstride;
@@ -561,17 +626,36 @@ __device__ __forceinline__ void walk_class(const WTensor& W, const GemvMap& m, c
             acc[q][t] = v;
           }
         }
-      if (jl == 0) sink(cx, p.s, lrow, acc);
+      if (jl == 0) op.sink(cx, p.s, lrow, acc);
     }
   };
-  Cursor pa{a0, g0, s0, 0, uni(C.ex_id[a0]), uni(C.ex_n[a0]), uni(C.ex_row[a0])}, pb = pa;
+  // first window: raw slots and per-row scales into registers, then the first weight
+  // loads, then the LDS stores
+  const int nrows0 = r1 - r0;
+  uint4 raw[kPreSlots];
+  const SlotMap<AK> smap(m, W.K);
+  park_rows<AK>(smap, nrows0, row_ld(r0), raw);
+  float ts_r = 0.0f, g0_r = 0.0f, g1_r = 0.0f;
+  if (threadIdx.x < nrows0) {
+    const int tk = C.r_tok[r0 + threadIdx.x], pr = C.r_pair[r0 + threadIdx.x], e = C.r_exp[r0 + threadIdx.x];
+    ts_r = op.tsc(tk, pr);
+    g0_r = op.gs(e, 0);
+    g1_r = op.gs(e, 1);
+  }
+  Cursor pa{sp.a0, sp.g0, sp.s0, 0, sp.e0, sp.n0, sp.rb0}, pb = pa;
   WeightRegs<RPL> A, B;
   {
     int64_t rr[RPL];
-    rows(pa.e, pa.s, lrow, rr);
+    op.rows(pa.e, pa.s, lrow, rr);
     fetch_batch<FMT, RPL>(W, m, rr, 0, jl, A);
   }
-  prep();
+  unpark_rows<AK, EPL>(smap, L.tile, nrows0, [&](uint4 r) { return op.cv(r); }, raw);
+  if (threadIdx.x < nrows0) {
+    L.w_tsc[threadIdx.x] = ts_r;
+    L.w_gs[2 * threadIdx.x] = g0_r;
+    L.w_gs[2 * threadIdx.x + 1] = g1_r;
+  }
+  lds_barrier();
   using Yes = std::integral_constant<bool, true>;
   using No = std::integral_constant<bool, false>;
   while (true) {
@@ -583,20 +667,18 @@ __device__ __forceinline__ void walk_class(const WTensor& W, const GemvMap& m, c
   }
 }
 
-// This workgroup's share [c_lo, c_hi) of the summed cost of both classes.
-__device__ __forceinline__ void wg_share(int total, int& c_lo, int& c_hi) {
-  c_lo = (int)((long long)total * blockIdx.x / gridDim.x);
-  c_hi = (int)((long long)total * (blockIdx.x + 1) / gridDim.x);
+// Activation slot sources, in two halves so that the loads can be issued long before
+// the LDS stores: a load returns the raw bytes behind 16 bytes of staged activations
+// (8 BF16 or 4 FP32 values) at element el, a convert turns them into those 16 bytes.
+__device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+__device__ __forceinline__ uint4 cv_same(uint4 r) { return r; }
+// NVFP4: 8 codes (4 bytes) and their E4M3 block scale; converted to 8 BF16 (v * S, exact).
+__device__ __forceinline__ uint4 nvfp4_ld(const uint8_t* codes, const uint8_t* scales, int el) {
+  return make_uint4(*reinterpret_cast<const uint32_t*>(codes + (el >> 1)), scales[el >> 4], 0u, 0u);
 }
-
-// Activation slot sources. Each returns 16 bytes: 8 BF16 values or 4 FP32 values.
-__device__ __forceinline__ uint4 bf16_slot(const uint16_t* row, int el) {
-  return *reinterpret_cast<const uint4*>(row + el);
-}
-// 8 NVFP4 values -> 8 BF16 (v * S, exact in BF16).
-__device__ __forceinline__ uint4 nvfp4_slot(const uint8_t* codes, const uint8_t* scales, int el) {
-  const uint32_t w = *reinterpret_cast<const uint32_t*>(codes + (el >> 1));
-  const float S = e4m3_to_f32(scales[el >> 4]);
+__device__ __forceinline__ uint4 nvfp4_cv(uint4 r) {
+  const float S = e4m3_to_f32(r.y);
+  const uint32_t w = r.x;
   uint32_t o[4];
   const f32x2_t v0 = fp4x2_to_f32<0>(w, 1.0f), v1 = fp4x2_to_f32<1>(w, 1.0f);
   const f32x2_t v2 = fp4x2_to_f32<2>(w, 1.0f), v3 = fp4x2_to_f32<3>(w, 1.0f);
@@ -606,143 +688,194 @@ __device__ __forceinline__ uint4 nvfp4_slot(const uint8_t* codes, const uint8_t*
   o[3] = (__float_as_uint(v3.x * S) >> 16) | (__float_as_uint(v3.y * S) & 0xFFFF0000u);
   return make_uint4(o[0], o[1], o[2], o[3]);
 }
-// 8 FP8-E4M3 values -> 8 BF16 (exact).
-__device__ __forceinline__ uint4 fp8_slot(const uint8_t* codes, int el) {
+// FP8-E4M3: 8 codes; converted to 8 BF16 (exact).
+__device__ __forceinline__ uint4 fp8_ld(const uint8_t* codes, int el) {
   const uint2 w = *reinterpret_cast<const uint2*>(codes + el);
-  return make_uint4(as_u32(fp8x2_to_bf16<false>(w.x, 1.0f)), as_u32(fp8x2_to_bf16<true>(w.x, 1.0f)),
-                    as_u32(fp8x2_to_bf16<false>(w.y, 1.0f)), as_u32(fp8x2_to_bf16<true>(w.y, 1.0f)));
+  return make_uint4(w.x, w.y, 0u, 0u);
 }
-__device__ __forceinline__ uint4 f32_slot(const float* row, int el) {
-  return *reinterpret_cast<const uint4*>(row + el);
+__device__ __forceinline__ uint4 fp8_cv(uint4 r) {
+  return make_uint4(as_u32(fp8x2_to_bf16<false>(r.x, 1.0f)), as_u32(fp8x2_to_bf16<true>(r.x, 1.0f)),
+                    as_u32(fp8x2_to_bf16<false>(r.y, 1.0f)), as_u32(fp8x2_to_bf16<true>(r.y, 1.0f)));
 }
 
 // ================================================================ gate/up kernel
 // Gate/up rows: at row-step s, lane row slot lrow is intermediate index
 // i = s * PS + lrow (PS = 4 * G pairs per step); the lane holds gate row i (q = 0) and
-// up row I + i (q = 1).
-template <int FMT, class Prep>
-__device__ __forceinline__ void gateup_walk(const ExpertArgs& a, const ExpertLds& L, const ClassTab& C,
-                                            bool routed, int c_lo, int c_hi, Prep prep) {
-  const WTensor& W = routed ? a.rw : a.sw;
-  const GemvMap& m = routed ? a.rmap : a.smap;
-  const int PS = 4 * m.G;
-  const int Iexp = routed ? a.I : a.Ish;
-  const int afmt = routed ? a.afmt : A_BF16;
-  const ClassCost k{m.NG, Iexp / PS, m.cw, m.ct};
-  auto rows = [&](int e, int st, int lrow, int64_t (&out)[2]) {
-    const int64_t base = (int64_t)e * W.rows;
+// up row I + i (q = 1). AF is the format the class's activations arrive in.
+template <int AF>
+struct GateupOps {
+  const uint16_t* x;
+  const uint8_t* xq_codes;
+  const uint8_t* xq_scales;
+  const float* xq_scale;
+  const float* gscale;
+  int gs_per_expert, wrows, Iexp, PS, H, hs;
+  float* h;
+  float* dbg_h;
+  const float* w_gs;
+  const float* w_tsc;
+  const int* r_pair;
+
+  __device__ __forceinline__ void rows(int e, int st, int lrow, int64_t (&out)[2]) const {
+    const int64_t base = (int64_t)e * wrows;
     const int i = st * PS + lrow;
     out[0] = base + i;
     out[1] = base + Iexp + i;
-  };
-  auto tsc = [&](int t, int) { return afmt == A_BF16 ? 1.0f : a.xq_scale[t]; };
-  auto gs = [&](int e, int q) { return W.gscale ? W.gscale[(int64_t)e * W.gs_per_expert + q] : 1.0f; };
-  auto sink = [&](const UnitCtx& cx, int st, int lrow, const float (&acc)[2][4]) {
+  }
+  __device__ __forceinline__ uint4 ld(int t, int, int el) const {
+    if constexpr (AF == A_NVFP4_4O6)
+      return nvfp4_ld(xq_codes + (int64_t)t * (H / 2), xq_scales + (int64_t)t * (H / 16), el);
+    else if constexpr (AF == A_FP8_TOKEN)
+      return fp8_ld(xq_codes + (int64_t)t * H, el);
+    else
+      return ld16(x + (int64_t)t * H + el);
+  }
+  __device__ __forceinline__ uint4 cv(uint4 r) const {
+    if constexpr (AF == A_NVFP4_4O6) return nvfp4_cv(r);
+    else if constexpr (AF == A_FP8_TOKEN) return fp8_cv(r);
+    else return r;
+  }
+  __device__ __forceinline__ float tsc(int t, int) const { return AF == A_BF16 ? 1.0f : xq_scale[t]; }
+  __device__ __forceinline__ float gs(int e, int q) const {
+    return gscale ? gscale[(int64_t)e * gs_per_expert + q] : 1.0f;
+  }
+  __device__ __forceinline__ void sink(const UnitCtx& cx, int st, int lrow, const float (&acc)[2][4]) const {
     const int i = st * PS + lrow;
-    const float gsg = L.w_gs[2 * cx.wrow], gsu = L.w_gs[2 * cx.wrow + 1];
+    const float gsg = w_gs[2 * cx.wrow], gsu = w_gs[2 * cx.wrow + 1];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       if (t < cx.n) {
-        const float ts = L.w_tsc[cx.wrow + t];
+        const float ts = w_tsc[cx.wrow + t];
         const float gv = acc[0][t] * gsg * ts;
         const float uv = acc[1][t] * gsu * ts;
         const float hv = gv / (1.0f + expf(-gv)) * uv;
-        const int64_t off = (int64_t)C.r_pair[cx.crow + t] * a.hs + i;
-        a.h[off] = hv;
-        if (a.dbg_h) a.dbg_h[off] = hv;
+        const int64_t off = (int64_t)r_pair[cx.crow + t] * hs + i;
+        h[off] = hv;
+        if (dbg_h) dbg_h[off] = hv;
       }
     }
-  };
-  if (afmt == A_NVFP4_4O6) {
-    walk_class<FMT, 0, 2>(W, m, L, a.lds_act_bytes, C, k, c_lo, c_hi, rows, prep,
-        [&](int t, int, int el) {
-          return nvfp4_slot(a.xq_codes + (int64_t)t * (a.H / 2), a.xq_scales + (int64_t)t * (a.H / 16), el);
-        }, tsc, gs, sink);
-  } else if (afmt == A_FP8_TOKEN) {
-    walk_class<FMT, 0, 2>(W, m, L, a.lds_act_bytes, C, k, c_lo, c_hi, rows, prep,
-        [&](int t, int, int el) { return fp8_slot(a.xq_codes + (int64_t)t * a.H, el); }, tsc, gs, sink);
-  } else {
-    walk_class<FMT, 0, 2>(W, m, L, a.lds_act_bytes, C, k, c_lo, c_hi, rows, prep,
-        [&](int t, int, int el) { return bf16_slot(a.x + (int64_t)t * a.H, el); }, tsc, gs, sink);
   }
+};
+
+__device__ __forceinline__ ClassCost gateup_cost(const ExpertArgs& a, bool routed) {
+  const GemvMap& m = routed ? a.rmap : a.smap;
+  return ClassCost{m.NG, (routed ? a.I : a.Ish) / (4 * m.G), m.cw, m.ct};
 }
 
-template <int RF, int SF>
+template <int FMT, int AF>
+__device__ __forceinline__ void gateup_walk(const ExpertArgs& a, const ExpertLds& L, const ClassTab& C,
+                                            bool routed, const Span& sp) {
+  const WTensor& W = routed ? a.rw : a.sw;
+  const GemvMap& m = routed ? a.rmap : a.smap;
+  const int Iexp = routed ? a.I : a.Ish;
+  const GateupOps<AF> op{a.x, a.xq_codes, a.xq_scales, a.xq_scale, W.gscale, W.gs_per_expert, W.rows, Iexp,
+                         4 * m.G, a.H, a.hs, a.h, a.dbg_h, L.w_gs, L.w_tsc, C.r_pair};
+  walk_class<FMT, 0, 2>(W, m, L, a.lds_act_bytes, C, gateup_cost(a, routed), sp, op);
+}
+
+// Workgroups [0, sh_wgs) walk the shared expert (BF16 activations, no dependency on the
+// routing), the others split the selected experts.
+template <int RF, int SF, int AF>
 __global__ void __launch_bounds__(kBlock, 2) gateup_kernel(ExpertArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
   ExpertLds L = carve(a, smem);
-  if (a.has_shared) build_shared(a, L.sh, a.smap.NG, a.Ish / (4 * a.smap.G), a.smap.cw, a.smap.ct);
-  build_routed(a, L, L.rt, a.rmap.NG, a.I / (4 * a.rmap.G), a.rmap.cw, a.rmap.ct);
-  const int cs = a.has_shared ? uni(L.sh.ex_cost[1]) : 0;
-  int c_lo, c_hi;
-  wg_share(cs + uni(L.rt.ex_cost[L.rt.A]), c_lo, c_hi);
-  if (c_lo < cs) gateup_walk<SF>(a, L, L.sh, false, c_lo, min(c_hi, cs), [] {});
-  if (c_hi > cs)
-    gateup_walk<RF>(a, L, L.rt, true, max(c_lo - cs, 0), c_hi - cs, [&] { build_rows(a, L, L.rt); });
+  const bool shared = (int)blockIdx.x < a.sh_wgs;
+  Span sp;
+  if (shared) {
+    const ClassCost k = gateup_cost(a, false);
+    build_shared(a, L.sh, k.NG, k.steps, k.cw, k.ct);
+    lds_barrier();
+    sp = shared_span(a.T, k, a.smap.NB, blockIdx.x, a.sh_wgs);
+  } else {
+    build_routed(a, L, L.rt, gateup_cost(a, true), a.rmap.NB, blockIdx.x - a.sh_wgs, gridDim.x - a.sh_wgs);
+    build_rows(a, L, L.rt);
+    sp = read_span(L);
+  }
+  if (shared) gateup_walk<SF, A_BF16>(a, L, L.sh, false, sp);
+  else gateup_walk<RF, AF>(a, L, L.rt, true, sp);
 }
 
 // =================================================================== down kernel
 // Writes each (pair, hidden row) partial output o, scaled by the weight's global scale
 // and the pair's activation scale; the combine kernel sums them. Each lane holds one row
-// (RPL = 1): at row-step s, lane row slot lrow is hidden row s * RS + lrow.
-template <int FMT, int AK, int RPL, class Prep>
-__device__ __forceinline__ void down_walk(const ExpertArgs& a, const ExpertLds& L, const ClassTab& C,
-                                          bool routed, int c_lo, int c_hi, Prep prep) {
-  const WTensor& W = routed ? a.rw : a.sw;
-  const GemvMap& m = routed ? a.rmap : a.smap;
-  const int RS = m.RS;
-  const int Kexp = routed ? a.I : a.Ish;
-  const int afmt = routed ? a.afmt : A_BF16;
-  const ClassCost k{m.NG, a.H / RS, m.cw, m.ct};
-  auto rows = [&](int e, int st, int lrow, int64_t (&out)[RPL]) {
-    const int64_t base = (int64_t)e * W.rows + st * RS + lrow * RPL;
-#pragma unroll
-    for (int q = 0; q < RPL; ++q) out[q] = base + q;
-  };
-  auto tsc = [&](int, int p) { return afmt == A_BF16 ? 1.0f : a.hq_scale[p]; };
-  auto gs = [&](int e, int q) {
-    return (q == 0 && W.gscale) ? W.gscale[(int64_t)e * W.gs_per_expert] : 1.0f;
-  };
-  auto sink = [&](const UnitCtx& cx, int st, int lrow, const float (&acc)[RPL][4]) {
-    const float g = L.w_gs[2 * cx.wrow];
-    const int row0 = st * RS + lrow * RPL;
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      if (t < cx.n) {
-        const float sc = g * L.w_tsc[cx.wrow + t];
-        float* o = a.o + (int64_t)C.r_pair[cx.crow + t] * a.H + row0;
-#pragma unroll
-        for (int q = 0; q < RPL; ++q) o[q] = acc[q][t] * sc;
-      }
-    }
-  };
-  if constexpr (AK == 1) {
-    walk_class<FMT, 1, RPL>(W, m, L, a.lds_act_bytes, C, k, c_lo, c_hi, rows, prep,
-        [&](int, int p, int el) { return f32_slot(a.h + (int64_t)p * a.hs, el); }, tsc, gs, sink);
-  } else if (afmt == A_NVFP4_4O6) {
-    walk_class<FMT, 0, RPL>(W, m, L, a.lds_act_bytes, C, k, c_lo, c_hi, rows, prep,
-        [&](int, int p, int el) {
-          return nvfp4_slot(a.hq_codes + (int64_t)p * (Kexp / 2), a.hq_scales + (int64_t)p * (Kexp / 16), el);
-        }, tsc, gs, sink);
-  } else {
-    walk_class<FMT, 0, RPL>(W, m, L, a.lds_act_bytes, C, k, c_lo, c_hi, rows, prep,
-        [&](int, int p, int el) { return fp8_slot(a.hq_codes + (int64_t)p * Kexp, el); }, tsc, gs, sink);
+// (RPL = 1): at row-step s, lane row slot lrow is hidden row s * RS + lrow. AF is the
+// routed experts' activation format: h is staged as FP32 for BF16 (and for the shared
+// expert), as BF16 values decoded from the re-quantized h otherwise.
+template <int AF>
+struct DownOps {
+  const float* hf;
+  const uint8_t* hq_codes;
+  const uint8_t* hq_scales;
+  const float* hq_scale;
+  const float* gscale;
+  int gs_per_expert, wrows, Kexp, RS, H, hs;
+  float* o;
+  const float* w_gs;
+  const float* w_tsc;
+  const int* r_pair;
+
+  __device__ __forceinline__ void rows(int e, int st, int lrow, int64_t (&out)[1]) const {
+    out[0] = (int64_t)e * wrows + st * RS + lrow;
   }
+  __device__ __forceinline__ uint4 ld(int, int p, int el) const {
+    if constexpr (AF == A_NVFP4_4O6)
+      return nvfp4_ld(hq_codes + (int64_t)p * (Kexp / 2), hq_scales + (int64_t)p * (Kexp / 16), el);
+    else if constexpr (AF == A_FP8_TOKEN)
+      return fp8_ld(hq_codes + (int64_t)p * Kexp, el);
+    else
+      return ld16(hf + (int64_t)p * hs + el);
+  }
+  __device__ __forceinline__ uint4 cv(uint4 r) const {
+    if constexpr (AF == A_NVFP4_4O6) return nvfp4_cv(r);
+    else if constexpr (AF == A_FP8_TOKEN) return fp8_cv(r);
+    else return r;
+  }
+  __device__ __forceinline__ float tsc(int, int p) const { return AF == A_BF16 ? 1.0f : hq_scale[p]; }
+  __device__ __forceinline__ float gs(int e, int q) const {
+    return (q == 0 && gscale) ? gscale[(int64_t)e * gs_per_expert] : 1.0f;
+  }
+  __device__ __forceinline__ void sink(const UnitCtx& cx, int st, int lrow, const float (&acc)[1][4]) const {
+    const float g = w_gs[2 * cx.wrow];
+    const int row = st * RS + lrow;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      if (t < cx.n) o[(int64_t)r_pair[cx.crow + t] * H + row] = acc[0][t] * g * w_tsc[cx.wrow + t];
+  }
+};
+
+__device__ __forceinline__ ClassCost down_cost(const ExpertArgs& a, bool routed) {
+  const GemvMap& m = routed ? a.rmap : a.smap;
+  return ClassCost{m.NG, a.H / m.RS, m.cw, m.ct};
 }
 
+template <int FMT, int AF>
+__device__ __forceinline__ void down_walk(const ExpertArgs& a, const ExpertLds& L, const ClassTab& C,
+                                          bool routed, const Span& sp) {
+  const WTensor& W = routed ? a.rw : a.sw;
+  const GemvMap& m = routed ? a.rmap : a.smap;
+  const DownOps<AF> op{a.h, a.hq_codes, a.hq_scales, a.hq_scale, W.gscale, W.gs_per_expert, W.rows,
+                       routed ? a.I : a.Ish, m.RS, a.H, a.hs, a.o, L.w_gs, L.w_tsc, C.r_pair};
+  walk_class<FMT, AF == A_BF16 ? 1 : 0, 1>(W, m, L, a.lds_act_bytes, C, down_cost(a, routed), sp, op);
+}
 
-template <int RF, int SF, int RAK>
+template <int RF, int SF, int AF>
 __global__ void __launch_bounds__(kBlock, 2) down_kernel(ExpertArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
   ExpertLds L = carve(a, smem);
-  if (a.has_shared) build_shared(a, L.sh, a.smap.NG, a.H / a.smap.RS, a.smap.cw, a.smap.ct);
-  build_routed(a, L, L.rt, a.rmap.NG, a.H / a.rmap.RS, a.rmap.cw, a.rmap.ct);
-  const int cs = a.has_shared ? uni(L.sh.ex_cost[1]) : 0;
-  int c_lo, c_hi;
-  wg_share(cs + uni(L.rt.ex_cost[L.rt.A]), c_lo, c_hi);
-  if (c_lo < cs) down_walk<SF, 1, 1>(a, L, L.sh, false, c_lo, min(c_hi, cs), [] {});
-  if (c_hi > cs)
-    down_walk<RF, RAK, 1>(a, L, L.rt, true, max(c_lo - cs, 0), c_hi - cs, [&] { build_rows(a, L, L.rt); });
+  const bool shared = (int)blockIdx.x < a.sh_wgs;
+  Span sp;
+  if (shared) {
+    const ClassCost k = down_cost(a, false);
+    build_shared(a, L.sh, k.NG, k.steps, k.cw, k.ct);
+    lds_barrier();
+    sp = shared_span(a.T, k, a.smap.NB, blockIdx.x, a.sh_wgs);
+  } else {
+    build_routed(a, L, L.rt, down_cost(a, true), a.rmap.NB, blockIdx.x - a.sh_wgs, gridDim.x - a.sh_wgs);
+    build_rows(a, L, L.rt);
+    sp = read_span(L);
+  }
+  if (shared) down_walk<SF, A_BF16>(a, L, L.sh, false, sp);
+  else down_walk<RF, AF>(a, L, L.rt, true, sp);
 }
 
 // ================================================================ host launchers
@@ -750,17 +883,32 @@ hipError_t launch_hquant(const ExpertArgs& a, hipStream_t s);
 hipError_t launch_combine(const ExpertArgs& a, hipStream_t s);
 
 // gate/up -> (h re-quantization) -> down -> combine, in stream order.
+template <int RF, int SF, int AF>
+hipError_t launch_experts_af(const ExpertArgs& gu, int gu_grid, size_t gu_lds,
+                             const ExpertArgs& dn, int dn_grid, size_t dn_lds, hipStream_t s) {
+  hipError_t err = launch_kernel(K_GATEUP, gateup_kernel<RF, SF, AF>, dim3(gu_grid), dim3(kBlock), gu_lds, s, gu);
+  if (err != hipSuccess) return err;
+  if (AF != A_BF16 && (err = launch_hquant(gu, s)) != hipSuccess) return err;
+  err = launch_kernel(K_DOWN, down_kernel<RF, SF, AF>, dim3(dn_grid), dim3(kBlock), dn_lds, s, dn);
+  if (err != hipSuccess) return err;
+  return launch_combine(dn, s);
+}
+
+// The activation formats each routed weight format supports (the ABI checks refuse the
+// other pairs before any launch).
 template <int RF, int SF>
 hipError_t launch_experts_t(const ExpertArgs& gu, int gu_grid, size_t gu_lds,
                             const ExpertArgs& dn, int dn_grid, size_t dn_lds, hipStream_t s) {
-  hipError_t err = launch_kernel(K_GATEUP, gateup_kernel<RF, SF>, dim3(gu_grid), dim3(kBlock), gu_lds, s, gu);
-  if (err != hipSuccess) return err;
-  if (gu.afmt != A_BF16 && (err = launch_hquant(gu, s)) != hipSuccess) return err;
-  err = dn.afmt == A_BF16
-      ? launch_kernel(K_DOWN, down_kernel<RF, SF, 1>, dim3(dn_grid), dim3(kBlock), dn_lds, s, dn)
-      : launch_kernel(K_DOWN, down_kernel<RF, SF, 0>, dim3(dn_grid), dim3(kBlock), dn_lds, s, dn);
-  if (err != hipSuccess) return err;
-  return launch_combine(dn, s);
+  if (gu.afmt == A_BF16) return launch_experts_af<RF, SF, A_BF16>(gu, gu_grid, gu_lds, dn, dn_grid, dn_lds, s);
+  if constexpr (RF == W_NVFP4) {
+    if (gu.afmt == A_NVFP4_4O6)
+      return launch_experts_af<RF, SF, A_NVFP4_4O6>(gu, gu_grid, gu_lds, dn, dn_grid, dn_lds, s);
+  }
+  if constexpr (RF == W_MXFP4 || RF == W_MXFP8) {
+    if (gu.afmt == A_FP8_TOKEN)
+      return launch_experts_af<RF, SF, A_FP8_TOKEN>(gu, gu_grid, gu_lds, dn, dn_grid, dn_lds, s);
+  }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace moe

@@ -27,12 +27,13 @@ struct GemvMap {
 };
 
 constexpr int kWinRows = 64;   // most token rows one staged window of units holds
-
-// Bytes of the expert kernels' LDS tables, before the activation tile: token masks,
-// row bases, ids, the routed and shared class tables, and the staged rows' scales.
-inline constexpr int expert_lds_list_bytes(int E, int T, int k) {
-  return (E * 12 + T * k * 4 + 16 + 4 * (5 * (E < T * k ? E : T * k) + 3) + 12 * T * k +
-          4 * (5 * 1 + 3) + 12 * T + 3 * kWinRows * 4 + 15) / 16 * 16;
+// Bytes of the expert kernels' LDS before the activation tile: token masks, first
+// pairs and row bases per expert, ids, span, the routed and shared class tables, and the
+// staged rows' scales. Am = min(E, T*k) selected-expert capacity, P = T*k class rows.
+inline int expert_lds_list_bytes(int E, int T, int k) {
+  const int P = T * k, Am = E < P ? E : P;
+  return (E * 16 + P * 4 + 16 + 32 + 4 * (5 * Am + 3) + 12 * P + 4 * (5 + 3) + 12 * T + 3 * kWinRows * 4 + 15) /
+         16 * 16;
 }
 
 struct WTensor {
@@ -72,6 +73,7 @@ struct ExpertArgs {
   GemvMap rmap, smap;
   int T, H, I, Ish, E, k, has_shared, afmt;
   int max_slots;         // routed expert slots launched: min(E, T * k)
+  int sh_wgs;            // workgroups of the launch that walk the shared expert
   float* h;              // [T*k + T][hs]
   int hs;
   uint8_t* hq_codes;     // [T*k][I/2 | I]

@@ -1,0 +1,89 @@
+// Work spans of the expert launches: the cost model and where a workgroup's share of a
+// class starts and ends.
+#pragma once
+#include "device.hpp"
+#include "plan.hpp"
+
+namespace moe {
+
+// Cost parameters of one class in one kernel.
+struct ClassCost {
+  int NG, steps, cw, ct;
+};
+
+// One workgroup's part of a class: its first position, how many positions it walks,
+// and one past the last class row it touches.
+struct Span {
+  int a0, g0, s0;     // first position (b = 0)
+  int e0, n0, rb0;    // expert id, tokens and first class row of expert index a0
+  int left;           // positions (row-steps x batches) to walk; 0 = none
+  int row_limit;
+};
+
+// The expert whose cost block holds cost c, with its prefix values (a = A past the end).
+struct Located {
+  int a, n, cost, unit, row, id;
+};
+
+// Step position (g, s) of cost c in the located expert: the first position whose start
+// cost is >= c. Rolls over to the next expert (id unknown: -1) past the expert's last.
+__device__ __forceinline__ void place(Located& x, int A, const ClassCost& k, int c, int& g, int& s) {
+  g = 0;
+  s = 0;
+  if (x.a >= A) return;
+  const int G = (x.n + k.NG - 1) / k.NG;
+  const int rem = c - x.cost;
+  const int F = k.steps * (k.cw + k.ct * k.NG);
+  g = min(rem / F, G - 1);
+  const int cs = k.cw + k.ct * min(k.NG, x.n - g * k.NG);
+  s = (rem - g * F + cs - 1) / cs;
+  if (s >= k.steps) {
+    s = 0;
+    if (++g >= G) {
+      g = 0;
+      ++x.a;
+      x.unit += G;
+      x.row += x.n;
+      x.id = -1;
+    }
+  }
+}
+
+// Span from the located start and end costs (positions walked: start <= p < end).
+__device__ __forceinline__ Span make_span(Located lo, Located hi, int A, const ClassCost& k, int c_lo,
+                                          int c_hi, int NB) {
+  int g0, s0, g1, s1;
+  place(lo, A, k, c_lo, g0, s0);
+  place(hi, A, k, c_hi, g1, s1);
+  Span sp;
+  sp.a0 = lo.a; sp.g0 = g0; sp.s0 = s0;
+  sp.e0 = lo.id; sp.n0 = lo.n; sp.rb0 = lo.row;
+  const int l0 = (lo.unit + g0) * k.steps + s0, l1 = (hi.unit + g1) * k.steps + s1;
+  sp.left = l1 > l0 ? (l1 - l0) * NB : 0;
+  sp.row_limit = hi.row + g1 * k.NG + (s1 > 0 ? min(k.NG, hi.n - g1 * k.NG) : 0);
+  return sp;
+}
+
+// This workgroup's share [c_lo, c_hi) of a class total over G workgroups.
+// floor(total * b / G) in 32-bit arithmetic (total < 2^31, b <= G <= 2^16).
+__device__ __forceinline__ int share_at(int total, int b, int G) {
+  const int q = total / G, r = total - q * G;
+  return q * b + (r * b) / G;
+}
+__device__ __forceinline__ void wg_share(int total, int b, int G, int& c_lo, int& c_hi) {
+  c_lo = share_at(total, b, G);
+  c_hi = share_at(total, b + 1, G);
+}
+
+// The shared expert's span for workgroup b of G: closed form, no table reads.
+__device__ __forceinline__ Span shared_span(int T, const ClassCost& k, int NB, int b, int G) {
+  const int units = (T + k.NG - 1) / k.NG;
+  const int total = k.steps * (k.cw * units + k.ct * T);
+  int c_lo, c_hi;
+  wg_share(total, b, G, c_lo, c_hi);
+  const Located in{0, T, 0, 0, 0, 0}, end{1, T, total, units, T, -1};
+  return make_span(c_lo < total ? in : end, c_hi < total ? in : end, 1, k, c_lo, c_hi, NB);
+}
+
+
+}  // namespace moe

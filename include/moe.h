@@ -173,8 +173,9 @@ moe_status_t quantize_nvfp4_4o6(const uint16_t *x_bf16, int32_t rows, int32_t co
  * Between moe_profile_begin() and moe_profile_end(), every kernel the library launches
  * is bracketed by a start/stop event pair taken by the dispatch itself
  * (hipExtLaunchKernel), on the stream it runs on. moe_profile_end() waits for those
- * events, fills up to max_entries records (one per kernel kind: route, gateup, down,
- * quantize_nvfp4, fill) with the launch count and summed milliseconds, ends the session
+ * events, fills up to max_entries records (one per kernel kind that ran: route, topk,
+ * gateup, hquant, down, combine, quantize_nvfp4, fill) with the launch count
+ * and summed milliseconds, ends the session
  * and returns the number of records written. Meant for measurement runs; do not use
  * while capturing a stream into a graph. One process-wide session. */
 typedef struct {
