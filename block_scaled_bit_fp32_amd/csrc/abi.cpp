@@ -43,7 +43,7 @@ namespace {
 
 thread_local std::string g_err;
 
-constexpr int kMaxTokens = 64;     // token masks are 64-bit
+constexpr int kMaxTokens = 256;    // tokens per call
 constexpr int kMaxE = 1024;
 constexpr int kMaxK = 16;
 constexpr int kRouteTT = 8;

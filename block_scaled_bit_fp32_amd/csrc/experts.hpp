@@ -42,7 +42,8 @@ struct ClassTab {
 };
 
 struct ExpertLds {
-  uint64_t* tmask;  // [E] token mask of each expert
+  uint64_t* tmask;  // [E][NW] token mask of each expert, NW = ceil(T / 64) words
+  int nw;
   int* first;       // [E] first pair (t*k + j) naming each expert
   int* ebase;       // [E] first routed class row of each selected expert
   int* ids;         // [T*k] topk_ids
@@ -57,8 +58,9 @@ struct ExpertLds {
 __device__ __forceinline__ ExpertLds carve(const ExpertArgs& a, uint8_t* smem) {
   ExpertLds L;
   const int P = a.T * a.k, Am = min(a.E, P);
+  L.nw = (a.T + 63) / 64;
   L.tmask = reinterpret_cast<uint64_t*>(smem);
-  L.first = reinterpret_cast<int*>(L.tmask + a.E);
+  L.first = reinterpret_cast<int*>(L.tmask + a.E * L.nw);
   L.ebase = L.first + a.E;
   L.ids = L.ebase + a.E;
   L.nA = L.ids + P;
@@ -371,26 +373,37 @@ __device__ __forceinline__ void build_shared(const ExpertArgs& a, ClassTab& C, i
   C.A = 1;
 }
 
+// Tokens of expert e, and the rank of token t among them (token masks in LDS).
+__device__ __forceinline__ int tok_count(const ExpertLds& L, int e) {
+  int n = 0;
+  for (int w = 0; w < L.nw; ++w) n += __popcll(L.tmask[e * L.nw + w]);
+  return n;
+}
+__device__ __forceinline__ int tok_rank(const ExpertLds& L, int e, int t) {
+  int r = __popcll(L.tmask[e * L.nw + (t >> 6)] & ((1ull << (t & 63)) - 1ull));
+  for (int w = 0; w < (t >> 6); ++w) r += __popcll(L.tmask[e * L.nw + w]);
+  return r;
+}
+
 // The routed class from topk_ids (synchronizes). The selected experts are taken in the
 // order of their first pair (t*k + j): an expert's first pair is its leader, so wave 0
-// scans the T*k pairs (64 per chunk, from registers) rather than all E experts. From
-// per-chunk DPP prefix sums of tokens, units and costs it writes the compacted tables
-// and locates the span of routed workgroup b of G, which it leaves in L.span. Entries
-// outside [0, E) are ignored. Class rows are filled by build_rows.
-constexpr int kMaxPChunks = 16;   // T*k <= 1024
+// scans the T*k pairs, 64 at a time, rather than all E experts: a first pass sums the
+// tokens, units and costs of the leaders, a second takes the prefix sums (DPP scans),
+// writes the compacted tables and locates the span of routed workgroup b of G, which
+// it leaves in L.span. Entries outside [0, E) are ignored. Class rows are filled by
+// build_rows.
 __device__ __forceinline__ void build_routed(const ExpertArgs& a, const ExpertLds& L, ClassTab& C,
                                              const ClassCost& k, int NB, int b, int G) {
   const int P = a.T * a.k;
-  for (int i = threadIdx.x; i < a.E; i += kBlock) {
-    L.tmask[i] = 0ull;
-    L.first[i] = 0x7FFFFFFF;
-  }
+  for (int i = threadIdx.x; i < a.E * L.nw; i += kBlock) L.tmask[i] = 0ull;
+  for (int i = threadIdx.x; i < a.E; i += kBlock) L.first[i] = 0x7FFFFFFF;
   __syncthreads();
   for (int p = threadIdx.x; p < P; p += kBlock) {
     const int e = a.ids[p];
     L.ids[p] = e;
     if ((unsigned)e < (unsigned)a.E) {
-      atomicOr(reinterpret_cast<unsigned long long*>(&L.tmask[e]), 1ull << (p / a.k));
+      const int t = p / a.k;
+      atomicOr(reinterpret_cast<unsigned long long*>(&L.tmask[e * L.nw + (t >> 6)]), 1ull << (t & 63));
       atomicMin(&L.first[e], p);
     }
   }
@@ -398,66 +411,63 @@ __device__ __forceinline__ void build_routed(const ExpertArgs& a, const ExpertLd
   if (threadIdx.x < kWave) {
     const int lane = threadIdx.x;
     const uint64_t below = (1ull << lane) - 1ull;
-    const int nch = (P + kWave - 1) / kWave;
-    int cnt[kMaxPChunks], cst[kMaxPChunks], eid[kMaxPChunks];
-    uint64_t lead[kMaxPChunks];
+    // one pair per lane: its expert, whether it leads it, and the leader's counts
+    auto pair_at = [&](int c0, int& e, bool& ld, int& nu, int& cost) {
+      const int p = c0 + lane;
+      e = p < P ? L.ids[p] : -1;
+      ld = (unsigned)e < (unsigned)a.E && L.first[e] == p;
+      const int n = ld ? tok_count(L, e) : 0;
+      const int u = (n + k.NG - 1) / k.NG;
+      nu = n | (u << 16);
+      cost = k.steps * (k.cw * u + k.ct * n);
+    };
     int tnu = 0, tc = 0, A = 0;
-#pragma unroll
-    for (int c = 0; c < kMaxPChunks; ++c) {
-      cnt[c] = 0; cst[c] = 0; eid[c] = -1; lead[c] = 0ull;
-      if (c < nch) {
-        const int p = c * kWave + lane;
-        const int e = p < P ? L.ids[p] : -1;
-        const bool ld = (unsigned)e < (unsigned)a.E && L.first[e] == p;
-        const int n = ld ? __popcll(L.tmask[e]) : 0;
-        const int u = (n + k.NG - 1) / k.NG;
-        eid[c] = e;
-        cnt[c] = n | (u << 16);
-        cst[c] = k.steps * (k.cw * u + k.ct * n);
-        lead[c] = __ballot(ld);
-        tnu += __builtin_amdgcn_readlane(wave_incl_sum(cnt[c]), kWave - 1);
-        tc += __builtin_amdgcn_readlane(wave_incl_sum(cst[c]), kWave - 1);
-        A += __popcll(lead[c]);
-      }
+    for (int c0 = 0; c0 < P; c0 += kWave) {
+      int e, nu, cost;
+      bool ld;
+      pair_at(c0, e, ld, nu, cost);
+      tnu += __builtin_amdgcn_readlane(wave_incl_sum(nu), kWave - 1);
+      tc += __builtin_amdgcn_readlane(wave_incl_sum(cost), kWave - 1);
+      A += __popcll(__ballot(ld));
     }
     int c_lo, c_hi;
     wg_share(tc, b, G, c_lo, c_hi);
     const Located end{A, 0, tc, tnu >> 16, tnu & 0xFFFF, -1};
     Located lo = end, hi = end;
     int bnu = 0, bc = 0, ba = 0;
-#pragma unroll
-    for (int c = 0; c < kMaxPChunks; ++c) {
-      if (c < nch) {
-        const int inu = wave_incl_sum(cnt[c]), ic = wave_incl_sum(cst[c]);
-        const int xnu = bnu + inu - cnt[c], xc = bc + ic - cst[c];   // exclusive
-        const int n = cnt[c] & 0xFFFF, e = eid[c];
-        const bool ld = (lead[c] >> lane) & 1ull;
-        const int i = ba + __popcll(lead[c] & below);
-        if (ld) {
-          C.ex_id[i] = e;
-          C.ex_n[i] = n;
-          C.ex_row[i] = xnu & 0xFFFF;
-          C.ex_unit[i] = xnu >> 16;
-          C.ex_cost[i] = xc;
-          L.ebase[e] = xnu & 0xFFFF;
-        }
-        const uint64_t blo = __ballot(ld && xc <= c_lo), bhi = __ballot(ld && xc <= c_hi);
-        if (blo && c_lo < tc) {
-          const int j = 63 - __clzll(blo);
-          lo = Located{__builtin_amdgcn_readlane(i, j), __builtin_amdgcn_readlane(n, j),
-                       __builtin_amdgcn_readlane(xc, j), __builtin_amdgcn_readlane(xnu >> 16, j),
-                       __builtin_amdgcn_readlane(xnu & 0xFFFF, j), __builtin_amdgcn_readlane(e, j)};
-        }
-        if (bhi && c_hi < tc) {
-          const int j = 63 - __clzll(bhi);
-          hi = Located{__builtin_amdgcn_readlane(i, j), __builtin_amdgcn_readlane(n, j),
-                       __builtin_amdgcn_readlane(xc, j), __builtin_amdgcn_readlane(xnu >> 16, j),
-                       __builtin_amdgcn_readlane(xnu & 0xFFFF, j), __builtin_amdgcn_readlane(e, j)};
-        }
-        bnu += __builtin_amdgcn_readlane(inu, kWave - 1);
-        bc += __builtin_amdgcn_readlane(ic, kWave - 1);
-        ba += __popcll(lead[c]);
+    for (int c0 = 0; c0 < P; c0 += kWave) {
+      int e, cnu, ccost;
+      bool ld;
+      pair_at(c0, e, ld, cnu, ccost);
+      const uint64_t lead = __ballot(ld);
+      const int inu = wave_incl_sum(cnu), ic = wave_incl_sum(ccost);
+      const int xnu = bnu + inu - cnu, xc = bc + ic - ccost;   // exclusive
+      const int n = cnu & 0xFFFF;
+      const int i = ba + __popcll(lead & below);
+      if (ld) {
+        C.ex_id[i] = e;
+        C.ex_n[i] = n;
+        C.ex_row[i] = xnu & 0xFFFF;
+        C.ex_unit[i] = xnu >> 16;
+        C.ex_cost[i] = xc;
+        L.ebase[e] = xnu & 0xFFFF;
       }
+      const uint64_t blo = __ballot(ld && xc <= c_lo), bhi = __ballot(ld && xc <= c_hi);
+      if (blo && c_lo < tc) {
+        const int j = 63 - __clzll(blo);
+        lo = Located{__builtin_amdgcn_readlane(i, j), __builtin_amdgcn_readlane(n, j),
+                     __builtin_amdgcn_readlane(xc, j), __builtin_amdgcn_readlane(xnu >> 16, j),
+                     __builtin_amdgcn_readlane(xnu & 0xFFFF, j), __builtin_amdgcn_readlane(e, j)};
+      }
+      if (bhi && c_hi < tc) {
+        const int j = 63 - __clzll(bhi);
+        hi = Located{__builtin_amdgcn_readlane(i, j), __builtin_amdgcn_readlane(n, j),
+                     __builtin_amdgcn_readlane(xc, j), __builtin_amdgcn_readlane(xnu >> 16, j),
+                     __builtin_amdgcn_readlane(xnu & 0xFFFF, j), __builtin_amdgcn_readlane(e, j)};
+      }
+      bnu += __builtin_amdgcn_readlane(inu, kWave - 1);
+      bc += __builtin_amdgcn_readlane(ic, kWave - 1);
+      ba += __popcll(lead);
     }
     Span sp = make_span(lo, hi, A, k, c_lo, c_hi, NB);
     if (sp.e0 < 0 && sp.a0 < A) {   // the start rolled over to the next expert
@@ -493,7 +503,7 @@ __device__ __forceinline__ void build_rows(const ExpertArgs& a, const ExpertLds&
     const int e = L.ids[p];
     if ((unsigned)e < (unsigned)a.E) {
       const int t = p / a.k;
-      const int r = L.ebase[e] + __popcll(L.tmask[e] & ((1ull << t) - 1ull));
+      const int r = L.ebase[e] + tok_rank(L, e, t);
       C.r_tok[r] = t;
       C.r_pair[r] = p;
       C.r_exp[r] = e;

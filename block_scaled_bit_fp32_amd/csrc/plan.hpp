@@ -27,13 +27,14 @@ struct GemvMap {
 };
 
 constexpr int kWinRows = 64;   // most token rows one staged window of units holds
-// Bytes of the expert kernels' LDS before the activation tile: token masks, first
-// pairs and row bases per expert, ids, span, the routed and shared class tables, and the
-// staged rows' scales. Am = min(E, T*k) selected-expert capacity, P = T*k class rows.
+// Bytes of the expert kernels' LDS before the activation tile: token masks (ceil(T/64)
+// words per expert), first pairs and row bases per expert, ids, span, the routed and
+// shared class tables, and the staged rows' scales. Am = min(E, T*k) selected-expert
+// capacity, P = T*k class rows.
 inline int expert_lds_list_bytes(int E, int T, int k) {
-  const int P = T * k, Am = E < P ? E : P;
-  return (E * 16 + P * 4 + 16 + 32 + 4 * (5 * Am + 3) + 12 * P + 4 * (5 + 3) + 12 * T + 3 * kWinRows * 4 + 15) /
-         16 * 16;
+  const int P = T * k, Am = E < P ? E : P, nw = (T + 63) / 64;
+  return (E * 8 * nw + E * 8 + P * 4 + 16 + 32 + 4 * (5 * Am + 3) + 12 * P + 4 * (5 + 3) + 12 * T +
+          3 * kWinRows * 4 + 15) / 16 * 16;
 }
 
 struct WTensor {

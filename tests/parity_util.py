@@ -96,3 +96,40 @@ def oracle_route_only(name: str, x: np.ndarray):
     cfg = L["cfg"]
     ids, w, lg = OR.route(x, L["router_w"], L["router_bias"], cfg.k)
     return {"ids": ids, "w": w, "logits": lg, "ambiguous": OR.ambiguous_tokens(lg, cfg.k)}
+
+
+def gpu_hq_rows(dbg: dict, afmt: str, pairs) -> np.ndarray:
+    """The GPU's re-quantized SwiGLU outputs of the given pairs, dequantized (FP64)."""
+    from oracle import quant as OQ
+    codes = dbg["hq_codes"].cpu().numpy()[pairs]
+    if afmt == "nvfp4_4o6":
+        return OQ.dequant_nvfp4_rows(codes, dbg["hq_scales"].cpu().numpy()[pairs],
+                                     dbg["hq_scale"].cpu().numpy()[pairs])
+    return OQ.dequant_fp8_token(codes, dbg["hq_scale"].cpu().numpy()[pairs])
+
+
+def oracle_y_given_hq(name: str, x_bits: np.ndarray, ids: np.ndarray, w: np.ndarray,
+                      hq: np.ndarray) -> np.ndarray:
+    """The oracle's layer output when the down projections take given quantized h rows
+    hq [T, k, I] (FP64): y_t = sum_j w_tj * W2_e(tj) hq_tj + shared(x_t).
+
+    For layers that re-quantize h, the GPU's FP32 h and the oracle's FP64 h differ in
+    the last bits, which can move an element across a rounding boundary of the
+    quantizer; the codes themselves are checked bit-exact against the oracle's
+    quantizer fed the GPU's h, and this comparison then checks the rest of the layer."""
+    L = host_layer(name)
+    cfg = L["cfg"]
+    T = x_bits.shape[0]
+    y = np.zeros((T, cfg.H), dtype=np.float64)
+    pos_of = {e: p for p, e in enumerate(L["expert_ids"])}
+    for e in np.unique(ids):
+        _, W2 = OL.expert_weights(L, "routed", pos_of[int(e)], cfg.wfmt)
+        tt, jj = np.nonzero(ids == e)
+        for t, j in zip(tt, jj):
+            y[t] += w[t, j] * (W2 @ hq[t, j])
+    if cfg.has_shared and T:
+        from oracle.formats import bf16_to_f64
+        W13, W2 = OL.expert_weights(L, "shared", 0, cfg.shared_wfmt)
+        _, _, _, o = OL.mlp_rows(W13, W2, bf16_to_f64(x_bits), "bf16")
+        y += o
+    return y

@@ -66,9 +66,9 @@ def test_every_config_is_accepted_and_sized(lib, name):
 
 def test_default_deny_lists_every_reason(lib):
     s = _fake_layer(lib, "flint_w4a16", H=100, k=0, afmt=1, router_w=None)
-    st, why = _check(lib, s, 65)
+    st, why = _check(lib, s, 257)
     assert st == lib.MOE_EUNSUPPORTED
-    assert "H=100" in why and "k=0" in why and "max_tokens=65" in why
+    assert "H=100" in why and "k=0" in why and "max_tokens=257" in why
     assert "router_w is NULL" in why
     s = _fake_layer(lib, "mistral_mxfp4", afmt=1)
     st, why = _check(lib, s, 8)

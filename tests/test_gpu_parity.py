@@ -11,8 +11,8 @@ import torch
 
 import synth
 from oracle import quant as OQ
-from parity_util import (bf16_bits_to_f64, check_ids, device_layer, host_layer, oracle_layer,
-                         say, y_close)
+from parity_util import (bf16_bits_to_f64, check_ids, device_layer, gpu_hq_rows, host_layer,
+                         oracle_layer, oracle_y_given_hq, say, y_close)
 
 pytestmark = pytest.mark.gpu
 
@@ -137,11 +137,87 @@ def test_layer_parity(lib, name, T):
             rc, rs = OQ.quantize_fp8_token(h32)
             assert np.array_equal(dbg["hq_codes"].cpu().numpy(), rc)
             assert np.array_equal(dbg["hq_scale"].cpu().numpy().view(np.uint32), rs.view(np.uint32))
-    # layer output
+    # layer output (with re-quantized h: the oracle's down path takes the GPU's h codes,
+    # which are checked above)
     if np.array_equal(ids_g, ref["ids"]):
-        ok, max_abs, rel = y_close(bf16_bits_to_f64(y), ref["y"])
+        if cfg.afmt == "bf16":
+            y_ref = ref["y"]
+        else:
+            hq = gpu_hq_rows(dbg, cfg.afmt, np.arange(T * cfg.k)).reshape(T, cfg.k, cfg.I)
+            y_ref = oracle_y_given_hq(name, x_np, ref["ids"], ref["w"], hq)
+        ok, max_abs, rel = y_close(bf16_bits_to_f64(y), y_ref)
         say(f"[parity]   y max_abs/r={max_abs:.3g} rel_l2={rel:.3g}")
         assert ok, (max_abs, rel)
+
+
+# Batches past the GEMV sizes (the grouped points of the configurations): routing and the
+# quantized tokens are checked on every token against the oracle, the layer output on a
+# sample of tokens (the oracle runs per token, so a sample needs only its own experts).
+LARGE_CASES = [
+    ("flint_bf16", 64),
+    ("flint_bf16", 256),
+    ("inkling_w4a4", 32),
+    ("inkling_mxfp8", 32),
+    ("mistral_mxfp4", 64),
+    ("mistral_mxfp4_a8", 64),
+]
+
+
+@pytest.mark.parametrize("name,T", LARGE_CASES)
+def test_layer_parity_large_batch(lib, name, T):
+    from oracle import layer as OL
+    from parity_util import oracle_route_only
+    say(f"[parity] large batch {name} T={T}")
+    dl = device_layer(name)
+    cfg = dl.cfg
+    ws = lib.Workspace(dl, T)
+    x_np = synth.make_x(name, T)
+    x = _x_dev(x_np)
+    ids, w, xq = lib.route(dl, x, ws)
+    quant_h = cfg.afmt != "bf16"
+    if quant_h:
+        y, dbg = lib.expert_forward(dl, x, xq, ids, w, ws, debug=True)
+    else:
+        y = lib.expert_forward(dl, x, xq, ids, w, ws)
+    torch.cuda.synchronize()
+    ref = oracle_route_only(name, x_np)
+    ids_g = ids.cpu().numpy()
+    bad = check_ids(ids_g, ref, cfg.k)
+    assert not bad, f"top-k mismatch on tokens {bad}"
+    if cfg.afmt == "nvfp4_4o6":
+        rc, rs, rg, _ = OQ.quantize_nvfp4_4o6(synth_bf16_to_f32(x_np))
+        parts = lib.split_xq(dl, xq, T)
+        assert np.array_equal(parts["codes"].cpu().numpy(), rc)
+        assert np.array_equal(parts["scales"].cpu().numpy(), rs)
+    elif cfg.afmt == "fp8_token":
+        rc, rs = OQ.quantize_fp8_token(synth_bf16_to_f32(x_np))
+        parts = lib.split_xq(dl, xq, T)
+        assert np.array_equal(parts["codes"].cpu().numpy(), rc)
+    sample = sorted({0, T // 3, (2 * T) // 3, T - 1})
+    sample = [t for t in sample if np.array_equal(ids_g[t], ref["ids"][t])]
+    assert sample, "no sampled token routed like the oracle"
+    if quant_h:
+        # the GPU's h codes of the sampled tokens: bit-exact against the oracle's quantizer
+        # fed the GPU's h; then the rest of the layer against the oracle given those codes
+        pairs = np.array([t * cfg.k + j for t in sample for j in range(cfg.k)])
+        h32 = dbg["h"].cpu().numpy()[pairs, :cfg.I]
+        if cfg.afmt == "nvfp4_4o6":
+            rc, rs, rg, _ = OQ.quantize_nvfp4_4o6(h32)
+        else:
+            rc, rg = OQ.quantize_fp8_token(h32)
+        assert np.array_equal(dbg["hq_codes"].cpu().numpy()[pairs], rc)
+        hq = gpu_hq_rows(dbg, cfg.afmt, pairs).reshape(len(sample), cfg.k, cfg.I)
+        y_ref = oracle_y_given_hq(name, x_np[sample], ref["ids"][sample], ref["w"][sample], hq)
+    else:
+        y_ref = OL.moe_layer(host_layer(name), x_np[sample])["y"]
+    yg = bf16_bits_to_f64(y)[sample]
+    ok, max_abs, rel = y_close(yg, y_ref)
+    say(f"[parity]   sampled tokens {sample}: y max_abs/r={max_abs:.3g} rel_l2={rel:.3g}")
+    assert ok, (max_abs, rel)
+
+
+def synth_bf16_to_f32(x_bits: np.ndarray) -> np.ndarray:
+    return (x_bits.astype(np.uint32) << 16).view(np.float32)
 
 
 def test_repeat_calls_are_bit_identical_and_workspace_is_reusable(lib):
