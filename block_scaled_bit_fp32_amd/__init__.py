@@ -25,7 +25,7 @@ LIB_PATH = os.path.join(_HERE, "libmoe_mi355x.so")
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_ELAUNCH = 0, -1, -2, -3, -4
 WFMT = {"bf16": 0, "nvfp4": 1, "mxfp4": 2, "mxfp8": 3}
 AFMT = {"bf16": 0, "nvfp4_4o6": 1, "fp8_token": 2}
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 
 class MoeError(RuntimeError):
@@ -48,7 +48,10 @@ class LayerT(ctypes.Structure):
 
 class DebugT(ctypes.Structure):
     _fields_ = [("h", ctypes.c_void_p), ("hq_codes", ctypes.c_void_p),
-                ("hq_scales", ctypes.c_void_p), ("hq_scale", ctypes.c_void_p)]
+                ("hq_scales", ctypes.c_void_p), ("hq_scale", ctypes.c_void_p), ("path", ctypes.c_int32)]
+
+
+PATH_AUTO, PATH_GEMV, PATH_GROUPED = 0, 1, 2
 
 
 class KernelTimeT(ctypes.Structure):
@@ -256,15 +259,17 @@ def split_xq(layer: DeviceLayer, xq: torch.Tensor, T: int) -> dict:
 
 
 def expert_forward(layer: DeviceLayer, x: torch.Tensor, xq, ids: torch.Tensor, w: torch.Tensor,
-                   ws: Workspace, debug: bool = False, y: Optional[torch.Tensor] = None):
+                   ws: Workspace, debug: bool = False, y: Optional[torch.Tensor] = None,
+                   path: int = PATH_AUTO):
     """moe_expert_forward: returns y (BF16 [T,H]); with debug=True also a dict of h and
-    the quantized h fields (pair p = t*k + j; rows T*k + t are the shared expert)."""
+    the quantized h fields (pair p = t*k + j; rows T*k + t are the shared expert).
+    ``path`` picks the expert kernels (PATH_AUTO, PATH_GEMV, PATH_GROUPED)."""
     x = _bits16(x)
     T = x.shape[0]
     cfg = layer.cfg
     if y is None:
         y = torch.empty((T, cfg.H), dtype=torch.bfloat16, device=x.device)
-    dbg = None
+    dbg = DebugT(None, None, None, None, path) if path != PATH_AUTO else None
     dd = {}
     if debug:
         rows = T * cfg.k + (T if cfg.has_shared else 0)
@@ -279,7 +284,7 @@ def expert_forward(layer: DeviceLayer, x: torch.Tensor, xq, ids: torch.Tensor, w
             dd["hq_codes"] = _aligned_empty(P * cfg.I, x.device).view(P, cfg.I)
             dd["hq_scale"] = torch.empty(P, dtype=torch.float32, device=x.device)
         dbg = DebugT(_ptr(dd.get("h")), _ptr(dd.get("hq_codes")), _ptr(dd.get("hq_scales")),
-                     _ptr(dd.get("hq_scale")))
+                     _ptr(dd.get("hq_scale")), path)
     _check(_lib.moe_expert_forward(ctypes.byref(layer.struct), x.data_ptr(), _ptr(xq), T,
                                    ids.data_ptr(), w.data_ptr(), y.data_ptr(), ws.ptr, ws.nbytes,
                                    ctypes.byref(dbg) if dbg is not None else None, _stream()))

@@ -104,7 +104,31 @@ struct Plan {
   GemvMap gu_r, gu_s, dn_r, dn_s;
   int max_slots;
   size_t gu_lds, dn_lds, list_bytes, gu_tile, dn_tile;
+  bool grouped;                       // batches of kGroupedMinT tokens and up
+  GroupMap gu_rg, gu_sg, dn_rg, dn_sg;
 };
+
+constexpr int kGroupedMinT = 32;      // the grouped (MFMA) kernels from this batch on
+constexpr int kGroupTok = 32;         // tokens per unit in the grouped kernels
+
+// Grouped map of one weight class: rows of K elements, `rows_per_tile` rows (or
+// intermediate indices for gate/up) per row tile of `tile_of` rows, FP32 activations
+// when split. False if the shape does not tile.
+bool plan_group(int fmt, int K, int rows, int rows_per_tile, bool split, GroupMap& g) {
+  const int KS = group_ks(fmt);
+  if (K % KS || rows % rows_per_tile) return false;
+  g.KS = KS;
+  g.NS = K / KS;
+  g.steps = rows / rows_per_tile;
+  g.NG = kGroupTok;
+  // a row tile moves NS stages of 4 waves x 64 bytes x 64 lanes of weights (cw: 256-byte
+  // units); each token adds a share of MFMA and staging work
+  g.cw = g.NS * 64;
+  g.ct = g.NS * (split ? 4 : 2);
+  g.split = split ? 1 : 0;
+  g.tstride = KS * (split ? 4 : 2) + 16;
+  return true;
+}
 
 // Weight bytes per element, times 2 (FP4 1, MXFP8 2, BF16 4; block scales ignored).
 int wbytes_x2(int fmt) { return fmt == W_BF16 ? 4 : (fmt == W_MXFP8 ? 2 : 1); }
@@ -120,7 +144,7 @@ void set_costs(GemvMap& m, int fmt, int K) {
 
 // Row maps of both expert kernels and their LDS needs. Gate/up row-steps cover RS / 2
 // intermediate indices (gate and up rows), down row-steps RS hidden rows.
-bool make_plan(const moe_layer_t& L, int T, Plan& p) {
+bool make_plan(const moe_layer_t& L, int T, int path, Plan& p) {
   const int Ish = L.has_shared ? L.I_shared : L.I;
   const int sfmt = L.has_shared ? L.shared_wfmt : L.wfmt;
   const int nt = std::max(1, T);
@@ -159,18 +183,45 @@ bool make_plan(const moe_layer_t& L, int T, Plan& p) {
   p.dn_tile = tile(p.dn_r, L.I, p.dn_s, Ish);
   p.gu_lds = p.list_bytes + p.gu_tile;
   p.dn_lds = p.list_bytes + p.dn_tile;
+  // grouped kernels: gate/up tiles of 64 intermediate indices, down tiles of 128 rows
+  // automatic choice: from kGroupedMinT tokens on, when units hold many tokens
+  const bool want = path == MOE_PATH_GROUPED ||
+                    (path == MOE_PATH_AUTO && T >= kGroupedMinT && (L.has_shared || T * L.k >= L.E));
+  p.grouped = want && plan_group(L.wfmt, L.H, L.I, 64, false, p.gu_rg) &&
+              plan_group(sfmt, L.H, Ish, 64, false, p.gu_sg) &&
+              plan_group(L.wfmt, L.I, L.H, 128, L.afmt == A_BF16, p.dn_rg) &&
+              plan_group(sfmt, Ish, L.H, 128, true, p.dn_sg);
+  if (p.grouped) {
+    auto gbound = [&](const GroupMap& g, int units) {
+      return (int64_t)units * g.steps * (g.cw + (int64_t)g.ct * g.NG);
+    };
+    if (gbound(p.gu_rg, ur) + gbound(p.gu_sg, us) > (1ll << 30) || gbound(p.dn_rg, ur) + gbound(p.dn_sg, us) > (1ll << 30))
+      p.grouped = false;
+  }
+  if (p.grouped) {
+    auto gtile = [&](const GroupMap& r, const GroupMap& s) {
+      return align_up((size_t)2 * kGroupTok * std::max(r.tstride, L.has_shared ? s.tstride : 0), 16);
+    };
+    p.gu_tile = gtile(p.gu_rg, p.gu_sg);
+    p.dn_tile = gtile(p.dn_rg, p.dn_sg);
+    p.gu_lds = p.list_bytes + p.gu_tile;
+    p.dn_lds = p.list_bytes + p.dn_tile;
+  }
   return true;
 }
 
 // Workgroups of a G-workgroup expert launch that walk the shared expert: its share of
 // the summed cost, with the routed cost bounded by min(E, T*k) one-group experts (the
-// routing is not known on the host). At least one workgroup each.
-int shared_wgs(const moe_layer_t& L, int T, const GemvMap& s, int steps_s, const GemvMap& r, int steps_r,
-               int G) {
+// routing is not known on the host). At least one workgroup each. Costs per class:
+// units of NG tokens, `steps` steps each, a step costing cw + ct * tokens.
+struct CostQ {
+  int NG, steps, cw, ct;
+};
+int shared_wgs(const moe_layer_t& L, int T, const CostQ& s, const CostQ& r, int G) {
   if (!L.has_shared || G < 2) return 0;
-  const int64_t cs = (int64_t)steps_s * (s.cw * (int64_t)((T + s.NG - 1) / s.NG) + (int64_t)s.ct * T);
+  const int64_t cs = (int64_t)s.steps * (s.cw * (int64_t)((T + s.NG - 1) / s.NG) + (int64_t)s.ct * T);
   const int64_t pairs = (int64_t)T * L.k, ur = std::min<int64_t>(L.E, pairs);
-  const int64_t cr = (int64_t)steps_r * (r.cw * ur + r.ct * pairs);
+  const int64_t cr = (int64_t)r.steps * (r.cw * ur + r.ct * pairs);
   const int64_t g = (G * cs + (cs + cr) / 2) / (cs + cr);
   return (int)std::min<int64_t>(std::max<int64_t>(g, 1), G - 1);
 }
@@ -241,7 +292,7 @@ std::string check_layer(const moe_layer_t* L, int max_tokens) {
   if (L->has_shared == 1 && sf_ok) { check_w(L->sh13, L->shared_wfmt, "sh13"); check_w(L->sh2, L->shared_wfmt, "sh2"); }
   if (why.empty()) {
     Plan p;
-    if (!make_plan(*L, std::max(1, max_tokens), p))
+    if (!make_plan(*L, std::max(1, max_tokens), MOE_PATH_AUTO, p))
       add("no workgroup row mapping fits these sizes (H, I, I_shared) and formats");
   }
   return why;
@@ -406,8 +457,12 @@ moe_status_t moe_expert_forward(const moe_layer_t* L, const uint16_t* x_bf16, co
   WsLayout w;
   if ((st = check_ws(*L, T, ws, ws_bytes, w)) != MOE_OK) return st;
   const int resident = kWgPerCu * device_cus();
+  const int path = dbg ? dbg->path : MOE_PATH_AUTO;
+  if (path < MOE_PATH_AUTO || path > MOE_PATH_GROUPED) return set_err(MOE_EINVAL, "dbg->path is not a moe_path_t");
   Plan p;
-  if (!make_plan(*L, T, p)) return set_err(MOE_EUNSUPPORTED, "no launch plan");
+  if (!make_plan(*L, T, path, p)) return set_err(MOE_EUNSUPPORTED, "no launch plan");
+  if (path == MOE_PATH_GROUPED && !p.grouped)
+    return set_err(MOE_EUNSUPPORTED, "grouped kernels need K and rows that tile (H, I multiples of the stage and tile sizes)");
   uint8_t* base = static_cast<uint8_t*>(ws);
   const int Ish = L->has_shared ? L->I_shared : L->I;
   const int sfmt = L->has_shared ? L->shared_wfmt : L->wfmt;
@@ -457,8 +512,18 @@ moe_status_t moe_expert_forward(const moe_layer_t* L, const uint16_t* x_bf16, co
   // persistent launches: every workgroup takes an equal share of its class's cost
   const int gu_grid = resident, dn_grid = resident;
   const int Ish_ = L->has_shared ? L->I_shared : L->I;
-  gu.sh_wgs = shared_wgs(*L, T, p.gu_s, Ish_ / (p.gu_s.RS / 2), p.gu_r, L->I / (p.gu_r.RS / 2), gu_grid);
-  dn.sh_wgs = shared_wgs(*L, T, p.dn_s, L->H / p.dn_s.RS, p.dn_r, L->H / p.dn_r.RS, dn_grid);
+  gu.grouped = dn.grouped = p.grouped ? 1 : 0;
+  if (p.grouped) {
+    gu.rgm = p.gu_rg; gu.sgm = p.gu_sg;
+    dn.rgm = p.dn_rg; dn.sgm = p.dn_sg;
+    auto q = [](const GroupMap& g) { return CostQ{g.NG, g.steps * g.NS, g.cw / g.NS, g.ct / g.NS}; };
+    gu.sh_wgs = shared_wgs(*L, T, q(p.gu_sg), q(p.gu_rg), gu_grid);
+    dn.sh_wgs = shared_wgs(*L, T, q(p.dn_sg), q(p.dn_rg), dn_grid);
+  } else {
+    auto q = [](const GemvMap& m, int steps) { return CostQ{m.NG, steps, m.cw, m.ct}; };
+    gu.sh_wgs = shared_wgs(*L, T, q(p.gu_s, Ish_ / (p.gu_s.RS / 2)), q(p.gu_r, L->I / (p.gu_r.RS / 2)), gu_grid);
+    dn.sh_wgs = shared_wgs(*L, T, q(p.dn_s, L->H / p.dn_s.RS), q(p.dn_r, L->H / p.dn_r.RS), dn_grid);
+  }
   if (launch_experts(gu, gu_grid, p.gu_lds, dn, dn_grid, p.dn_lds, stream) != hipSuccess)
     return set_err(MOE_ELAUNCH, "expert kernel launch failed");
   return MOE_OK;

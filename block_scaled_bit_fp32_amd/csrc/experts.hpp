@@ -894,12 +894,21 @@ hipError_t launch_combine(const ExpertArgs& a, hipStream_t s);
 
 // gate/up -> (h re-quantization) -> down -> combine, in stream order.
 template <int RF, int SF, int AF>
+__global__ void ggateup_kernel(ExpertArgs a);
+template <int RF, int SF, int AF>
+__global__ void gdown_kernel(ExpertArgs a);
+
+template <int RF, int SF, int AF>
 hipError_t launch_experts_af(const ExpertArgs& gu, int gu_grid, size_t gu_lds,
                              const ExpertArgs& dn, int dn_grid, size_t dn_lds, hipStream_t s) {
-  hipError_t err = launch_kernel(K_GATEUP, gateup_kernel<RF, SF, AF>, dim3(gu_grid), dim3(kBlock), gu_lds, s, gu);
+  hipError_t err = gu.grouped
+      ? launch_kernel(K_GATEUP, ggateup_kernel<RF, SF, AF>, dim3(gu_grid), dim3(kBlock), gu_lds, s, gu)
+      : launch_kernel(K_GATEUP, gateup_kernel<RF, SF, AF>, dim3(gu_grid), dim3(kBlock), gu_lds, s, gu);
   if (err != hipSuccess) return err;
   if (AF != A_BF16 && (err = launch_hquant(gu, s)) != hipSuccess) return err;
-  err = launch_kernel(K_DOWN, down_kernel<RF, SF, AF>, dim3(dn_grid), dim3(kBlock), dn_lds, s, dn);
+  err = dn.grouped
+      ? launch_kernel(K_DOWN, gdown_kernel<RF, SF, AF>, dim3(dn_grid), dim3(kBlock), dn_lds, s, dn)
+      : launch_kernel(K_DOWN, down_kernel<RF, SF, AF>, dim3(dn_grid), dim3(kBlock), dn_lds, s, dn);
   if (err != hipSuccess) return err;
   return launch_combine(dn, s);
 }

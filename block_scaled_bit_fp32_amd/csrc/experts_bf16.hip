@@ -1,5 +1,5 @@
 // Expert kernels for BF16 routed weights (shared expert: BF16).
-#include "experts.hpp"
+#include "grouped.hpp"
 
 namespace moe {
 

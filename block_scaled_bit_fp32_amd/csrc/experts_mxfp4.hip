@@ -1,5 +1,5 @@
 // Expert kernels for MXFP4 routed weights (shared expert: MXFP4, BF16).
-#include "experts.hpp"
+#include "grouped.hpp"
 
 namespace moe {
 

@@ -1,5 +1,5 @@
 // Expert kernels for MXFP8 routed weights (shared expert: MXFP8, BF16).
-#include "experts.hpp"
+#include "grouped.hpp"
 
 namespace moe {
 

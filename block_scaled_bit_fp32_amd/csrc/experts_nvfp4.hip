@@ -1,5 +1,5 @@
 // Expert kernels for NVFP4 routed weights (shared expert: NVFP4, BF16).
-#include "experts.hpp"
+#include "grouped.hpp"
 
 namespace moe {
 

@@ -1,0 +1,329 @@
+// Grouped expert kernels for batches of 32 tokens and more (gfx950 MFMA).
+//
+// The same work split as the GEMV kernels (experts.hpp: shared-expert workgroups,
+// per-workgroup cost spans over the units of the selected experts), with units of up
+// to 32 tokens, so an expert's weights are read once per 32 of its tokens instead of
+// once per 4. Each wave owns 32 weight rows of a row tile and computes them against
+// the unit's (up to) 32 tokens with v_mfma_f32_32x32x16_bf16:
+//   A (32 rows x 16 K): weights, decoded exactly to BF16 in registers (E2M1 and E4M3
+//     values times their block scale have at most 6 significant bits);
+//   B (16 K x 32 tokens): activations, staged per K stage in LDS as BF16 (exact for
+//     BF16 tokens and for decoded NVFP4 / FP8 activations), or as FP32 for the down
+//     projection of FP32 h, fed as three BF16 parts hi + mid + lo that sum to h exactly;
+//   accumulation in FP32. Lane l holds row l % 32 of A and token l % 32 of B and takes
+//   its K elements from half l / 32 of the stage; A and B use the same K order, which
+//   is all the dot products need.
+// A lane holds 64 bytes of weights per stage, loaded one stage ahead (two register
+// sets alternate), and the next stage's activations and scales are loaded before those
+// weights and stored to the other LDS buffer after the current stage's MFMAs.
+#pragma once
+#include "experts.hpp"
+
+namespace moe {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4v_t __attribute__((ext_vector_type(4)));
+
+constexpr int kGTok = 32;        // tokens per unit (MFMA N)
+constexpr int kGActSlots = 8;    // 16-byte activation slots per thread per stage
+
+// One stage's raw operands of this lane: weights, their block scales, and the
+// activation slots this thread stages for the workgroup.
+struct GStage {
+  uint4 w[4];
+  uint2 sc;
+  uint4 act[kGActSlots];
+  float tsc;                     // the scale of this lane's token (stage 0 of a tile)
+  float gs[2];                   // the expert's global weight scales (stage 0)
+};
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) {
+  return __builtin_bit_cast(bf16x8_t, make_uint4(v.x, v.y, v.z, v.w));
+}
+__device__ __forceinline__ bf16x8_t pack_bf16x8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  return __builtin_bit_cast(bf16x8_t, make_uint4(a, b, c, d));
+}
+// Upper 16 bits of two FP32 values as a BF16 pair (exact when the values fit BF16).
+__device__ __forceinline__ uint32_t trunc_pair(float lo, float hi) {
+  return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);
+}
+
+// A fragment of MFMA step s: the lane's weight elements [8s, 8s + 8) of the stage, as BF16.
+template <int FMT>
+__device__ __forceinline__ bf16x8_t weight_frag(const GStage& g, int s) {
+  if constexpr (FMT == W_BF16) {
+    return as_bf16x8(g.w[s]);
+  } else if constexpr (FMT == W_MXFP8) {
+    // 8 E4M3 bytes [8s, 8s + 8); E8M0 scale per 32 elements
+    const uint4 q = g.w[s >> 1];
+    const uint32_t lo = (s & 1) ? q.z : q.x, hi = (s & 1) ? q.w : q.y;
+    const float sc = e8m0_to_f32((g.sc.x >> (8 * (s >> 2))) & 0xFFu);
+    return pack_bf16x8(as_u32(fp8x2_to_bf16<false>(lo, sc)), as_u32(fp8x2_to_bf16<true>(lo, sc)),
+                       as_u32(fp8x2_to_bf16<false>(hi, sc)), as_u32(fp8x2_to_bf16<true>(hi, sc)));
+  } else {
+    // 8 E2M1 nibbles = bytes [4s, 4s + 4)
+    const uint4 q = g.w[s >> 2];
+    const uint32_t word = (s & 3) == 0 ? q.x : (s & 3) == 1 ? q.y : (s & 3) == 2 ? q.z : q.w;
+    if constexpr (FMT == W_MXFP4) {
+      const float sc = e8m0_to_f32((g.sc.x >> (8 * (s >> 2))) & 0xFFu);
+      return pack_bf16x8(as_u32(fp4x2_to_bf16<0>(word, sc)), as_u32(fp4x2_to_bf16<1>(word, sc)),
+                         as_u32(fp4x2_to_bf16<2>(word, sc)), as_u32(fp4x2_to_bf16<3>(word, sc)));
+    } else {   // NVFP4: E4M3 scale per 16 elements, applied in FP32 (exact), then truncated
+      const uint32_t sb = (s >> 1) < 4 ? (g.sc.x >> (8 * (s >> 1))) : (g.sc.y >> (8 * ((s >> 1) - 4)));
+      const float S = e4m3_to_f32(sb & 0xFFu);
+      const f32x2_t v0 = fp4x2_to_f32<0>(word, 1.0f), v1 = fp4x2_to_f32<1>(word, 1.0f);
+      const f32x2_t v2 = fp4x2_to_f32<2>(word, 1.0f), v3 = fp4x2_to_f32<3>(word, 1.0f);
+      return pack_bf16x8(trunc_pair(v0.x * S, v0.y * S), trunc_pair(v1.x * S, v1.y * S),
+                         trunc_pair(v2.x * S, v2.y * S), trunc_pair(v3.x * S, v3.y * S));
+    }
+  }
+}
+
+// Walks one workgroup's span of a class. `row_of(e, tile, r)` is the weight row of
+// this wave's row r (0..31) of row tile `tile` of expert e; `op` is the class's
+// GateupOps / DownOps (activation loads and scales); `sink(cx, tile, acc, tsc, gs)`
+// consumes a finished row tile (lane token l % 32, rows per the MFMA layout).
+template <int FMT, bool SPLIT, class Ops, class RowOf, class Sink>
+__device__ __forceinline__ void walk_grouped(const WTensor& W, const GroupMap& gm, const ExpertLds& L,
+                                             const ClassTab& C, const Span& sp, const Ops& op, RowOf row_of,
+                                             Sink sink) {
+  constexpr int PER = SPLIT ? 4 : 8;      // staged elements per 16-byte slot
+  constexpr int KS = group_ks(FMT);
+  constexpr int SPR = KS / PER;           // slots per staged token row
+  constexpr int NSTEP = KS / 16;          // MFMA steps per stage
+  static_assert(kGTok * SPR <= kGActSlots * kBlock, "stage does not fit the staging slots");
+  if (sp.left <= 0) return;
+  int left = sp.left;
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int half = lane >> 5, lr = lane & 31;
+  const ClassCost k{gm.NG, gm.steps, gm.cw, gm.ct};
+  auto advance = [&](Cursor& p) {
+    if (++p.b < gm.NS) return;
+    p.b = 0;
+    if (++p.s < k.steps) return;
+    p.s = 0;
+    if (++p.g * k.NG < p.n) return;
+    p.g = 0;
+    if (++p.a < C.A) {
+      p.e = uni(C.ex_id[p.a]);
+      p.n = uni(C.ex_n[p.a]);
+      p.rb = uni(C.ex_row[p.a]);
+    }
+  };
+  // loads of one position: activation slots and (stage 0) scales first, weights last
+  auto fetch = [&](const Cursor& p, GStage& g) {
+    const int crow = p.rb + p.g * k.NG, n = min(k.NG, p.n - p.g * k.NG);
+#pragma unroll
+    for (int i = 0; i < kGActSlots; ++i) {
+      const int u = i * kBlock + threadIdx.x;
+      const int j = u / SPR, c = u % SPR;
+      g.act[i] = make_uint4(0u, 0u, 0u, 0u);
+      if (u < kGTok * SPR && j < n)
+        g.act[i] = op.ld(C.r_tok[crow + j], C.r_pair[crow + j], p.b * KS + c * PER);
+    }
+    if (p.b == 0) {
+      g.tsc = lr < n ? op.tsc(C.r_tok[crow + lr], C.r_pair[crow + lr]) : 0.0f;
+      g.gs[0] = op.gs(p.e, 0);
+      g.gs[1] = op.gs(p.e, 1);
+    }
+    const int64_t row = row_of(p.e, p.s, lr);
+    const int k0 = p.b * KS + half * (KS / 2);
+    const uint8_t* wp = W.codes + row * W.code_row_bytes + elem_byte<FMT>(k0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) g.w[i] = load_stream16(wp + 16 * i);
+    if constexpr (FMT == W_NVFP4) {
+      g.sc = *reinterpret_cast<const uint2*>(W.scales + row * W.scale_row_bytes + (k0 >> 4));
+    } else if constexpr (FMT == W_MXFP4) {
+      g.sc = make_uint2(*reinterpret_cast<const uint32_t*>(W.scales + row * W.scale_row_bytes + (k0 >> 5)), 0u);
+    } else if constexpr (FMT == W_MXFP8) {
+      g.sc = make_uint2(*reinterpret_cast<const uint16_t*>(W.scales + row * W.scale_row_bytes + (k0 >> 5)), 0u);
+    } else {
+      g.sc = make_uint2(0u, 0u);
+    }
+  };
+  // stores of one position's staged data into LDS buffer `buf`
+  float* s_tsc = L.w_tsc;       // [32] token scales of the current row tile
+  float* s_gs = L.w_gs;         // [2] its expert's global scales
+  auto store = [&](const Cursor& p, const GStage& g, int buf) {
+    uint8_t* tile = L.tile + buf * (kGTok * gm.tstride);
+#pragma unroll
+    for (int i = 0; i < kGActSlots; ++i) {
+      const int u = i * kBlock + threadIdx.x;
+      if (u < kGTok * SPR)
+        *reinterpret_cast<uint4*>(tile + (u / SPR) * gm.tstride + (u % SPR) * 16) = op.cv(g.act[i]);
+    }
+    if (p.b == 0) {
+      if (wave == 0 && half == 0) s_tsc[lr] = g.tsc;
+      if (threadIdx.x == 0) { s_gs[0] = g.gs[0]; s_gs[1] = g.gs[1]; }
+    }
+  };
+  f32x16_t acc;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+  int buf = 0;
+  auto do_step = [&](auto pf, const Cursor& p, GStage& cur, GStage& nxt, Cursor& np) {
+    if constexpr (decltype(pf)::value) {
+      np = p;
+      advance(np);
+      fetch(np, nxt);
+    }
+    const uint8_t* tile = L.tile + buf * (kGTok * gm.tstride) + lr * gm.tstride;
+#pragma unroll
+    for (int s = 0; s < NSTEP; ++s) {
+      const bf16x8_t a = weight_frag<FMT>(cur, s);
+      const int kk = half * (KS / 2) + 8 * s;   // K offset of this lane's B fragment
+      if constexpr (SPLIT) {
+        const float4 b0 = *reinterpret_cast<const float4*>(tile + kk * 4);
+        const float4 b1 = *reinterpret_cast<const float4*>(tile + kk * 4 + 16);
+        const float v[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+        uint32_t hi[4], mi[4], lo[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float x0 = v[2 * q], x1 = v[2 * q + 1];
+          const float h0 = __uint_as_float(__float_as_uint(x0) & 0xFFFF0000u);
+          const float h1 = __uint_as_float(__float_as_uint(x1) & 0xFFFF0000u);
+          const float r0 = x0 - h0, r1 = x1 - h1;
+          const float m0 = __uint_as_float(__float_as_uint(r0) & 0xFFFF0000u);
+          const float m1 = __uint_as_float(__float_as_uint(r1) & 0xFFFF0000u);
+          hi[q] = trunc_pair(h0, h1);
+          mi[q] = trunc_pair(m0, m1);
+          lo[q] = trunc_pair(r0 - m0, r1 - m1);
+        }
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pack_bf16x8(hi[0], hi[1], hi[2], hi[3]), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pack_bf16x8(mi[0], mi[1], mi[2], mi[3]), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pack_bf16x8(lo[0], lo[1], lo[2], lo[3]), acc, 0, 0, 0);
+      } else {
+        const bf16x8_t b = as_bf16x8(*reinterpret_cast<const uint4*>(tile + kk * 2));
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
+      }
+    }
+    if (p.b == gm.NS - 1) {   // row tile done
+      const int crow = p.rb + p.g * k.NG, n = min(k.NG, p.n - p.g * k.NG);
+      sink(UnitCtx{crow, 0, n}, p.s, acc, s_tsc[lr], s_gs[0], s_gs[1]);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+    }
+    if constexpr (decltype(pf)::value) {
+      if (np.b == 0) lds_barrier();   // every wave has read this tile's scales
+      store(np, nxt, buf ^ 1);
+    }
+    lds_barrier();
+    buf ^= 1;
+  };
+  Cursor pa{sp.a0, sp.g0, sp.s0, 0, sp.e0, sp.n0, sp.rb0}, pb = pa;
+  GStage A, B;
+  fetch(pa, A);
+  store(pa, A, 0);
+  lds_barrier();
+  using Yes = std::integral_constant<bool, true>;
+  using No = std::integral_constant<bool, false>;
+  while (true) {
+    if (left == 1) { do_step(No{}, pa, A, B, pb); break; }
+    do_step(Yes{}, pa, A, B, pb);
+    if (left == 2) { do_step(No{}, pb, B, A, pa); break; }
+    do_step(Yes{}, pb, B, A, pa);
+    left -= 2;
+  }
+}
+
+// Output row (0..31) of accumulator register r on this lane (32x32 MFMA layout).
+__device__ __forceinline__ int acc_row(int r, int half) { return 8 * (r >> 2) + 4 * half + (r & 3); }
+
+// ============================================================ grouped gate/up kernel
+// Row tile t of an expert: intermediate indices [64 t, 64 t + 64), 16 per wave; a wave's
+// rows 0..15 are gate rows, 16..31 the matching up rows, so accumulator registers r and
+// r + 8 of a lane hold the gate and up value of the same (index, token).
+template <int FMT, int AF>
+__device__ __forceinline__ void ggateup_walk(const ExpertArgs& a, const ExpertLds& L, const ClassTab& C,
+                                             bool routed, const Span& sp) {
+  const WTensor& W = routed ? a.rw : a.sw;
+  const GemvMap& m = routed ? a.rmap : a.smap;
+  const GroupMap& gm = routed ? a.rgm : a.sgm;
+  const int Iexp = routed ? a.I : a.Ish;
+  const GateupOps<AF> op{a.x, a.xq_codes, a.xq_scales, a.xq_scale, W.gscale, W.gs_per_expert, W.rows, Iexp,
+                         4 * m.G, a.H, a.hs, a.h, a.dbg_h, L.w_gs, L.w_tsc, C.r_pair};
+  const int wave = threadIdx.x / kWave, half = (threadIdx.x & (kWave - 1)) >> 5, lr = threadIdx.x & 31;
+  auto row_of = [&](int e, int t, int r) -> int64_t {
+    const int i = 64 * t + 16 * wave + (r & 15);
+    return (int64_t)e * W.rows + (r < 16 ? i : Iexp + i);
+  };
+  auto sink = [&](const UnitCtx& cx, int t, const f32x16_t& acc, float ts, float gsg, float gsu) {
+    if (lr >= cx.n) return;
+    const int64_t off = (int64_t)C.r_pair[cx.crow + lr] * a.hs + 64 * t + 16 * wave;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const float gv = acc[r] * gsg * ts, uv = acc[r + 8] * gsu * ts;
+      const float hv = gv / (1.0f + expf(-gv)) * uv;
+      a.h[off + acc_row(r, half)] = hv;
+      if (a.dbg_h) a.dbg_h[off + acc_row(r, half)] = hv;
+    }
+  };
+  walk_grouped<FMT, false>(W, gm, L, C, sp, op, row_of, sink);
+}
+
+template <int RF, int SF, int AF>
+__global__ void __launch_bounds__(kBlock, 2) ggateup_kernel(ExpertArgs a) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  ExpertLds L = carve(a, smem);
+  const bool shared = (int)blockIdx.x < a.sh_wgs;
+  const GroupMap& gm = shared ? a.sgm : a.rgm;
+  const ClassCost k{gm.NG, gm.steps, gm.cw, gm.ct};
+  Span sp;
+  if (shared) {
+    build_shared(a, L.sh, k.NG, k.steps, k.cw, k.ct);
+    lds_barrier();
+    sp = shared_span(a.T, k, gm.NS, blockIdx.x, a.sh_wgs);
+  } else {
+    build_routed(a, L, L.rt, k, gm.NS, blockIdx.x - a.sh_wgs, gridDim.x - a.sh_wgs);
+    build_rows(a, L, L.rt);
+    sp = read_span(L);
+  }
+  if (shared) ggateup_walk<SF, A_BF16>(a, L, L.sh, false, sp);
+  else ggateup_walk<RF, AF>(a, L, L.rt, true, sp);
+}
+
+// =============================================================== grouped down kernel
+// Row tile t: hidden rows [128 t, 128 t + 128), 32 per wave.
+template <int FMT, int AF>
+__device__ __forceinline__ void gdown_walk(const ExpertArgs& a, const ExpertLds& L, const ClassTab& C,
+                                           bool routed, const Span& sp) {
+  const WTensor& W = routed ? a.rw : a.sw;
+  const GemvMap& m = routed ? a.rmap : a.smap;
+  const GroupMap& gm = routed ? a.rgm : a.sgm;
+  const DownOps<AF> op{a.h, a.hq_codes, a.hq_scales, a.hq_scale, W.gscale, W.gs_per_expert, W.rows,
+                       routed ? a.I : a.Ish, m.RS, a.H, a.hs, a.o, L.w_gs, L.w_tsc, C.r_pair};
+  const int wave = threadIdx.x / kWave, half = (threadIdx.x & (kWave - 1)) >> 5, lr = threadIdx.x & 31;
+  auto row_of = [&](int e, int t, int r) -> int64_t { return (int64_t)e * W.rows + 128 * t + 32 * wave + r; };
+  auto sink = [&](const UnitCtx& cx, int t, const f32x16_t& acc, float ts, float g, float) {
+    if (lr >= cx.n) return;
+    float* o = a.o + (int64_t)C.r_pair[cx.crow + lr] * a.H + 128 * t + 32 * wave;
+    const float sc = g * ts;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[acc_row(r, half)] = acc[r] * sc;
+  };
+  walk_grouped<FMT, AF == A_BF16>(W, gm, L, C, sp, op, row_of, sink);
+}
+
+template <int RF, int SF, int AF>
+__global__ void __launch_bounds__(kBlock, 2) gdown_kernel(ExpertArgs a) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  ExpertLds L = carve(a, smem);
+  const bool shared = (int)blockIdx.x < a.sh_wgs;
+  const GroupMap& gm = shared ? a.sgm : a.rgm;
+  const ClassCost k{gm.NG, gm.steps, gm.cw, gm.ct};
+  Span sp;
+  if (shared) {
+    build_shared(a, L.sh, k.NG, k.steps, k.cw, k.ct);
+    lds_barrier();
+    sp = shared_span(a.T, k, gm.NS, blockIdx.x, a.sh_wgs);
+  } else {
+    build_routed(a, L, L.rt, k, gm.NS, blockIdx.x - a.sh_wgs, gridDim.x - a.sh_wgs);
+    build_rows(a, L, L.rt);
+    sp = read_span(L);
+  }
+  if (shared) gdown_walk<SF, A_BF16>(a, L, L.sh, false, sp);
+  else gdown_walk<RF, AF>(a, L, L.rt, true, sp);
+}
+
+}  // namespace moe

@@ -37,6 +37,25 @@ inline int expert_lds_list_bytes(int E, int T, int k) {
           3 * kWinRows * 4 + 15) / 16 * 16;
 }
 
+// Grouped (MFMA) expert kernels, one weight class: each wave owns 32 weight rows of a
+// row tile (gate/up: 16 gate rows and the 16 matching up rows; down: 32 hidden rows),
+// a unit is an expert with up to NG = 32 of its tokens, and the K dimension is walked in
+// stages of KS elements (each lane holds 64 bytes of weights per stage: FP4 256, FP8
+// 128, BF16 64 elements per stage). Activations of a stage sit in LDS as BF16 (FP32
+// when split: the down projection of FP32 h, taken as three exact BF16 parts).
+// K elements per stage of the grouped kernels: 64 bytes of weights per lane, both
+// halves of the wave.
+inline constexpr int group_ks(int fmt) { return fmt == W_BF16 ? 64 : (fmt == W_MXFP8 ? 128 : 256); }
+
+struct GroupMap {
+  int KS, NS;        // K elements per stage, stages per row tile
+  int steps;         // row tiles per expert
+  int NG;            // tokens per unit
+  int cw, ct;        // cost of one stage of a row tile: cw + ct * tokens
+  int split;         // FP32 activations
+  int tstride;       // LDS bytes per staged token row (padded)
+};
+
 struct WTensor {
   const uint8_t* codes;
   const uint8_t* scales;
@@ -72,6 +91,8 @@ struct ExpertArgs {
   const float* topk_w;
   WTensor rw, sw;        // routed / shared weights of this stage
   GemvMap rmap, smap;
+  GroupMap rgm, sgm;     // grouped kernels (batches of 32 tokens and up)
+  int grouped;           // run the grouped kernels
   int T, H, I, Ish, E, k, has_shared, afmt;
   int max_slots;         // routed expert slots launched: min(E, T * k)
   int sh_wgs;            // workgroups of the launch that walk the shared expert

@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 
 typedef enum {
   MOE_OK = 0,
@@ -101,14 +101,20 @@ typedef struct {
  *   MOE_A_FP8_TOKEN: codes E4M3 [T][H] | s FP32 [T]
  * Each part starts at a 256-byte boundary from the start of xq. */
 
-/* Optional per-call debug outputs of moe_expert_forward (any field may be NULL).
- * Pair p = t*k + j is token t's j-th selected expert; rows T*k + t hold token t's
- * shared expert. */
+/* Optional per-call debug outputs and controls of moe_expert_forward (any pointer may
+ * be NULL). Pair p = t*k + j is token t's j-th selected expert; rows T*k + t hold token
+ * t's shared expert. */
+typedef enum { MOE_PATH_AUTO = 0, MOE_PATH_GEMV = 1, MOE_PATH_GROUPED = 2 } moe_path_t;
 typedef struct {
   float *h;             /* FP32 [T*k + T*has_shared][max(I, I_shared)]: SwiGLU outputs   */
   uint8_t *hq_codes;    /* quantized routed h: NVFP4 [T*k][I/2] or FP8 [T*k][I]           */
   uint8_t *hq_scales;   /* NVFP4: E4M3 [T*k][I/16]                                        */
   float *hq_scale;      /* NVFP4: g [T*k]; FP8: s [T*k]                                   */
+  int32_t path;         /* moe_path_t: which expert kernels run. AUTO picks the grouped
+                           (MFMA, 32 tokens per unit) kernels from 32 tokens on when units
+                           hold many tokens (a shared expert, or T*k >= E), else the GEMV
+                           kernels (4 tokens per unit); GROUPED is refused where the
+                           shapes do not tile (see moe_layer_check)                       */
 } moe_debug_t;
 
 /* Host only; no device access. Checks every constraint the kernels rely on for a

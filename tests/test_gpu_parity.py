@@ -88,21 +88,27 @@ LAYER_CASES = [
 ]
 
 
-def _run_layer(lib, name, T, debug=True):
+def _run_layer(lib, name, T, debug=True, path=0):
     dl = device_layer(name)
     ws = lib.Workspace(dl, max(T, 8))
     x_np, ref = oracle_layer(name, T)
     x = _x_dev(x_np)
     ids, w, xq = lib.route(dl, x, ws)
-    y, dbg = lib.expert_forward(dl, x, xq, ids, w, ws, debug=True)
+    y, dbg = lib.expert_forward(dl, x, xq, ids, w, ws, debug=True, path=path)
     torch.cuda.synchronize()
     return dl, x_np, ref, ids, w, xq, y, dbg
 
 
-@pytest.mark.parametrize("name,T", [(n, t) for n, ts in LAYER_CASES for t in ts])
-def test_layer_parity(lib, name, T):
-    say(f"[parity] layer {name} T={T}")
-    dl, x_np, ref, ids, w, xq, y, dbg = _run_layer(lib, name, T)
+# the grouped (MFMA) kernels forced at small, ragged batches, every weight format
+GROUPED_SMALL = [("tiny_bf16", 3), ("flint_w4a16", 8), ("flint_bf16", 5), ("inkling_w4a4", 5),
+                 ("inkling_mxfp8", 8), ("mistral_mxfp4", 3), ("mistral_mxfp4_a8", 8)]
+
+
+@pytest.mark.parametrize("name,T,path", [(n, t, 0) for n, ts in LAYER_CASES for t in ts] +
+                         [(n, t, 2) for n, t in GROUPED_SMALL])
+def test_layer_parity(lib, name, T, path):
+    say(f"[parity] layer {name} T={T} path={path}")
+    dl, x_np, ref, ids, w, xq, y, dbg = _run_layer(lib, name, T, path=path)
     cfg = dl.cfg
     ids_g = ids.cpu().numpy()
     bad = check_ids(ids_g, ref, cfg.k)
@@ -163,11 +169,11 @@ LARGE_CASES = [
 ]
 
 
-@pytest.mark.parametrize("name,T", LARGE_CASES)
-def test_layer_parity_large_batch(lib, name, T):
+@pytest.mark.parametrize("name,T,path", [(n, t, p) for n, t in LARGE_CASES for p in (1, 2)])
+def test_layer_parity_large_batch(lib, name, T, path):
     from oracle import layer as OL
     from parity_util import oracle_route_only
-    say(f"[parity] large batch {name} T={T}")
+    say(f"[parity] large batch {name} T={T} path={path}")
     dl = device_layer(name)
     cfg = dl.cfg
     ws = lib.Workspace(dl, T)
@@ -176,9 +182,9 @@ def test_layer_parity_large_batch(lib, name, T):
     ids, w, xq = lib.route(dl, x, ws)
     quant_h = cfg.afmt != "bf16"
     if quant_h:
-        y, dbg = lib.expert_forward(dl, x, xq, ids, w, ws, debug=True)
+        y, dbg = lib.expert_forward(dl, x, xq, ids, w, ws, debug=True, path=path)
     else:
-        y = lib.expert_forward(dl, x, xq, ids, w, ws)
+        y = lib.expert_forward(dl, x, xq, ids, w, ws, path=path)
     torch.cuda.synchronize()
     ref = oracle_route_only(name, x_np)
     ids_g = ids.cpu().numpy()
