@@ -219,7 +219,7 @@ def main() -> int:
         from oracle import layer as OL  # the CPU baseline leg: the oracle as it stands
         x_np = synth.make_x(cfg, args.batch)
         runs, t_tot = 0, 0.0
-        while runs < 1 or (t_tot < args.cpu_sample_s and runs < 5):
+        while runs < 1 or (t_tot < args.cpu_sample_s and runs < 100):
             t0 = time.perf_counter()
             OL.moe_layer(host, x_np)
             t_tot += time.perf_counter() - t0
