@@ -109,6 +109,10 @@ struct Plan {
 };
 
 constexpr int kGroupedMinT = 32;      // the grouped (MFMA) kernels from this batch on
+constexpr int kTokPctGateup = 270;    // GEMV cost model: token-term scale (see set_costs)
+constexpr int kTokPctDown = 37;
+constexpr int kLateGateup16 = 14;     // GEMV kernels: weight of a second-round workgroup,
+constexpr int kLateDown16 = 15;       // in 16ths (timestamps: they end ~15% / ~7% later)
 constexpr int kGroupTok = 32;         // tokens per unit in the grouped kernels
 
 // Grouped map of one weight class: rows of K elements, `rows_per_tile` rows (or
@@ -136,10 +140,13 @@ int wbytes_x2(int fmt) { return fmt == W_BF16 ? 4 : (fmt == W_MXFP8 ? 2 : 1); }
 // Cost weights of one row-step (see GemvMap) over rows of K elements: weight bytes
 // against activation work (a token costs half a step's weight bytes for FP4 weights and
 // BF16 activations).
-void set_costs(GemvMap& m, int fmt, int K) {
+// tok_pct scales the token term: per-workgroup timestamps on the NVFP4 Flint layer at
+// T = 8 put a 4-token BF16 gate/up step at 2.7x a 1-token step (token term x2.7) and a
+// 2-token FP32 down step at 1.4x (token term x0.37).
+void set_costs(GemvMap& m, int fmt, int K, int tok_pct) {
   const int64_t elems = (int64_t)m.RS * K;
   m.cw = (int)std::max<int64_t>(1, elems * wbytes_x2(fmt) / 256);
-  m.ct = (int)std::max<int64_t>(1, elems * m.esize / 1024);
+  m.ct = (int)std::max<int64_t>(1, elems * m.esize * tok_pct / (1024 * 100));
 }
 
 // Row maps of both expert kernels and their LDS needs. Gate/up row-steps cover RS / 2
@@ -155,10 +162,10 @@ bool make_plan(const moe_layer_t& L, int T, int path, Plan& p) {
   if (!plan_class(L.wfmt, L.I, nt, r_es, false, p.dn_r) || !plan_class(sfmt, Ish, nt, 4, false, p.dn_s))
     return false;
   if (L.H % p.dn_r.RS || L.H % p.dn_s.RS) return false;
-  set_costs(p.gu_r, L.wfmt, L.H);
-  set_costs(p.gu_s, sfmt, L.H);
-  set_costs(p.dn_r, L.wfmt, L.I);
-  set_costs(p.dn_s, sfmt, Ish);
+  set_costs(p.gu_r, L.wfmt, L.H, kTokPctGateup);
+  set_costs(p.gu_s, sfmt, L.H, kTokPctGateup);
+  set_costs(p.dn_r, L.wfmt, L.I, kTokPctDown);
+  set_costs(p.dn_s, sfmt, Ish, kTokPctDown);
   // summed costs must fit an int: bound every unit by NG tokens
   auto bound = [&](const GemvMap& m, int steps, int units) {
     return (int64_t)units * steps * (m.cw + (int64_t)m.ct * m.NG);
@@ -217,13 +224,18 @@ bool make_plan(const moe_layer_t& L, int T, int path, Plan& p) {
 struct CostQ {
   int NG, steps, cw, ct;
 };
-int shared_wgs(const moe_layer_t& L, int T, const CostQ& s, const CostQ& r, int G) {
+// The split weighs workgroups as the kernels do: the first ncu blocks 16, later ones
+// late16 (shared workgroups come first, so they are all full-weight ones when the shared
+// share stays under ncu blocks).
+int shared_wgs(const moe_layer_t& L, int T, const CostQ& s, const CostQ& r, int G, int ncu, int late16,
+               bool pair_mode = false) {
   if (!L.has_shared || G < 2) return 0;
   const int64_t cs = (int64_t)s.steps * (s.cw * (int64_t)((T + s.NG - 1) / s.NG) + (int64_t)s.ct * T);
-  const int64_t pairs = (int64_t)T * L.k, ur = std::min<int64_t>(L.E, pairs);
+  const int64_t pairs = (int64_t)T * L.k, ur = pair_mode ? pairs : std::min<int64_t>(L.E, pairs);
   const int64_t cr = (int64_t)r.steps * (r.cw * ur + r.ct * pairs);
-  const int64_t g = (G * cs + (cs + cr) / 2) / (cs + cr);
-  return (int)std::min<int64_t>(std::max<int64_t>(g, 1), G - 1);
+  const int64_t W = 16 * (int64_t)std::min(G, ncu) + (int64_t)late16 * std::max(0, G - ncu);
+  const int64_t g = (W * cs + 8 * (cs + cr)) / (16 * (cs + cr));
+  return (int)std::min<int64_t>(std::max<int64_t>(g, 1), std::min(G, ncu) - 1);
 }
 
 struct WsLayout {
@@ -509,20 +521,29 @@ moe_status_t moe_expert_forward(const moe_layer_t* L, const uint16_t* x_bf16, co
   dn.rmap = p.dn_r;
   dn.smap = p.dn_s;
   dn.lds_act_bytes = (int)p.dn_tile;
-  // persistent launches: every workgroup takes an equal share of its class's cost
+  // persistent launches: every workgroup takes a share of its class's cost, the
+  // second-round blocks (dispatched once every compute unit holds one) a smaller one
   const int gu_grid = resident, dn_grid = resident;
+  const int ncu = device_cus();
+  gu.ncu = dn.ncu = ncu;
+  gu.late16 = p.grouped ? 16 : kLateGateup16;
+  dn.late16 = p.grouped ? 16 : kLateDown16;
   const int Ish_ = L->has_shared ? L->I_shared : L->I;
   gu.grouped = dn.grouped = p.grouped ? 1 : 0;
   if (p.grouped) {
     gu.rgm = p.gu_rg; gu.sgm = p.gu_sg;
     dn.rgm = p.dn_rg; dn.sgm = p.dn_sg;
     auto q = [](const GroupMap& g) { return CostQ{g.NG, g.steps * g.NS, g.cw / g.NS, g.ct / g.NS}; };
-    gu.sh_wgs = shared_wgs(*L, T, q(p.gu_sg), q(p.gu_rg), gu_grid);
-    dn.sh_wgs = shared_wgs(*L, T, q(p.dn_sg), q(p.dn_rg), dn_grid);
+    gu.sh_wgs = shared_wgs(*L, T, q(p.gu_sg), q(p.gu_rg), gu_grid, ncu, gu.late16);
+    dn.sh_wgs = shared_wgs(*L, T, q(p.dn_sg), q(p.dn_rg), dn_grid, ncu, dn.late16);
   } else {
+    const bool pm = T * L->k <= kPairMax;
+    gu.pair_mode = dn.pair_mode = pm ? 1 : 0;
     auto q = [](const GemvMap& m, int steps) { return CostQ{m.NG, steps, m.cw, m.ct}; };
-    gu.sh_wgs = shared_wgs(*L, T, q(p.gu_s, Ish_ / (p.gu_s.RS / 2)), q(p.gu_r, L->I / (p.gu_r.RS / 2)), gu_grid);
-    dn.sh_wgs = shared_wgs(*L, T, q(p.dn_s, L->H / p.dn_s.RS), q(p.dn_r, L->H / p.dn_r.RS), dn_grid);
+    gu.sh_wgs = shared_wgs(*L, T, q(p.gu_s, Ish_ / (p.gu_s.RS / 2)), q(p.gu_r, L->I / (p.gu_r.RS / 2)), gu_grid,
+                           ncu, gu.late16, pm);
+    dn.sh_wgs = shared_wgs(*L, T, q(p.dn_s, L->H / p.dn_s.RS), q(p.dn_r, L->H / p.dn_r.RS), dn_grid,
+                           ncu, dn.late16, pm);
   }
   if (launch_experts(gu, gu_grid, p.gu_lds, dn, dn_grid, p.dn_lds, stream) != hipSuccess)
     return set_err(MOE_ELAUNCH, "expert kernel launch failed");

@@ -52,12 +52,14 @@ struct ExpertLds {
   ClassTab rt, sh;
   float* w_gs;      // [2 * kWinRows] global weight scales of the staged rows' experts
   float* w_tsc;     // [kWinRows] activation scales of the staged rows
+  float* gs_rt;     // [2 * E] global weight scales of the routed experts (GEMV kernels)
+  float* gs_sh;     // [2] those of the shared expert
   uint8_t* tile;    // activations of the staged rows, K * esize bytes each
 };
 
 __device__ __forceinline__ ExpertLds carve(const ExpertArgs& a, uint8_t* smem) {
   ExpertLds L;
-  const int P = a.T * a.k, Am = min(a.E, P);
+  const int P = a.T * a.k, Am = routed_capacity(a.E, P);
   L.nw = (a.T + 63) / 64;
   L.tmask = reinterpret_cast<uint64_t*>(smem);
   L.first = reinterpret_cast<int*>(L.tmask + a.E * L.nw);
@@ -81,6 +83,8 @@ __device__ __forceinline__ ExpertLds carve(const ExpertArgs& a, uint8_t* smem) {
   tab(L.sh, 1, a.T);
   L.w_gs = reinterpret_cast<float*>(q);
   L.w_tsc = L.w_gs + 2 * kWinRows;
+  L.gs_rt = L.w_tsc + kWinRows;
+  L.gs_sh = L.gs_rt + 2 * a.E;
   L.tile = smem + a.lds_list_bytes;
   return L;
 }
@@ -135,16 +139,16 @@ __device__ __forceinline__ void stage_tile(uint8_t* tile, const GemvMap& m, int 
 // thread): the loads are issued before the first weight loads and stored afterwards, so
 // waiting for them never waits for weight bytes (vector-memory counters retire in order).
 constexpr int kPreSlots = 12;
+// Every slot issues its load (slots past the rows re-read the last one): one basic block,
+// no per-slot branches. nt >= 1.
 template <int AK, class Ld>
 __device__ __forceinline__ void park_rows(const SlotMap<AK>& sm, int nt, Ld ld, uint4 (&raw)[kPreSlots]) {
   const int n = nt * sm.units;
 #pragma unroll
   for (int i = 0; i < kPreSlots; ++i) {
-    const int u = i * kBlock + threadIdx.x;
-    if (u < n) {
-      const int t = sm.row(u);
-      raw[i] = ld(t, sm.elem(u, t));
-    }
+    const int u = min(i * kBlock + (int)threadIdx.x, n - 1);
+    const int t = sm.row(u);
+    raw[i] = ld(t, sm.elem(u, t));
   }
 }
 template <int AK, int EPL, class Cv>
@@ -431,7 +435,7 @@ __device__ __forceinline__ void build_routed(const ExpertArgs& a, const ExpertLd
       A += __popcll(__ballot(ld));
     }
     int c_lo, c_hi;
-    wg_share(tc, b, G, c_lo, c_hi);
+    wg_share(tc, b, G, ShareW{a.sh_wgs, a.ncu, a.late16}, c_lo, c_hi);
     const Located end{A, 0, tc, tnu >> 16, tnu & 0xFFFF, -1};
     Located lo = end, hi = end;
     int bnu = 0, bc = 0, ba = 0;
@@ -487,6 +491,32 @@ __device__ __forceinline__ void build_routed(const ExpertArgs& a, const ExpertLd
   C.A = uni(L.nA[0]);
 }
 
+// Pair mode, for small batches (T*k <= kPairMax): every (token, expert) pair is its own
+// unit of one token, in pair order, so every step of every unit costs the same and the
+// workgroup's span is closed-form (no table build); the first unit's expert is one
+// scalar load of topk_ids. An expert named by several tokens is read once per token (at
+// decode sizes a few percent more bytes). Entries outside [0, E) read expert 0 (their
+// outputs are unspecified).
+__device__ __forceinline__ Span pair_span(const ExpertArgs& a, const ClassCost& k, int NB, int b, int G) {
+  const int P = a.T * a.k, steps = k.steps, total = P * steps;
+  const ShareW w{a.sh_wgs, a.ncu, a.late16};
+  const int l0 = share_at(total, b, G, w), l1 = share_at(total, b + 1, G, w);
+  Span sp;
+  sp.a0 = l0 / steps;
+  sp.s0 = l0 - sp.a0 * steps;
+  sp.g0 = 0;
+  sp.n0 = 1;
+  sp.rb0 = sp.a0;
+  sp.left = (l1 - l0) * NB;
+  sp.row_limit = (l1 + steps - 1) / steps;
+  sp.e0 = 0;
+  if (sp.a0 < P) {
+    const int e = a.ids[sp.a0];
+    sp.e0 = (unsigned)e < (unsigned)a.E ? e : 0;
+  }
+  return sp;
+}
+
 __device__ __forceinline__ Span read_span(const ExpertLds& L) {
   Span sp;
   sp.a0 = uni(L.span[0]); sp.g0 = uni(L.span[1]); sp.s0 = uni(L.span[2]); sp.e0 = uni(L.span[3]);
@@ -512,32 +542,78 @@ __device__ __forceinline__ void build_rows(const ExpertArgs& a, const ExpertLds&
   lds_barrier();
 }
 
-// Where the current unit's data sits: its first class row, its first staged row, and
-// its token count.
+// Where the current unit's data sits: its first class row, its first staged row, its
+// token count, its expert and the pair index of each of its rows.
 struct UnitCtx {
-  int crow, wrow, n;
+  int crow, wrow, n, e;
+  int pr[4];
 };
+
+// How a walk reads its class: units (expert, token count, first row), the unit count, and
+// each class row's token and pair index.
+//   VW_TAB     routed experts from the LDS tables (build_routed / build_rows)
+//   VW_PAIR    pair mode: unit a is pair a (one token, row a), its expert from topk_ids
+//              staged in LDS (entries outside [0, E) read expert 0)
+//   VW_SHARED  the shared expert: one unit of all T tokens, row t = token t
+enum { VW_TAB = 0, VW_PAIR = 1, VW_SHARED = 2 };
+template <int VW>
+struct ClassView {
+  const ClassTab* C;
+  const int* lids;
+  int k, E, T, P;
+  float inv_k;   // 1 / k: token r / k of pair row r as (r + 1/2) / k in FP32, exact for r < 2^16
+  __device__ __forceinline__ int count() const {
+    if constexpr (VW == VW_TAB) return C->A;
+    else if constexpr (VW == VW_PAIR) return P;
+    else return 1;
+  }
+  __device__ __forceinline__ void unit(int a, int& e, int& n, int& rb) const {
+    if constexpr (VW == VW_TAB) {
+      e = uni(C->ex_id[a]); n = uni(C->ex_n[a]); rb = uni(C->ex_row[a]);
+    } else if constexpr (VW == VW_PAIR) {
+      const int v = uni(lids[a]);
+      e = (unsigned)v < (unsigned)E ? v : 0; n = 1; rb = a;
+    } else {
+      e = 0; n = T; rb = 0;
+    }
+  }
+  __device__ __forceinline__ int tok(int r) const {
+    if constexpr (VW == VW_TAB) return C->r_tok[r];
+    else if constexpr (VW == VW_PAIR) return (int)(((float)r + 0.5f) * inv_k);
+    else return r;
+  }
+  __device__ __forceinline__ int pair(int r) const {
+    if constexpr (VW == VW_TAB) return C->r_pair[r];
+    else if constexpr (VW == VW_PAIR) return r;
+    else return P + r;
+  }
+};
+
+constexpr int kGsPer = 8;   // global weight scales staged per thread: 2 * E <= 8 * kBlock
 
 // Walks one workgroup's span of a class. The class's operations (workgroup-uniform):
 //   op.rows(e, s, lrow, out[RPL])  global weight rows of this lane at step s of expert e
 //   op.ld(tok, pair, el) -> uint4  raw bytes behind 16 staged bytes of a row at element el
 //   op.cv(uint4) -> uint4          those 16 staged bytes
 //   op.tsc(tok, pair) -> float     a row's activation scale
-//   op.gs(e, q) -> float           global weight scale q of expert e
-//   op.sink(ctx, s, lrow, acc)     results, on the lanes with jl == 0
+//   op.sink(ctx, s, lrow, acc)     results, on the lanes with jl == 0 (global weight
+//                                  scales from the class's table in LDS, gs_tab)
 // Ops is a plain struct per (projection, activation format), so the shared and routed
-// classes run the same code whenever their formats agree (the kernels stay small
-// enough for the instruction cache).
-// The first staged window (rows of the first units) is loaded into registers before
-// the first weight loads are issued and stored to LDS after them. Two register sets
-// alternate (no loop-carried copy); every step but the last issues the same number of
-// weight loads for the next one, so the compiler waits for one step's loads while the
-// next step's are in flight. Later windows are staged when a unit does not fit; only
-// LDS barriers are used, so weight loads stream across them.
-template <int FMT, int AK, int RPL, class Ops>
+// classes run the same code whenever their formats agree.
+// Prologue: the first staged window (rows of the first units, which the span alone
+// names), the class's global weight scales (ngs of them, from gscale or 1) and, in pair
+// mode, topk_ids are loaded into registers; then the first weight loads are issued (they
+// need only the first unit's expert, sp.e0); then everything goes to LDS. So the weights
+// are in flight one memory round trip after launch. Two register sets alternate (no
+// loop-carried copy); every step but the last issues the same number of weight loads for
+// the next one, so the compiler waits for one step's loads while the next step's are in
+// flight. Later windows are staged when a unit does not fit; only LDS barriers are used,
+// so weight loads stream across them.
+template <int FMT, int AK, int RPL, int VW, class Ops>
 __device__ __forceinline__ void walk_class(const WTensor& W, const GemvMap& m, const ExpertLds& L,
-                                           int lds_tile_bytes, const ClassTab& C, const ClassCost& k,
-                                           const Span& sp, const Ops& op) {
+                                           int lds_tile_bytes, const ClassView<VW>& V, const ClassCost& k,
+                                           const Span& sp, const Ops& op, float* gs_tab, int ngs,
+                                           const int32_t* ids) {
   constexpr int EPL = elems_per_piece(FMT);
   constexpr int PER = AK == 0 ? 8 : 4;
   if (sp.left <= 0) return;
@@ -546,6 +622,7 @@ __device__ __forceinline__ void walk_class(const WTensor& W, const GemvMap& m, c
   const int jl = lane % m.LPR, lrow = wave * m.G + lane / m.LPR;
   const int tstride = W.K * m.esize;
   const int cap = min(kWinRows, lds_tile_bytes / tstride);
+  const int A = V.count();
   auto advance = [&](Cursor& p) {
     if (++p.b < m.NB) return;
     p.b = 0;
@@ -553,14 +630,10 @@ __device__ __forceinline__ void walk_class(const WTensor& W, const GemvMap& m, c
     p.s = 0;
     if (++p.g * k.NG < p.n) return;
     p.g = 0;
-    if (++p.a < C.A) {
-      p.e = uni(C.ex_id[p.a]);
-      p.n = uni(C.ex_n[p.a]);
-      p.rb = uni(C.ex_row[p.a]);
-    }
+    if (++p.a < A) V.unit(p.a, p.e, p.n, p.rb);
   };
   auto row_ld = [&](int r0) {
-    return [&, r0](int t, int el) { return op.ld(C.r_tok[r0 + t], C.r_pair[r0 + t], el); };
+    return [&, r0](int t, int el) { return op.ld(V.tok(r0 + t), V.pair(r0 + t), el); };
   };
   int r0 = sp.rb0 + sp.g0 * k.NG;   // staged class rows [r0, r1)
   int r1 = min(min(r0 + cap, sp.row_limit), r0 + kPreSlots * kBlock / (W.K / PER));
@@ -570,17 +643,12 @@ __device__ __forceinline__ void walk_class(const WTensor& W, const GemvMap& m, c
     r1 = min(ra + cap, sp.row_limit);
     const int nrows = r1 - r0;
     stage_tile<AK, EPL>(L.tile, m, W.K, nrows, row_ld(r0), [&](uint4 r) { return op.cv(r); });
-    for (int i = threadIdx.x; i < nrows; i += kBlock) {
-      const int tk = C.r_tok[r0 + i], pr = C.r_pair[r0 + i], e = C.r_exp[r0 + i];
-      L.w_tsc[i] = op.tsc(tk, pr);
-      L.w_gs[2 * i] = op.gs(e, 0);
-      L.w_gs[2 * i + 1] = op.gs(e, 1);
-    }
+    for (int i = threadIdx.x; i < nrows; i += kBlock) L.w_tsc[i] = op.tsc(V.tok(r0 + i), V.pair(r0 + i));
     lds_barrier();
   };
   float acc[RPL][4];
   int cur_a = -1, cur_g = -1;
-  UnitCtx cx{0, 0, 0};
+  UnitCtx cx{0, 0, 0, 0, {0, 0, 0, 0}};
   auto do_step = [&](auto pf, const Cursor& p, WeightRegs<RPL>& cur, WeightRegs<RPL>& nxt, Cursor& np) {
     if (p.a != cur_a || p.g != cur_g) {   // next unit
       cur_a = p.a;
@@ -591,6 +659,9 @@ __device__ __forceinline__ void walk_class(const WTensor& W, const GemvMap& m, c
       cx.crow = ur;
       cx.wrow = ur - r0;
       cx.n = nt;
+      cx.e = p.e;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) cx.pr[t] = t < nt ? V.pair(ur + t) : 0;
     }
     if (p.b == 0) {
 #pragma unroll
@@ -639,40 +710,46 @@ __device__ __forceinline__ void walk_class(const WTensor& W, const GemvMap& m, c
       if (jl == 0) op.sink(cx, p.s, lrow, acc);
     }
   };
-  // first window: raw slots and per-row scales into registers, then the first weight
-  // loads, then the LDS stores
+  // prologue: loads that need no expert id, then the first weight loads, then LDS
   const int nrows0 = r1 - r0;
   uint4 raw[kPreSlots];
   const SlotMap<AK> smap(m, W.K);
   park_rows<AK>(smap, nrows0, row_ld(r0), raw);
-  float ts_r = 0.0f, g0_r = 0.0f, g1_r = 0.0f;
-  if (threadIdx.x < nrows0) {
-    const int tk = C.r_tok[r0 + threadIdx.x], pr = C.r_pair[r0 + threadIdx.x], e = C.r_exp[r0 + threadIdx.x];
-    ts_r = op.tsc(tk, pr);
-    g0_r = op.gs(e, 0);
-    g1_r = op.gs(e, 1);
-  }
+  float ts_r = 0.0f;
+  if ((int)threadIdx.x < nrows0) ts_r = op.tsc(V.tok(r0 + threadIdx.x), V.pair(r0 + threadIdx.x));
+  // (every load issues, at a clamped index; without gscale it reads the first codes)
+  const float* gsrc = W.gscale ? W.gscale : reinterpret_cast<const float*>(W.codes);
+  const int gmax = W.gscale ? ngs - 1 : 0;
+  float gsv[kGsPer];
+#pragma unroll
+  for (int j = 0; j < kGsPer; ++j) gsv[j] = gsrc[min((int)threadIdx.x + j * kBlock, gmax)];
+  int idv = 0;
+  if constexpr (VW == VW_PAIR) idv = ids[min((int)threadIdx.x, V.P - 1)];
   Cursor pa{sp.a0, sp.g0, sp.s0, 0, sp.e0, sp.n0, sp.rb0}, pb = pa;
-  WeightRegs<RPL> A, B;
+  WeightRegs<RPL> A_, B_;
   {
     int64_t rr[RPL];
     op.rows(pa.e, pa.s, lrow, rr);
-    fetch_batch<FMT, RPL>(W, m, rr, 0, jl, A);
+    fetch_batch<FMT, RPL>(W, m, rr, 0, jl, A_);
   }
   unpark_rows<AK, EPL>(smap, L.tile, nrows0, [&](uint4 r) { return op.cv(r); }, raw);
-  if (threadIdx.x < nrows0) {
-    L.w_tsc[threadIdx.x] = ts_r;
-    L.w_gs[2 * threadIdx.x] = g0_r;
-    L.w_gs[2 * threadIdx.x + 1] = g1_r;
+  if ((int)threadIdx.x < nrows0) L.w_tsc[threadIdx.x] = ts_r;
+#pragma unroll
+  for (int j = 0; j < kGsPer; ++j) {
+    const int i = threadIdx.x + j * kBlock;
+    if (i < ngs) gs_tab[i] = W.gscale ? gsv[j] : 1.0f;
+  }
+  if constexpr (VW == VW_PAIR) {
+    if ((int)threadIdx.x < V.P) L.ids[threadIdx.x] = idv;
   }
   lds_barrier();
   using Yes = std::integral_constant<bool, true>;
   using No = std::integral_constant<bool, false>;
   while (true) {
-    if (left == 1) { do_step(No{}, pa, A, B, pb); break; }
-    do_step(Yes{}, pa, A, B, pb);
-    if (left == 2) { do_step(No{}, pb, B, A, pa); break; }
-    do_step(Yes{}, pb, B, A, pa);
+    if (left == 1) { do_step(No{}, pa, A_, B_, pb); break; }
+    do_step(Yes{}, pa, A_, B_, pb);
+    if (left == 2) { do_step(No{}, pb, B_, A_, pa); break; }
+    do_step(Yes{}, pb, B_, A_, pa);
     left -= 2;
   }
 }
@@ -751,7 +828,7 @@ struct GateupOps {
   }
   __device__ __forceinline__ void sink(const UnitCtx& cx, int st, int lrow, const float (&acc)[2][4]) const {
     const int i = st * PS + lrow;
-    const float gsg = w_gs[2 * cx.wrow], gsu = w_gs[2 * cx.wrow + 1];
+    const float gsg = w_gs[cx.e * gs_per_expert], gsu = w_gs[cx.e * gs_per_expert + 1];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       if (t < cx.n) {
@@ -759,7 +836,7 @@ struct GateupOps {
         const float gv = acc[0][t] * gsg * ts;
         const float uv = acc[1][t] * gsu * ts;
         const float hv = gv / (1.0f + expf(-gv)) * uv;
-        const int64_t off = (int64_t)r_pair[cx.crow + t] * hs + i;
+        const int64_t off = (int64_t)cx.pr[t] * hs + i;
         h[off] = hv;
         if (dbg_h) dbg_h[off] = hv;
       }
@@ -772,15 +849,22 @@ __device__ __forceinline__ ClassCost gateup_cost(const ExpertArgs& a, bool route
   return ClassCost{m.NG, (routed ? a.I : a.Ish) / (4 * m.G), m.cw, m.ct};
 }
 
-template <int FMT, int AF>
-__device__ __forceinline__ void gateup_walk(const ExpertArgs& a, const ExpertLds& L, const ClassTab& C,
-                                            bool routed, const Span& sp) {
+template <int VW>
+__device__ __forceinline__ ClassView<VW> class_view(const ExpertArgs& a, const ExpertLds& L) {
+  return ClassView<VW>{&L.rt, L.ids, a.k, a.E, a.T, a.T * a.k, 1.0f / (float)a.k};
+}
+
+template <int FMT, int AF, int VW>
+__device__ __forceinline__ void gateup_walk(const ExpertArgs& a, const ExpertLds& L, const Span& sp) {
+  constexpr bool routed = VW != VW_SHARED;
   const WTensor& W = routed ? a.rw : a.sw;
   const GemvMap& m = routed ? a.rmap : a.smap;
   const int Iexp = routed ? a.I : a.Ish;
+  float* gs_tab = routed ? L.gs_rt : L.gs_sh;
   const GateupOps<AF> op{a.x, a.xq_codes, a.xq_scales, a.xq_scale, W.gscale, W.gs_per_expert, W.rows, Iexp,
-                         4 * m.G, a.H, a.hs, a.h, a.dbg_h, L.w_gs, L.w_tsc, C.r_pair};
-  walk_class<FMT, 0, 2>(W, m, L, a.lds_act_bytes, C, gateup_cost(a, routed), sp, op);
+                         4 * m.G, a.H, a.hs, a.h, a.dbg_h, gs_tab, L.w_tsc, nullptr};
+  walk_class<FMT, 0, 2, VW>(W, m, L, a.lds_act_bytes, class_view<VW>(a, L), gateup_cost(a, routed), sp, op,
+                            gs_tab, (routed ? a.E : 1) * W.gs_per_expert, a.ids);
 }
 
 // Workgroups [0, sh_wgs) walk the shared expert (BF16 activations, no dependency on the
@@ -790,19 +874,18 @@ __global__ void __launch_bounds__(kBlock, 2) gateup_kernel(ExpertArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
   ExpertLds L = carve(a, smem);
   const bool shared = (int)blockIdx.x < a.sh_wgs;
-  Span sp;
   if (shared) {
-    const ClassCost k = gateup_cost(a, false);
-    build_shared(a, L.sh, k.NG, k.steps, k.cw, k.ct);
-    lds_barrier();
-    sp = shared_span(a.T, k, a.smap.NB, blockIdx.x, a.sh_wgs);
+    const Span sp = shared_span(a.T, gateup_cost(a, false), a.smap.NB, blockIdx.x, a.sh_wgs,
+                                ShareW{0, a.ncu, a.late16});
+    gateup_walk<SF, A_BF16, VW_SHARED>(a, L, sp);
+  } else if (a.pair_mode) {
+    const Span sp = pair_span(a, gateup_cost(a, true), a.rmap.NB, blockIdx.x - a.sh_wgs, gridDim.x - a.sh_wgs);
+    gateup_walk<RF, AF, VW_PAIR>(a, L, sp);
   } else {
     build_routed(a, L, L.rt, gateup_cost(a, true), a.rmap.NB, blockIdx.x - a.sh_wgs, gridDim.x - a.sh_wgs);
     build_rows(a, L, L.rt);
-    sp = read_span(L);
+    gateup_walk<RF, AF, VW_TAB>(a, L, read_span(L));
   }
-  if (shared) gateup_walk<SF, A_BF16>(a, L, L.sh, false, sp);
-  else gateup_walk<RF, AF>(a, L, L.rt, true, sp);
 }
 
 // =================================================================== down kernel
@@ -845,11 +928,11 @@ struct DownOps {
     return (q == 0 && gscale) ? gscale[(int64_t)e * gs_per_expert] : 1.0f;
   }
   __device__ __forceinline__ void sink(const UnitCtx& cx, int st, int lrow, const float (&acc)[1][4]) const {
-    const float g = w_gs[2 * cx.wrow];
+    const float g = w_gs[cx.e * gs_per_expert];
     const int row = st * RS + lrow;
 #pragma unroll
     for (int t = 0; t < 4; ++t)
-      if (t < cx.n) o[(int64_t)r_pair[cx.crow + t] * H + row] = acc[0][t] * g * w_tsc[cx.wrow + t];
+      if (t < cx.n) o[(int64_t)cx.pr[t] * H + row] = acc[0][t] * g * w_tsc[cx.wrow + t];
   }
 };
 
@@ -858,14 +941,17 @@ __device__ __forceinline__ ClassCost down_cost(const ExpertArgs& a, bool routed)
   return ClassCost{m.NG, a.H / m.RS, m.cw, m.ct};
 }
 
-template <int FMT, int AF>
-__device__ __forceinline__ void down_walk(const ExpertArgs& a, const ExpertLds& L, const ClassTab& C,
-                                          bool routed, const Span& sp) {
+template <int FMT, int AF, int VW>
+__device__ __forceinline__ void down_walk(const ExpertArgs& a, const ExpertLds& L, const Span& sp) {
+  constexpr bool routed = VW != VW_SHARED;
   const WTensor& W = routed ? a.rw : a.sw;
   const GemvMap& m = routed ? a.rmap : a.smap;
+  float* gs_tab = routed ? L.gs_rt : L.gs_sh;
   const DownOps<AF> op{a.h, a.hq_codes, a.hq_scales, a.hq_scale, W.gscale, W.gs_per_expert, W.rows,
-                       routed ? a.I : a.Ish, m.RS, a.H, a.hs, a.o, L.w_gs, L.w_tsc, C.r_pair};
-  walk_class<FMT, AF == A_BF16 ? 1 : 0, 1>(W, m, L, a.lds_act_bytes, C, down_cost(a, routed), sp, op);
+                       routed ? a.I : a.Ish, m.RS, a.H, a.hs, a.o, gs_tab, L.w_tsc, nullptr};
+  walk_class<FMT, AF == A_BF16 ? 1 : 0, 1, VW>(W, m, L, a.lds_act_bytes, class_view<VW>(a, L),
+                                               down_cost(a, routed), sp, op, gs_tab,
+                                               (routed ? a.E : 1) * W.gs_per_expert, a.ids);
 }
 
 template <int RF, int SF, int AF>
@@ -873,19 +959,18 @@ __global__ void __launch_bounds__(kBlock, 2) down_kernel(ExpertArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
   ExpertLds L = carve(a, smem);
   const bool shared = (int)blockIdx.x < a.sh_wgs;
-  Span sp;
   if (shared) {
-    const ClassCost k = down_cost(a, false);
-    build_shared(a, L.sh, k.NG, k.steps, k.cw, k.ct);
-    lds_barrier();
-    sp = shared_span(a.T, k, a.smap.NB, blockIdx.x, a.sh_wgs);
+    const Span sp = shared_span(a.T, down_cost(a, false), a.smap.NB, blockIdx.x, a.sh_wgs,
+                                ShareW{0, a.ncu, a.late16});
+    down_walk<SF, A_BF16, VW_SHARED>(a, L, sp);
+  } else if (a.pair_mode) {
+    const Span sp = pair_span(a, down_cost(a, true), a.rmap.NB, blockIdx.x - a.sh_wgs, gridDim.x - a.sh_wgs);
+    down_walk<RF, AF, VW_PAIR>(a, L, sp);
   } else {
     build_routed(a, L, L.rt, down_cost(a, true), a.rmap.NB, blockIdx.x - a.sh_wgs, gridDim.x - a.sh_wgs);
     build_rows(a, L, L.rt);
-    sp = read_span(L);
+    down_walk<RF, AF, VW_TAB>(a, L, read_span(L));
   }
-  if (shared) down_walk<SF, A_BF16>(a, L, L.sh, false, sp);
-  else down_walk<RF, AF>(a, L, L.rt, true, sp);
 }
 
 // ================================================================ host launchers

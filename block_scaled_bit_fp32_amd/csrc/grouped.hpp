@@ -273,7 +273,7 @@ __global__ void __launch_bounds__(kBlock, 2) ggateup_kernel(ExpertArgs a) {
   if (shared) {
     build_shared(a, L.sh, k.NG, k.steps, k.cw, k.ct);
     lds_barrier();
-    sp = shared_span(a.T, k, gm.NS, blockIdx.x, a.sh_wgs);
+    sp = shared_span(a.T, k, gm.NS, blockIdx.x, a.sh_wgs, ShareW{0, a.ncu, a.late16});
   } else {
     build_routed(a, L, L.rt, k, gm.NS, blockIdx.x - a.sh_wgs, gridDim.x - a.sh_wgs);
     build_rows(a, L, L.rt);
@@ -316,7 +316,7 @@ __global__ void __launch_bounds__(kBlock, 2) gdown_kernel(ExpertArgs a) {
   if (shared) {
     build_shared(a, L.sh, k.NG, k.steps, k.cw, k.ct);
     lds_barrier();
-    sp = shared_span(a.T, k, gm.NS, blockIdx.x, a.sh_wgs);
+    sp = shared_span(a.T, k, gm.NS, blockIdx.x, a.sh_wgs, ShareW{0, a.ncu, a.late16});
   } else {
     build_routed(a, L, L.rt, k, gm.NS, blockIdx.x - a.sh_wgs, gridDim.x - a.sh_wgs);
     build_rows(a, L, L.rt);

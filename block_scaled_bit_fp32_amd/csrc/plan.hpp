@@ -27,14 +27,18 @@ struct GemvMap {
 };
 
 constexpr int kWinRows = 64;   // most token rows one staged window of units holds
+constexpr int kPairMax = 64;   // GEMV kernels: one unit per (token, expert) pair up to this many pairs
+
+// Routed class table capacity: one entry per selected expert, or per pair in pair mode.
+inline constexpr int routed_capacity(int E, int P) { return P <= kPairMax ? P : (E < P ? E : P); }
 // Bytes of the expert kernels' LDS before the activation tile: token masks (ceil(T/64)
 // words per expert), first pairs and row bases per expert, ids, span, the routed and
-// shared class tables, and the staged rows' scales. Am = min(E, T*k) selected-expert
-// capacity, P = T*k class rows.
+// shared class tables, the staged rows' scales and the global weight scales of every
+// expert. Am = routed class capacity, P = T*k class rows.
 inline int expert_lds_list_bytes(int E, int T, int k) {
-  const int P = T * k, Am = E < P ? E : P, nw = (T + 63) / 64;
+  const int P = T * k, Am = routed_capacity(E, P), nw = (T + 63) / 64;
   return (E * 8 * nw + E * 8 + P * 4 + 16 + 32 + 4 * (5 * Am + 3) + 12 * P + 4 * (5 + 3) + 12 * T +
-          3 * kWinRows * 4 + 15) / 16 * 16;
+          3 * kWinRows * 4 + 4 * (2 * E + 2) + 15) / 16 * 16;
 }
 
 // Grouped (MFMA) expert kernels, one weight class: each wave owns 32 weight rows of a
@@ -93,9 +97,12 @@ struct ExpertArgs {
   GemvMap rmap, smap;
   GroupMap rgm, sgm;     // grouped kernels (batches of 32 tokens and up)
   int grouped;           // run the grouped kernels
+  int pair_mode;         // GEMV kernels: one unit per (token, expert) pair
   int T, H, I, Ish, E, k, has_shared, afmt;
   int max_slots;         // routed expert slots launched: min(E, T * k)
   int sh_wgs;            // workgroups of the launch that walk the shared expert
+  int ncu, late16;       // compute units; weight (in 16ths) of a block dispatched after
+                         // the first ncu, against 16 for the first ones
   float* h;              // [T*k + T][hs]
   int hs;
   uint8_t* hq_codes;     // [T*k][I/2 | I]

@@ -49,23 +49,26 @@ __global__ void __launch_bounds__(kBlock) route_gemv_kernel(RouteArgs a) {
   for (int e = 0; e < ET; ++e)
 #pragma unroll
     for (int t = 0; t < TT; ++t) acc[e][t] = 0.0f;
+  // Rows past the tile's last expert or token re-read its last one (results unused), so
+  // every load of an iteration issues before the first use.
+#pragma unroll 2
   for (int c = lane * 4; c < quarter; c += kWave * 4) {
     const int h = kb + c;
     float4 wv[ET];
+    uint2 xb[TT];
 #pragma unroll
     for (int e = 0; e < ET; ++e)
-      wv[e] = e < ne ? *reinterpret_cast<const float4*>(a.wr + (int64_t)(e0 + e) * a.H + h)
-                     : make_float4(0.f, 0.f, 0.f, 0.f);
+      wv[e] = *reinterpret_cast<const float4*>(a.wr + (int64_t)(e0 + min(e, ne - 1)) * a.H + h);
+#pragma unroll
+    for (int t = 0; t < TT; ++t)
+      xb[t] = *reinterpret_cast<const uint2*>(a.x + (int64_t)(t0 + min(t, nt - 1)) * a.H + h);
 #pragma unroll
     for (int t = 0; t < TT; ++t) {
-      if (t < nt) {
-        const uint2 xb = *reinterpret_cast<const uint2*>(a.x + (int64_t)(t0 + t) * a.H + h);
-        const float x0 = bf16_to_f32(xb.x & 0xFFFFu), x1 = bf16_to_f32(xb.x >> 16);
-        const float x2 = bf16_to_f32(xb.y & 0xFFFFu), x3 = bf16_to_f32(xb.y >> 16);
+      const float x0 = bf16_to_f32(xb[t].x & 0xFFFFu), x1 = bf16_to_f32(xb[t].x >> 16);
+      const float x2 = bf16_to_f32(xb[t].y & 0xFFFFu), x3 = bf16_to_f32(xb[t].y >> 16);
 #pragma unroll
-        for (int e = 0; e < ET; ++e)
-          acc[e][t] = fmaf(wv[e].w, x3, fmaf(wv[e].z, x2, fmaf(wv[e].y, x1, fmaf(wv[e].x, x0, acc[e][t]))));
-      }
+      for (int e = 0; e < ET; ++e)
+        acc[e][t] = fmaf(wv[e].w, x3, fmaf(wv[e].z, x2, fmaf(wv[e].y, x1, fmaf(wv[e].x, x0, acc[e][t]))));
     }
   }
 #pragma unroll
@@ -92,30 +95,43 @@ __global__ void __launch_bounds__(kBlock) route_gemv_kernel(RouteArgs a) {
 
 // Top-k: one wave per token, k rounds of a wave argmax. The key (order-preserving bits
 // of the logit, then the complement of the expert index) makes "larger logit, then
-// lower index" a plain unsigned maximum. Weights = sigmoid of the selected logits,
+// lower index" a plain unsigned maximum. Expert e sits in lane e % 64, slot e / 64 (NK
+// slots cover E <= 64 * NK); each lane keeps the best of its slots, and only the lane
+// that lost its best to a round rescans them. Weights = sigmoid of the selected logits,
 // renormalized in selection order.
+template <int NK>
 __global__ void __launch_bounds__(kBlock) topk_kernel(RouteArgs a) {
   const int lane = threadIdx.x & (kWave - 1);
   const int t = blockIdx.x * (kBlock / kWave) + threadIdx.x / kWave;
   if (t >= a.T) return;
   const float* lg = a.logits + (int64_t)t * a.E;
-  uint64_t key[16];
+  uint64_t key[NK];
+  float lv[NK];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
+  for (int i = 0; i < NK; ++i) lv[i] = lg[min(lane + kWave * i, a.E - 1)];
+#pragma unroll
+  for (int i = 0; i < NK; ++i) {
     const int e = lane + kWave * i;
-    key[i] = e < a.E ? ((uint64_t)float_order_key(lg[e]) << 32) | (0xFFFFFFFFu - (uint32_t)e) : 0ull;
+    key[i] = e < a.E ? ((uint64_t)float_order_key(lv[i]) << 32) | (0xFFFFFFFFu - (uint32_t)e) : 0ull;
   }
+  auto local_best = [&]() {
+    uint64_t b = key[0];
+#pragma unroll
+    for (int i = 1; i < NK; ++i) b = key[i] > b ? key[i] : b;
+    return b;
+  };
+  uint64_t lb = local_best();
   float myv = 0.0f;
   int mye = 0;
   for (int j = 0; j < a.k; ++j) {
-    uint64_t best = 0ull;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) best = key[i] > best ? key[i] : best;
-    best = wave_max_u64(best);
+    const uint64_t best = wave_max_u64(lb);
     const int be = (int)(0xFFFFFFFFu - (uint32_t)best);
+    if (lane == (be & (kWave - 1))) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i)
-      if (lane + kWave * i == be) key[i] = 0ull;      // taken
+      for (int i = 0; i < NK; ++i)
+        if (i == be / kWave) key[i] = 0ull;      // taken
+      lb = local_best();
+    }
     if (lane == j) {
       myv = float_from_order_key((uint32_t)(best >> 32));
       mye = be;
@@ -155,8 +171,12 @@ hipError_t launch_route(const RouteArgs& a, int n_quant, hipStream_t s) {
       ? launch_kernel(K_ROUTE, route_gemv_kernel<1, 8>, dim3(grid), dim3(kBlock), 0, s, a)
       : launch_kernel(K_ROUTE, route_gemv_kernel<4, 8>, dim3(grid), dim3(kBlock), 0, s, a);
   if (err != hipSuccess) return err;
-  const int waves = kBlock / kWave;
-  return launch_kernel(K_TOPK, topk_kernel, dim3((a.T + waves - 1) / waves), dim3(kBlock), 0, s, a);
+  const dim3 tg((a.T + kBlock / kWave - 1) / (kBlock / kWave));
+  if (a.E <= 64) return launch_kernel(K_TOPK, topk_kernel<1>, tg, dim3(kBlock), 0, s, a);
+  if (a.E <= 128) return launch_kernel(K_TOPK, topk_kernel<2>, tg, dim3(kBlock), 0, s, a);
+  if (a.E <= 256) return launch_kernel(K_TOPK, topk_kernel<4>, tg, dim3(kBlock), 0, s, a);
+  if (a.E <= 512) return launch_kernel(K_TOPK, topk_kernel<8>, tg, dim3(kBlock), 0, s, a);
+  return launch_kernel(K_TOPK, topk_kernel<16>, tg, dim3(kBlock), 0, s, a);
 }
 
 }  // namespace moe

@@ -64,23 +64,35 @@ __device__ __forceinline__ Span make_span(Located lo, Located hi, int A, const C
   return sp;
 }
 
-// This workgroup's share [c_lo, c_hi) of a class total over G workgroups.
-// floor(total * b / G) in 32-bit arithmetic (total < 2^31, b <= G <= 2^16).
-__device__ __forceinline__ int share_at(int total, int b, int G) {
-  const int q = total / G, r = total - q * G;
-  return q * b + (r * b) / G;
+// How the workgroups of a class weigh against each other: the class starts at launch
+// block B0; blocks at or past ncu (one per compute unit) are dispatched in a second round,
+// start later and share their compute unit, so they take late16 / 16 of a full share.
+struct ShareW {
+  int B0, ncu, late16;
+};
+
+// Start of workgroup b's share of a class total over G workgroups: floor(total * W(b) /
+// W(G)), W the summed weights of the blocks before b (64-bit: total < 2^30, W < 2^21).
+__device__ __forceinline__ int share_at(int total, int b, int G, const ShareW& w) {
+  if (b >= G) return total;
+  auto W = [&](int i) {
+    const int g = w.B0 + i;
+    return (int64_t)16 * min(g, w.ncu) + (int64_t)w.late16 * max(0, g - w.ncu);
+  };
+  const int64_t w0 = W(0);
+  return (int)((int64_t)total * (W(b) - w0) / (W(G) - w0));
 }
-__device__ __forceinline__ void wg_share(int total, int b, int G, int& c_lo, int& c_hi) {
-  c_lo = share_at(total, b, G);
-  c_hi = share_at(total, b + 1, G);
+__device__ __forceinline__ void wg_share(int total, int b, int G, const ShareW& w, int& c_lo, int& c_hi) {
+  c_lo = share_at(total, b, G, w);
+  c_hi = share_at(total, b + 1, G, w);
 }
 
 // The shared expert's span for workgroup b of G: closed form, no table reads.
-__device__ __forceinline__ Span shared_span(int T, const ClassCost& k, int NB, int b, int G) {
+__device__ __forceinline__ Span shared_span(int T, const ClassCost& k, int NB, int b, int G, const ShareW& w) {
   const int units = (T + k.NG - 1) / k.NG;
   const int total = k.steps * (k.cw * units + k.ct * T);
   int c_lo, c_hi;
-  wg_share(total, b, G, c_lo, c_hi);
+  wg_share(total, b, G, w, c_lo, c_hi);
   const Located in{0, T, 0, 0, 0, 0}, end{1, T, total, units, T, -1};
   return make_span(c_lo < total ? in : end, c_hi < total ? in : end, 1, k, c_lo, c_hi, NB);
 }
