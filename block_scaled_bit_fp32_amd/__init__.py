@@ -68,6 +68,8 @@ _SIGNATURES = {
     "moe_route": (_I32, [ctypes.POINTER(LayerT), _P, _I32, _P, _P, _P, _P, _SZ, _P]),
     "moe_expert_forward": (_I32, [ctypes.POINTER(LayerT), _P, _P, _I32, _P, _P, _P, _P, _SZ,
                                   ctypes.POINTER(DebugT), _P]),
+    "moe_forward": (_I32, [ctypes.POINTER(LayerT), _P, _I32, _P, _P, _P, _P, _P, _SZ,
+                           ctypes.POINTER(DebugT), _P]),
     "quantize_nvfp4_4o6": (_I32, [_P, _I32, _I32, _P, _P, _P, _P, _P]),
     "moe_profile_begin": (_I32, []),
     "moe_profile_end": (_I32, [ctypes.POINTER(KernelTimeT), _I32]),
@@ -289,6 +291,27 @@ def expert_forward(layer: DeviceLayer, x: torch.Tensor, xq, ids: torch.Tensor, w
                                    ids.data_ptr(), w.data_ptr(), y.data_ptr(), ws.ptr, ws.nbytes,
                                    ctypes.byref(dbg) if dbg is not None else None, _stream()))
     return (y, dd) if debug else y
+
+
+def forward(layer: DeviceLayer, x: torch.Tensor, ws: Workspace, out=None, path: int = PATH_AUTO):
+    """moe_forward (route and experts in one call): returns (y BF16 [T,H], topk_ids int32
+    [T,k], topk_w FP32 [T,k], xq uint8 or None). ``out`` = (y, ids, w, xq) reuses buffers."""
+    x = _bits16(x)
+    T = x.shape[0]
+    cfg = layer.cfg
+    if out is None:
+        y = torch.empty((T, cfg.H), dtype=torch.bfloat16, device=x.device)
+        ids = torch.empty((T, cfg.k), dtype=torch.int32, device=x.device)
+        w = torch.empty((T, cfg.k), dtype=torch.float32, device=x.device)
+        nq = xq_bytes(layer, T)
+        xq = _aligned_empty(nq, x.device) if nq else None
+    else:
+        y, ids, w, xq = out
+    dbg = DebugT(None, None, None, None, path) if path != PATH_AUTO else None
+    _check(_lib.moe_forward(ctypes.byref(layer.struct), x.data_ptr(), T, ids.data_ptr(), w.data_ptr(),
+                            _ptr(xq), y.data_ptr(), ws.ptr, ws.nbytes,
+                            ctypes.byref(dbg) if dbg is not None else None, _stream()))
+    return y, ids, w, xq
 
 
 def quantize_nvfp4_4o6(x: torch.Tensor, want_choice: bool = True):

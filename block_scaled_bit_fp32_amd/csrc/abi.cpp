@@ -13,7 +13,7 @@ namespace moe {
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 hipError_t launch_quantize_nvfp4(const uint16_t* x, int rows, int cols, uint8_t* codes,
                                  uint8_t* scales, float* g, uint8_t* choice, hipStream_t s);
-hipError_t launch_route(const RouteArgs& a, int n_quant, hipStream_t s);
+hipError_t launch_route(const RouteArgs& a, int n_quant, bool topk, hipStream_t s);
 #define MOE_DECL_EXPERTS(NAME)                                                              \
   hipError_t NAME(const ExpertArgs& gu, int gu_grid, size_t gu_lds, const ExpertArgs& dn,  \
                   int dn_grid, size_t dn_lds, int sf, hipStream_t s);
@@ -105,14 +105,15 @@ struct Plan {
   int max_slots;
   size_t gu_lds, dn_lds, list_bytes, gu_tile, dn_tile;
   bool grouped;                       // batches of kGroupedMinT tokens and up
+  bool token;                         // the down GEMV can run in token mode
   GroupMap gu_rg, gu_sg, dn_rg, dn_sg;
 };
 
 constexpr int kGroupedMinT = 32;      // the grouped (MFMA) kernels from this batch on
-constexpr int kTokPctGateup = 270;    // GEMV cost model: token-term scale (see set_costs)
-constexpr int kTokPctDown = 37;
-constexpr int kLateGateup16 = 14;     // GEMV kernels: weight of a second-round workgroup,
-constexpr int kLateDown16 = 15;       // in 16ths (timestamps: they end ~15% / ~7% later)
+constexpr int kTokPctGateup = 200;    // GEMV cost model: token-term scale (see set_costs)
+constexpr int kTokPctDown = 100;
+constexpr int kLateGateup16 = 13;     // GEMV kernels: weight of a second-round workgroup,
+constexpr int kLateDown16 = 14;       // in 16ths (timestamps: they end ~15% / ~7% later)
 constexpr int kGroupTok = 32;         // tokens per unit in the grouped kernels
 
 // Grouped map of one weight class: rows of K elements, `rows_per_tile` rows (or
@@ -141,8 +142,8 @@ int wbytes_x2(int fmt) { return fmt == W_BF16 ? 4 : (fmt == W_MXFP8 ? 2 : 1); }
 // against activation work (a token costs half a step's weight bytes for FP4 weights and
 // BF16 activations).
 // tok_pct scales the token term: per-workgroup timestamps on the NVFP4 Flint layer at
-// T = 8 put a 4-token BF16 gate/up step at 2.7x a 1-token step (token term x2.7) and a
-// 2-token FP32 down step at 1.4x (token term x0.37).
+// T = 8 put a 4-token BF16 gate/up step at about 2.4x a 1-token step (token term x2);
+// the FP32 down steps fit the byte model (x1).
 void set_costs(GemvMap& m, int fmt, int K, int tok_pct) {
   const int64_t elems = (int64_t)m.RS * K;
   m.cw = (int)std::max<int64_t>(1, elems * wbytes_x2(fmt) / 256);
@@ -188,6 +189,18 @@ bool make_plan(const moe_layer_t& L, int T, int path, Plan& p) {
   };
   p.gu_tile = tile(p.gu_r, L.H, p.gu_s, L.H);
   p.dn_tile = tile(p.dn_r, L.I, p.dn_s, Ish);
+  // token mode of the down GEMV (pair mode; a shared expert of the routed format and
+  // size taking the same FP32 h): the J activation rows of one token in the tile and in
+  // the prologue's registers
+  {
+    const int J = L.k + (L.has_shared ? 1 : 0);
+    const size_t jb = (size_t)J * L.I * p.dn_r.esize;
+    const size_t room = 64 * 1024 > p.list_bytes ? 64 * 1024 - p.list_bytes : 0;
+    p.token = nt * L.k <= kPairMax &&
+              (!L.has_shared || (sfmt == L.wfmt && Ish == L.I && L.afmt == A_BF16)) &&
+              jb <= (size_t)kParkBytes && jb <= room;
+    if (p.token) p.dn_tile = std::max(p.dn_tile, align_up(jb, 16));
+  }
   p.gu_lds = p.list_bytes + p.gu_tile;
   p.dn_lds = p.list_bytes + p.dn_tile;
   // grouped kernels: gate/up tiles of 64 intermediate indices, down tiles of 128 rows
@@ -405,8 +418,15 @@ moe_status_t moe_workspace_init(void* ws, size_t ws_bytes, hipStream_t stream) {
   return MOE_OK;
 }
 
-moe_status_t moe_route(const moe_layer_t* L, const uint16_t* x_bf16, int32_t T, int32_t* topk_ids,
-                       float* topk_w, void* xq, void* ws, size_t ws_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Router GEMV (+ token quantization) and, if `topk`, the top-k launch.
+// dry: check the arguments only.
+moe_status_t enqueue_route(const moe_layer_t* L, const uint16_t* x_bf16, int32_t T, int32_t* topk_ids,
+                           float* topk_w, void* xq, void* ws, size_t ws_bytes, bool topk, bool dry,
+                           hipStream_t stream) {
   moe_status_t st = check_or_fail(L, std::max(1, T));
   if (st != MOE_OK) return st;
   if (T < 0) return set_err(MOE_EINVAL, "T must be >= 0");
@@ -419,6 +439,7 @@ moe_status_t moe_route(const moe_layer_t* L, const uint16_t* x_bf16, int32_t T, 
   if (!bad.empty()) return set_err(MOE_EINVAL, bad);
   WsLayout w;
   if ((st = check_ws(*L, T, ws, ws_bytes, w)) != MOE_OK) return st;
+  if (dry) return MOE_OK;
   uint8_t* base = static_cast<uint8_t*>(ws);
   RouteArgs a{};
   a.x = x_bf16;
@@ -444,13 +465,23 @@ moe_status_t moe_route(const moe_layer_t* L, const uint16_t* x_bf16, int32_t T, 
     }
     n_quant = T;
   }
-  if (launch_route(a, n_quant, stream) != hipSuccess) return set_err(MOE_ELAUNCH, "route kernel launch failed");
+  if (launch_route(a, n_quant, topk, stream) != hipSuccess) return set_err(MOE_ELAUNCH, "route kernel launch failed");
   return MOE_OK;
 }
 
-moe_status_t moe_expert_forward(const moe_layer_t* L, const uint16_t* x_bf16, const void* xq, int32_t T,
-                                const int32_t* topk_ids, const float* topk_w, uint16_t* y_bf16,
-                                void* ws, size_t ws_bytes, const moe_debug_t* dbg, hipStream_t stream) {
+// Whether the experts of a T-token call run the GEMV kernels in pair mode, where the
+// gate/up kernel can do the routing itself (for E <= 64 * kFusedTopkSlots).
+bool pair_mode_plan(const moe_layer_t& L, int T, int path) {
+  Plan p;
+  return T * L.k <= kPairMax && L.E <= 64 * kFusedTopkSlots && make_plan(L, T, path, p) && !p.grouped;
+}
+
+// Expert kernels (and combine); with fused_topk the gate/up kernel selects the experts
+// from the router logits in the workspace and writes topk_ids / topk_w itself.
+moe_status_t enqueue_experts(const moe_layer_t* L, const uint16_t* x_bf16, const void* xq, int32_t T,
+                             const int32_t* topk_ids, const float* topk_w, uint16_t* y_bf16, void* ws,
+                             size_t ws_bytes, const moe_debug_t* dbg, bool fused_topk, bool dry,
+                             hipStream_t stream) {
   moe_status_t st = check_or_fail(L, std::max(1, T));
   if (st != MOE_OK) return st;
   if (T < 0) return set_err(MOE_EINVAL, "T must be >= 0");
@@ -475,6 +506,8 @@ moe_status_t moe_expert_forward(const moe_layer_t* L, const uint16_t* x_bf16, co
   if (!make_plan(*L, T, path, p)) return set_err(MOE_EUNSUPPORTED, "no launch plan");
   if (path == MOE_PATH_GROUPED && !p.grouped)
     return set_err(MOE_EUNSUPPORTED, "grouped kernels need K and rows that tile (H, I multiples of the stage and tile sizes)");
+  if (fused_topk && (p.grouped || T * L->k > kPairMax)) return set_err(MOE_EINVAL, "fused routing needs pair mode");
+  if (dry) return MOE_OK;
   uint8_t* base = static_cast<uint8_t*>(ws);
   const int Ish = L->has_shared ? L->I_shared : L->I;
   const int sfmt = L->has_shared ? L->shared_wfmt : L->wfmt;
@@ -539,15 +572,59 @@ moe_status_t moe_expert_forward(const moe_layer_t* L, const uint16_t* x_bf16, co
   } else {
     const bool pm = T * L->k <= kPairMax;
     gu.pair_mode = dn.pair_mode = pm ? 1 : 0;
+    if (fused_topk) {
+      gu.fuse_topk = 1;
+      gu.logits = reinterpret_cast<const float*>(base + w.logits);
+      gu.ids_out = const_cast<int32_t*>(topk_ids);
+      gu.w_out = const_cast<float*>(topk_w);
+    }
+    // token mode needs enough (token, row-step) items to occupy every compute unit
+    dn.token_mode = pm && p.token && T * (L->H / p.dn_r.RS) >= ncu ? 1 : 0;
     auto q = [](const GemvMap& m, int steps) { return CostQ{m.NG, steps, m.cw, m.ct}; };
     gu.sh_wgs = shared_wgs(*L, T, q(p.gu_s, Ish_ / (p.gu_s.RS / 2)), q(p.gu_r, L->I / (p.gu_r.RS / 2)), gu_grid,
                            ncu, gu.late16, pm);
-    dn.sh_wgs = shared_wgs(*L, T, q(p.dn_s, L->H / p.dn_s.RS), q(p.dn_r, L->H / p.dn_r.RS), dn_grid,
-                           ncu, dn.late16, pm);
+    dn.sh_wgs = dn.token_mode ? 0
+                              : shared_wgs(*L, T, q(p.dn_s, L->H / p.dn_s.RS), q(p.dn_r, L->H / p.dn_r.RS),
+                                           dn_grid, ncu, dn.late16, pm);
   }
   if (launch_experts(gu, gu_grid, p.gu_lds, dn, dn_grid, p.dn_lds, stream) != hipSuccess)
     return set_err(MOE_ELAUNCH, "expert kernel launch failed");
   return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status_t moe_route(const moe_layer_t* L, const uint16_t* x_bf16, int32_t T, int32_t* topk_ids,
+                       float* topk_w, void* xq, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return enqueue_route(L, x_bf16, T, topk_ids, topk_w, xq, ws, ws_bytes, true, false, stream);
+}
+
+moe_status_t moe_expert_forward(const moe_layer_t* L, const uint16_t* x_bf16, const void* xq, int32_t T,
+                                const int32_t* topk_ids, const float* topk_w, uint16_t* y_bf16,
+                                void* ws, size_t ws_bytes, const moe_debug_t* dbg, hipStream_t stream) {
+  return enqueue_experts(L, x_bf16, xq, T, topk_ids, topk_w, y_bf16, ws, ws_bytes, dbg, false, false, stream);
+}
+
+moe_status_t moe_forward(const moe_layer_t* L, const uint16_t* x_bf16, int32_t T, int32_t* topk_ids,
+                         float* topk_w, void* xq, uint16_t* y_bf16, void* ws, size_t ws_bytes,
+                         const moe_debug_t* dbg, hipStream_t stream) {
+  moe_status_t st = check_or_fail(L, std::max(1, T));
+  if (st != MOE_OK) return st;
+  if (T < 0) return set_err(MOE_EINVAL, "T must be >= 0");
+  if (T == 0) return MOE_OK;
+  const int path = dbg ? dbg->path : MOE_PATH_AUTO;
+  if (path < MOE_PATH_AUTO || path > MOE_PATH_GROUPED) return set_err(MOE_EINVAL, "dbg->path is not a moe_path_t");
+  const bool fused = pair_mode_plan(*L, T, path);
+  // every check of both halves before the first launch
+  if ((st = enqueue_route(L, x_bf16, T, topk_ids, topk_w, xq, ws, ws_bytes, !fused, true, stream)) != MOE_OK ||
+      (st = enqueue_experts(L, x_bf16, xq, T, topk_ids, topk_w, y_bf16, ws, ws_bytes, dbg, fused, true, stream)) !=
+          MOE_OK)
+    return st;
+  if ((st = enqueue_route(L, x_bf16, T, topk_ids, topk_w, xq, ws, ws_bytes, !fused, false, stream)) != MOE_OK)
+    return st;
+  return enqueue_experts(L, x_bf16, xq, T, topk_ids, topk_w, y_bf16, ws, ws_bytes, dbg, fused, false, stream);
 }
 
 moe_status_t quantize_nvfp4_4o6(const uint16_t* x_bf16, int32_t rows, int32_t cols, uint8_t* codes,

@@ -113,6 +113,20 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t k) {
   return r;
 }
 
+// The same for 32-bit values (maximum, and minimum), returned as a scalar.
+template <bool MAX>
+__device__ __forceinline__ uint32_t wave_ext_u32(uint32_t k) {
+  auto pick = [](uint32_t a, uint32_t b) { return MAX ? (a > b ? a : b) : (a < b ? a : b); };
+  k = pick(k, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)k, 0xB1, 0xF, 0xF, false));    // quad_perm [1,0,3,2]
+  k = pick(k, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)k, 0x4E, 0xF, 0xF, false));    // quad_perm [2,3,0,1]
+  k = pick(k, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)k, 0x124, 0xF, 0xF, false));   // row_ror:4
+  k = pick(k, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)k, 0x128, 0xF, 0xF, false));   // row_ror:8
+  uint32_t r = (uint32_t)__builtin_amdgcn_readlane((int)k, 0);
+  r = pick(r, (uint32_t)__builtin_amdgcn_readlane((int)k, 16));
+  r = pick(r, (uint32_t)__builtin_amdgcn_readlane((int)k, 32));
+  return pick(r, (uint32_t)__builtin_amdgcn_readlane((int)k, 48));
+}
+
 // Wave-wide inclusive prefix sum (lane i gets the sum over lanes 0..i). Within each row
 // of 16 lanes, DPP row shifts by 1, 2, 4, 8 (lanes shifted in from outside the row add
 // 0); then row_bcast:15 adds row 0's and row 2's totals to rows 1 and 3, and

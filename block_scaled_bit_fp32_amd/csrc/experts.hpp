@@ -22,6 +22,7 @@
 #include "launch.hpp"
 #include "rows.hpp"
 #include "span.hpp"
+#include "topk.hpp"
 
 namespace moe {
 
@@ -139,6 +140,7 @@ __device__ __forceinline__ void stage_tile(uint8_t* tile, const GemvMap& m, int 
 // thread): the loads are issued before the first weight loads and stored afterwards, so
 // waiting for them never waits for weight bytes (vector-memory counters retire in order).
 constexpr int kPreSlots = 12;
+static_assert(kPreSlots * kBlock * 16 == kParkBytes, "prologue register slots");
 // Every slot issues its load (slots past the rows re-read the last one): one basic block,
 // no per-slot branches. nt >= 1.
 template <int AK, class Ld>
@@ -510,11 +512,33 @@ __device__ __forceinline__ Span pair_span(const ExpertArgs& a, const ClassCost& 
   sp.left = (l1 - l0) * NB;
   sp.row_limit = (l1 + steps - 1) / steps;
   sp.e0 = 0;
-  if (sp.a0 < P) {
-    const int e = a.ids[sp.a0];
-    sp.e0 = (unsigned)e < (unsigned)a.E ? e : 0;
-  }
   return sp;
+}
+
+// Routing fused into the gate/up kernel (pair mode): the workgroup selects the experts of
+// the tokens its span touches from their router logits (wave_topk, one wave per token),
+// puts them in LDS (L.ids) and writes them, with the weights, to ids_out / w_out (every
+// workgroup touching a token writes the same values). Whole-workgroup call; ends with an
+// LDS barrier.
+__device__ __forceinline__ void fused_topk(const ExpertArgs& a, const ExpertLds& L, const Span& sp) {
+  if (sp.left > 0) {
+    const int t_lo = sp.a0 / a.k, t_hi = (sp.row_limit - 1) / a.k;
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    for (int tb = t_lo; tb <= t_hi; tb += kBlock / kWave) {
+      const int t = tb + wave;
+      if (t <= t_hi) {
+        int e;
+        float w;
+        wave_topk<kFusedTopkSlots>(a.logits + (int64_t)t * a.E, a.E, a.k, e, w);
+        if (lane < a.k) {
+          L.ids[t * a.k + lane] = e;
+          a.ids_out[t * a.k + lane] = e;
+          a.w_out[t * a.k + lane] = w;
+        }
+      }
+    }
+  }
+  lds_barrier();
 }
 
 __device__ __forceinline__ Span read_span(const ExpertLds& L) {
@@ -724,7 +748,9 @@ __device__ __forceinline__ void walk_class(const WTensor& W, const GemvMap& m, c
 #pragma unroll
   for (int j = 0; j < kGsPer; ++j) gsv[j] = gsrc[min((int)threadIdx.x + j * kBlock, gmax)];
   int idv = 0;
-  if constexpr (VW == VW_PAIR) idv = ids[min((int)threadIdx.x, V.P - 1)];
+  if constexpr (VW == VW_PAIR) {
+    if (ids) idv = ids[min((int)threadIdx.x, V.P - 1)];
+  }
   Cursor pa{sp.a0, sp.g0, sp.s0, 0, sp.e0, sp.n0, sp.rb0}, pb = pa;
   WeightRegs<RPL> A_, B_;
   {
@@ -740,7 +766,7 @@ __device__ __forceinline__ void walk_class(const WTensor& W, const GemvMap& m, c
     if (i < ngs) gs_tab[i] = W.gscale ? gsv[j] : 1.0f;
   }
   if constexpr (VW == VW_PAIR) {
-    if ((int)threadIdx.x < V.P) L.ids[threadIdx.x] = idv;
+    if (ids && (int)threadIdx.x < V.P) L.ids[threadIdx.x] = idv;
   }
   lds_barrier();
   using Yes = std::integral_constant<bool, true>;
@@ -855,7 +881,8 @@ __device__ __forceinline__ ClassView<VW> class_view(const ExpertArgs& a, const E
 }
 
 template <int FMT, int AF, int VW>
-__device__ __forceinline__ void gateup_walk(const ExpertArgs& a, const ExpertLds& L, const Span& sp) {
+__device__ __forceinline__ void gateup_walk(const ExpertArgs& a, const ExpertLds& L, const Span& sp,
+                                            const int32_t* ids) {
   constexpr bool routed = VW != VW_SHARED;
   const WTensor& W = routed ? a.rw : a.sw;
   const GemvMap& m = routed ? a.rmap : a.smap;
@@ -864,7 +891,7 @@ __device__ __forceinline__ void gateup_walk(const ExpertArgs& a, const ExpertLds
   const GateupOps<AF> op{a.x, a.xq_codes, a.xq_scales, a.xq_scale, W.gscale, W.gs_per_expert, W.rows, Iexp,
                          4 * m.G, a.H, a.hs, a.h, a.dbg_h, gs_tab, L.w_tsc, nullptr};
   walk_class<FMT, 0, 2, VW>(W, m, L, a.lds_act_bytes, class_view<VW>(a, L), gateup_cost(a, routed), sp, op,
-                            gs_tab, (routed ? a.E : 1) * W.gs_per_expert, a.ids);
+                            gs_tab, (routed ? a.E : 1) * W.gs_per_expert, ids);
 }
 
 // Workgroups [0, sh_wgs) walk the shared expert (BF16 activations, no dependency on the
@@ -877,14 +904,22 @@ __global__ void __launch_bounds__(kBlock, 2) gateup_kernel(ExpertArgs a) {
   if (shared) {
     const Span sp = shared_span(a.T, gateup_cost(a, false), a.smap.NB, blockIdx.x, a.sh_wgs,
                                 ShareW{0, a.ncu, a.late16});
-    gateup_walk<SF, A_BF16, VW_SHARED>(a, L, sp);
+    gateup_walk<SF, A_BF16, VW_SHARED>(a, L, sp, nullptr);
   } else if (a.pair_mode) {
-    const Span sp = pair_span(a, gateup_cost(a, true), a.rmap.NB, blockIdx.x - a.sh_wgs, gridDim.x - a.sh_wgs);
-    gateup_walk<RF, AF, VW_PAIR>(a, L, sp);
+    Span sp = pair_span(a, gateup_cost(a, true), a.rmap.NB, blockIdx.x - a.sh_wgs, gridDim.x - a.sh_wgs);
+    const int P = a.T * a.k;
+    if (a.fuse_topk) {
+      fused_topk(a, L, sp);
+      if (sp.a0 < P) sp.e0 = uni(L.ids[sp.a0]);
+    } else if (sp.a0 < P) {
+      sp.e0 = a.ids[sp.a0];
+    }
+    sp.e0 = (unsigned)sp.e0 < (unsigned)a.E ? sp.e0 : 0;
+    gateup_walk<RF, AF, VW_PAIR>(a, L, sp, a.fuse_topk ? nullptr : a.ids);
   } else {
     build_routed(a, L, L.rt, gateup_cost(a, true), a.rmap.NB, blockIdx.x - a.sh_wgs, gridDim.x - a.sh_wgs);
     build_rows(a, L, L.rt);
-    gateup_walk<RF, AF, VW_TAB>(a, L, read_span(L));
+    gateup_walk<RF, AF, VW_TAB>(a, L, read_span(L), nullptr);
   }
 }
 
@@ -954,17 +989,158 @@ __device__ __forceinline__ void down_walk(const ExpertArgs& a, const ExpertLds& 
                                                (routed ? a.E : 1) * W.gs_per_expert, a.ids);
 }
 
+// Token mode of the down projection (pair mode, when the shared expert, if any, has the
+// routed format and size and takes the same FP32 h): a work item is (token t, row-step
+// s), i.e. RS hidden rows of y[t]; it walks the token's J = k (+1 shared) experts in turn
+// (sub-steps j), scales each sub-step's dot products by its combine weight, global weight
+// scale and activation scale, and writes the BF16 sum: the weighted combine happens in
+// registers, with no per-pair output. Items split evenly over the workgroups. The J
+// activation rows of the current token sit in LDS (rows j of the tile); the first
+// token's are loaded before the first weight loads, as in walk_class.
+template <int FMT, int AK, int AF>
+__device__ __forceinline__ void walk_tokens(const ExpertArgs& a, const ExpertLds& L, int i0, int i1) {
+  constexpr int EPL = elems_per_piece(FMT);
+  if (i1 <= i0) return;
+  const GemvMap& m = a.rmap;
+  const int steps = a.H / m.RS, J = a.k + a.has_shared, P = a.T * a.k;
+  int left = (i1 - i0) * J * m.NB;
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int jl = lane % m.LPR, lrow = wave * m.G + lane / m.LPR;
+  const int tstride = a.rw.K * m.esize;
+  const DownOps<AF> op{a.h, a.hq_codes, a.hq_scales, a.hq_scale, a.rw.gscale, a.rw.gs_per_expert, a.rw.rows,
+                       a.I, m.RS, a.H, a.hs, a.o, L.gs_rt, L.w_tsc, nullptr};
+  auto pair_of = [&](int t, int j) { return j < a.k ? t * a.k + j : P + t; };
+  // cursor: token t, row-step s, sub-step j, batch b, expert e of (t, j)
+  struct TCur {
+    int t, s, j, b, e;
+  };
+  auto expert_of = [&](int t, int j) {
+    if (j >= a.k) return 0;
+    const int v = uni(L.ids[t * a.k + j]);
+    return (unsigned)v < (unsigned)a.E ? v : 0;
+  };
+  auto advance = [&](TCur& c) {
+    if (++c.b < m.NB) return;
+    c.b = 0;
+    if (++c.j == J) {
+      c.j = 0;
+      if (++c.s == steps) { c.s = 0; ++c.t; }
+    }
+    c.e = expert_of(c.t, c.j);
+  };
+  auto fetch = [&](const TCur& c, WeightRegs<1>& R) {
+    WTensor W = a.rw;
+    if (c.j >= a.k) { W.codes = a.sw.codes; W.scales = a.sw.scales; }
+    const int64_t r[1] = {(int64_t)c.e * W.rows + c.s * m.RS + lrow};
+    fetch_batch<FMT, 1>(W, m, r, c.b, jl, R);
+  };
+  auto row_ld = [&](int t) {
+    return [&, t](int j, int el) { return op.ld(t, pair_of(t, j), el); };
+  };
+  // per-row factor: combine weight (1 for the shared row) times activation scale
+  auto row_fac = [&](int t, int j) {
+    const int p = pair_of(t, j);
+    return op.tsc(t, p) * (j < a.k ? a.topk_w[p] : 1.0f);
+  };
+  int staged_t = i0 / steps;
+  auto stage = [&](int t) {
+    lds_barrier();
+    stage_tile<AK, EPL>(L.tile, m, a.rw.K, J, row_ld(t), [&](uint4 r) { return op.cv(r); });
+    if ((int)threadIdx.x < J) L.w_tsc[threadIdx.x] = row_fac(t, threadIdx.x);
+    staged_t = t;
+    lds_barrier();
+  };
+  float part[1][4], tot = 0.0f;
+  auto do_step = [&](auto pf, const TCur& c, WeightRegs<1>& cur, WeightRegs<1>& nxt, TCur& nc) {
+    if (c.t != staged_t) stage(c.t);
+    if (c.b == 0) part[0][0] = 0.0f;
+    if constexpr (decltype(pf)::value) {
+      nc = c;
+      advance(nc);
+      fetch(nc, nxt);
+    }
+    const uint8_t* tile = L.tile + c.j * tstride;
+#pragma unroll
+    for (int i = 0; i < WeightRegs<1>::NPB; ++i)
+      if (i < m.NPB) accumulate_piece<FMT, AK, 1, 1>(cur.w[i], cur.s[i], tile, tstride, m.LPR, c.b * m.NPB + i, jl, part);
+    if (c.b == m.NB - 1) {
+      const float g = c.j < a.k ? L.gs_rt[c.e * a.rw.gs_per_expert] : L.gs_sh[0];
+      tot = fmaf(L.w_tsc[c.j] * g, part[0][0], tot);
+      if (c.j == J - 1) {
+        float v = tot;
+        for (int o = m.LPR / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+        if (jl == 0) a.y[(int64_t)c.t * a.H + c.s * m.RS + lrow] = (uint16_t)f32_to_bf16_rne(v);
+        tot = 0.0f;
+      }
+    }
+  };
+  // prologue: the first token's rows, factors, global scales and topk_ids, then the first
+  // weight loads, then LDS
+  uint4 raw[kPreSlots];
+  const SlotMap<AK> smap(m, a.rw.K);
+  park_rows<AK>(smap, J, row_ld(staged_t), raw);
+  const float fac_r = row_fac(staged_t, min((int)threadIdx.x, J - 1));
+  const int ngs = a.E * a.rw.gs_per_expert;
+  const float* gsrc = a.rw.gscale ? a.rw.gscale : reinterpret_cast<const float*>(a.rw.codes);
+  const int gmax = a.rw.gscale ? ngs - 1 : 0;
+  float gsv[kGsPer];
+#pragma unroll
+  for (int j = 0; j < kGsPer; ++j) gsv[j] = gsrc[min((int)threadIdx.x + j * kBlock, gmax)];
+  const float* ssrc = a.sw.gscale ? a.sw.gscale : reinterpret_cast<const float*>(a.sw.codes);
+  const float gss = ssrc[0];
+  const int idv = a.ids[min((int)threadIdx.x, P - 1)];
+  TCur ca{staged_t, i0 - staged_t * steps, 0, 0, 0}, cb = ca;
+  {
+    const int v = a.ids[staged_t * a.k];
+    ca.e = (unsigned)v < (unsigned)a.E ? v : 0;
+  }
+  WeightRegs<1> A_, B_;
+  fetch(ca, A_);
+  unpark_rows<AK, EPL>(smap, L.tile, J, [&](uint4 r) { return op.cv(r); }, raw);
+  if ((int)threadIdx.x < J) L.w_tsc[threadIdx.x] = fac_r;
+#pragma unroll
+  for (int j = 0; j < kGsPer; ++j) {
+    const int i = threadIdx.x + j * kBlock;
+    if (i < ngs) L.gs_rt[i] = a.rw.gscale ? gsv[j] : 1.0f;
+  }
+  if (threadIdx.x == 0) L.gs_sh[0] = a.sw.gscale ? gss : 1.0f;
+  if ((int)threadIdx.x < P) L.ids[threadIdx.x] = idv;
+  lds_barrier();
+  using Yes = std::integral_constant<bool, true>;
+  using No = std::integral_constant<bool, false>;
+  while (true) {
+    if (left == 1) { do_step(No{}, ca, A_, B_, cb); break; }
+    do_step(Yes{}, ca, A_, B_, cb);
+    if (left == 2) { do_step(No{}, cb, B_, A_, ca); break; }
+    do_step(Yes{}, cb, B_, A_, ca);
+    left -= 2;
+  }
+}
+
 template <int RF, int SF, int AF>
 __global__ void __launch_bounds__(kBlock, 2) down_kernel(ExpertArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
   ExpertLds L = carve(a, smem);
+  if constexpr (SF == RF) {
+    if (a.token_mode) {
+      const int total = a.T * (a.H / a.rmap.RS);
+      const ShareW w{0, a.ncu, a.late16};
+      walk_tokens<RF, AF == A_BF16 ? 1 : 0, AF>(a, L, share_at(total, blockIdx.x, gridDim.x, w),
+                                                share_at(total, blockIdx.x + 1, gridDim.x, w));
+      return;
+    }
+  }
   const bool shared = (int)blockIdx.x < a.sh_wgs;
   if (shared) {
     const Span sp = shared_span(a.T, down_cost(a, false), a.smap.NB, blockIdx.x, a.sh_wgs,
                                 ShareW{0, a.ncu, a.late16});
     down_walk<SF, A_BF16, VW_SHARED>(a, L, sp);
   } else if (a.pair_mode) {
-    const Span sp = pair_span(a, down_cost(a, true), a.rmap.NB, blockIdx.x - a.sh_wgs, gridDim.x - a.sh_wgs);
+    Span sp = pair_span(a, down_cost(a, true), a.rmap.NB, blockIdx.x - a.sh_wgs, gridDim.x - a.sh_wgs);
+    if (sp.a0 < a.T * a.k) {
+      const int e = a.ids[sp.a0];
+      sp.e0 = (unsigned)e < (unsigned)a.E ? e : 0;
+    }
     down_walk<RF, AF, VW_PAIR>(a, L, sp);
   } else {
     build_routed(a, L, L.rt, down_cost(a, true), a.rmap.NB, blockIdx.x - a.sh_wgs, gridDim.x - a.sh_wgs);
@@ -995,7 +1171,7 @@ hipError_t launch_experts_af(const ExpertArgs& gu, int gu_grid, size_t gu_lds,
       ? launch_kernel(K_DOWN, gdown_kernel<RF, SF, AF>, dim3(dn_grid), dim3(kBlock), dn_lds, s, dn)
       : launch_kernel(K_DOWN, down_kernel<RF, SF, AF>, dim3(dn_grid), dim3(kBlock), dn_lds, s, dn);
   if (err != hipSuccess) return err;
-  return launch_combine(dn, s);
+  return dn.token_mode ? hipSuccess : launch_combine(dn, s);
 }
 
 // The activation formats each routed weight format supports (the ABI checks refuse the

@@ -28,6 +28,8 @@ struct GemvMap {
 
 constexpr int kWinRows = 64;   // most token rows one staged window of units holds
 constexpr int kPairMax = 64;   // GEMV kernels: one unit per (token, expert) pair up to this many pairs
+constexpr int kFusedTopkSlots = 8;          // routing fused into gate/up: E <= 64 * this
+constexpr int kParkBytes = 12 * 256 * 16;   // activation bytes a workgroup's prologue holds in registers
 
 // Routed class table capacity: one entry per selected expert, or per pair in pair mode.
 inline constexpr int routed_capacity(int E, int P) { return P <= kPairMax ? P : (E < P ? E : P); }
@@ -98,6 +100,12 @@ struct ExpertArgs {
   GroupMap rgm, sgm;     // grouped kernels (batches of 32 tokens and up)
   int grouped;           // run the grouped kernels
   int pair_mode;         // GEMV kernels: one unit per (token, expert) pair
+  int token_mode;        // down GEMV: items (token, row-step) over all of a token's
+                         // experts, writing y (no combine launch)
+  int fuse_topk;         // gate/up GEMV in pair mode: routing from logits in the prologue,
+  const float* logits;   // writing ids_out / w_out (the buffers ids / topk_w point at)
+  int32_t* ids_out;
+  float* w_out;
   int T, H, I, Ish, E, k, has_shared, afmt;
   int max_slots;         // routed expert slots launched: min(E, T * k)
   int sh_wgs;            // workgroups of the launch that walk the shared expert

@@ -5,6 +5,7 @@
 
 #include "launch.hpp"
 #include "rows.hpp"
+#include "topk.hpp"
 
 namespace moe {
 
@@ -93,56 +94,18 @@ __global__ void __launch_bounds__(kBlock) route_gemv_kernel(RouteArgs a) {
   }
 }
 
-// Top-k: one wave per token, k rounds of a wave argmax. The key (order-preserving bits
-// of the logit, then the complement of the expert index) makes "larger logit, then
-// lower index" a plain unsigned maximum. Expert e sits in lane e % 64, slot e / 64 (NK
-// slots cover E <= 64 * NK); each lane keeps the best of its slots, and only the lane
-// that lost its best to a round rescans them. Weights = sigmoid of the selected logits,
-// renormalized in selection order.
+// Top-k: one wave per token (wave_topk).
 template <int NK>
 __global__ void __launch_bounds__(kBlock) topk_kernel(RouteArgs a) {
   const int lane = threadIdx.x & (kWave - 1);
   const int t = blockIdx.x * (kBlock / kWave) + threadIdx.x / kWave;
   if (t >= a.T) return;
-  const float* lg = a.logits + (int64_t)t * a.E;
-  uint64_t key[NK];
-  float lv[NK];
-#pragma unroll
-  for (int i = 0; i < NK; ++i) lv[i] = lg[min(lane + kWave * i, a.E - 1)];
-#pragma unroll
-  for (int i = 0; i < NK; ++i) {
-    const int e = lane + kWave * i;
-    key[i] = e < a.E ? ((uint64_t)float_order_key(lv[i]) << 32) | (0xFFFFFFFFu - (uint32_t)e) : 0ull;
-  }
-  auto local_best = [&]() {
-    uint64_t b = key[0];
-#pragma unroll
-    for (int i = 1; i < NK; ++i) b = key[i] > b ? key[i] : b;
-    return b;
-  };
-  uint64_t lb = local_best();
-  float myv = 0.0f;
-  int mye = 0;
-  for (int j = 0; j < a.k; ++j) {
-    const uint64_t best = wave_max_u64(lb);
-    const int be = (int)(0xFFFFFFFFu - (uint32_t)best);
-    if (lane == (be & (kWave - 1))) {
-#pragma unroll
-      for (int i = 0; i < NK; ++i)
-        if (i == be / kWave) key[i] = 0ull;      // taken
-      lb = local_best();
-    }
-    if (lane == j) {
-      myv = float_from_order_key((uint32_t)(best >> 32));
-      mye = be;
-    }
-  }
-  const float s = lane < a.k ? 1.0f / (1.0f + expf(-myv)) : 0.0f;
-  float tot = 0.0f;
-  for (int j = 0; j < a.k; ++j) tot += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s), j));
+  int e;
+  float w;
+  wave_topk<NK>(a.logits + (int64_t)t * a.E, a.E, a.k, e, w);
   if (lane < a.k) {
-    a.ids[(int64_t)t * a.k + lane] = mye;
-    a.w[(int64_t)t * a.k + lane] = s / tot;
+    a.ids[(int64_t)t * a.k + lane] = e;
+    a.w[(int64_t)t * a.k + lane] = w;
   }
 }
 
@@ -165,12 +128,12 @@ hipError_t launch_quantize_nvfp4(const uint16_t* x, int rows, int cols, uint8_t*
                        scales, g, choice);
 }
 
-hipError_t launch_route(const RouteArgs& a, int n_quant, hipStream_t s) {
+hipError_t launch_route(const RouteArgs& a, int n_quant, bool topk, hipStream_t s) {
   const int grid = a.n_tt * a.n_et + n_quant;
   hipError_t err = a.ET == 1
       ? launch_kernel(K_ROUTE, route_gemv_kernel<1, 8>, dim3(grid), dim3(kBlock), 0, s, a)
       : launch_kernel(K_ROUTE, route_gemv_kernel<4, 8>, dim3(grid), dim3(kBlock), 0, s, a);
-  if (err != hipSuccess) return err;
+  if (err != hipSuccess || !topk) return err;
   const dim3 tg((a.T + kBlock / kWave - 1) / (kBlock / kWave));
   if (a.E <= 64) return launch_kernel(K_TOPK, topk_kernel<1>, tg, dim3(kBlock), 0, s, a);
   if (a.E <= 128) return launch_kernel(K_TOPK, topk_kernel<2>, tg, dim3(kBlock), 0, s, a);

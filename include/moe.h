@@ -21,8 +21,8 @@
  * Conventions for every entry point:
  *   - Tensor pointers are DEVICE pointers owned by the caller (e.g. a torch tensor's
  *     data_ptr()). The library never allocates, frees or synchronizes inside
- *     moe_route, moe_expert_forward or quantize_nvfp4_4o6; they enqueue kernels on
- *     `stream` and return.
+ *     moe_route, moe_expert_forward, moe_forward or quantize_nvfp4_4o6; they enqueue
+ *     kernels on `stream` and return.
  *   - Every entry returns a moe_status_t and never throws. Arguments are validated
  *     before anything is launched; on error nothing is enqueued and moe_last_error()
  *     returns a message (thread-local) naming every problem found.
@@ -162,6 +162,18 @@ moe_status_t moe_expert_forward(const moe_layer_t *L, const uint16_t *x_bf16,
                                 const float *topk_w, uint16_t *y_bf16, void *ws,
                                 size_t ws_bytes, const moe_debug_t *dbg,
                                 hipStream_t stream);
+
+/* The whole layer in one call: moe_route then moe_expert_forward, with the arguments,
+ * layouts, results and checks of both (topk_ids / topk_w are outputs; xq is written
+ * and read). Where the experts run the GEMV kernels in pair mode (T*k <= 64, not the
+ * grouped kernels), the top-k runs inside the gate/up kernel's prologue, from the
+ * router logits in ws, instead of in a launch of its own: the same selection and
+ * weights as moe_route (the Flint page's low-latency decode path, routing fused into
+ * the neighbouring kernels). Arguments are all validated before the first launch. */
+moe_status_t moe_forward(const moe_layer_t *L, const uint16_t *x_bf16, int32_t T,
+                         int32_t *topk_ids, float *topk_w, void *xq, uint16_t *y_bf16,
+                         void *ws, size_t ws_bytes, const moe_debug_t *dbg,
+                         hipStream_t stream);
 
 /* Four-Over-Six NVFP4 quantization of rows x[rows][cols] (BF16), cols % 16 == 0
  * ("Inkling 2 Small on vLLM: Day-0 Support", mixed-precision MoE and Four-Over-Six

@@ -19,7 +19,7 @@ def _declared_functions():
 
 def test_header_declares_the_boundary():
     names = _declared_functions()
-    for n in ("moe_route", "moe_expert_forward", "quantize_nvfp4_4o6", "moe_layer_check",
+    for n in ("moe_route", "moe_expert_forward", "moe_forward", "quantize_nvfp4_4o6", "moe_layer_check",
               "moe_workspace_bytes", "moe_workspace_init", "moe_xq_bytes", "moe_last_error",
               "moe_abi_version"):
         assert n in names
@@ -102,6 +102,16 @@ def test_calls_validate_before_launching(lib):
     assert so.moe_route(None, None, 1, None, None, None, None, 0, None) == lib.MOE_EINVAL
     # zero rows / zero tokens enqueue nothing and succeed
     assert so.quantize_nvfp4_4o6(None, 0, 32, None, None, None, None, None) == 0
+    # moe_forward: every check of both halves before the first launch
+    st = so.moe_forward(ctypes.byref(s), 1 << 20, 1, 1 << 20, 1 << 20, None, None, 1 << 20, 1 << 24, None, None)
+    assert st == lib.MOE_EINVAL and "y_bf16" in so.moe_last_error().decode()
+    st = so.moe_forward(ctypes.byref(s), None, 1, None, None, None, 1 << 20, 1 << 20, 1 << 24, None, None)
+    assert st == lib.MOE_EINVAL
+    msg = so.moe_last_error().decode()
+    assert "x_bf16" in msg and "topk_ids" in msg
+    st = so.moe_forward(ctypes.byref(s), 1 << 20, 1, 1 << 20, 1 << 20, None, 1 << 20, 1 << 20, 16, None, None)
+    assert st == lib.MOE_EWORKSPACE
+    assert so.moe_forward(ctypes.byref(s), None, 0, None, None, None, None, None, 0, None, None) == 0
 
 
 def test_xq_bytes_layout(lib):

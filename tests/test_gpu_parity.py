@@ -156,6 +156,42 @@ def test_layer_parity(lib, name, T, path):
         assert ok, (max_abs, rel)
 
 
+# moe_forward: routing fused into the gate/up kernel (pair mode) or the two launches
+# (larger batches); the same ids, weights, quantized tokens and y as moe_route followed
+# by moe_expert_forward, bit for bit, and the oracle's routing and output.
+FORWARD_CASES = [("tiny_bf16", 1), ("tiny_bf16", 8), ("flint_w4a16", 1), ("flint_w4a16", 3),
+                 ("flint_w4a16", 8), ("flint_w4a16", 16), ("flint_bf16", 8), ("inkling_w4a4", 8),
+                 ("inkling_mxfp8", 5), ("mistral_mxfp4", 16), ("mistral_mxfp4_a8", 8)]
+
+
+@pytest.mark.parametrize("name,T", FORWARD_CASES)
+def test_forward_matches_route_and_experts(lib, name, T):
+    say(f"[parity] forward {name} T={T}")
+    dl = device_layer(name)
+    cfg = dl.cfg
+    ws = lib.Workspace(dl, max(T, 8))
+    x_np, ref = oracle_layer(name, T)
+    x = _x_dev(x_np)
+    y2, ids2, w2, xq2 = lib.forward(dl, x, ws)
+    ids, w, xq = lib.route(dl, x, ws)
+    y = lib.expert_forward(dl, x, xq, ids, w, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(ids2.cpu().numpy(), ids.cpu().numpy())
+    assert np.array_equal(w2.cpu().numpy().view(np.uint32), w.cpu().numpy().view(np.uint32))
+    if xq is not None:   # the parts (the padding between them is never written)
+        p2, p1 = lib.split_xq(dl, xq2, T), lib.split_xq(dl, xq, T)
+        for key in p1:
+            assert np.array_equal(p2[key].cpu().numpy(), p1[key].cpu().numpy()), key
+    assert np.array_equal(y2.view(torch.int16).cpu().numpy(), y.view(torch.int16).cpu().numpy())
+    ids_g = ids2.cpu().numpy()
+    bad = check_ids(ids_g, ref, cfg.k)
+    assert not bad, f"top-k mismatch on tokens {bad}"
+    if cfg.afmt == "bf16" and np.array_equal(ids_g, ref["ids"]):
+        ok, max_abs, rel = y_close(bf16_bits_to_f64(y2), ref["y"])
+        say(f"[parity]   y max_abs/r={max_abs:.3g} rel_l2={rel:.3g}")
+        assert ok, (max_abs, rel)
+
+
 # Batches past the GEMV sizes (the grouped points of the configurations): routing and the
 # quantized tokens are checked on every token against the oracle, the layer output on a
 # sample of tokens (the oracle runs per token, so a sample needs only its own experts).
