@@ -153,16 +153,14 @@ def main() -> int:
     for T in sweep:
         x = torch.from_numpy(synth.make_x(cfg, T).view(np.int16)).to(dev)
         ws = moe.Workspace(dl0, T, device=dev)
-        ids, w, xq = moe.route(dl0, x, ws)
-        y = moe.expert_forward(dl0, x, xq, ids, w, ws)
+        y, ids, w, xq = moe.forward(dl0, x, ws)
         torch.cuda.synchronize()
         U = len(np.unique(ids.cpu().numpy()))
         bpl = moe.routed_bytes(dl0, ids.cpu().numpy(), T)
 
-        def one_pass():
+        def one_pass():   # one moe_forward call per layer: router, experts, combine
             for dl in layers:
-                moe.route(dl, x, ws, out=(ids, w, xq))
-                moe.expert_forward(dl, x, xq, ids, w, ws, y=y)
+                moe.forward(dl, x, ws, out=(y, ids, w, xq))
 
         one_pass()
         torch.cuda.synchronize()
