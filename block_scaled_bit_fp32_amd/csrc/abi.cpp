@@ -159,8 +159,8 @@ bool make_plan(const moe_layer_t& L, int T, int path, Plan& p) {
   if (!plan_class(L.wfmt, L.H, nt, 2, true, p.gu_r) || !plan_class(sfmt, L.H, nt, 2, true, p.gu_s))
     return false;
   if (L.I % (p.gu_r.RS / 2) || Ish % (p.gu_s.RS / 2)) return false;
-  const int r_es = L.afmt == A_BF16 ? 4 : 2;
-  if (!plan_class(L.wfmt, L.I, nt, r_es, false, p.dn_r) || !plan_class(sfmt, Ish, nt, 4, false, p.dn_s))
+  // the down GEMV stages BF16: h stored as BF16, or decoded from its FP4 / FP8 codes
+  if (!plan_class(L.wfmt, L.I, nt, 2, false, p.dn_r) || !plan_class(sfmt, Ish, nt, 2, false, p.dn_s))
     return false;
   if (L.H % p.dn_r.RS || L.H % p.dn_s.RS) return false;
   set_costs(p.gu_r, L.wfmt, L.H, kTokPctGateup);
@@ -196,7 +196,7 @@ bool make_plan(const moe_layer_t& L, int T, int path, Plan& p) {
     const int J = L.k + (L.has_shared ? 1 : 0);
     const size_t jb = (size_t)J * L.I * p.dn_r.esize;
     const size_t room = 64 * 1024 > p.list_bytes ? 64 * 1024 - p.list_bytes : 0;
-    p.token = nt * L.k <= kPairMax &&
+    p.token = nt * L.k <= kPairMax && J <= kTokJMax && p.dn_r.NP == kTokPieces && p.dn_r.NB == 1 &&
               (!L.has_shared || (sfmt == L.wfmt && Ish == L.I && L.afmt == A_BF16)) &&
               jb <= (size_t)kParkBytes && jb <= room;
     if (p.token) p.dn_tile = std::max(p.dn_tile, align_up(jb, 16));
@@ -578,8 +578,9 @@ moe_status_t enqueue_experts(const moe_layer_t* L, const uint16_t* x_bf16, const
       gu.ids_out = const_cast<int32_t*>(topk_ids);
       gu.w_out = const_cast<float*>(topk_w);
     }
-    // token mode needs enough (token, row-step) items to occupy every compute unit
-    dn.token_mode = pm && p.token && T * (L->H / p.dn_r.RS) >= ncu ? 1 : 0;
+    // token mode: one workgroup per (token, row-step) item; with fewer items than half the
+    // compute units the per-pair walk (and the combine launch) is faster
+    dn.token_mode = pm && p.token && 2 * T * (L->H / p.dn_r.RS) >= ncu ? 1 : 0;
     auto q = [](const GemvMap& m, int steps) { return CostQ{m.NG, steps, m.cw, m.ct}; };
     gu.sh_wgs = shared_wgs(*L, T, q(p.gu_s, Ish_ / (p.gu_s.RS / 2)), q(p.gu_r, L->I / (p.gu_r.RS / 2)), gu_grid,
                            ncu, gu.late16, pm);

@@ -176,6 +176,16 @@ __device__ __forceinline__ void accumulate_piece(const uint4 (&wv)[RPL], const u
   constexpr int NSUB = AK == 0 ? EPL / 8 : EPL / 4;
   const uint8_t* base = tile + ((s * NSUB) * LPR + jl) * 16;
   const int sstride = LPR * 16;  // next sub-piece of the same piece
+  // BF16 activations: every token's sub-pieces of this piece are read once, up front, for
+  // all RPL rows (into registers of their own, so the LDS reads overlap)
+  constexpr int NSA = AK == 0 ? NSUB : 1;
+  uint4 ab[NT][NSA];
+  if constexpr (AK == 0) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int sb = 0; sb < NSA; ++sb) ab[t][sb] = *reinterpret_cast<const uint4*>(base + t * tstride + sb * sstride);
+  }
 #pragma unroll
   for (int q = 0; q < RPL; ++q) {
     const uint32_t w[4] = {wv[q].x, wv[q].y, wv[q].z, wv[q].w};
@@ -192,11 +202,7 @@ __device__ __forceinline__ void accumulate_piece(const uint4 (&wv)[RPL], const u
         }
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-          const uint8_t* p = base + t * tstride;
-          const uint4 a0 = *reinterpret_cast<const uint4*>(p);
-          const uint4 a1 = *reinterpret_cast<const uint4*>(p + sstride);
-          const uint4 a2 = *reinterpret_cast<const uint4*>(p + 2 * sstride);
-          const uint4 a3 = *reinterpret_cast<const uint4*>(p + 3 * sstride);
+          const uint4 a0 = ab[t][0], a1 = ab[t][1], a2 = ab[t][2], a3 = ab[t][3];
           float p0 = 0.0f, p1 = 0.0f;
           p0 = dot2(wb[0], a0.x, p0); p0 = dot2(wb[1], a0.y, p0);
           p0 = dot2(wb[2], a0.z, p0); p0 = dot2(wb[3], a0.w, p0);
@@ -223,9 +229,7 @@ __device__ __forceinline__ void accumulate_piece(const uint4 (&wv)[RPL], const u
         }
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-          const uint8_t* p = base + t * tstride;
-          const uint4 a0 = *reinterpret_cast<const uint4*>(p);
-          const uint4 a1 = *reinterpret_cast<const uint4*>(p + sstride);
+          const uint4 a0 = ab[t][0], a1 = ab[t][1];
           float r = acc[q][t];
           r = dot2(wb[0], a0.x, r); r = dot2(wb[1], a0.y, r);
           r = dot2(wb[2], a0.z, r); r = dot2(wb[3], a0.w, r);
@@ -236,16 +240,22 @@ __device__ __forceinline__ void accumulate_piece(const uint4 (&wv)[RPL], const u
       } else {  // BF16 weights
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-          const uint4 a0 = *reinterpret_cast<const uint4*>(base + t * tstride);
+          const uint4 a0 = ab[t][0];
           float r = acc[q][t];
           r = dot2(w[0], a0.x, r); r = dot2(w[1], a0.y, r);
           r = dot2(w[2], a0.z, r); r = dot2(w[3], a0.w, r);
           acc[q][t] = r;
         }
       }
-    } else {  // FP32 activations
+    } else {  // FP32 activations (all of a piece's LDS reads are issued before the first
+              // use, into registers of their own, so that they overlap)
       if constexpr (FMT == W_NVFP4 || FMT == W_MXFP4) {
         const float sc = FMT == W_MXFP4 ? e8m0_to_f32(sv[q] & 0xFFu) : 1.0f;
+        float4 av[NT][8];
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+          for (int sb = 0; sb < 8; ++sb) av[t][sb] = *reinterpret_cast<const float4*>(base + t * tstride + sb * sstride);
 #pragma unroll
         for (int half = 0; half < 2; ++half) {  // elements 16*half .. 16*half + 15
           float wf[16];
@@ -260,15 +270,14 @@ __device__ __forceinline__ void accumulate_piece(const uint4 (&wv)[RPL], const u
           const float S = FMT == W_NVFP4 ? e4m3_to_f32((sv[q] >> (8 * half)) & 0xFFu) : 1.0f;
 #pragma unroll
           for (int t = 0; t < NT; ++t) {
-            const uint8_t* p = base + t * tstride + 4 * half * sstride;
             float pp = 0.0f;
 #pragma unroll
             for (int sb = 0; sb < 4; ++sb) {
-              const float4 av = *reinterpret_cast<const float4*>(p + sb * sstride);
-              pp = fmaf(wf[4 * sb + 0], av.x, pp);
-              pp = fmaf(wf[4 * sb + 1], av.y, pp);
-              pp = fmaf(wf[4 * sb + 2], av.z, pp);
-              pp = fmaf(wf[4 * sb + 3], av.w, pp);
+              const float4 v = av[t][4 * half + sb];
+              pp = fmaf(wf[4 * sb + 0], v.x, pp);
+              pp = fmaf(wf[4 * sb + 1], v.y, pp);
+              pp = fmaf(wf[4 * sb + 2], v.z, pp);
+              pp = fmaf(wf[4 * sb + 3], v.w, pp);
             }
             acc[q][t] = FMT == W_NVFP4 ? fmaf(pp, S, acc[q][t]) : acc[q][t] + pp;
           }
@@ -281,15 +290,19 @@ __device__ __forceinline__ void accumulate_piece(const uint4 (&wv)[RPL], const u
           f32x2_t lo = fp8x2_to_f32<false>(w[wi], sc), hi = fp8x2_to_f32<true>(w[wi], sc);
           wf[4 * wi + 0] = lo.x; wf[4 * wi + 1] = lo.y; wf[4 * wi + 2] = hi.x; wf[4 * wi + 3] = hi.y;
         }
+        float4 av[NT][4];
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+          for (int sb = 0; sb < 4; ++sb) av[t][sb] = *reinterpret_cast<const float4*>(base + t * tstride + sb * sstride);
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-          const uint8_t* p = base + t * tstride;
           float r = acc[q][t];
 #pragma unroll
           for (int sb = 0; sb < 4; ++sb) {
-            const float4 av = *reinterpret_cast<const float4*>(p + sb * sstride);
-            r = fmaf(wf[4 * sb + 0], av.x, r); r = fmaf(wf[4 * sb + 1], av.y, r);
-            r = fmaf(wf[4 * sb + 2], av.z, r); r = fmaf(wf[4 * sb + 3], av.w, r);
+            const float4 v = av[t][sb];
+            r = fmaf(wf[4 * sb + 0], v.x, r); r = fmaf(wf[4 * sb + 1], v.y, r);
+            r = fmaf(wf[4 * sb + 2], v.z, r); r = fmaf(wf[4 * sb + 3], v.w, r);
           }
           acc[q][t] = r;
         }
@@ -828,6 +841,7 @@ struct GateupOps {
   const float* w_gs;
   const float* w_tsc;
   const int* r_pair;
+  int h_bf16;            // GEMV kernels: store h as BF16 (RNE) for the down GEMV
 
   __device__ __forceinline__ void rows(int e, int st, int lrow, int64_t (&out)[2]) const {
     const int64_t base = (int64_t)e * wrows;
@@ -863,7 +877,9 @@ struct GateupOps {
         const float uv = acc[1][t] * gsu * ts;
         const float hv = gv / (1.0f + expf(-gv)) * uv;
         const int64_t off = (int64_t)cx.pr[t] * hs + i;
-        h[off] = hv;
+        // a BF16 row keeps the byte position of its FP32 row (rows of both kinds share h)
+        if (h_bf16) reinterpret_cast<uint16_t*>(h)[off + (int64_t)cx.pr[t] * hs] = (uint16_t)f32_to_bf16_rne(hv);
+        else h[off] = hv;
         if (dbg_h) dbg_h[off] = hv;
       }
     }
@@ -889,7 +905,7 @@ __device__ __forceinline__ void gateup_walk(const ExpertArgs& a, const ExpertLds
   const int Iexp = routed ? a.I : a.Ish;
   float* gs_tab = routed ? L.gs_rt : L.gs_sh;
   const GateupOps<AF> op{a.x, a.xq_codes, a.xq_scales, a.xq_scale, W.gscale, W.gs_per_expert, W.rows, Iexp,
-                         4 * m.G, a.H, a.hs, a.h, a.dbg_h, gs_tab, L.w_tsc, nullptr};
+                         4 * m.G, a.H, a.hs, a.h, a.dbg_h, gs_tab, L.w_tsc, nullptr, AF == A_BF16};
   walk_class<FMT, 0, 2, VW>(W, m, L, a.lds_act_bytes, class_view<VW>(a, L), gateup_cost(a, routed), sp, op,
                             gs_tab, (routed ? a.E : 1) * W.gs_per_expert, ids);
 }
@@ -897,7 +913,7 @@ __device__ __forceinline__ void gateup_walk(const ExpertArgs& a, const ExpertLds
 // Workgroups [0, sh_wgs) walk the shared expert (BF16 activations, no dependency on the
 // routing), the others split the selected experts.
 template <int RF, int SF, int AF>
-__global__ void __launch_bounds__(kBlock, 2) gateup_kernel(ExpertArgs a) {
+__global__ void __launch_bounds__(kBlock, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) gateup_kernel(ExpertArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
   ExpertLds L = carve(a, smem);
   const bool shared = (int)blockIdx.x < a.sh_wgs;
@@ -941,6 +957,7 @@ struct DownOps {
   const float* w_gs;
   const float* w_tsc;
   const int* r_pair;
+  int h_bf16;            // h stored as BF16 (GEMV kernels)
 
   __device__ __forceinline__ void rows(int e, int st, int lrow, int64_t (&out)[1]) const {
     out[0] = (int64_t)e * wrows + st * RS + lrow;
@@ -950,6 +967,8 @@ struct DownOps {
       return nvfp4_ld(hq_codes + (int64_t)p * (Kexp / 2), hq_scales + (int64_t)p * (Kexp / 16), el);
     else if constexpr (AF == A_FP8_TOKEN)
       return fp8_ld(hq_codes + (int64_t)p * Kexp, el);
+    else if (h_bf16)   // BF16 rows at the byte positions of FP32 rows
+      return ld16(reinterpret_cast<const uint16_t*>(hf) + (int64_t)p * (2 * hs) + el);
     else
       return ld16(hf + (int64_t)p * hs + el);
   }
@@ -983,56 +1002,60 @@ __device__ __forceinline__ void down_walk(const ExpertArgs& a, const ExpertLds& 
   const GemvMap& m = routed ? a.rmap : a.smap;
   float* gs_tab = routed ? L.gs_rt : L.gs_sh;
   const DownOps<AF> op{a.h, a.hq_codes, a.hq_scales, a.hq_scale, W.gscale, W.gs_per_expert, W.rows,
-                       routed ? a.I : a.Ish, m.RS, a.H, a.hs, a.o, gs_tab, L.w_tsc, nullptr};
-  walk_class<FMT, AF == A_BF16 ? 1 : 0, 1, VW>(W, m, L, a.lds_act_bytes, class_view<VW>(a, L),
+                       routed ? a.I : a.Ish, m.RS, a.H, a.hs, a.o, gs_tab, L.w_tsc, nullptr, 1};
+  walk_class<FMT, 0, 1, VW>(W, m, L, a.lds_act_bytes, class_view<VW>(a, L),
                                                down_cost(a, routed), sp, op, gs_tab,
                                                (routed ? a.E : 1) * W.gs_per_expert, a.ids);
 }
 
 // Token mode of the down projection (pair mode, when the shared expert, if any, has the
 // routed format and size and takes the same FP32 h): a work item is (token t, row-step
-// s), i.e. RS hidden rows of y[t]; it walks the token's J = k (+1 shared) experts in turn
-// (sub-steps j), scales each sub-step's dot products by its combine weight, global weight
-// scale and activation scale, and writes the BF16 sum: the weighted combine happens in
-// registers, with no per-pair output. Items split evenly over the workgroups. The J
-// activation rows of the current token sit in LDS (rows j of the tile); the first
+// s), i.e. RS hidden rows of y[t]; its J = k (+1 shared) sub-steps are the token's
+// experts. All J sub-steps' weight loads of an item are issued at once (kTokJMax
+// register sets of kTokPieces pieces: a row-step of the down projection is one batch of
+// at most kTokPieces pieces per lane), so an item costs one memory round trip. Each
+// sub-step's dot products are scaled by its combine weight, global weight scale and
+// activation scale and summed in registers; the item writes the BF16 sum to y: the
+// weighted combine needs no per-pair output. Items split evenly over the workgroups.
+// The J activation rows of the current token sit in LDS (rows j of the tile); the first
 // token's are loaded before the first weight loads, as in walk_class.
 template <int FMT, int AK, int AF>
 __device__ __forceinline__ void walk_tokens(const ExpertArgs& a, const ExpertLds& L, int i0, int i1) {
   constexpr int EPL = elems_per_piece(FMT);
+  constexpr int NPT = kTokPieces;
   if (i1 <= i0) return;
   const GemvMap& m = a.rmap;
   const int steps = a.H / m.RS, J = a.k + a.has_shared, P = a.T * a.k;
-  int left = (i1 - i0) * J * m.NB;
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int jl = lane % m.LPR, lrow = wave * m.G + lane / m.LPR;
   const int tstride = a.rw.K * m.esize;
   const DownOps<AF> op{a.h, a.hq_codes, a.hq_scales, a.hq_scale, a.rw.gscale, a.rw.gs_per_expert, a.rw.rows,
-                       a.I, m.RS, a.H, a.hs, a.o, L.gs_rt, L.w_tsc, nullptr};
+                       a.I, m.RS, a.H, a.hs, a.o, L.gs_rt, L.w_tsc, nullptr, 1};
   auto pair_of = [&](int t, int j) { return j < a.k ? t * a.k + j : P + t; };
-  // cursor: token t, row-step s, sub-step j, batch b, expert e of (t, j)
-  struct TCur {
-    int t, s, j, b, e;
+  auto clamp_e = [&](int v) { return (unsigned)v < (unsigned)a.E ? v : 0; };
+  struct Regs {
+    uint4 w[NPT];
+    uint32_t s[NPT];
   };
-  auto expert_of = [&](int t, int j) {
-    if (j >= a.k) return 0;
-    const int v = uni(L.ids[t * a.k + j]);
-    return (unsigned)v < (unsigned)a.E ? v : 0;
-  };
-  auto advance = [&](TCur& c) {
-    if (++c.b < m.NB) return;
-    c.b = 0;
-    if (++c.j == J) {
-      c.j = 0;
-      if (++c.s == steps) { c.s = 0; ++c.t; }
+  // sub-step j of row-step s of token t, expert e: this lane's NPT pieces of its row
+  auto fetch = [&](int s, int j, int e, Regs& R) {
+    const bool sh = j >= a.k;
+    const uint8_t* codes = sh ? a.sw.codes : a.rw.codes;
+    const uint8_t* scales = sh ? a.sw.scales : a.rw.scales;
+    const int64_t row = (int64_t)(sh ? 0 : e) * a.rw.rows + s * m.RS + lrow;
+    const uint8_t* rp = codes + row * a.rw.code_row_bytes;
+    const uint8_t* sp = scales ? scales + row * a.rw.scale_row_bytes : nullptr;
+#pragma unroll
+    for (int i = 0; i < NPT; ++i) {
+      const int el = (min(i, m.NPB - 1) * m.LPR + jl) * EPL;
+      R.w[i] = load_stream16(rp + elem_byte<FMT>(el));
+      if constexpr (FMT == W_NVFP4)
+        R.s[i] = *reinterpret_cast<const uint16_t*>(sp + (el >> 4));
+      else if constexpr (FMT == W_MXFP4 || FMT == W_MXFP8)
+        R.s[i] = sp[el >> 5];
+      else
+        R.s[i] = 0u;
     }
-    c.e = expert_of(c.t, c.j);
-  };
-  auto fetch = [&](const TCur& c, WeightRegs<1>& R) {
-    WTensor W = a.rw;
-    if (c.j >= a.k) { W.codes = a.sw.codes; W.scales = a.sw.scales; }
-    const int64_t r[1] = {(int64_t)c.e * W.rows + c.s * m.RS + lrow};
-    fetch_batch<FMT, 1>(W, m, r, c.b, jl, R);
   };
   auto row_ld = [&](int t) {
     return [&, t](int j, int el) { return op.ld(t, pair_of(t, j), el); };
@@ -1050,32 +1073,37 @@ __device__ __forceinline__ void walk_tokens(const ExpertArgs& a, const ExpertLds
     staged_t = t;
     lds_barrier();
   };
-  float part[1][4], tot = 0.0f;
-  auto do_step = [&](auto pf, const TCur& c, WeightRegs<1>& cur, WeightRegs<1>& nxt, TCur& nc) {
-    if (c.t != staged_t) stage(c.t);
-    if (c.b == 0) part[0][0] = 0.0f;
-    if constexpr (decltype(pf)::value) {
-      nc = c;
-      advance(nc);
-      fetch(nc, nxt);
-    }
-    const uint8_t* tile = L.tile + c.j * tstride;
+  Regs R[kTokJMax];
+  int ex[kTokJMax];
+  auto item = [&](int it) {
+    const int t = it / steps, s = it - t * steps;
+    float tot = 0.0f;
 #pragma unroll
-    for (int i = 0; i < WeightRegs<1>::NPB; ++i)
-      if (i < m.NPB) accumulate_piece<FMT, AK, 1, 1>(cur.w[i], cur.s[i], tile, tstride, m.LPR, c.b * m.NPB + i, jl, part);
-    if (c.b == m.NB - 1) {
-      const float g = c.j < a.k ? L.gs_rt[c.e * a.rw.gs_per_expert] : L.gs_sh[0];
-      tot = fmaf(L.w_tsc[c.j] * g, part[0][0], tot);
-      if (c.j == J - 1) {
-        float v = tot;
-        for (int o = m.LPR / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-        if (jl == 0) a.y[(int64_t)c.t * a.H + c.s * m.RS + lrow] = (uint16_t)f32_to_bf16_rne(v);
-        tot = 0.0f;
+    for (int j = 0; j < kTokJMax; ++j) {
+      if (j < J) {
+        float part[1][4];
+        part[0][0] = 0.0f;
+        const uint8_t* tile = L.tile + j * tstride;
+        WeightRegs<1> wr;
+#pragma unroll
+        for (int i = 0; i < WeightRegs<1>::NPB; ++i) {
+          wr.w[i][0] = R[j].w[min(i, NPT - 1)];
+          wr.s[i][0] = R[j].s[min(i, NPT - 1)];
+        }
+#pragma unroll
+        for (int i = 0; i < NPT; ++i)
+          if (i < m.NPB) accumulate_piece<FMT, AK, 1, 1>(wr.w[i], wr.s[i], tile, tstride, m.LPR, i, jl, part);
+        const float g = j < a.k ? L.gs_rt[ex[j] * a.rw.gs_per_expert] : L.gs_sh[0];
+        tot = fmaf(L.w_tsc[j] * g, part[0][0], tot);
       }
     }
+    for (int o = m.LPR / 2; o > 0; o >>= 1) tot += __shfl_xor(tot, o, kWave);
+    if (jl == 0) a.y[(int64_t)t * a.H + s * m.RS + lrow] = (uint16_t)f32_to_bf16_rne(tot);
   };
-  // prologue: the first token's rows, factors, global scales and topk_ids, then the first
-  // weight loads, then LDS
+  // prologue: the first token's experts (scalar loads), rows, factors, global scales and
+  // topk_ids, then every sub-step's weight loads of the first item, then LDS
+#pragma unroll
+  for (int j = 0; j < kTokJMax; ++j) ex[j] = j < a.k && j < J ? clamp_e(a.ids[staged_t * a.k + j]) : 0;
   uint4 raw[kPreSlots];
   const SlotMap<AK> smap(m, a.rw.K);
   park_rows<AK>(smap, J, row_ld(staged_t), raw);
@@ -1089,13 +1117,12 @@ __device__ __forceinline__ void walk_tokens(const ExpertArgs& a, const ExpertLds
   const float* ssrc = a.sw.gscale ? a.sw.gscale : reinterpret_cast<const float*>(a.sw.codes);
   const float gss = ssrc[0];
   const int idv = a.ids[min((int)threadIdx.x, P - 1)];
-  TCur ca{staged_t, i0 - staged_t * steps, 0, 0, 0}, cb = ca;
   {
-    const int v = a.ids[staged_t * a.k];
-    ca.e = (unsigned)v < (unsigned)a.E ? v : 0;
+    const int s0 = i0 - staged_t * steps;
+#pragma unroll
+    for (int j = 0; j < kTokJMax; ++j)
+      if (j < J) fetch(s0, j, ex[j], R[j]);
   }
-  WeightRegs<1> A_, B_;
-  fetch(ca, A_);
   unpark_rows<AK, EPL>(smap, L.tile, J, [&](uint4 r) { return op.cv(r); }, raw);
   if ((int)threadIdx.x < J) L.w_tsc[threadIdx.x] = fac_r;
 #pragma unroll
@@ -1106,26 +1133,30 @@ __device__ __forceinline__ void walk_tokens(const ExpertArgs& a, const ExpertLds
   if (threadIdx.x == 0) L.gs_sh[0] = a.sw.gscale ? gss : 1.0f;
   if ((int)threadIdx.x < P) L.ids[threadIdx.x] = idv;
   lds_barrier();
-  using Yes = std::integral_constant<bool, true>;
-  using No = std::integral_constant<bool, false>;
-  while (true) {
-    if (left == 1) { do_step(No{}, ca, A_, B_, cb); break; }
-    do_step(Yes{}, ca, A_, B_, cb);
-    if (left == 2) { do_step(No{}, cb, B_, A_, ca); break; }
-    do_step(Yes{}, cb, B_, A_, ca);
-    left -= 2;
+  item(i0);
+  for (int it = i0 + 1; it < i1; ++it) {
+    const int t = it / steps;
+    if (t != staged_t) stage(t);
+#pragma unroll
+    for (int j = 0; j < kTokJMax; ++j) {
+      if (j < J) {
+        ex[j] = j < a.k ? clamp_e(uni(L.ids[t * a.k + j])) : 0;
+        fetch(it - t * steps, j, ex[j], R[j]);
+      }
+    }
+    item(it);
   }
 }
 
 template <int RF, int SF, int AF>
-__global__ void __launch_bounds__(kBlock, 2) down_kernel(ExpertArgs a) {
+__global__ void __launch_bounds__(kBlock, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) down_kernel(ExpertArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
   ExpertLds L = carve(a, smem);
   if constexpr (SF == RF) {
     if (a.token_mode) {
       const int total = a.T * (a.H / a.rmap.RS);
       const ShareW w{0, a.ncu, a.late16};
-      walk_tokens<RF, AF == A_BF16 ? 1 : 0, AF>(a, L, share_at(total, blockIdx.x, gridDim.x, w),
+      walk_tokens<RF, 0, AF>(a, L, share_at(total, blockIdx.x, gridDim.x, w),
                                                 share_at(total, blockIdx.x + 1, gridDim.x, w));
       return;
     }
