@@ -198,7 +198,7 @@ bool make_plan(const moe_layer_t& L, int T, int path, Plan& p) {
     const size_t room = 64 * 1024 > p.list_bytes ? 64 * 1024 - p.list_bytes : 0;
     p.token = nt * L.k <= kPairMax && J <= kTokJMax && p.dn_r.NP == kTokPieces && p.dn_r.NB == 1 &&
               (!L.has_shared || (sfmt == L.wfmt && Ish == L.I && L.afmt == A_BF16)) &&
-              jb <= (size_t)kParkBytes && jb <= room;
+              jb <= (size_t)kTokParkBytes && jb <= room;
     if (p.token) p.dn_tile = std::max(p.dn_tile, align_up(jb, 16));
   }
   p.gu_lds = p.list_bytes + p.gu_tile;

@@ -139,26 +139,29 @@ __device__ __forceinline__ void stage_tile(uint8_t* tile, const GemvMap& m, int 
 // The same in two phases with the raw slots parked in registers (at most kPreSlots per
 // thread): the loads are issued before the first weight loads and stored afterwards, so
 // waiting for them never waits for weight bytes (vector-memory counters retire in order).
+// Slots per thread: 4 for gate/up (a 4 KB token row takes one), 12 for down windows,
+// kTokParkBytes / 4 KB for the token walk.
 constexpr int kPreSlots = 12;
-static_assert(kPreSlots * kBlock * 16 == kParkBytes, "prologue register slots");
+constexpr int kPreSlotsGateup = 4;
+constexpr int kPreSlotsTok = kTokParkBytes / (kBlock * 16);
 // Every slot issues its load (slots past the rows re-read the last one): one basic block,
 // no per-slot branches. nt >= 1.
-template <int AK, class Ld>
-__device__ __forceinline__ void park_rows(const SlotMap<AK>& sm, int nt, Ld ld, uint4 (&raw)[kPreSlots]) {
+template <int AK, int NS, class Ld>
+__device__ __forceinline__ void park_rows(const SlotMap<AK>& sm, int nt, Ld ld, uint4 (&raw)[NS]) {
   const int n = nt * sm.units;
 #pragma unroll
-  for (int i = 0; i < kPreSlots; ++i) {
+  for (int i = 0; i < NS; ++i) {
     const int u = min(i * kBlock + (int)threadIdx.x, n - 1);
     const int t = sm.row(u);
     raw[i] = ld(t, sm.elem(u, t));
   }
 }
-template <int AK, int EPL, class Cv>
+template <int AK, int EPL, int NS, class Cv>
 __device__ __forceinline__ void unpark_rows(const SlotMap<AK>& sm, uint8_t* tile, int nt, Cv cv,
-                                            const uint4 (&raw)[kPreSlots]) {
+                                            const uint4 (&raw)[NS]) {
   const int n = nt * sm.units;
 #pragma unroll
-  for (int i = 0; i < kPreSlots; ++i) {
+  for (int i = 0; i < NS; ++i) {
     const int u = i * kBlock + threadIdx.x;
     if (u < n) {
       const int t = sm.row(u);
@@ -528,32 +531,6 @@ __device__ __forceinline__ Span pair_span(const ExpertArgs& a, const ClassCost& 
   return sp;
 }
 
-// Routing fused into the gate/up kernel (pair mode): the workgroup selects the experts of
-// the tokens its span touches from their router logits (wave_topk, one wave per token),
-// puts them in LDS (L.ids) and writes them, with the weights, to ids_out / w_out (every
-// workgroup touching a token writes the same values). Whole-workgroup call; ends with an
-// LDS barrier.
-__device__ __forceinline__ void fused_topk(const ExpertArgs& a, const ExpertLds& L, const Span& sp) {
-  if (sp.left > 0) {
-    const int t_lo = sp.a0 / a.k, t_hi = (sp.row_limit - 1) / a.k;
-    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-    for (int tb = t_lo; tb <= t_hi; tb += kBlock / kWave) {
-      const int t = tb + wave;
-      if (t <= t_hi) {
-        int e;
-        float w;
-        wave_topk<kFusedTopkSlots>(a.logits + (int64_t)t * a.E, a.E, a.k, e, w);
-        if (lane < a.k) {
-          L.ids[t * a.k + lane] = e;
-          a.ids_out[t * a.k + lane] = e;
-          a.w_out[t * a.k + lane] = w;
-        }
-      }
-    }
-  }
-  lds_barrier();
-}
-
 __device__ __forceinline__ Span read_span(const ExpertLds& L) {
   Span sp;
   sp.a0 = uni(L.span[0]); sp.g0 = uni(L.span[1]); sp.s0 = uni(L.span[2]); sp.e0 = uni(L.span[3]);
@@ -628,6 +605,15 @@ struct ClassView {
 
 constexpr int kGsPer = 8;   // global weight scales staged per thread: 2 * E <= 8 * kBlock
 
+// Routing fused into the gate/up walk (pair mode): where the router logits are and where
+// the selection goes (logits == nullptr: not fused).
+struct FusedRoute {
+  const float* logits;
+  int32_t* ids_out;
+  float* w_out;
+  int E, k;
+};
+
 // Walks one workgroup's span of a class. The class's operations (workgroup-uniform):
 //   op.rows(e, s, lrow, out[RPL])  global weight rows of this lane at step s of expert e
 //   op.ld(tok, pair, el) -> uint4  raw bytes behind 16 staged bytes of a row at element el
@@ -650,7 +636,7 @@ template <int FMT, int AK, int RPL, int VW, class Ops>
 __device__ __forceinline__ void walk_class(const WTensor& W, const GemvMap& m, const ExpertLds& L,
                                            int lds_tile_bytes, const ClassView<VW>& V, const ClassCost& k,
                                            const Span& sp, const Ops& op, float* gs_tab, int ngs,
-                                           const int32_t* ids) {
+                                           const int32_t* ids, const FusedRoute fr = FusedRoute{}) {
   constexpr int EPL = elems_per_piece(FMT);
   constexpr int PER = AK == 0 ? 8 : 4;
   if (sp.left <= 0) return;
@@ -673,7 +659,8 @@ __device__ __forceinline__ void walk_class(const WTensor& W, const GemvMap& m, c
     return [&, r0](int t, int el) { return op.ld(V.tok(r0 + t), V.pair(r0 + t), el); };
   };
   int r0 = sp.rb0 + sp.g0 * k.NG;   // staged class rows [r0, r1)
-  int r1 = min(min(r0 + cap, sp.row_limit), r0 + kPreSlots * kBlock / (W.K / PER));
+  constexpr int NS = RPL == 2 ? kPreSlotsGateup : kPreSlots;   // prologue register slots
+  int r1 = min(min(r0 + cap, sp.row_limit), r0 + NS * kBlock / (W.K / PER));
   auto stage = [&](int ra) {
     lds_barrier();                  // everyone is done with the previous rows
     r0 = ra;
@@ -747,11 +734,22 @@ __device__ __forceinline__ void walk_class(const WTensor& W, const GemvMap& m, c
       if (jl == 0) op.sink(cx, p.s, lrow, acc);
     }
   };
-  // prologue: loads that need no expert id, then the first weight loads, then LDS
+  // prologue: loads that need no expert id, then the first weight loads, then LDS. With
+  // fused routing (fr, pair mode) the router logits of the span's tokens are loaded first
+  // and the experts are selected while the other prologue loads are in flight.
   const int nrows0 = r1 - r0;
-  uint4 raw[kPreSlots];
+  float lv[kFusedTopkSlots];
+  int t_lo = 0, t_hi = -1;
+  if constexpr (VW == VW_PAIR) {
+    if (fr.logits) {
+      t_lo = sp.a0 / fr.k;
+      t_hi = (sp.row_limit - 1) / fr.k;
+      wave_topk_load<kFusedTopkSlots>(fr.logits + (int64_t)min(t_lo + wave, t_hi) * fr.E, fr.E, lv);
+    }
+  }
+  uint4 raw[NS];
   const SlotMap<AK> smap(m, W.K);
-  park_rows<AK>(smap, nrows0, row_ld(r0), raw);
+  park_rows<AK, NS>(smap, nrows0, row_ld(r0), raw);
   float ts_r = 0.0f;
   if ((int)threadIdx.x < nrows0) ts_r = op.tsc(V.tok(r0 + threadIdx.x), V.pair(r0 + threadIdx.x));
   // (every load issues, at a clamped index; without gscale it reads the first codes)
@@ -765,13 +763,32 @@ __device__ __forceinline__ void walk_class(const WTensor& W, const GemvMap& m, c
     if (ids) idv = ids[min((int)threadIdx.x, V.P - 1)];
   }
   Cursor pa{sp.a0, sp.g0, sp.s0, 0, sp.e0, sp.n0, sp.rb0}, pb = pa;
+  if constexpr (VW == VW_PAIR) {
+    if (fr.logits) {   // one token per wave (more rounds for longer spans), then the first expert
+      for (int tb = t_lo; tb <= t_hi; tb += kBlock / kWave) {
+        const int t = tb + wave;
+        if (tb != t_lo) wave_topk_load<kFusedTopkSlots>(fr.logits + (int64_t)min(t, t_hi) * fr.E, fr.E, lv);
+        int e;
+        float w;
+        wave_topk_select<kFusedTopkSlots>(lv, fr.E, fr.k, e, w);
+        if (t <= t_hi && lane < fr.k) {
+          L.ids[t * fr.k + lane] = e;
+          fr.ids_out[t * fr.k + lane] = e;
+          fr.w_out[t * fr.k + lane] = w;
+        }
+      }
+      lds_barrier();
+      const int e0 = uni(L.ids[sp.a0]);
+      pa.e = (unsigned)e0 < (unsigned)fr.E ? e0 : 0;
+    }
+  }
   WeightRegs<RPL> A_, B_;
   {
     int64_t rr[RPL];
     op.rows(pa.e, pa.s, lrow, rr);
     fetch_batch<FMT, RPL>(W, m, rr, 0, jl, A_);
   }
-  unpark_rows<AK, EPL>(smap, L.tile, nrows0, [&](uint4 r) { return op.cv(r); }, raw);
+  unpark_rows<AK, EPL, NS>(smap, L.tile, nrows0, [&](uint4 r) { return op.cv(r); }, raw);
   if ((int)threadIdx.x < nrows0) L.w_tsc[threadIdx.x] = ts_r;
 #pragma unroll
   for (int j = 0; j < kGsPer; ++j) {
@@ -898,7 +915,7 @@ __device__ __forceinline__ ClassView<VW> class_view(const ExpertArgs& a, const E
 
 template <int FMT, int AF, int VW>
 __device__ __forceinline__ void gateup_walk(const ExpertArgs& a, const ExpertLds& L, const Span& sp,
-                                            const int32_t* ids) {
+                                            const int32_t* ids, const FusedRoute fr = FusedRoute{}) {
   constexpr bool routed = VW != VW_SHARED;
   const WTensor& W = routed ? a.rw : a.sw;
   const GemvMap& m = routed ? a.rmap : a.smap;
@@ -907,7 +924,7 @@ __device__ __forceinline__ void gateup_walk(const ExpertArgs& a, const ExpertLds
   const GateupOps<AF> op{a.x, a.xq_codes, a.xq_scales, a.xq_scale, W.gscale, W.gs_per_expert, W.rows, Iexp,
                          4 * m.G, a.H, a.hs, a.h, a.dbg_h, gs_tab, L.w_tsc, nullptr, AF == A_BF16};
   walk_class<FMT, 0, 2, VW>(W, m, L, a.lds_act_bytes, class_view<VW>(a, L), gateup_cost(a, routed), sp, op,
-                            gs_tab, (routed ? a.E : 1) * W.gs_per_expert, ids);
+                            gs_tab, (routed ? a.E : 1) * W.gs_per_expert, ids, fr);
 }
 
 // Workgroups [0, sh_wgs) walk the shared expert (BF16 activations, no dependency on the
@@ -923,15 +940,14 @@ __global__ void __launch_bounds__(kBlock, 2) __attribute__((amdgpu_waves_per_eu(
     gateup_walk<SF, A_BF16, VW_SHARED>(a, L, sp, nullptr);
   } else if (a.pair_mode) {
     Span sp = pair_span(a, gateup_cost(a, true), a.rmap.NB, blockIdx.x - a.sh_wgs, gridDim.x - a.sh_wgs);
-    const int P = a.T * a.k;
-    if (a.fuse_topk) {
-      fused_topk(a, L, sp);
-      if (sp.a0 < P) sp.e0 = uni(L.ids[sp.a0]);
-    } else if (sp.a0 < P) {
-      sp.e0 = a.ids[sp.a0];
+    if (!a.fuse_topk && sp.a0 < a.T * a.k) {
+      const int e = a.ids[sp.a0];
+      sp.e0 = (unsigned)e < (unsigned)a.E ? e : 0;
     }
-    sp.e0 = (unsigned)sp.e0 < (unsigned)a.E ? sp.e0 : 0;
-    gateup_walk<RF, AF, VW_PAIR>(a, L, sp, a.fuse_topk ? nullptr : a.ids);
+    // fused routing: the walk's prologue selects the experts (a workgroup with an empty
+    // span selects nothing)
+    const FusedRoute fr = a.fuse_topk ? FusedRoute{a.logits, a.ids_out, a.w_out, a.E, a.k} : FusedRoute{};
+    gateup_walk<RF, AF, VW_PAIR>(a, L, sp, a.fuse_topk ? nullptr : a.ids, fr);
   } else {
     build_routed(a, L, L.rt, gateup_cost(a, true), a.rmap.NB, blockIdx.x - a.sh_wgs, gridDim.x - a.sh_wgs);
     build_rows(a, L, L.rt);
@@ -1104,9 +1120,9 @@ __device__ __forceinline__ void walk_tokens(const ExpertArgs& a, const ExpertLds
   // topk_ids, then every sub-step's weight loads of the first item, then LDS
 #pragma unroll
   for (int j = 0; j < kTokJMax; ++j) ex[j] = j < a.k && j < J ? clamp_e(a.ids[staged_t * a.k + j]) : 0;
-  uint4 raw[kPreSlots];
+  uint4 raw[kPreSlotsTok];
   const SlotMap<AK> smap(m, a.rw.K);
-  park_rows<AK>(smap, J, row_ld(staged_t), raw);
+  park_rows<AK, kPreSlotsTok>(smap, J, row_ld(staged_t), raw);
   const float fac_r = row_fac(staged_t, min((int)threadIdx.x, J - 1));
   const int ngs = a.E * a.rw.gs_per_expert;
   const float* gsrc = a.rw.gscale ? a.rw.gscale : reinterpret_cast<const float*>(a.rw.codes);
@@ -1123,7 +1139,7 @@ __device__ __forceinline__ void walk_tokens(const ExpertArgs& a, const ExpertLds
     for (int j = 0; j < kTokJMax; ++j)
       if (j < J) fetch(s0, j, ex[j], R[j]);
   }
-  unpark_rows<AK, EPL>(smap, L.tile, J, [&](uint4 r) { return op.cv(r); }, raw);
+  unpark_rows<AK, EPL, kPreSlotsTok>(smap, L.tile, J, [&](uint4 r) { return op.cv(r); }, raw);
   if ((int)threadIdx.x < J) L.w_tsc[threadIdx.x] = fac_r;
 #pragma unroll
   for (int j = 0; j < kGsPer; ++j) {

@@ -29,9 +29,9 @@ struct GemvMap {
 constexpr int kWinRows = 64;   // most token rows one staged window of units holds
 constexpr int kPairMax = 64;   // GEMV kernels: one unit per (token, expert) pair up to this many pairs
 constexpr int kFusedTopkSlots = 8;          // routing fused into gate/up: E <= 64 * this
-constexpr int kParkBytes = 12 * 256 * 16;
+constexpr int kTokParkBytes = 8 * 256 * 16;   // activation bytes the token walk's prologue holds in registers
 constexpr int kTokJMax = 8;     // token mode of the down GEMV: experts per token (k + shared)
-constexpr int kTokPieces = 3;   // and pieces per lane of a row-step (NP, one batch)   // activation bytes a workgroup's prologue holds in registers
+constexpr int kTokPieces = 3;   // and pieces per lane of a row-step (NP, one batch)
 
 // Routed class table capacity: one entry per selected expert, or per pair in pair mode.
 inline constexpr int routed_capacity(int E, int P) { return P <= kPairMax ? P : (E < P ? E : P); }

@@ -14,15 +14,22 @@ namespace moe {
 // wave maximum of those, the lane holding it (the lowest index if several do), and only
 // that lane rescans its slots. Lane j < k returns the j-th expert and its weight.
 // Whole-wave call (uniform arguments).
+// The loads (one logit per slot) and the selection are separate steps, so that a caller
+// can issue the loads early: wave_topk_load then wave_topk_select (wave_topk does both).
 template <int NK>
-__device__ __forceinline__ void wave_topk(const float* lg, int E, int k, int& mye, float& myw) {
+__device__ __forceinline__ void wave_topk_load(const float* lg, int E, float (&lv)[NK]) {
+  const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+  for (int i = 0; i < NK; ++i) lv[i] = lg[min(lane + kWave * i, E - 1)];
+}
+template <int NK>
+__device__ __forceinline__ void wave_topk_select(const float (&lv)[NK], int E, int k, int& mye, float& myw) {
   const int lane = threadIdx.x & (kWave - 1);
   uint32_t key[NK];
 #pragma unroll
   for (int i = 0; i < NK; ++i) {
     const int e = lane + kWave * i;
-    const float v = lg[min(e, E - 1)];
-    const uint32_t o = float_order_key(v);
+    const uint32_t o = float_order_key(lv[i]);
     key[i] = e < E ? (o > 1u ? o : 1u) : 0u;
   }
   uint32_t lb = 0;
@@ -63,6 +70,12 @@ __device__ __forceinline__ void wave_topk(const float* lg, int E, int k, int& my
   float tot = 0.0f;
   for (int j = 0; j < k; ++j) tot += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s), j));
   myw = lane < k ? s / tot : 0.0f;
+}
+template <int NK>
+__device__ __forceinline__ void wave_topk(const float* lg, int E, int k, int& mye, float& myw) {
+  float lv[NK];
+  wave_topk_load<NK>(lg, E, lv);
+  wave_topk_select<NK>(lv, E, k, mye, myw);
 }
 
 }  // namespace moe
