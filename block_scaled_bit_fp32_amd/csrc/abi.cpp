@@ -203,6 +203,20 @@ bool make_plan(const moe_layer_t& L, int T, int path, Plan& p) {
   }
   p.gu_lds = p.list_bytes + p.gu_tile;
   p.dn_lds = p.list_bytes + p.dn_tile;
+  // the kernels' launch constants (so that their prologues divide nothing): steps per
+  // unit, rows the tile holds, rows the first window's register slots hold (4 slots per
+  // thread for gate/up, 12 for down, 16-byte slots)
+  auto consts = [&](GemvMap& m, int K, int steps, size_t tile, int slots) {
+    m.lg = __builtin_ctz((unsigned)m.LPR);
+    m.steps = steps;
+    m.inv_steps = 1.0f / (float)steps;
+    m.cap = (int)std::min<size_t>(kWinRows, tile / ((size_t)K * m.esize));
+    m.win = slots * 256 / (K * m.esize / 16);
+  };
+  consts(p.gu_r, L.H, L.I / (p.gu_r.RS / 2), p.gu_tile, 4);
+  consts(p.gu_s, L.H, Ish / (p.gu_s.RS / 2), p.gu_tile, 4);
+  consts(p.dn_r, L.I, L.H / p.dn_r.RS, p.dn_tile, 12);
+  consts(p.dn_s, Ish, L.H / p.dn_s.RS, p.dn_tile, 12);
   // grouped kernels: gate/up tiles of 64 intermediate indices, down tiles of 128 rows
   // automatic choice: from kGroupedMinT tokens on, when units hold many tokens
   const bool want = path == MOE_PATH_GROUPED ||
@@ -526,6 +540,7 @@ moe_status_t enqueue_experts(const moe_layer_t* L, const uint16_t* x_bf16, const
   a.ids = topk_ids;
   a.topk_w = topk_w;
   a.T = T; a.H = L->H; a.I = L->I; a.Ish = Ish; a.E = L->E; a.k = L->k;
+  a.inv_k = 1.0f / (float)L->k;
   a.has_shared = L->has_shared; a.afmt = L->afmt;
   a.max_slots = p.max_slots;
   a.h = reinterpret_cast<float*>(base + w.h);
@@ -581,6 +596,9 @@ moe_status_t enqueue_experts(const moe_layer_t* L, const uint16_t* x_bf16, const
     // token mode: one workgroup per (token, row-step) item; with fewer items than half the
     // compute units the per-pair walk (and the combine launch) is faster
     dn.token_mode = pm && p.token && 2 * T * (L->H / p.dn_r.RS) >= ncu ? 1 : 0;
+    // token-mode items are whole (token, row-step) items, about one per workgroup: up to one
+    // per compute unit they go to the first-round workgroups only, beyond that evenly
+    if (dn.token_mode) dn.late16 = T * (L->H / p.dn_r.RS) <= ncu ? 0 : 16;
     auto q = [](const GemvMap& m, int steps) { return CostQ{m.NG, steps, m.cw, m.ct}; };
     gu.sh_wgs = shared_wgs(*L, T, q(p.gu_s, Ish_ / (p.gu_s.RS / 2)), q(p.gu_r, L->I / (p.gu_r.RS / 2)), gu_grid,
                            ncu, gu.late16, pm);

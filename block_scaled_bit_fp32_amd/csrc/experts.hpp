@@ -145,9 +145,11 @@ constexpr int kPreSlots = 12;
 constexpr int kPreSlotsGateup = 4;
 constexpr int kPreSlotsTok = kTokParkBytes / (kBlock * 16);
 // Every slot issues its load (slots past the rows re-read the last one): one basic block,
-// no per-slot branches. nt >= 1.
+// no per-slot branches. An empty first window (a row longer than the slots: nt = 0)
+// parks nothing; the walk stages it instead.
 template <int AK, int NS, class Ld>
 __device__ __forceinline__ void park_rows(const SlotMap<AK>& sm, int nt, Ld ld, uint4 (&raw)[NS]) {
+  if (nt <= 0) return;
   const int n = nt * sm.units;
 #pragma unroll
   for (int i = 0; i < NS; ++i) {
@@ -159,6 +161,7 @@ __device__ __forceinline__ void park_rows(const SlotMap<AK>& sm, int nt, Ld ld, 
 template <int AK, int EPL, int NS, class Cv>
 __device__ __forceinline__ void unpark_rows(const SlotMap<AK>& sm, uint8_t* tile, int nt, Cv cv,
                                             const uint4 (&raw)[NS]) {
+  if (nt <= 0) return;
   const int n = nt * sm.units;
 #pragma unroll
   for (int i = 0; i < NS; ++i) {
@@ -515,18 +518,20 @@ __device__ __forceinline__ void build_routed(const ExpertArgs& a, const ExpertLd
 // scalar load of topk_ids. An expert named by several tokens is read once per token (at
 // decode sizes a few percent more bytes). Entries outside [0, E) read expert 0 (their
 // outputs are unspecified).
-__device__ __forceinline__ Span pair_span(const ExpertArgs& a, const ClassCost& k, int NB, int b, int G) {
+__device__ __forceinline__ Span pair_span(const ExpertArgs& a, const ClassCost& k, float inv_steps, int NB, int b,
+                                          int G) {
   const int P = a.T * a.k, steps = k.steps, total = P * steps;
   const ShareW w{a.sh_wgs, a.ncu, a.late16};
-  const int l0 = share_at(total, b, G, w), l1 = share_at(total, b + 1, G, w);
+  const int l0 = share_at_f(total, b, G, w), l1 = share_at_f(total, b + 1, G, w);
   Span sp;
-  sp.a0 = l0 / steps;
+  sp.a0 = div_by(l0, inv_steps);
   sp.s0 = l0 - sp.a0 * steps;
   sp.g0 = 0;
   sp.n0 = 1;
   sp.rb0 = sp.a0;
   sp.left = (l1 - l0) * NB;
-  sp.row_limit = (l1 + steps - 1) / steps;
+  const int a1 = div_by(l1, inv_steps);
+  sp.row_limit = a1 + (l1 - a1 * steps > 0 ? 1 : 0);
   sp.e0 = 0;
   return sp;
 }
@@ -612,6 +617,7 @@ struct FusedRoute {
   int32_t* ids_out;
   float* w_out;
   int E, k;
+  float inv_k;
 };
 
 // Walks one workgroup's span of a class. The class's operations (workgroup-uniform):
@@ -642,9 +648,9 @@ __device__ __forceinline__ void walk_class(const WTensor& W, const GemvMap& m, c
   if (sp.left <= 0) return;
   int left = sp.left;
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-  const int jl = lane % m.LPR, lrow = wave * m.G + lane / m.LPR;
+  const int jl = lane & (m.LPR - 1), lrow = wave * m.G + (lane >> m.lg);
   const int tstride = W.K * m.esize;
-  const int cap = min(kWinRows, lds_tile_bytes / tstride);
+  const int cap = m.cap;
   const int A = V.count();
   auto advance = [&](Cursor& p) {
     if (++p.b < m.NB) return;
@@ -660,7 +666,7 @@ __device__ __forceinline__ void walk_class(const WTensor& W, const GemvMap& m, c
   };
   int r0 = sp.rb0 + sp.g0 * k.NG;   // staged class rows [r0, r1)
   constexpr int NS = RPL == 2 ? kPreSlotsGateup : kPreSlots;   // prologue register slots
-  int r1 = min(min(r0 + cap, sp.row_limit), r0 + NS * kBlock / (W.K / PER));
+  int r1 = min(min(r0 + cap, sp.row_limit), r0 + m.win);
   auto stage = [&](int ra) {
     lds_barrier();                  // everyone is done with the previous rows
     r0 = ra;
@@ -742,8 +748,8 @@ __device__ __forceinline__ void walk_class(const WTensor& W, const GemvMap& m, c
   int t_lo = 0, t_hi = -1;
   if constexpr (VW == VW_PAIR) {
     if (fr.logits) {
-      t_lo = sp.a0 / fr.k;
-      t_hi = (sp.row_limit - 1) / fr.k;
+      t_lo = div_by(sp.a0, fr.inv_k);
+      t_hi = div_by(sp.row_limit - 1, fr.inv_k);
       wave_topk_load<kFusedTopkSlots>(fr.logits + (int64_t)min(t_lo + wave, t_hi) * fr.E, fr.E, lv);
     }
   }
@@ -905,12 +911,12 @@ struct GateupOps {
 
 __device__ __forceinline__ ClassCost gateup_cost(const ExpertArgs& a, bool routed) {
   const GemvMap& m = routed ? a.rmap : a.smap;
-  return ClassCost{m.NG, (routed ? a.I : a.Ish) / (4 * m.G), m.cw, m.ct};
+  return ClassCost{m.NG, m.steps, m.cw, m.ct};
 }
 
 template <int VW>
 __device__ __forceinline__ ClassView<VW> class_view(const ExpertArgs& a, const ExpertLds& L) {
-  return ClassView<VW>{&L.rt, L.ids, a.k, a.E, a.T, a.T * a.k, 1.0f / (float)a.k};
+  return ClassView<VW>{&L.rt, L.ids, a.k, a.E, a.T, a.T * a.k, a.inv_k};
 }
 
 template <int FMT, int AF, int VW>
@@ -939,14 +945,16 @@ __global__ void __launch_bounds__(kBlock, 2) __attribute__((amdgpu_waves_per_eu(
                                 ShareW{0, a.ncu, a.late16});
     gateup_walk<SF, A_BF16, VW_SHARED>(a, L, sp, nullptr);
   } else if (a.pair_mode) {
-    Span sp = pair_span(a, gateup_cost(a, true), a.rmap.NB, blockIdx.x - a.sh_wgs, gridDim.x - a.sh_wgs);
+    Span sp = pair_span(a, gateup_cost(a, true), a.rmap.inv_steps, a.rmap.NB, blockIdx.x - a.sh_wgs,
+                        gridDim.x - a.sh_wgs);
     if (!a.fuse_topk && sp.a0 < a.T * a.k) {
       const int e = a.ids[sp.a0];
       sp.e0 = (unsigned)e < (unsigned)a.E ? e : 0;
     }
     // fused routing: the walk's prologue selects the experts (a workgroup with an empty
     // span selects nothing)
-    const FusedRoute fr = a.fuse_topk ? FusedRoute{a.logits, a.ids_out, a.w_out, a.E, a.k} : FusedRoute{};
+    const FusedRoute fr =
+        a.fuse_topk ? FusedRoute{a.logits, a.ids_out, a.w_out, a.E, a.k, a.inv_k} : FusedRoute{};
     gateup_walk<RF, AF, VW_PAIR>(a, L, sp, a.fuse_topk ? nullptr : a.ids, fr);
   } else {
     build_routed(a, L, L.rt, gateup_cost(a, true), a.rmap.NB, blockIdx.x - a.sh_wgs, gridDim.x - a.sh_wgs);
@@ -1008,7 +1016,7 @@ struct DownOps {
 
 __device__ __forceinline__ ClassCost down_cost(const ExpertArgs& a, bool routed) {
   const GemvMap& m = routed ? a.rmap : a.smap;
-  return ClassCost{m.NG, a.H / m.RS, m.cw, m.ct};
+  return ClassCost{m.NG, m.steps, m.cw, m.ct};
 }
 
 template <int FMT, int AF, int VW>
@@ -1041,9 +1049,9 @@ __device__ __forceinline__ void walk_tokens(const ExpertArgs& a, const ExpertLds
   constexpr int NPT = kTokPieces;
   if (i1 <= i0) return;
   const GemvMap& m = a.rmap;
-  const int steps = a.H / m.RS, J = a.k + a.has_shared, P = a.T * a.k;
+  const int steps = m.steps, J = a.k + a.has_shared, P = a.T * a.k;
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-  const int jl = lane % m.LPR, lrow = wave * m.G + lane / m.LPR;
+  const int jl = lane & (m.LPR - 1), lrow = wave * m.G + (lane >> m.lg);
   const int tstride = a.rw.K * m.esize;
   const DownOps<AF> op{a.h, a.hq_codes, a.hq_scales, a.hq_scale, a.rw.gscale, a.rw.gs_per_expert, a.rw.rows,
                        a.I, m.RS, a.H, a.hs, a.o, L.gs_rt, L.w_tsc, nullptr, 1};
@@ -1081,7 +1089,7 @@ __device__ __forceinline__ void walk_tokens(const ExpertArgs& a, const ExpertLds
     const int p = pair_of(t, j);
     return op.tsc(t, p) * (j < a.k ? a.topk_w[p] : 1.0f);
   };
-  int staged_t = i0 / steps;
+  int staged_t = div_by(i0, m.inv_steps);
   auto stage = [&](int t) {
     lds_barrier();
     stage_tile<AK, EPL>(L.tile, m, a.rw.K, J, row_ld(t), [&](uint4 r) { return op.cv(r); });
@@ -1092,7 +1100,7 @@ __device__ __forceinline__ void walk_tokens(const ExpertArgs& a, const ExpertLds
   Regs R[kTokJMax];
   int ex[kTokJMax];
   auto item = [&](int it) {
-    const int t = it / steps, s = it - t * steps;
+    const int t = div_by(it, m.inv_steps), s = it - t * steps;
     float tot = 0.0f;
 #pragma unroll
     for (int j = 0; j < kTokJMax; ++j) {
@@ -1151,7 +1159,7 @@ __device__ __forceinline__ void walk_tokens(const ExpertArgs& a, const ExpertLds
   lds_barrier();
   item(i0);
   for (int it = i0 + 1; it < i1; ++it) {
-    const int t = it / steps;
+    const int t = div_by(it, m.inv_steps);
     if (t != staged_t) stage(t);
 #pragma unroll
     for (int j = 0; j < kTokJMax; ++j) {
@@ -1170,10 +1178,10 @@ __global__ void __launch_bounds__(kBlock, 2) __attribute__((amdgpu_waves_per_eu(
   ExpertLds L = carve(a, smem);
   if constexpr (SF == RF) {
     if (a.token_mode) {
-      const int total = a.T * (a.H / a.rmap.RS);
+      const int total = a.T * a.rmap.steps;
       const ShareW w{0, a.ncu, a.late16};
-      walk_tokens<RF, 0, AF>(a, L, share_at(total, blockIdx.x, gridDim.x, w),
-                                                share_at(total, blockIdx.x + 1, gridDim.x, w));
+      walk_tokens<RF, 0, AF>(a, L, share_at_f(total, blockIdx.x, gridDim.x, w),
+                             share_at_f(total, blockIdx.x + 1, gridDim.x, w));
       return;
     }
   }
@@ -1183,7 +1191,8 @@ __global__ void __launch_bounds__(kBlock, 2) __attribute__((amdgpu_waves_per_eu(
                                 ShareW{0, a.ncu, a.late16});
     down_walk<SF, A_BF16, VW_SHARED>(a, L, sp);
   } else if (a.pair_mode) {
-    Span sp = pair_span(a, down_cost(a, true), a.rmap.NB, blockIdx.x - a.sh_wgs, gridDim.x - a.sh_wgs);
+    Span sp = pair_span(a, down_cost(a, true), a.rmap.inv_steps, a.rmap.NB, blockIdx.x - a.sh_wgs,
+                        gridDim.x - a.sh_wgs);
     if (sp.a0 < a.T * a.k) {
       const int e = a.ids[sp.a0];
       sp.e0 = (unsigned)e < (unsigned)a.E ? e : 0;

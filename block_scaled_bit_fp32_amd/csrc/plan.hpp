@@ -24,6 +24,12 @@ inline constexpr int elems_per_piece(int fmt) {
 //   cost evenly).
 struct GemvMap {
   int LPR, G, RPL, RS, NP, NPB, NB, NG, esize, cw, ct;
+  // launch constants the host works out, so that kernel prologues divide nothing:
+  int lg;          // log2(LPR)
+  int steps;       // row-steps per unit
+  float inv_steps; // 1 / steps
+  int cap;         // rows of the class the LDS tile holds (at most kWinRows)
+  int win;         // rows the first window may hold (prologue register slots)
 };
 
 constexpr int kWinRows = 64;   // most token rows one staged window of units holds
@@ -104,6 +110,7 @@ struct ExpertArgs {
   int pair_mode;         // GEMV kernels: one unit per (token, expert) pair
   int token_mode;        // down GEMV: items (token, row-step) over all of a token's
                          // experts, writing y (no combine launch)
+  float inv_k;           // 1 / k
   int fuse_topk;         // gate/up GEMV in pair mode: routing from logits in the prologue,
   const float* logits;   // writing ids_out / w_out (the buffers ids / topk_w point at)
   int32_t* ids_out;

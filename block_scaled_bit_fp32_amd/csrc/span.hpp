@@ -82,6 +82,22 @@ __device__ __forceinline__ int share_at(int total, int b, int G, const ShareW& w
   const int64_t w0 = W(0);
   return (int)((int64_t)total * (W(b) - w0) / (W(G) - w0));
 }
+// The same through FP32 (no integer division): floor(total * W(b) / W(G)) up to rounding.
+// Neighbouring workgroups evaluate the same expression, so the shares still tile
+// [0, total) exactly, in order; the last one ends at total.
+__device__ __forceinline__ int share_at_f(int total, int b, int G, const ShareW& w) {
+  if (b >= G) return total;
+  auto W = [&](int i) {
+    const int g = w.B0 + i;
+    return 16 * min(g, w.ncu) + w.late16 * max(0, g - w.ncu);
+  };
+  const int w0 = W(0);
+  const float f = (float)(W(b) - w0) * __builtin_amdgcn_rcpf((float)(W(G) - w0));
+  return min(total, (int)((float)total * f));
+}
+// x / d for 0 <= x < 2^20 and d >= 1 given inv = 1/d (FP32): (x + 1/2) / d is at least
+// 1/(2d) away from an integer, far more than the FP32 error.
+__device__ __forceinline__ int div_by(int x, float inv) { return (int)(((float)x + 0.5f) * inv); }
 __device__ __forceinline__ void wg_share(int total, int b, int G, const ShareW& w, int& c_lo, int& c_hi) {
   c_lo = share_at(total, b, G, w);
   c_hi = share_at(total, b + 1, G, w);
@@ -91,8 +107,7 @@ __device__ __forceinline__ void wg_share(int total, int b, int G, const ShareW& 
 __device__ __forceinline__ Span shared_span(int T, const ClassCost& k, int NB, int b, int G, const ShareW& w) {
   const int units = (T + k.NG - 1) / k.NG;
   const int total = k.steps * (k.cw * units + k.ct * T);
-  int c_lo, c_hi;
-  wg_share(total, b, G, w, c_lo, c_hi);
+  const int c_lo = share_at_f(total, b, G, w), c_hi = share_at_f(total, b + 1, G, w);
   const Located in{0, T, 0, 0, 0, 0}, end{1, T, total, units, T, -1};
   return make_span(c_lo < total ? in : end, c_hi < total ? in : end, 1, k, c_lo, c_hi, NB);
 }
