@@ -596,15 +596,29 @@ moe_status_t enqueue_experts(const moe_layer_t* L, const uint16_t* x_bf16, const
     // token mode: one workgroup per (token, row-step) item; with fewer items than half the
     // compute units the per-pair walk (and the combine launch) is faster
     dn.token_mode = pm && p.token && 2 * T * (L->H / p.dn_r.RS) >= ncu ? 1 : 0;
-    // token-mode items are whole (token, row-step) items, about one per workgroup: up to one
-    // per compute unit they go to the first-round workgroups only, beyond that evenly
-    if (dn.token_mode) dn.late16 = T * (L->H / p.dn_r.RS) <= ncu ? 0 : 16;
     auto q = [](const GemvMap& m, int steps) { return CostQ{m.NG, steps, m.cw, m.ct}; };
     gu.sh_wgs = shared_wgs(*L, T, q(p.gu_s, Ish_ / (p.gu_s.RS / 2)), q(p.gu_r, L->I / (p.gu_r.RS / 2)), gu_grid,
                            ncu, gu.late16, pm);
     dn.sh_wgs = dn.token_mode ? 0
                               : shared_wgs(*L, T, q(p.dn_s, L->H / p.dn_s.RS), q(p.dn_r, L->H / p.dn_r.RS),
                                            dn_grid, ncu, dn.late16, pm);
+    // pair and token modes: every position of the class costs the same, so each workgroup
+    // takes q or q + 1 of them, the extra ones going to the first (earliest dispatched)
+    // workgroups; token-mode items (about one per workgroup) go to the first-round
+    // workgroups only while there are at most as many as compute units
+    auto split = [](ExpertArgs& x, int positions, int wgs) {
+      x.pq = positions / wgs;
+      x.pr = positions - x.pq * wgs;
+    };
+    if (pm) {
+      split(gu, T * L->k * p.gu_r.steps, gu_grid - gu.sh_wgs);
+      if (!dn.token_mode) split(dn, T * L->k * p.dn_r.steps, dn_grid - dn.sh_wgs);
+    }
+    if (dn.token_mode) {
+      const int items = T * p.dn_r.steps;
+      split(dn, items, items <= ncu ? std::min(ncu, dn_grid) : dn_grid);
+      if (items <= ncu) dn.pq = 0, dn.pr = items;   // one item each for the first workgroups
+    }
   }
   if (launch_experts(gu, gu_grid, p.gu_lds, dn, dn_grid, p.dn_lds, stream) != hipSuccess)
     return set_err(MOE_ELAUNCH, "expert kernel launch failed");

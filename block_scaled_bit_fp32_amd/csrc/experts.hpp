@@ -520,9 +520,9 @@ __device__ __forceinline__ void build_routed(const ExpertArgs& a, const ExpertLd
 // outputs are unspecified).
 __device__ __forceinline__ Span pair_span(const ExpertArgs& a, const ClassCost& k, float inv_steps, int NB, int b,
                                           int G) {
-  const int P = a.T * a.k, steps = k.steps, total = P * steps;
-  const ShareW w{a.sh_wgs, a.ncu, a.late16};
-  const int l0 = share_at_f(total, b, G, w), l1 = share_at_f(total, b + 1, G, w);
+  const int steps = k.steps;
+  (void)G;
+  const int l0 = b * a.pq + min(b, a.pr), l1 = l0 + a.pq + (b < a.pr ? 1 : 0);
   Span sp;
   sp.a0 = div_by(l0, inv_steps);
   sp.s0 = l0 - sp.a0 * steps;
@@ -1178,10 +1178,9 @@ __global__ void __launch_bounds__(kBlock, 2) __attribute__((amdgpu_waves_per_eu(
   ExpertLds L = carve(a, smem);
   if constexpr (SF == RF) {
     if (a.token_mode) {
-      const int total = a.T * a.rmap.steps;
-      const ShareW w{0, a.ncu, a.late16};
-      walk_tokens<RF, 0, AF>(a, L, share_at_f(total, blockIdx.x, gridDim.x, w),
-                             share_at_f(total, blockIdx.x + 1, gridDim.x, w));
+      const int b = blockIdx.x;   // items q or q + 1 per workgroup (the host's pq, pr)
+      const int i0 = b * a.pq + min(b, a.pr);
+      walk_tokens<RF, 0, AF>(a, L, i0, i0 + a.pq + (b < a.pr ? 1 : 0));
       return;
     }
   }

@@ -111,6 +111,9 @@ struct ExpertArgs {
   int token_mode;        // down GEMV: items (token, row-step) over all of a token's
                          // experts, writing y (no combine launch)
   float inv_k;           // 1 / k
+  int pq, pr;            // pair and token modes: positions (all of one cost) per workgroup of
+                         // the class, q or q + 1; the first r workgroups (the earliest
+                         // dispatched) take q + 1
   int fuse_topk;         // gate/up GEMV in pair mode: routing from logits in the prologue,
   const float* logits;   // writing ids_out / w_out (the buffers ids / topk_w point at)
   int32_t* ids_out;
