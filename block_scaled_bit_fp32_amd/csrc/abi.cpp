@@ -265,6 +265,36 @@ int shared_wgs(const moe_layer_t& L, int T, const CostQ& s, const CostQ& r, int 
   return (int)std::min<int64_t>(std::max<int64_t>(g, 1), std::min(G, ncu) - 1);
 }
 
+// Positions of one cost (pair and token modes) over G workgroups, the first n1 of which
+// are dispatched in the first round (one per compute unit). Per-workgroup timestamps on
+// the Flint W4A16 layer at T = 8 put the second-round workgroups' start about 0.8 of a
+// row-step later and their steps about 15 % slower. The split takes the whole numbers of
+// positions per round that minimize the later finish: q2 (+1) per second-round
+// workgroup, the rest over the first round.
+void split_rounds(ExpertArgs& x, int A, int G, int n1) {
+  n1 = std::min(n1, G);
+  const int n2 = G - n1;
+  auto fill = [&](int A1) {
+    x.pn1 = n1;
+    x.pq1 = n1 ? A1 / n1 : 0;
+    x.pr1 = n1 ? A1 - x.pq1 * n1 : 0;
+    const int A2 = A - A1;
+    x.pq2 = n2 ? A2 / n2 : 0;
+    x.pr2 = n2 ? A2 - x.pq2 * n2 : 0;
+  };
+  if (n1 == 0 || n2 == 0) { fill(n2 == 0 ? A : 0); return; }
+  double best = 1e30;
+  int best_A1 = A;
+  for (int q2 = 0; q2 <= (A + n2 - 1) / n2; ++q2) {
+    const int A2 = std::min(A, n2 * q2), A1 = A - A2;
+    const double t1 = A1 > 0 ? (double)((A1 + n1 - 1) / n1) : 0.0;
+    const double t2 = A2 > 0 ? 0.8 + 1.15 * (double)((A2 + n2 - 1) / n2) : 0.0;
+    const double t = std::max(t1, t2);
+    if (t < best) { best = t; best_A1 = A1; }
+  }
+  fill(best_A1);
+}
+
 struct WsLayout {
   size_t logits, h, hq_codes, hq_scales, hq_scale, o, total;
   int hs;
@@ -602,23 +632,13 @@ moe_status_t enqueue_experts(const moe_layer_t* L, const uint16_t* x_bf16, const
     dn.sh_wgs = dn.token_mode ? 0
                               : shared_wgs(*L, T, q(p.dn_s, L->H / p.dn_s.RS), q(p.dn_r, L->H / p.dn_r.RS),
                                            dn_grid, ncu, dn.late16, pm);
-    // pair and token modes: every position of the class costs the same, so each workgroup
-    // takes q or q + 1 of them, the extra ones going to the first (earliest dispatched)
-    // workgroups; token-mode items (about one per workgroup) go to the first-round
-    // workgroups only while there are at most as many as compute units
-    auto split = [](ExpertArgs& x, int positions, int wgs) {
-      x.pq = positions / wgs;
-      x.pr = positions - x.pq * wgs;
-    };
+    // pair and token modes: every position of the class costs the same
     if (pm) {
-      split(gu, T * L->k * p.gu_r.steps, gu_grid - gu.sh_wgs);
-      if (!dn.token_mode) split(dn, T * L->k * p.dn_r.steps, dn_grid - dn.sh_wgs);
+      split_rounds(gu, T * L->k * p.gu_r.steps, gu_grid - gu.sh_wgs, std::max(0, ncu - gu.sh_wgs));
+      if (!dn.token_mode)
+        split_rounds(dn, T * L->k * p.dn_r.steps, dn_grid - dn.sh_wgs, std::max(0, ncu - dn.sh_wgs));
     }
-    if (dn.token_mode) {
-      const int items = T * p.dn_r.steps;
-      split(dn, items, items <= ncu ? std::min(ncu, dn_grid) : dn_grid);
-      if (items <= ncu) dn.pq = 0, dn.pr = items;   // one item each for the first workgroups
-    }
+    if (dn.token_mode) split_rounds(dn, T * p.dn_r.steps, dn_grid, ncu);
   }
   if (launch_experts(gu, gu_grid, p.gu_lds, dn, dn_grid, p.dn_lds, stream) != hipSuccess)
     return set_err(MOE_ELAUNCH, "expert kernel launch failed");

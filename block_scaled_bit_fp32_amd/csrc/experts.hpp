@@ -522,7 +522,9 @@ __device__ __forceinline__ Span pair_span(const ExpertArgs& a, const ClassCost& 
                                           int G) {
   const int steps = k.steps;
   (void)G;
-  const int l0 = b * a.pq + min(b, a.pr), l1 = l0 + a.pq + (b < a.pr ? 1 : 0);
+  int l0, len;
+  split_at(b, a.pn1, a.pq1, a.pr1, a.pq2, a.pr2, l0, len);
+  const int l1 = l0 + len;
   Span sp;
   sp.a0 = div_by(l0, inv_steps);
   sp.s0 = l0 - sp.a0 * steps;
@@ -1178,9 +1180,9 @@ __global__ void __launch_bounds__(kBlock, 2) __attribute__((amdgpu_waves_per_eu(
   ExpertLds L = carve(a, smem);
   if constexpr (SF == RF) {
     if (a.token_mode) {
-      const int b = blockIdx.x;   // items q or q + 1 per workgroup (the host's pq, pr)
-      const int i0 = b * a.pq + min(b, a.pr);
-      walk_tokens<RF, 0, AF>(a, L, i0, i0 + a.pq + (b < a.pr ? 1 : 0));
+      int i0, len;   // items per workgroup: the host's two-round split
+      split_at(blockIdx.x, a.pn1, a.pq1, a.pr1, a.pq2, a.pr2, i0, len);
+      walk_tokens<RF, 0, AF>(a, L, i0, i0 + len);
       return;
     }
   }

@@ -111,9 +111,10 @@ struct ExpertArgs {
   int token_mode;        // down GEMV: items (token, row-step) over all of a token's
                          // experts, writing y (no combine launch)
   float inv_k;           // 1 / k
-  int pq, pr;            // pair and token modes: positions (all of one cost) per workgroup of
-                         // the class, q or q + 1; the first r workgroups (the earliest
-                         // dispatched) take q + 1
+  // pair and token modes, positions of one cost: the class's first n1 workgroups (those
+  // dispatched in the first round) take q1 or q1 + 1 (the first r1 of them q1 + 1), the
+  // others q2 or q2 + 1
+  int pn1, pq1, pr1, pq2, pr2;
   int fuse_topk;         // gate/up GEMV in pair mode: routing from logits in the prologue,
   const float* logits;   // writing ids_out / w_out (the buffers ids / topk_w point at)
   int32_t* ids_out;

@@ -103,6 +103,19 @@ __device__ __forceinline__ void wg_share(int total, int b, int G, const ShareW& 
   c_hi = share_at(total, b + 1, G, w);
 }
 
+// Workgroup b's positions [l0, l0 + len) of a class whose positions all cost the same,
+// in the host's two-round split (see ExpertArgs::pn1).
+__device__ __forceinline__ void split_at(int b, int n1, int q1, int r1, int q2, int r2, int& l0, int& len) {
+  if (b < n1) {
+    l0 = b * q1 + min(b, r1);
+    len = q1 + (b < r1 ? 1 : 0);
+  } else {
+    const int bb = b - n1;
+    l0 = n1 * q1 + r1 + bb * q2 + min(bb, r2);
+    len = q2 + (bb < r2 ? 1 : 0);
+  }
+}
+
 // The shared expert's span for workgroup b of G: closed form, no table reads.
 __device__ __forceinline__ Span shared_span(int T, const ClassCost& k, int NB, int b, int G, const ShareW& w) {
   const int units = (T + k.NG - 1) / k.NG;
