@@ -254,10 +254,18 @@ struct CostQ {
 // The split weighs workgroups as the kernels do: the first ncu blocks 16, later ones
 // late16 (shared workgroups come first, so they are all full-weight ones when the shared
 // share stays under ncu blocks).
+// In pair mode the routed units hold one token each, the shared ones up to NG. With
+// block-scaled shared weights (FP4 / FP8) a unit decodes each weight piece once for all
+// its tokens, so a unit's tokens after the first cost 3/5 of the token term (graph-timed
+// sweep of the shared workgroup count on the Flint W4A16 layer at T = 2..8: 1.2 us per
+// layer at T = 8; with BF16 shared weights nothing is amortized and the term stays).
 int shared_wgs(const moe_layer_t& L, int T, const CostQ& s, const CostQ& r, int G, int ncu, int late16,
                bool pair_mode = false) {
   if (!L.has_shared || G < 2) return 0;
-  const int64_t cs = (int64_t)s.steps * (s.cw * (int64_t)((T + s.NG - 1) / s.NG) + (int64_t)s.ct * T);
+  const int64_t units = (T + s.NG - 1) / s.NG;
+  const bool amortized = pair_mode && L.shared_wfmt != MOE_W_BF16;
+  const int64_t cs = amortized ? (int64_t)s.steps * (5 * (s.cw + s.ct) * units + 3 * (int64_t)s.ct * (T - units)) / 5
+                               : (int64_t)s.steps * (s.cw * units + (int64_t)s.ct * T);
   const int64_t pairs = (int64_t)T * L.k, ur = pair_mode ? pairs : std::min<int64_t>(L.E, pairs);
   const int64_t cr = (int64_t)r.steps * (r.cw * ur + r.ct * pairs);
   const int64_t W = 16 * (int64_t)std::min(G, ncu) + (int64_t)late16 * std::max(0, G - ncu);
