@@ -46,7 +46,8 @@ thread_local std::string g_err;
 constexpr int kMaxTokens = 256;    // tokens per call
 constexpr int kMaxE = 1024;
 constexpr int kMaxK = 16;
-constexpr int kRouteTT = 8;
+constexpr int kRouteTT = 8;         // router GEMV: tokens per workgroup past kRouteSmallT tokens
+constexpr int kRouteSmallT = 16;    // up to here one token per workgroup
 constexpr int kLdsActBudget = 48 * 1024;   // activation tile per workgroup
 constexpr size_t kAlign = 256;
 
@@ -498,9 +499,12 @@ moe_status_t enqueue_route(const moe_layer_t* L, const uint16_t* x_bf16, int32_t
   a.wr = L->router_w;
   a.bias = L->router_bias;
   a.T = T; a.H = L->H; a.E = L->E; a.k = L->k; a.afmt = L->afmt;
-  a.TT = kRouteTT;
-  a.ET = T <= kRouteTT ? 1 : 4;
-  a.n_tt = (T + kRouteTT - 1) / kRouteTT;
+  // decode sizes: one token per workgroup and enough experts per workgroup to keep the
+  // launch near 1024 workgroups (graph-timed on the Flint layers: the latency of a
+  // workgroup grows with its loads per lane, fastest at 1024 short workgroups)
+  a.TT = T <= kRouteSmallT ? 1 : kRouteTT;
+  a.ET = T <= 4 ? 1 : (T <= 8 ? 2 : 4);
+  a.n_tt = (T + a.TT - 1) / a.TT;
   a.n_et = (L->E + a.ET - 1) / a.ET;
   a.logits = reinterpret_cast<float*>(base + w.logits);
   a.ids = topk_ids;

@@ -130,9 +130,12 @@ hipError_t launch_quantize_nvfp4(const uint16_t* x, int rows, int cols, uint8_t*
 
 hipError_t launch_route(const RouteArgs& a, int n_quant, bool topk, hipStream_t s) {
   const int grid = a.n_tt * a.n_et + n_quant;
-  hipError_t err = a.ET == 1
-      ? launch_kernel(K_ROUTE, route_gemv_kernel<1, 8>, dim3(grid), dim3(kBlock), 0, s, a)
-      : launch_kernel(K_ROUTE, route_gemv_kernel<4, 8>, dim3(grid), dim3(kBlock), 0, s, a);
+  auto go = [&](auto kern) { return launch_kernel(K_ROUTE, kern, dim3(grid), dim3(kBlock), 0, s, a); };
+  // tiles the host picks: one token (1, 2 or 4 experts), or 8 tokens x 4 experts
+  hipError_t err = a.TT == 8 ? go(route_gemv_kernel<4, 8>)
+                   : a.ET == 1 ? go(route_gemv_kernel<1, 1>)
+                   : a.ET == 2 ? go(route_gemv_kernel<2, 1>)
+                               : go(route_gemv_kernel<4, 1>);
   if (err != hipSuccess || !topk) return err;
   const dim3 tg((a.T + kBlock / kWave - 1) / (kBlock / kWave));
   if (a.E <= 64) return launch_kernel(K_TOPK, topk_kernel<1>, tg, dim3(kBlock), 0, s, a);
