@@ -4,7 +4,7 @@
 //                   row) -- the quantize-before-down step of the Inkling page's MoE with
 //                   fused activation quantization, done once per pair.
 //   combine_kernel  y[t][r] = sum_j w[t][j] * o[t*k+j][r] (+ o_shared[t][r]), FP32 in that
-//                   order, rounded to BF16 -- the weighted combine.
+//                   order, rounded to BF16 -- the weighted combine (k <= 16).
 #include "launch.hpp"
 #include "rows.hpp"
 
@@ -26,17 +26,27 @@ __global__ void __launch_bounds__(kBlock) hquant_kernel(ExpertArgs a) {
   }
 }
 
+// One thread per (token, hidden row); grid (ceil(H / kBlock), T). Every load is issued
+// before the first use (KM >= k pairs at clamped indices; the extra ones are not summed),
+// then the sum runs in pair order.
+template <int KM>
 __global__ void __launch_bounds__(kBlock) combine_kernel(ExpertArgs a) {
-  const int64_t idx = (int64_t)blockIdx.x * kBlock + threadIdx.x;
-  if (idx >= (int64_t)a.T * a.H) return;
-  const int t = (int)(idx / a.H), r = (int)(idx % a.H);
-  float s = 0.0f;
-  for (int j = 0; j < a.k; ++j) {
-    const int p = t * a.k + j;
-    s = fmaf(a.topk_w[p], a.o[(int64_t)p * a.H + r], s);
+  const int t = blockIdx.y, r = blockIdx.x * kBlock + threadIdx.x;
+  if (r >= a.H) return;
+  float wv[KM], ov[KM];
+#pragma unroll
+  for (int j = 0; j < KM; ++j) {
+    const int p = t * a.k + min(j, a.k - 1);
+    wv[j] = a.topk_w[p];
+    ov[j] = a.o[(int64_t)p * a.H + r];
   }
-  if (a.has_shared) s += a.o[(int64_t)(a.T * a.k + t) * a.H + r];
-  a.y[idx] = (uint16_t)f32_to_bf16_rne(s);
+  const float osh = a.has_shared ? a.o[(int64_t)(a.T * a.k + t) * a.H + r] : 0.0f;
+  float s = 0.0f;
+#pragma unroll
+  for (int j = 0; j < KM; ++j)
+    if (j < a.k) s = fmaf(wv[j], ov[j], s);
+  if (a.has_shared) s += osh;
+  a.y[(int64_t)t * a.H + r] = (uint16_t)f32_to_bf16_rne(s);
 }
 
 hipError_t launch_hquant(const ExpertArgs& a, hipStream_t s) {
@@ -44,9 +54,11 @@ hipError_t launch_hquant(const ExpertArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_combine(const ExpertArgs& a, hipStream_t s) {
-  const int64_t n = (int64_t)a.T * a.H;
-  return launch_kernel(K_COMBINE, combine_kernel, dim3((unsigned)((n + kBlock - 1) / kBlock)), dim3(kBlock),
-                       0, s, a);
+  const dim3 grid((a.H + kBlock - 1) / kBlock, a.T);
+  if (a.k <= 2) return launch_kernel(K_COMBINE, combine_kernel<2>, grid, dim3(kBlock), 0, s, a);
+  if (a.k <= 4) return launch_kernel(K_COMBINE, combine_kernel<4>, grid, dim3(kBlock), 0, s, a);
+  if (a.k <= 8) return launch_kernel(K_COMBINE, combine_kernel<8>, grid, dim3(kBlock), 0, s, a);
+  return launch_kernel(K_COMBINE, combine_kernel<16>, grid, dim3(kBlock), 0, s, a);
 }
 
 }  // namespace moe
