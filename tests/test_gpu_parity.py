@@ -159,8 +159,9 @@ def test_layer_parity(lib, name, T, path):
 # moe_forward: routing fused into the gate/up kernel (pair mode) or the two launches
 # (larger batches); the same ids, weights, quantized tokens and y as moe_route followed
 # by moe_expert_forward, bit for bit, and the oracle's routing and output.
-FORWARD_CASES = [("tiny_bf16", 1), ("tiny_bf16", 8), ("flint_w4a16", 1), ("flint_w4a16", 3),
-                 ("flint_w4a16", 8), ("flint_w4a16", 16), ("flint_bf16", 8), ("inkling_w4a4", 8),
+FORWARD_CASES = [("tiny_bf16", 1), ("tiny_bf16", 8), ("flint_w4a16", 1), ("flint_w4a16", 2),
+                 ("flint_w4a16", 3), ("flint_w4a16", 4), ("flint_w4a16", 8), ("flint_w4a16", 10),
+                 ("flint_w4a16", 16), ("flint_bf16", 8), ("inkling_w4a4", 8),
                  ("inkling_mxfp8", 5), ("mistral_mxfp4", 16), ("mistral_mxfp4_a8", 8)]
 
 
