@@ -25,7 +25,8 @@ LIB_PATH = os.path.join(_HERE, "libmoe_mi355x.so")
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_ELAUNCH = 0, -1, -2, -3, -4
 WFMT = {"bf16": 0, "nvfp4": 1, "mxfp4": 2, "mxfp8": 3}
 AFMT = {"bf16": 0, "nvfp4_4o6": 1, "fp8_token": 2}
-ABI_VERSION = 2
+SCORE = {"sigmoid": 0, "softmax": 1}
+ABI_VERSION = 3
 
 
 class MoeError(RuntimeError):
@@ -43,7 +44,8 @@ class LayerT(ctypes.Structure):
                 ("k", ctypes.c_int32), ("has_shared", ctypes.c_int32), ("I_shared", ctypes.c_int32),
                 ("wfmt", ctypes.c_int32), ("shared_wfmt", ctypes.c_int32), ("afmt", ctypes.c_int32),
                 ("router_w", ctypes.c_void_p), ("router_bias", ctypes.c_void_p),
-                ("w13", WeightsT), ("w2", WeightsT), ("sh13", WeightsT), ("sh2", WeightsT)]
+                ("w13", WeightsT), ("w2", WeightsT), ("sh13", WeightsT), ("sh2", WeightsT),
+                ("router_score", ctypes.c_int32), ("bias_select_only", ctypes.c_int32)]
 
 
 class DebugT(ctypes.Structure):
@@ -140,6 +142,8 @@ class DeviceLayer:
         s.afmt = AFMT[cfg.afmt]
         s.router_w = _ptr(tensors["router_w"])
         s.router_bias = _ptr(tensors.get("router_bias"))
+        s.router_score = SCORE[getattr(cfg, "score", "sigmoid")]
+        s.bias_select_only = 1 if getattr(cfg, "bias_select_only", False) else 0
         for name in ("w13", "w2", "sh13", "sh2"):
             part = tensors.get(name)
             if part is None:

@@ -316,7 +316,7 @@ WsLayout ws_layout(const moe_layer_t& L, int maxT) {
   w.hs = std::max(L.I, Ish);
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t at = off; off = align_up(off + bytes); return at; };
-  w.logits = take(4 * (size_t)maxT * L.E);
+  w.logits = take(8 * (size_t)maxT * L.E);   // logits (keys), then bare logits (selection-only bias)
   w.h = take(4 * Pt * w.hs);
   const size_t qrow = L.afmt == A_NVFP4_4O6 ? L.I / 2 : (L.afmt == A_FP8_TOKEN ? L.I : 0);
   w.hq_codes = take(Pr * qrow);
@@ -340,6 +340,10 @@ std::string check_layer(const moe_layer_t* L, int max_tokens) {
     snprintf(b, sizeof b, "k=%d must be in [1, min(E, %d)]", L->k, kMaxK); add(b);
   }
   if (L->has_shared != 0 && L->has_shared != 1) add("has_shared must be 0 or 1");
+  if (L->router_score != MOE_SCORE_SIGMOID && L->router_score != MOE_SCORE_SOFTMAX) {
+    snprintf(b, sizeof b, "router_score=%d is not a moe_score_t", L->router_score); add(b);
+  }
+  if (L->bias_select_only != 0 && L->bias_select_only != 1) add("bias_select_only must be 0 or 1");
   if (L->has_shared == 1 && (L->I_shared < 32 || L->I_shared % 32)) {
     snprintf(b, sizeof b, "I_shared=%d must be a positive multiple of 32", L->I_shared); add(b);
   }
@@ -499,6 +503,10 @@ moe_status_t enqueue_route(const moe_layer_t* L, const uint16_t* x_bf16, int32_t
   a.wr = L->router_w;
   a.bias = L->router_bias;
   a.T = T; a.H = L->H; a.E = L->E; a.k = L->k; a.afmt = L->afmt;
+  a.softmax = L->router_score == MOE_SCORE_SOFTMAX;
+  // bias for selection only: the bare logits go to the second half of the logits area
+  a.raw = L->router_bias && L->bias_select_only ? reinterpret_cast<float*>(base + w.logits) + (size_t)T * L->E
+                                                : nullptr;
   // decode sizes: one token per workgroup and enough experts per workgroup to keep the
   // launch near 1024 workgroups (graph-timed on the Flint layers: the latency of a
   // workgroup grows with its loads per lane, fastest at 1024 short workgroups)
@@ -634,6 +642,9 @@ moe_status_t enqueue_experts(const moe_layer_t* L, const uint16_t* x_bf16, const
       gu.logits = reinterpret_cast<const float*>(base + w.logits);
       gu.ids_out = const_cast<int32_t*>(topk_ids);
       gu.w_out = const_cast<float*>(topk_w);
+      gu.raw = L->router_bias && L->bias_select_only
+                   ? reinterpret_cast<const float*>(base + w.logits) + (size_t)T * L->E : nullptr;
+      gu.softmax = L->router_score == MOE_SCORE_SOFTMAX;
     }
     // token mode: one workgroup per (token, row-step) item; with fewer items than half the
     // compute units the per-pair walk (and the combine launch) is faster

@@ -620,6 +620,8 @@ struct FusedRoute {
   float* w_out;
   int E, k;
   float inv_k;
+  const float* raw;        // bare logits [T][E] when the bias only selects, or NULL
+  int softmax;             // combine weights from the softmax (1) or the sigmoid (0)
 };
 
 // Walks one workgroup's span of a class. The class's operations (workgroup-uniform):
@@ -778,7 +780,11 @@ __device__ __forceinline__ void walk_class(const WTensor& W, const GemvMap& m, c
         if (tb != t_lo) wave_topk_load<kFusedTopkSlots>(fr.logits + (int64_t)min(t, t_hi) * fr.E, fr.E, lv);
         int e;
         float w;
-        wave_topk_select<kFusedTopkSlots>(lv, fr.E, fr.k, e, w);
+        if (fr.raw)
+          wave_topk_select<kFusedTopkSlots, true>(lv, fr.E, fr.k, fr.raw + (int64_t)min(t, t_hi) * fr.E, fr.softmax,
+                                                  e, w);
+        else
+          wave_topk_select<kFusedTopkSlots, false>(lv, fr.E, fr.k, nullptr, fr.softmax, e, w);
         if (t <= t_hi && lane < fr.k) {
           L.ids[t * fr.k + lane] = e;
           fr.ids_out[t * fr.k + lane] = e;
@@ -956,7 +962,8 @@ __global__ void __launch_bounds__(kBlock, 2) __attribute__((amdgpu_waves_per_eu(
     // fused routing: the walk's prologue selects the experts (a workgroup with an empty
     // span selects nothing)
     const FusedRoute fr =
-        a.fuse_topk ? FusedRoute{a.logits, a.ids_out, a.w_out, a.E, a.k, a.inv_k} : FusedRoute{};
+        a.fuse_topk ? FusedRoute{a.logits, a.ids_out, a.w_out, a.E, a.k, a.inv_k, a.raw, a.softmax}
+                    : FusedRoute{};
     gateup_walk<RF, AF, VW_PAIR>(a, L, sp, a.fuse_topk ? nullptr : a.ids, fr);
   } else {
     build_routed(a, L, L.rt, gateup_cost(a, true), a.rmap.NB, blockIdx.x - a.sh_wgs, gridDim.x - a.sh_wgs);

@@ -94,6 +94,9 @@ struct RouteArgs {
   uint8_t* xq_codes;
   uint8_t* xq_scales;
   float* xq_scale;
+  int softmax;              // combine weights: softmax (1) or sigmoid (0) of the selected
+  float* raw;               // [T][E] bare logits (bias for selection only: logits hold
+                            // logit + bias, the weights take these), or NULL
 };
 
 struct ExpertArgs {
@@ -119,6 +122,8 @@ struct ExpertArgs {
   const float* logits;   // writing ids_out / w_out (the buffers ids / topk_w point at)
   int32_t* ids_out;
   float* w_out;
+  const float* raw;      // bare logits [T][E] (bias for selection only) or NULL
+  int softmax;           // softmax (1) or sigmoid (0) combine weights
   int T, H, I, Ish, E, k, has_shared, afmt;
   int max_slots;         // routed expert slots launched: min(E, T * k)
   int sh_wgs;            // workgroups of the launch that walk the shared expert

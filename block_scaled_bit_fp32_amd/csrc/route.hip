@@ -88,6 +88,7 @@ __global__ void __launch_bounds__(kBlock) route_gemv_kernel(RouteArgs a) {
       float v = red[(0 * ET + e) * TT + t];
 #pragma unroll
       for (int w = 1; w < kBlock / kWave; ++w) v += red[(w * ET + e) * TT + t];
+      if (a.raw) a.raw[(int64_t)(t0 + t) * a.E + e0 + e] = v;
       if (a.bias) v += a.bias[e0 + e];
       a.logits[(int64_t)(t0 + t) * a.E + e0 + e] = v;
     }
@@ -102,7 +103,7 @@ __global__ void __launch_bounds__(kBlock) topk_kernel(RouteArgs a) {
   if (t >= a.T) return;
   int e;
   float w;
-  wave_topk<NK>(a.logits + (int64_t)t * a.E, a.E, a.k, e, w);
+  wave_topk<NK>(a.logits + (int64_t)t * a.E, a.E, a.k, a.raw ? a.raw + (int64_t)t * a.E : nullptr, a.softmax, e, w);
   if (lane < a.k) {
     a.ids[(int64_t)t * a.k + lane] = e;
     a.w[(int64_t)t * a.k + lane] = w;

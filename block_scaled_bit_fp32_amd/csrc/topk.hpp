@@ -7,7 +7,10 @@
 namespace moe {
 
 // The k largest of lg[0..E), largest first, ties to the lower expert index; weights are
-// the sigmoids of the selected logits, renormalized in selection order (FP32). Expert e
+// the sigmoids (softmax = 0) or the exponentials (softmax = 1) of the selected values,
+// renormalized over the selection in selection order (FP32). The values are the
+// selected entries of lg, or, when raw is given (a router bias that only selects: lg
+// holds logit + bias, raw the bare logits), the selected entries of raw. Expert e
 // sits in lane e % 64, slot e / 64 (E <= 64 * NK); keys are the logits' order-preserving
 // bits (0 marks an empty or taken slot; a valid key is at least 1). Each lane keeps its
 // best slot (the lowest slot among equal keys, i.e. the lowest index); a round takes the
@@ -22,8 +25,12 @@ __device__ __forceinline__ void wave_topk_load(const float* lg, int E, float (&l
 #pragma unroll
   for (int i = 0; i < NK; ++i) lv[i] = lg[min(lane + kWave * i, E - 1)];
 }
-template <int NK>
-__device__ __forceinline__ void wave_topk_select(const float (&lv)[NK], int E, int k, int& mye, float& myw) {
+// RAW: the weights take raw[] (a load per selected expert). A compile-time choice: a
+// load behind a run-time branch would make the wait for its value drain every load the
+// caller has in flight.
+template <int NK, bool RAW>
+__device__ __forceinline__ void wave_topk_select(const float (&lv)[NK], int E, int k, const float* raw, bool softmax,
+                                                 int& mye, float& myw) {
   const int lane = threadIdx.x & (kWave - 1);
   uint32_t key[NK];
 #pragma unroll
@@ -66,16 +73,28 @@ __device__ __forceinline__ void wave_topk_select(const float (&lv)[NK], int E, i
       mye = be;
     }
   }
-  const float s = lane < k ? 1.0f / (1.0f + expf(-myv)) : 0.0f;
+  if constexpr (RAW) myv = raw[lane < k ? mye : 0];   // one load per selected expert
+  float s;
+  if (softmax) {   // exp(v - max v): with a selection bias the largest value need not come first
+    float mx = -INFINITY;
+    for (int j = 0; j < k; ++j) mx = fmaxf(mx, __int_as_float(__builtin_amdgcn_readlane(__float_as_int(myv), j)));
+    s = lane < k ? expf(myv - mx) : 0.0f;
+  } else {
+    s = lane < k ? 1.0f / (1.0f + expf(-myv)) : 0.0f;
+  }
   float tot = 0.0f;
   for (int j = 0; j < k; ++j) tot += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s), j));
   myw = lane < k ? s / tot : 0.0f;
 }
 template <int NK>
-__device__ __forceinline__ void wave_topk(const float* lg, int E, int k, int& mye, float& myw) {
+__device__ __forceinline__ void wave_topk(const float* lg, int E, int k, const float* raw, bool softmax, int& mye,
+                                          float& myw) {
   float lv[NK];
   wave_topk_load<NK>(lg, E, lv);
-  wave_topk_select<NK>(lv, E, k, mye, myw);
+  if (raw)
+    wave_topk_select<NK, true>(lv, E, k, raw, softmax, mye, myw);
+  else
+    wave_topk_select<NK, false>(lv, E, k, nullptr, softmax, mye, myw);
 }
 
 }  // namespace moe

@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 2
+#define MOE_ABI_VERSION 3
 
 typedef enum {
   MOE_OK = 0,
@@ -68,6 +68,16 @@ typedef enum {
   MOE_A_FP8_TOKEN = 2    /* FP8-E4M3 with one FP32 scale amax/448 per row (MX weights)  */
 } moe_afmt_t;
 
+/* How the router turns the selected logits into combine weights (the experts are always
+ * the k largest selection keys, ties to the lower index):
+ *   MOE_SCORE_SIGMOID: w_j = sigmoid(l_j) / sum sigmoid(l_j') over the selected
+ *                      (the sigmoid top-k of the Flint and Inkling pages);
+ *   MOE_SCORE_SOFTMAX: w_j = exp(l_j) / sum exp(l_j') over the selected, i.e. the
+ *                      softmax over all experts renormalised to the selection (the
+ *                      softmax top-k router of the Mistral Large 4 page's ROCm decode).
+ * l is the logit plus the bias, or the bare logit with bias_select_only. */
+typedef enum { MOE_SCORE_SIGMOID = 0, MOE_SCORE_SOFTMAX = 1 } moe_score_t;
+
 /* One stacked weight set: n experts x [rows][K]. Expert e's codes start at
  * codes + e * rows * (bytes per row); scales and gscale likewise. */
 typedef struct {
@@ -89,11 +99,14 @@ typedef struct {
                            FP32 h)                                                        */
   const float *router_w;     /* FP32 [E][H]                                              */
   const float *router_bias;  /* FP32 [E], added to the logits before selection and
-                                weighting, or NULL                                        */
+                                weighting (see bias_select_only), or NULL                 */
   moe_weights_t w13;    /* routed gate/up: [E][2I][H], gate rows 0..I-1 then up rows      */
   moe_weights_t w2;     /* routed down: [E][H][I]                                         */
   moe_weights_t sh13;   /* shared gate/up: [1][2*I_shared][H] (ignored if !has_shared)    */
   moe_weights_t sh2;    /* shared down: [1][H][I_shared]                                  */
+  int32_t router_score;     /* moe_score_t                                               */
+  int32_t bias_select_only; /* 1: router_bias enters the selection keys only; the weights
+                               use the bare logits. 0: both                              */
 } moe_layer_t;
 
 /* Layout of the quantized-token buffer `xq` for T tokens (see moe_xq_bytes):
@@ -138,10 +151,11 @@ size_t moe_xq_bytes(const moe_layer_t *L, int32_t T);
  * that may overlap (different streams). */
 moe_status_t moe_workspace_init(void *ws, size_t ws_bytes, hipStream_t stream);
 
-/* Router: logits = x * router_w^T (+ bias) in FP32; per token the k largest logits,
- * largest first, ties to the lower expert index; topk_w = sigmoid of the selected
- * logits, renormalized to sum to 1 (FP32). With afmt != MOE_A_BF16 also quantizes
- * every token into xq (layout above) in the same launch.
+/* Router: logits = x * router_w^T in FP32, keys = logits + bias; per token the k
+ * largest keys, largest first, ties to the lower expert index; topk_w = the
+ * router_score of the selected keys (or bare logits with bias_select_only),
+ * renormalized to sum to 1 (FP32). With afmt != MOE_A_BF16 also quantizes every token
+ * into xq (layout above) in the same launch.
  *   x_bf16   [T][H] BF16, device.      topk_ids [T][k] int32, device (output).
  *   topk_w   [T][k] FP32 (output).     xq: NULL for MOE_A_BF16, else moe_xq_bytes.
  *   0 <= T <= the max_tokens ws was sized for; T = 0 enqueues nothing. */

@@ -3,7 +3,7 @@
 Test infrastructure (see oracle/__init__.py).
 
 What the layer computes, as the pages describe it:
-* router and sigmoid top-k (oracle/router.py);
+* router and sigmoid or softmax top-k (oracle/router.py);
 * "vLLM Day-0 support for Recursive's Flint", optimization strategy: the expert GEMVs
   read only the selected experts' weights; routing and the expert combine sit next to
   them;
@@ -99,7 +99,8 @@ def moe_layer(layer: dict, x_bits: np.ndarray) -> dict:
     cfg = layer["cfg"]
     x_bits = np.asarray(x_bits, dtype=np.uint16)
     T = x_bits.shape[0]
-    ids, w, lg = route(x_bits, layer["router_w"], layer["router_bias"], cfg.k)
+    ids, w, lg = route(x_bits, layer["router_w"], layer["router_bias"], cfg.k,
+                       getattr(cfg, "score", "sigmoid"), getattr(cfg, "bias_select_only", False))
     x32 = bf16_to_f64(x_bits).astype(np.float32)          # exact
     x64 = x32.astype(np.float64)
     xhat, xq = quantize_rows(cfg.afmt, x32) if T else (x64, {})

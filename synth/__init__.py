@@ -59,6 +59,8 @@ class LayerConfig:
     x_outliers: bool = False
     batches: tuple = (1,)
     I_shared: Optional[int] = None
+    score: str = "sigmoid"            # combine weights from "sigmoid" or "softmax" scores
+    bias_select_only: bool = False    # the router bias enters the selection keys only
 
     @property
     def Ish(self) -> int:
@@ -93,6 +95,21 @@ CONFIGS: Dict[str, LayerConfig] = {
     "mistral_mxfp4_a8": LayerConfig("mistral_mxfp4_a8", 6, H=6144, I=2048, E=128, k=4,
                                     has_shared=True, wfmt=W_MXFP4, shared_wfmt=W_BF16,
                                     afmt=A_FP8_TOKEN, batches=(1, 8, 64)),
+    # Softmax top-k routing (the router of the Mistral Large 4 page's ROCm decode) on the
+    # Mistral-shaped layer: the same draws as mistral_mxfp4.
+    "mistral_mxfp4_softmax": LayerConfig("mistral_mxfp4_softmax", 4, H=6144, I=2048, E=128, k=4,
+                                         has_shared=True, wfmt=W_MXFP4, shared_wfmt=W_BF16,
+                                         afmt=A_BF16, score="softmax", batches=(1, 8, 64)),
+    # Router bias used for expert selection only, on the bias-skewed Flint BF16 layer.
+    "flint_bf16_selbias": LayerConfig("flint_bf16_selbias", 2, H=2048, I=768, E=256, k=6,
+                                      has_shared=True, wfmt=W_BF16, shared_wfmt=W_BF16,
+                                      afmt=A_BF16, router_bias=True, bias_select_only=True,
+                                      batches=(1, 8, 64)),
+    # Tiny layer with a router bias, softmax weights and selection-only bias.
+    "tiny_softmax_selbias": LayerConfig("tiny_softmax_selbias", 7, H=256, I=128, E=8, k=2,
+                                        has_shared=True, wfmt=W_BF16, shared_wfmt=W_BF16,
+                                        afmt=A_BF16, router_bias=True, score="softmax",
+                                        bias_select_only=True, batches=(1,)),
 }
 
 

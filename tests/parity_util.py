@@ -94,7 +94,7 @@ def oracle_layer(name: str, T: int):
 def oracle_route_only(name: str, x: np.ndarray):
     L = host_layer(name)
     cfg = L["cfg"]
-    ids, w, lg = OR.route(x, L["router_w"], L["router_bias"], cfg.k)
+    ids, w, lg = OR.route(x, L["router_w"], L["router_bias"], cfg.k, cfg.score, cfg.bias_select_only)
     return {"ids": ids, "w": w, "logits": lg, "ambiguous": OR.ambiguous_tokens(lg, cfg.k)}
 
 

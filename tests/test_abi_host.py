@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol(lib):
     so = ctypes.CDLL(lib.LIB_PATH)
     for n in _declared_functions():
         assert hasattr(so, n), n
-    assert so.moe_abi_version() == 2
+    assert so.moe_abi_version() == 3
 
 
 def _fake_layer(lib, name, **over):
@@ -73,6 +73,10 @@ def test_default_deny_lists_every_reason(lib):
     s = _fake_layer(lib, "mistral_mxfp4", afmt=1)
     st, why = _check(lib, s, 8)
     assert "NVFP4_4O6 needs NVFP4" in why
+    s = _fake_layer(lib, "flint_w4a16", router_score=5, bias_select_only=2)
+    st, why = _check(lib, s, 8)
+    assert st == lib.MOE_EUNSUPPORTED
+    assert "router_score=5" in why and "bias_select_only must be 0 or 1" in why
     s = _fake_layer(lib, "flint_w4a16", shared_wfmt=2)
     st, why = _check(lib, s, 8)
     assert "shared expert must use" in why

@@ -85,6 +85,9 @@ LAYER_CASES = [
     ("inkling_mxfp8", [1, 8]),
     ("mistral_mxfp4", [1, 8]),
     ("mistral_mxfp4_a8", [1, 8]),
+    ("tiny_softmax_selbias", [1, 3]),
+    ("mistral_mxfp4_softmax", [1, 8]),
+    ("flint_bf16_selbias", [1, 8]),
 ]
 
 
@@ -162,7 +165,9 @@ def test_layer_parity(lib, name, T, path):
 FORWARD_CASES = [("tiny_bf16", 1), ("tiny_bf16", 8), ("flint_w4a16", 1), ("flint_w4a16", 2),
                  ("flint_w4a16", 3), ("flint_w4a16", 4), ("flint_w4a16", 8), ("flint_w4a16", 10),
                  ("flint_w4a16", 16), ("flint_bf16", 8), ("inkling_w4a4", 8),
-                 ("inkling_mxfp8", 5), ("mistral_mxfp4", 16), ("mistral_mxfp4_a8", 8)]
+                 ("inkling_mxfp8", 5), ("mistral_mxfp4", 16), ("mistral_mxfp4_a8", 8),
+                 ("tiny_softmax_selbias", 8), ("mistral_mxfp4_softmax", 8), ("flint_bf16_selbias", 8),
+                 ("flint_bf16_selbias", 16)]
 
 
 @pytest.mark.parametrize("name,T", FORWARD_CASES)
