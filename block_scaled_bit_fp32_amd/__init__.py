@@ -73,6 +73,7 @@ _SIGNATURES = {
     "moe_forward": (_I32, [ctypes.POINTER(LayerT), _P, _I32, _P, _P, _P, _P, _P, _SZ,
                            ctypes.POINTER(DebugT), _P]),
     "quantize_nvfp4_4o6": (_I32, [_P, _I32, _I32, _P, _P, _P, _P, _P]),
+    "moe_requant_mxfp4": (_I32, [_P, ctypes.c_int64, _I32, _P, _P, _P]),
     "moe_profile_begin": (_I32, []),
     "moe_profile_end": (_I32, [ctypes.POINTER(KernelTimeT), _I32]),
     "moe_last_error": (ctypes.c_char_p, []),
@@ -330,6 +331,17 @@ def quantize_nvfp4_4o6(x: torch.Tensor, want_choice: bool = True):
     _check(_lib.quantize_nvfp4_4o6(x.data_ptr(), rows, cols, codes.data_ptr(), scales.data_ptr(),
                                    g.data_ptr(), _ptr(choice), _stream()))
     return codes, scales, g, choice
+
+
+def requant_mxfp4(w: torch.Tensor):
+    """moe_requant_mxfp4 of BF16 rows w [rows, cols]: returns (codes [rows, cols/2],
+    E8M0 scales [rows, cols/32]), the MOE_W_MXFP4 layout."""
+    w = _bits16(w)
+    rows, cols = w.shape
+    codes = _aligned_empty(rows * cols // 2, w.device).view(rows, cols // 2)
+    scales = torch.empty((rows, cols // 32), dtype=torch.uint8, device=w.device)
+    _check(_lib.moe_requant_mxfp4(w.data_ptr(), rows, cols, codes.data_ptr(), scales.data_ptr(), _stream()))
+    return codes, scales
 
 
 def profile_begin() -> None:

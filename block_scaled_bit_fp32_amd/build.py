@@ -18,7 +18,7 @@ OUT = os.path.join(HERE, "libmoe_mi355x.so")
 BUILD = os.path.join(ROOT, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["route.hip", "combine.hip", "experts_bf16.hip", "experts_nvfp4.hip", "experts_mxfp4.hip",
+SOURCES = ["route.hip", "combine.hip", "requant.hip", "experts_bf16.hip", "experts_nvfp4.hip", "experts_mxfp4.hip",
            "experts_mxfp8.hip", "abi.cpp", "profile.cpp"]
 COMMON = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
           "-I" + os.path.join(ROOT, "include")]

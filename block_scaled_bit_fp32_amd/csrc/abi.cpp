@@ -11,6 +11,8 @@
 
 namespace moe {
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
+hipError_t launch_requant_mxfp4(const uint16_t* x, int64_t nblocks, uint8_t* codes, uint8_t* scales,
+                                hipStream_t s);
 hipError_t launch_quantize_nvfp4(const uint16_t* x, int rows, int cols, uint8_t* codes,
                                  uint8_t* scales, float* g, uint8_t* choice, hipStream_t s);
 hipError_t launch_route(const RouteArgs& a, int n_quant, bool topk, hipStream_t s);
@@ -701,6 +703,23 @@ moe_status_t moe_forward(const moe_layer_t* L, const uint16_t* x_bf16, int32_t T
   if ((st = enqueue_route(L, x_bf16, T, topk_ids, topk_w, xq, ws, ws_bytes, !fused, false, stream)) != MOE_OK)
     return st;
   return enqueue_experts(L, x_bf16, xq, T, topk_ids, topk_w, y_bf16, ws, ws_bytes, dbg, fused, false, stream);
+}
+
+moe_status_t moe_requant_mxfp4(const uint16_t* w_bf16, int64_t rows, int32_t cols, uint8_t* codes, uint8_t* scales,
+                               hipStream_t stream) {
+  std::string bad;
+  if (rows < 0) bad += "rows must be >= 0; ";
+  if (cols <= 0 || cols % 32) bad += "cols must be a positive multiple of 32; ";
+  if (rows > 0) {
+    if (!w_bf16 || !aligned(w_bf16, 16)) bad += "w_bf16 must be non-NULL and 16-byte aligned; ";
+    if (!codes || !aligned(codes, 16)) bad += "codes must be non-NULL and 16-byte aligned; ";
+    if (!scales) bad += "scales is NULL; ";
+  }
+  if (!bad.empty()) return set_err(MOE_EINVAL, bad);
+  if (rows == 0) return MOE_OK;
+  if (launch_requant_mxfp4(w_bf16, rows * (cols / 32), codes, scales, stream) != hipSuccess)
+    return set_err(MOE_ELAUNCH, "requant kernel launch failed");
+  return MOE_OK;
 }
 
 moe_status_t quantize_nvfp4_4o6(const uint16_t* x_bf16, int32_t rows, int32_t cols, uint8_t* codes,

@@ -1,0 +1,50 @@
+// Load-time weight requantization (off the decode path): BF16 rows to MXFP4, E2M1
+// values with one E8M0 scale per 32 (the Mistral Large 4 page's ROCm load path requantizes
+// each expert this way, one layer at a time). The scale follows the OCP MX v1.0 rule:
+// shared exponent floor(log2(block amax)) - 2, clamped to [-127, 127]; elements are the
+// values times 2^-exponent (exact), rounded to E2M1 with ties to even and saturation at
+// 6; an all-zero block takes exponent -127 and signed zero codes.
+#include "launch.hpp"
+#include "device.hpp"
+
+namespace moe {
+
+// One thread per 32-element block; blocks are contiguous (cols % 32 == 0), so block b's
+// 16 code bytes start at 16 b and its scale byte is b.
+__global__ void __launch_bounds__(kBlock) requant_mxfp4_kernel(const uint16_t* x, int64_t nblocks, uint8_t* codes,
+                                                               uint8_t* scales) {
+  const int64_t b = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+  if (b >= nblocks) return;
+  const uint4* src = reinterpret_cast<const uint4*>(x + b * 32);
+  float v[32];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint4 r = src[q];
+    const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[8 * q + 2 * i] = bf16_to_f32(w[i] & 0xFFFFu);
+      v[8 * q + 2 * i + 1] = bf16_to_f32(w[i] >> 16);
+    }
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  // floor(log2(amax)) = frexp exponent - 1 (amax = m * 2^e, m in [0.5, 1)), then - 2
+  int e = amax > 0.0f ? __builtin_amdgcn_frexp_expf(amax) - 3 : -127;
+  e = min(max(e, -127), 127);
+  uint32_t w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int i = 0; i < 32; ++i) w[i >> 3] |= e2m1_encode(ldexpf(v[i], -e)) << (4 * (i & 7));
+  *reinterpret_cast<uint4*>(codes + 16 * b) = make_uint4(w[0], w[1], w[2], w[3]);
+  scales[b] = (uint8_t)(e + 127);
+}
+
+hipError_t launch_requant_mxfp4(const uint16_t* x, int64_t nblocks, uint8_t* codes, uint8_t* scales,
+                                hipStream_t s) {
+  const int64_t grid = (nblocks + kBlock - 1) / kBlock;
+  return launch_kernel(K_QUANT, requant_mxfp4_kernel, dim3((unsigned)grid), dim3(kBlock), 0, s, x, nblocks, codes,
+                       scales);
+}
+
+}  // namespace moe

@@ -21,7 +21,8 @@
  * Conventions for every entry point:
  *   - Tensor pointers are DEVICE pointers owned by the caller (e.g. a torch tensor's
  *     data_ptr()). The library never allocates, frees or synchronizes inside
- *     moe_route, moe_expert_forward, moe_forward or quantize_nvfp4_4o6; they enqueue
+ *     moe_route, moe_expert_forward, moe_forward, quantize_nvfp4_4o6 or
+ *     moe_requant_mxfp4; they enqueue
  *     kernels on `stream` and return.
  *   - Every entry returns a moe_status_t and never throws. Arguments are validated
  *     before anything is launched; on error nothing is enqueued and moe_last_error()
@@ -200,6 +201,21 @@ moe_status_t moe_forward(const moe_layer_t *L, const uint16_t *x_bf16, int32_t T
 moe_status_t quantize_nvfp4_4o6(const uint16_t *x_bf16, int32_t rows, int32_t cols,
                                 uint8_t *codes, uint8_t *scales, float *gscale,
                                 uint8_t *choice, hipStream_t stream);
+
+/* Load-time weight requantization to MXFP4 (MOE_W_MXFP4 layout), following the load
+ * path of the Mistral Large 4 page's ROCm implementation details (each expert
+ * dequantized to BF16, then requantized to E2M1 values with one E8M0 scale per 32).
+ * Per 32-element block, the OCP MX v1.0 rule: shared exponent floor(log2(block amax))
+ * - 2, clamped to [-127, 127], scale byte = exponent + 127; elements = value *
+ * 2^-exponent (exact), rounded to E2M1 with ties to even, saturating at 6, sign kept
+ * (so -0 gives code 8). An all-zero block takes scale byte 0.
+ *   w_bf16 [rows][cols] BF16, device, 16-byte aligned; cols a positive multiple of 32.
+ *   codes  [rows][cols/2] (element 2i in the low nibble), 16-byte aligned (output).
+ *   scales [rows][cols/32] E8M0 bytes (output).
+ *   rows = 0 enqueues nothing. Asynchronous on stream; caller-owned buffers. A stack
+ *   of experts is one call with rows = experts * rows per expert. */
+moe_status_t moe_requant_mxfp4(const uint16_t *w_bf16, int64_t rows, int32_t cols,
+                               uint8_t *codes, uint8_t *scales, hipStream_t stream);
 
 /* Diagnostics: per-kernel device time.
  * Between moe_profile_begin() and moe_profile_end(), every kernel the library launches

@@ -10,6 +10,13 @@ Test infrastructure (see oracle/__init__.py).
 * quantize_fp8_token -- "Day 0 support for Mistral Large 4 on vLLM", AMD section,
   MXFP4 experts: a8w4 runs MXFP4 experts on FP8 activations with dynamic scales;
   here one FP32 scale per row, amax / 448.
+* quantize_mxfp4 -- the same page, ROCm implementation details (load-time expert
+  requantization): each expert is dequantized to BF16 and requantized to MXFP4, E2M1
+  values with one E8M0 scale per 32. The scale follows the OCP MX v1.0 rule: shared
+  exponent floor(log2(block amax)) minus 2 (the largest E2M1 exponent), clamped to the
+  E8M0 range [-127, 127]; elements are the block values times 2^-exponent, rounded to
+  E2M1 (nearest, ties to even, saturating at 6). An all-zero block takes the smallest
+  scale, 2^-127 (byte 0), and zero codes carrying the input signs.
 
 The pages fix neither the floating-point operation order nor the zero and saturation
 cases. The quantizer is defined as exact IEEE FP32 operations in the order written
@@ -141,6 +148,23 @@ def quantize_fp8_token(x: np.ndarray):
 
 def dequant_fp8_token(codes: np.ndarray, s: np.ndarray) -> np.ndarray:
     return E4M3_TABLE[codes] * np.asarray(s, dtype=np.float64)[:, None]
+
+
+def quantize_mxfp4(x: np.ndarray):
+    """MXFP4 of rows x [rows, cols] (FP32 values, cols % 32 == 0): returns (packed codes
+    [rows, cols/2] uint8, element 2i in the low nibble; E8M0 scale bytes [rows, cols/32])."""
+    x = np.asarray(x, dtype=np.float32)
+    rows, cols = x.shape
+    if cols % MX_BLOCK:
+        raise ValueError("cols must be a multiple of 32")
+    xb = x.reshape(rows, cols // MX_BLOCK, MX_BLOCK)
+    amax = np.abs(xb).max(axis=2).astype(np.float64)
+    _, e = np.frexp(amax)                          # amax = m * 2^e, m in [0.5, 1): floor(log2) = e - 1
+    shared = np.where(amax > 0, e - 1 - 2, -127)
+    shared = np.clip(shared, -127, 127).astype(np.int64)
+    y = np.ldexp(xb.astype(np.float64), -shared[:, :, None]).astype(np.float32)   # exact scaling
+    codes = e2m1_encode(y).reshape(rows, cols)
+    return pack_fp4(codes), (shared + 127).astype(np.uint8)
 
 
 def dequant_weights(fmt: str, codes: np.ndarray, scales, gscale) -> np.ndarray:

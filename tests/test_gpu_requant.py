@@ -1,0 +1,56 @@
+"""GPU parity of moe_requant_mxfp4 (load-time BF16 -> MXFP4 requantization): codes and
+E8M0 scales bit-exact against the oracle's quantize_mxfp4 on the same BF16 rows."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import quant as OQ
+from parity_util import bf16_bits_to_f64, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _check(lib, xb):
+    say(f"[requant] mxfp4 rows={xb.shape[0]} cols={xb.shape[1]}")
+    codes, scales = lib.requant_mxfp4(torch.from_numpy(xb.view(np.int16)).cuda())
+    torch.cuda.synchronize()
+    x32 = bf16_bits_to_f64(torch.from_numpy(xb.view(np.int16))).astype(np.float32)
+    rc, rs = OQ.quantize_mxfp4(x32)
+    assert np.array_equal(scales.cpu().numpy(), rs)
+    assert np.array_equal(codes.cpu().numpy(), rc)
+
+
+def test_requant_mxfp4_wide_range_rows(lib):
+    rng = np.random.default_rng(41)
+    x = rng.normal(size=(64, 2048)) * np.exp(rng.normal(size=(64, 1)) * 6)
+    _check(lib, synth.to_bf16_bits(x))
+
+
+def test_requant_mxfp4_ragged_grid(lib):
+    """300 x 96: 900 blocks, not a multiple of the 256-thread launch."""
+    rng = np.random.default_rng(42)
+    _check(lib, synth.to_bf16_bits(rng.normal(size=(300, 96)) * 0.02))
+
+
+def test_requant_mxfp4_special_blocks(lib):
+    rows = np.zeros((6, 64))
+    rows[0, 3] = -0.0
+    rows[1, :32] = 2.0 ** -133                     # BF16 subnormal: exponent clamps to -127
+    rows[2, :32] = 3.0e38                          # exponent 125, values saturate
+    ties = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0])
+    rows[3, :8] = ties                              # amax 6: exponent 0, every tie of E2M1
+    rows[3, 8:16] = -ties
+    rows[4, :8] = ties * 2.0 ** -10                 # the same ties, scaled
+    rows[5, :32] = np.linspace(-7.9, 7.9, 32)       # amax 7.9: exponent 0, saturation at 6
+    xb = synth.to_bf16_bits(rows)
+    xb[0, 3] = 0x8000                               # an exact -0
+    _check(lib, xb)
+
+
+def test_requant_mxfp4_all_bf16_values(lib):
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    v = (bits.astype(np.uint32) << 16).view(np.float32)
+    bits = bits[np.isfinite(v)]
+    n = len(bits) // 2048 * 2048
+    _check(lib, bits[:n].reshape(-1, 2048).copy())

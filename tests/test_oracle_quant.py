@@ -257,3 +257,68 @@ def test_weight_dequant_formats():
     c8 = np.full((1, 32), 0x3C, np.uint8)       # 1.5
     w = Q.dequant_weights("mxfp8", c8, np.array([[128]], np.uint8), None)
     assert np.all(w == 3.0)
+
+
+# ------------------------------------------------------------------ MXFP4 requant
+def _mx_decode(packed, sbytes):
+    """MXFP4 rows back to FP64 from the format's own tables (E2M1 value times 2^(byte-127))."""
+    from oracle.formats import e2m1_value
+    c = Q.unpack_fp4(packed).astype(np.int64)
+    v = np.vectorize(e2m1_value)(c)
+    rows, cols = c.shape
+    ex = np.repeat(sbytes.astype(np.int64) - 127, 32, axis=1)
+    return np.ldexp(v, ex)
+
+
+def test_mxfp4_worked_block():
+    """amax 7 -> floor(log2 7) = 2 -> exponent 0 (byte 127); 6 -> code 7, 0.1 -> 0,
+    -3 -> 13, 7 saturates to 6 (code 7)."""
+    x = np.zeros((1, 32), np.float32)
+    x[0, :4] = [6.0, 0.1, -3.0, 7.0]
+    codes, s = Q.quantize_mxfp4(x)
+    assert s.tolist() == [[127]]
+    assert codes[0, :2].tolist() == [7 | (0 << 4), 13 | (7 << 4)]
+    assert np.all(codes[0, 2:] == 0)
+
+
+def test_mxfp4_round_trip_of_representable_blocks():
+    """Blocks built from E2M1 values times 2^X come back bit for bit."""
+    from oracle.formats import e2m1_value
+    rng = np.random.default_rng(31)
+    c = rng.integers(0, 16, size=(20, 256))
+    X = rng.integers(-20, 20, size=(20, 8))
+    v = np.ldexp(np.vectorize(e2m1_value)(c), np.repeat(X, 32, axis=1)).astype(np.float32)
+    codes, s = Q.quantize_mxfp4(v)
+    back = _mx_decode(codes, s)
+    assert np.array_equal(back, v.astype(np.float64))
+
+
+def test_mxfp4_scale_is_floor_log2_minus_2_and_error_bounded():
+    """The scale byte from math.log2 (another route than frexp), and every element within
+    half an E2M1 step of its value, or saturated at 6 when the block exceeds 6 * 2^X."""
+    import math
+    rng = np.random.default_rng(32)
+    x = (rng.normal(size=(16, 512)) * np.exp(rng.normal(size=(16, 1)) * 4)).astype(np.float32)
+    codes, s = Q.quantize_mxfp4(x)
+    blocks = np.abs(x.reshape(16, -1, 32)).max(axis=2)
+    want = np.vectorize(lambda a: min(127, max(-127, math.floor(math.log2(a)) - 2)) + 127)(blocks.astype(np.float64))
+    assert np.array_equal(s, want)
+    back = _mx_decode(codes, s)
+    X = np.ldexp(1.0, np.repeat(s.astype(np.int64) - 127, 32, axis=1))
+    y = np.abs(x.astype(np.float64)) / X
+    half = np.where(y < 2, 0.25, np.where(y < 4, 0.5, 1.0))
+    bound = np.maximum(half, y - 6.0) * X
+    assert np.all(np.abs(back - x) <= bound * (1 + 1e-12))
+
+
+def test_mxfp4_zero_and_extreme_blocks():
+    x = np.zeros((1, 96), np.float32)
+    x[0, 5] = -0.0
+    x[0, 32] = 2.0 ** -133            # below the E8M0 range: exponent clamps to -127
+    x[0, 64] = 3.0e38                 # near the FP32 top: exponent 125
+    codes, s = Q.quantize_mxfp4(x)
+    assert s.tolist() == [[0, 0, 127 + 125]]
+    c = Q.unpack_fp4(codes)[0]
+    assert c[5] == 8 and c[0] == 0                  # signed zero kept
+    assert c[32] == 0                               # 2^-133 / 2^-127 = 2^-6 rounds to 0
+    assert c[64] == 7                               # 3e38 / 2^125 = 7.05 saturates to 6 (code 7)
