@@ -54,3 +54,38 @@ def test_requant_mxfp4_all_bf16_values(lib):
     bits = bits[np.isfinite(v)]
     n = len(bits) // 2048 * 2048
     _check(lib, bits[:n].reshape(-1, 2048).copy())
+
+
+def test_requantized_layer_runs_end_to_end(lib):
+    """The load path end to end: a Flint-shaped BF16 layer (16 experts, top-4, BF16
+    shared expert) has its routed experts requantized to MXFP4 on the GPU, the codes are
+    loaded as an MXFP4 layer, and moe_forward's ids and y match the oracle evaluated on
+    those same codes."""
+    import dataclasses
+    from oracle import layer as OL
+    from parity_util import check_ids, y_close
+    base = dataclasses.replace(synth.CONFIGS["flint_bf16"], name="flint_bf16_e16", E=16, k=4,
+                               router_bias=False)
+    L = synth.make_layer(base)
+    cfg = dataclasses.replace(base, name="flint_mxfp4_requant", wfmt=synth.W_MXFP4)
+    Lq = dict(L, cfg=cfg)
+    for name in ("w13", "w2"):
+        c = L[name]["codes"]                                   # BF16 bits [E][rows][K]
+        say(f"[requant] layer {name} {c.shape}")
+        codes, scales = lib.requant_mxfp4(torch.from_numpy(c.reshape(-1, c.shape[2]).view(np.int16)).cuda())
+        torch.cuda.synchronize()
+        Lq[name] = {"codes": codes.cpu().numpy().reshape(c.shape[0], c.shape[1], -1),
+                    "scales": scales.cpu().numpy().reshape(c.shape[0], c.shape[1], -1), "gscale": None}
+    dl = lib.DeviceLayer.from_host(Lq)
+    for T in (1, 8):
+        x_np = synth.make_x(base, T)
+        ref = OL.moe_layer(Lq, x_np)
+        ws = lib.Workspace(dl, T)
+        y, ids, w, _ = lib.forward(dl, torch.from_numpy(x_np.view(np.int16)).cuda(), ws)
+        torch.cuda.synchronize()
+        ids_g = ids.cpu().numpy()
+        assert not check_ids(ids_g, ref, cfg.k)
+        if np.array_equal(ids_g, ref["ids"]):
+            ok, max_abs, rel = y_close(bf16_bits_to_f64(y), ref["y"])
+            say(f"[requant]   T={T} y max_abs/r={max_abs:.3g} rel_l2={rel:.3g}")
+            assert ok, (max_abs, rel)
