@@ -74,6 +74,7 @@ _SIGNATURES = {
                            ctypes.POINTER(DebugT), _P]),
     "quantize_nvfp4_4o6": (_I32, [_P, _I32, _I32, _P, _P, _P, _P, _P]),
     "moe_requant_mxfp4": (_I32, [_P, ctypes.c_int64, _I32, _P, _P, _P]),
+    "moe_requant_nvfp4": (_I32, [_P, _I32, ctypes.c_int64, _I32, _P, _P, _P, _P]),
     "moe_profile_begin": (_I32, []),
     "moe_profile_end": (_I32, [ctypes.POINTER(KernelTimeT), _I32]),
     "moe_last_error": (ctypes.c_char_p, []),
@@ -342,6 +343,19 @@ def requant_mxfp4(w: torch.Tensor):
     scales = torch.empty((rows, cols // 32), dtype=torch.uint8, device=w.device)
     _check(_lib.moe_requant_mxfp4(w.data_ptr(), rows, cols, codes.data_ptr(), scales.data_ptr(), _stream()))
     return codes, scales
+
+
+def requant_nvfp4(w: torch.Tensor):
+    """moe_requant_nvfp4 of BF16 tensors w [n, rows, cols]: returns (codes [n, rows, cols/2],
+    E4M3 scales [n, rows, cols/16], gscale [n] FP32), the MOE_W_NVFP4 layout."""
+    w = _bits16(w)
+    n, rows, cols = w.shape
+    codes = _aligned_empty(n * rows * cols // 2, w.device).view(n, rows, cols // 2)
+    scales = torch.empty((n, rows, cols // 16), dtype=torch.uint8, device=w.device)
+    g = torch.empty(n, dtype=torch.float32, device=w.device)
+    _check(_lib.moe_requant_nvfp4(w.data_ptr(), n, rows, cols, codes.data_ptr(), scales.data_ptr(), g.data_ptr(),
+                                  _stream()))
+    return codes, scales, g
 
 
 def profile_begin() -> None:

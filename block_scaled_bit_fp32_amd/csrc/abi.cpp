@@ -13,6 +13,8 @@ namespace moe {
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 hipError_t launch_requant_mxfp4(const uint16_t* x, int64_t nblocks, uint8_t* codes, uint8_t* scales,
                                 hipStream_t s);
+hipError_t launch_requant_nvfp4(const uint16_t* x, int ntensors, int64_t n, uint8_t* codes, uint8_t* scales,
+                                float* gscale, hipStream_t s);
 hipError_t launch_quantize_nvfp4(const uint16_t* x, int rows, int cols, uint8_t* codes,
                                  uint8_t* scales, float* g, uint8_t* choice, hipStream_t s);
 hipError_t launch_route(const RouteArgs& a, int n_quant, bool topk, hipStream_t s);
@@ -718,6 +720,26 @@ moe_status_t moe_requant_mxfp4(const uint16_t* w_bf16, int64_t rows, int32_t col
   if (!bad.empty()) return set_err(MOE_EINVAL, bad);
   if (rows == 0) return MOE_OK;
   if (launch_requant_mxfp4(w_bf16, rows * (cols / 32), codes, scales, stream) != hipSuccess)
+    return set_err(MOE_ELAUNCH, "requant kernel launch failed");
+  return MOE_OK;
+}
+
+moe_status_t moe_requant_nvfp4(const uint16_t* w_bf16, int32_t ntensors, int64_t rows, int32_t cols,
+                               uint8_t* codes, uint8_t* scales, float* gscale, hipStream_t stream) {
+  std::string bad;
+  if (ntensors < 0) bad += "ntensors must be >= 0; ";
+  if (rows < 0) bad += "rows must be >= 0; ";
+  if (cols <= 0 || cols % 16) bad += "cols must be a positive multiple of 16; ";
+  if (rows > 0 && (int64_t)cols * rows / 16 > (int64_t)0x7FFFFFFF) bad += "a tensor may hold at most 2^31 blocks; ";
+  if (ntensors > 0 && rows > 0) {
+    if (!w_bf16 || !aligned(w_bf16, 16)) bad += "w_bf16 must be non-NULL and 16-byte aligned; ";
+    if (!codes || !aligned(codes, 8)) bad += "codes must be non-NULL and 8-byte aligned; ";
+    if (!scales) bad += "scales is NULL; ";
+    if (!gscale) bad += "gscale is NULL; ";
+  }
+  if (!bad.empty()) return set_err(MOE_EINVAL, bad);
+  if (ntensors == 0 || rows == 0) return MOE_OK;
+  if (launch_requant_nvfp4(w_bf16, ntensors, rows * cols, codes, scales, gscale, stream) != hipSuccess)
     return set_err(MOE_ELAUNCH, "requant kernel launch failed");
   return MOE_OK;
 }

@@ -1,11 +1,14 @@
-// Load-time weight requantization (off the decode path): BF16 rows to MXFP4, E2M1
+// Load-time weight requantization (off the decode path). MXFP4: BF16 rows to E2M1
 // values with one E8M0 scale per 32 (the Mistral Large 4 page's ROCm load path requantizes
 // each expert this way, one layer at a time). The scale follows the OCP MX v1.0 rule:
 // shared exponent floor(log2(block amax)) - 2, clamped to [-127, 127]; elements are the
 // values times 2^-exponent (exact), rounded to E2M1 with ties to even and saturation at
-// 6; an all-zero block takes exponent -127 and signed zero codes.
+// 6; an all-zero block takes exponent -127 and signed zero codes. NVFP4: the two-level
+// recipe, one FP32 scale per tensor g = amax / 2688 and per 16-block the Four-Over-Six
+// arithmetic with the target 6 only (E4M3 block scale (m / g) / 6, elements x / (S g)).
 #include "launch.hpp"
 #include "device.hpp"
+#include "rows.hpp"
 
 namespace moe {
 
@@ -38,6 +41,49 @@ __global__ void __launch_bounds__(kBlock) requant_mxfp4_kernel(const uint16_t* x
   for (int i = 0; i < 32; ++i) w[i >> 3] |= e2m1_encode(ldexpf(v[i], -e)) << (4 * (i & 7));
   *reinterpret_cast<uint4*>(codes + 16 * b) = make_uint4(w[0], w[1], w[2], w[3]);
   scales[b] = (uint8_t)(e + 127);
+}
+
+// One workgroup per tensor of n elements (n % 16 == 0): the tensor's amax, then every
+// 16-block with the c = 6 candidate.
+__global__ void __launch_bounds__(kBlock) requant_nvfp4_kernel(const uint16_t* x, int64_t n, uint8_t* codes,
+                                                               uint8_t* scales, float* gscale) {
+  __shared__ float red[kBlock / kWave];
+  const int64_t t = blockIdx.x, nb = n / 16;
+  const Bf16Row row{x + t * n};
+  float amax = 0.0f;
+  for (int64_t b = threadIdx.x; b < nb; b += kBlock) {
+    float v[16];
+    row.load((int)b, v);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  }
+  amax = block_max(amax, red);
+  const float g = amax / 2688.0f;
+  uint8_t* ct = codes + t * (n / 2);
+  uint8_t* st = scales + t * nb;
+  for (int64_t b = threadIdx.x; b < nb; b += kBlock) {
+    float v[16];
+    row.load((int)b, v);
+    uint32_t sb = 0, c[2] = {0u, 0u};
+    if (amax == 0.0f) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) c[i >> 3] |= ((__float_as_uint(v[i]) >> 28) & 8u) << (4 * (i & 7));
+    } else {
+      float m = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(v[i]));
+      nvfp4_candidate(v, m, g, 6.0f, sb, c);
+    }
+    *reinterpret_cast<uint2*>(ct + 8 * b) = make_uint2(c[0], c[1]);
+    st[b] = (uint8_t)sb;
+  }
+  if (threadIdx.x == 0) gscale[t] = g;
+}
+
+hipError_t launch_requant_nvfp4(const uint16_t* x, int ntensors, int64_t n, uint8_t* codes, uint8_t* scales,
+                                float* gscale, hipStream_t s) {
+  return launch_kernel(K_QUANT, requant_nvfp4_kernel, dim3(ntensors), dim3(kBlock), 0, s, x, n, codes, scales,
+                       gscale);
 }
 
 hipError_t launch_requant_mxfp4(const uint16_t* x, int64_t nblocks, uint8_t* codes, uint8_t* scales,

@@ -21,8 +21,8 @@
  * Conventions for every entry point:
  *   - Tensor pointers are DEVICE pointers owned by the caller (e.g. a torch tensor's
  *     data_ptr()). The library never allocates, frees or synchronizes inside
- *     moe_route, moe_expert_forward, moe_forward, quantize_nvfp4_4o6 or
- *     moe_requant_mxfp4; they enqueue
+ *     moe_route, moe_expert_forward, moe_forward, quantize_nvfp4_4o6,
+ *     moe_requant_mxfp4 or moe_requant_nvfp4; they enqueue
  *     kernels on `stream` and return.
  *   - Every entry returns a moe_status_t and never throws. Arguments are validated
  *     before anything is launched; on error nothing is enqueued and moe_last_error()
@@ -216,6 +216,21 @@ moe_status_t quantize_nvfp4_4o6(const uint16_t *x_bf16, int32_t rows, int32_t co
  *   of experts is one call with rows = experts * rows per expert. */
 moe_status_t moe_requant_mxfp4(const uint16_t *w_bf16, int64_t rows, int32_t cols,
                                uint8_t *codes, uint8_t *scales, hipStream_t stream);
+
+/* Load-time weight requantization to NVFP4 (MOE_W_NVFP4 layout), the load path's other
+ * target: ntensors tensors of [rows][cols], each with its own FP32 scale (gate, up and
+ * down of every expert are separate tensors, so a w13 stack is 2E tensors of I rows in
+ * gscale order [E][2], a w2 stack E tensors of H rows). Per tensor, in FP32: a = max
+ * |x|; g = a / 2688; per 16-block with maximum m: S = E4M3((m / g) / 6) (nearest-even,
+ * saturating at 448), elements E2M1(x / (S * g)) (nearest-even, saturating at 6); a
+ * zero S * g or an all-zero tensor gives sign-only codes (and g = 0, scale bytes 0).
+ *   w_bf16 [ntensors][rows][cols] BF16, device, 16-byte aligned; cols a positive
+ *   multiple of 16. codes [ntensors][rows][cols/2] (element 2i in the low nibble),
+ *   8-byte aligned; scales [ntensors][rows][cols/16] E4M3 bytes; gscale [ntensors]
+ *   FP32 (outputs). ntensors = 0 or rows = 0 enqueues nothing. One workgroup per tensor. */
+moe_status_t moe_requant_nvfp4(const uint16_t *w_bf16, int32_t ntensors, int64_t rows,
+                               int32_t cols, uint8_t *codes, uint8_t *scales,
+                               float *gscale, hipStream_t stream);
 
 /* Diagnostics: per-kernel device time.
  * Between moe_profile_begin() and moe_profile_end(), every kernel the library launches

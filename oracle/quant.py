@@ -17,6 +17,10 @@ Test infrastructure (see oracle/__init__.py).
   E8M0 range [-127, 127]; elements are the block values times 2^-exponent, rounded to
   E2M1 (nearest, ties to even, saturating at 6). An all-zero block takes the smallest
   scale, 2^-127 (byte 0), and zero codes carrying the input signs.
+* quantize_nvfp4_weights -- BF16 -> NVFP4 weight requantization (the load path's other
+  target format; the pages do not spell its rule out): the two-level NVFP4 recipe, one
+  FP32 scale per tensor g = amax / 2688 and, per 16-block, the Four-Over-Six arithmetic
+  above with the target 6 only (no 4 candidate).
 
 The pages fix neither the floating-point operation order nor the zero and saturation
 cases. The quantizer is defined as exact IEEE FP32 operations in the order written
@@ -165,6 +169,30 @@ def quantize_mxfp4(x: np.ndarray):
     y = np.ldexp(xb.astype(np.float64), -shared[:, :, None]).astype(np.float32)   # exact scaling
     codes = e2m1_encode(y).reshape(rows, cols)
     return pack_fp4(codes), (shared + 127).astype(np.uint8)
+
+
+def quantize_nvfp4_weights(x: np.ndarray):
+    """NVFP4 of tensors x [n, rows, cols] (FP32 values, cols % 16 == 0), one global scale
+    per tensor: returns (packed codes [n, rows, cols/2], scale bytes [n, rows, cols/16],
+    g [n] FP32). Per tensor, in FP32: a = max |x|; a == 0 gives g = 0, scale bytes 0 and
+    sign-only codes; else g = a / 2688 and every 16-block takes the c = 6 candidate."""
+    x = np.asarray(x, dtype=F32)
+    n, rows, cols = x.shape
+    if cols % NVFP4_BLOCK:
+        raise ValueError("cols must be a multiple of 16")
+    if not np.all(np.isfinite(x)):
+        raise ValueError("quantize_nvfp4_weights: non-finite input")
+    xb = x.reshape(n, rows * cols // NVFP4_BLOCK, NVFP4_BLOCK)
+    a = np.abs(x).reshape(n, -1).max(axis=1).astype(F32)
+    live = a > 0
+    g = np.where(live, a / NVFP4_GLOBAL_DIV, F32(0.0)).astype(F32)
+    g_safe = np.where(live, g, F32(1.0))[:, None]
+    m = np.max(np.abs(xb), axis=2).astype(F32)
+    sbytes, q, _ = _candidate(xb, m, g_safe, F32(6.0))
+    sbytes = np.where(live[:, None], sbytes, 0).astype(np.uint8)
+    q = np.where(live[:, None, None], q, (np.signbit(xb).astype(np.uint8) << 3)).astype(np.uint8)
+    return (pack_fp4(q.reshape(n * rows, cols)).reshape(n, rows, cols // 2),
+            sbytes.reshape(n, rows, cols // NVFP4_BLOCK), g)
 
 
 def dequant_weights(fmt: str, codes: np.ndarray, scales, gscale) -> np.ndarray:

@@ -1,5 +1,6 @@
-"""GPU parity of moe_requant_mxfp4 (load-time BF16 -> MXFP4 requantization): codes and
-E8M0 scales bit-exact against the oracle's quantize_mxfp4 on the same BF16 rows."""
+"""GPU parity of the load-time requantizers: moe_requant_mxfp4 (codes and E8M0 scales)
+and moe_requant_nvfp4 (codes, E4M3 scales and tensor scales) bit-exact against the
+oracle on the same BF16 inputs, and layers built from their output against the oracle."""
 import numpy as np
 import pytest
 import torch
@@ -76,6 +77,73 @@ def test_requantized_layer_runs_end_to_end(lib):
         torch.cuda.synchronize()
         Lq[name] = {"codes": codes.cpu().numpy().reshape(c.shape[0], c.shape[1], -1),
                     "scales": scales.cpu().numpy().reshape(c.shape[0], c.shape[1], -1), "gscale": None}
+    dl = lib.DeviceLayer.from_host(Lq)
+    for T in (1, 8):
+        x_np = synth.make_x(base, T)
+        ref = OL.moe_layer(Lq, x_np)
+        ws = lib.Workspace(dl, T)
+        y, ids, w, _ = lib.forward(dl, torch.from_numpy(x_np.view(np.int16)).cuda(), ws)
+        torch.cuda.synchronize()
+        ids_g = ids.cpu().numpy()
+        assert not check_ids(ids_g, ref, cfg.k)
+        if np.array_equal(ids_g, ref["ids"]):
+            ok, max_abs, rel = y_close(bf16_bits_to_f64(y), ref["y"])
+            say(f"[requant]   T={T} y max_abs/r={max_abs:.3g} rel_l2={rel:.3g}")
+            assert ok, (max_abs, rel)
+
+
+def _check_nv(lib, x32):
+    """x32 [n, rows, cols] FP32 values that are exact BF16."""
+    n, rows, cols = x32.shape
+    say(f"[requant] nvfp4 tensors={n} rows={rows} cols={cols}")
+    xb = synth.to_bf16_bits(x32)
+    codes, scales, g = lib.requant_nvfp4(torch.from_numpy(xb.view(np.int16)).cuda())
+    torch.cuda.synchronize()
+    rc, rs, rg = OQ.quantize_nvfp4_weights(bf16_bits_to_f64(torch.from_numpy(xb.view(np.int16))).astype(np.float32))
+    assert np.array_equal(g.cpu().numpy().view(np.uint32), rg.view(np.uint32))
+    assert np.array_equal(scales.cpu().numpy(), rs)
+    assert np.array_equal(codes.cpu().numpy(), rc)
+
+
+def test_requant_nvfp4_tensors(lib):
+    """Tensors of very different ranges, one of them all zero (with a -0), one with an
+    outlier that pushes small blocks' scales into E4M3 subnormals and to zero."""
+    rng = np.random.default_rng(61)
+    x = rng.normal(size=(5, 40, 256)) * np.array([0.02, 1.0, 300.0, 0.0, 1e-3])[:, None, None]
+    x[3] = 0.0
+    x[4, 0, 0] = 1e4
+    _check_nv(lib, x)
+
+
+def test_requant_nvfp4_all_bf16_values(lib):
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    v = (bits.astype(np.uint32) << 16).view(np.float32)
+    v = v[np.isfinite(v)]
+    n = len(v) // 4096 * 4096
+    _check_nv(lib, v[:n].reshape(-1, 1, 4096).copy().astype(np.float64))
+
+
+def test_nvfp4_requantized_layer_runs_end_to_end(lib):
+    """A Flint-shaped BF16 layer (16 experts, top-4, BF16 shared expert) with its routed
+    experts requantized to NVFP4 on the GPU (gate, up and down as separate tensors) runs
+    through moe_forward; ids and y match the oracle on the same codes and scales."""
+    import dataclasses
+    from oracle import layer as OL
+    from parity_util import check_ids, y_close
+    base = dataclasses.replace(synth.CONFIGS["flint_bf16"], name="flint_bf16_e16", E=16, k=4,
+                               router_bias=False)
+    L = synth.make_layer(base)
+    cfg = dataclasses.replace(base, name="flint_nvfp4_requant", wfmt=synth.W_NVFP4)
+    Lq = dict(L, cfg=cfg)
+    for name, parts in (("w13", 2), ("w2", 1)):
+        c = L[name]["codes"]                                      # BF16 bits [E][rows][K]
+        E, R, K = c.shape
+        say(f"[requant] layer {name} {c.shape}")
+        codes, scales, g = lib.requant_nvfp4(torch.from_numpy(c.reshape(E * parts, R // parts, K).view(np.int16)).cuda())
+        torch.cuda.synchronize()
+        Lq[name] = {"codes": codes.cpu().numpy().reshape(E, R, K // 2),
+                    "scales": scales.cpu().numpy().reshape(E, R, K // 16),
+                    "gscale": g.cpu().numpy().reshape(E, parts)}
     dl = lib.DeviceLayer.from_host(Lq)
     for T in (1, 8):
         x_np = synth.make_x(base, T)

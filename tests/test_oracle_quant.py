@@ -322,3 +322,49 @@ def test_mxfp4_zero_and_extreme_blocks():
     assert c[5] == 8 and c[0] == 0                  # signed zero kept
     assert c[32] == 0                               # 2^-133 / 2^-127 = 2^-6 rounds to 0
     assert c[64] == 7                               # 3e38 / 2^125 = 7.05 saturates to 6 (code 7)
+
+
+# ------------------------------------------------------------- NVFP4 weight requant
+def test_nvfp4_weights_match_the_activation_quantizer_where_it_picks_6():
+    """One tensor of one row is one activation row: the global scale is the same, and on
+    every block where Four-Over-Six keeps the 6 candidate the codes and scales agree."""
+    rng = np.random.default_rng(51)
+    for trial in range(4):
+        row = (rng.normal(size=(1, 2048)) * 10.0 ** rng.uniform(-3, 3)).astype(np.float32)
+        c4, s4, g4, ch = Q.quantize_nvfp4_4o6(row)
+        cw, sw, gw = Q.quantize_nvfp4_weights(row[None])
+        assert gw[0] == g4[0]
+        six = ch[0] == 6
+        assert six.sum() > 0
+        assert np.array_equal(sw[0, 0][six], s4[0][six])
+        cu_w, cu_a = Q.unpack_fp4(cw[0]).reshape(-1, 16), Q.unpack_fp4(c4).reshape(-1, 16)
+        assert np.array_equal(cu_w[six], cu_a[six])
+
+
+def test_nvfp4_weights_worked_tensor():
+    """amax 2688 -> g = 1; a block with max 6 takes S = 1 (byte 0x38), exact E2M1 values
+    stay exact; a block with max 12 takes S = 2 (byte 0x40)."""
+    x = np.zeros((1, 2, 32), np.float32)
+    x[0, 0, :4] = [6.0, -3.0, 0.5, 1.5]
+    x[0, 0, 16:18] = [12.0, 3.0]
+    x[0, 1, 0] = 2688.0
+    codes, s, g = Q.quantize_nvfp4_weights(x)
+    assert g.tolist() == [1.0]
+    assert s[0, 0].tolist() == [0x38, 0x40]
+    c = Q.unpack_fp4(codes[0, 0])
+    assert c[:4].tolist() == [7, 8 | 5, 1, 3] and c[16:18].tolist() == [7, 3]
+
+
+def test_nvfp4_weights_zero_tensor_and_error_bound():
+    rng = np.random.default_rng(52)
+    x = rng.normal(size=(3, 8, 64)).astype(np.float32) * np.array([0.02, 1.0, 5.0], np.float32)[:, None, None]
+    x[1] = 0.0
+    x[1, 2, 3] = -0.0
+    codes, s, g = Q.quantize_nvfp4_weights(x)
+    assert g[1] == 0 and np.all(s[1] == 0)
+    cz = Q.unpack_fp4(codes[1].reshape(8, 32))
+    assert cz[2, 3] == 8 and np.all(np.delete(cz.ravel(), 2 * 64 + 3) == 0)
+    for t in (0, 2):
+        back = Q.dequant_nvfp4_rows(codes[t], s[t], np.full(8, g[t], np.float32))
+        rel = np.linalg.norm(back - x[t]) / np.linalg.norm(x[t])
+        assert rel < 0.12, rel
