@@ -67,6 +67,47 @@ def read_traffic(kernel: str, workload: str, sha: str):
         return None
 
 
+def requant_bench(args, dev) -> int:
+    """Load-time requantization of the Flint-shaped routed gate/up stack (256 experts x
+    [2I = 1536][H = 2048] BF16, 805 MB, seeded N(0, 0.02) drawn on the device) to MXFP4
+    and to NVFP4 (512 tensors: gate and up of each expert). Algorithmic bytes: the BF16
+    input read once plus the codes and scales (and tensor scales) written."""
+    import torch
+
+    import block_scaled_bit_fp32_amd as moe
+    import synth
+
+    cfg = synth.CONFIGS["flint_bf16"]
+    E, I, H = cfg.E, cfg.I, cfg.H
+    gen = torch.Generator(device=dev).manual_seed(0x4F36)
+    w = (torch.randn(E * 2 * I, H, device=dev, generator=gen) * 0.02).to(torch.bfloat16).view(torch.int16)
+    n = w.numel()
+    runs = {
+        "mxfp4": (lambda: moe.requant_mxfp4(w), n * 2 + n // 2 + n // 32),
+        "nvfp4": (lambda: moe.requant_nvfp4(w.view(E * 2, I, H)), n * 2 + n // 2 + n // 16 + 4 * E * 2),
+    }
+    res = {}
+    for name, (fn, nbytes) in runs.items():
+        for _ in range(max(1, args.warmup)):
+            fn()
+        torch.cuda.synchronize()
+        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s0.record()
+        for _ in range(args.steps):
+            fn()
+        s1.record()
+        torch.cuda.synchronize()
+        us = s0.elapsed_time(s1) * 1e3 / args.steps
+        res[name] = {"us": round(us, 2), "bytes": nbytes, "GBps": round(nbytes / us / 1e3, 1),
+                     "frac": round(nbytes / us / 1e3 / HBM_PEAK_GBPS, 4)}
+        log(f"[bench] requant {name}: {us:.1f} us for {nbytes / 1e6:.1f} MB, {nbytes / us / 1e3:.0f} GB/s")
+    print(json.dumps({"metric": "load-time requantization, achieved HBM GB/s", "unit": "GB/s",
+                      "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "data": "synthetic",
+                      "config": {"workload": f"BF16 routed gate/up stack E={E} x [{2 * I}][{H}]"},
+                      "dtype": "bf16->fp4", "peak": HBM_PEAK_GBPS, "results": res}))
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -78,6 +119,8 @@ def main() -> int:
     ap.add_argument("--replicas", type=int, default=0, help="0: enough to touch >= 1 GiB per step")
     ap.add_argument("--cpu-sample-s", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--requant", action="store_true",
+                    help="time the load-time requantizers instead (BF16 -> MXFP4 / NVFP4)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -94,6 +137,8 @@ def main() -> int:
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.requant:
+        return requant_bench(args, dev)
     cfg = synth.CONFIGS[args.config]
     sweep = sorted(set([int(t) for t in args.sweep.split(",") if t] + [args.batch]))
     log(f"[bench] drawing layer {cfg.name}")
