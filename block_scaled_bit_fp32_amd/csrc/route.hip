@@ -1,4 +1,4 @@
-// Router GEMV and sigmoid top-k (two launches: the top-k needs every logit of a token),
+// Router GEMV and top-k (two launches: the top-k needs every logit of a token),
 // token quantization, the standalone Four-Over-Six quantizer and the workspace fill
 // kernel.
 #include <algorithm>

@@ -7,7 +7,8 @@
  *     Day-0 Support", accuracy evaluation: FP32 router; "Day 0 support for Mistral
  *     Large 4 on vLLM", breakable CUDA graphs and fusions: FP32 router GEMM;
  *     "vLLM Day-0 support for Recursive's Flint", architecture: sigmoid top-6 of 256
- *     experts plus one shared expert);
+ *     experts plus one shared expert), or softmax top-k (Mistral Large 4 page, ROCm
+ *     implementation details: the fused decode's softmax top-4 router);
  *   - gate/up and down projections that read only the selected experts' weights
  *     (Flint page, optimization strategy: small-batch MoE kernels), with SwiGLU;
  *   - block-scaled weights: NVFP4 (Inkling page, mixed-precision MoE), OCP MXFP4 and
@@ -16,7 +17,9 @@
  *     Four-Over-Six NVFP4; MoE with fused activation quantization) or FP8-E4M3 with
  *     one scale per token (Mistral Large 4 page, MXFP4 experts, a8w4);
  *   - a weighted combine of the routed outputs plus the shared expert (Flint page,
- *     low-latency decode path: routing and expert combine fused into the GEMVs).
+ *     low-latency decode path: routing and expert combine fused into the GEMVs);
+ *   - at load time, BF16 weights requantized to MXFP4 (Mistral Large 4 page, ROCm
+ *     implementation details: experts requantized to MXFP4 one layer at a time) or NVFP4.
  *
  * Conventions for every entry point:
  *   - Tensor pointers are DEVICE pointers owned by the caller (e.g. a torch tensor's
