@@ -125,8 +125,9 @@ def main() -> int:
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py runs on one GPU only: this build measures the single-GPU decode MoE "
-              "layer (see DESIGN.md for how it would shard); pass --gpus 1.", file=sys.stderr)
+        print("bench.py runs on one GPU only: it measures the decode MoE layer on a single "
+              "MI355X (across GPUs the layer would be split over the expert intermediate "
+              "dimension with one all-reduce of y); pass --gpus 1.", file=sys.stderr)
         return 2
 
     import numpy as np
