@@ -105,6 +105,16 @@ CONFIGS: Dict[str, LayerConfig] = {
                                       has_shared=True, wfmt=W_BF16, shared_wfmt=W_BF16,
                                       afmt=A_BF16, router_bias=True, bias_select_only=True,
                                       batches=(1, 8, 64)),
+    # Edge shapes: k = 1 over 5 experts (not a multiple of 64) at the smallest sizes; k = E
+    # = 16 (the largest k, every expert selected); the largest E, 1024 (unfused top-k, 16
+    # slots per lane).
+    "edge_k1_e5": LayerConfig("edge_k1_e5", 8, H=256, I=128, E=5, k=1, has_shared=True,
+                              wfmt=W_BF16, shared_wfmt=W_BF16, afmt=A_BF16, I_shared=256,
+                              batches=(1, 7)),
+    "edge_k16_e16": LayerConfig("edge_k16_e16", 9, H=512, I=256, E=16, k=16, has_shared=False,
+                                wfmt=W_NVFP4, shared_wfmt=W_NVFP4, afmt=A_BF16, batches=(1, 3)),
+    "edge_e1024": LayerConfig("edge_e1024", 10, H=512, I=256, E=1024, k=8, has_shared=False,
+                              wfmt=W_MXFP4, shared_wfmt=W_MXFP4, afmt=A_BF16, batches=(1, 5)),
     # Tiny layer with a router bias, softmax weights and selection-only bias.
     "tiny_softmax_selbias": LayerConfig("tiny_softmax_selbias", 7, H=256, I=128, E=8, k=2,
                                         has_shared=True, wfmt=W_BF16, shared_wfmt=W_BF16,

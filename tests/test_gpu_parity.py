@@ -88,6 +88,9 @@ LAYER_CASES = [
     ("tiny_softmax_selbias", [1, 3]),
     ("mistral_mxfp4_softmax", [1, 8]),
     ("flint_bf16_selbias", [1, 8]),
+    ("edge_k1_e5", [1, 7]),
+    ("edge_k16_e16", [1, 3]),
+    ("edge_e1024", [1, 5]),
 ]
 
 
@@ -104,7 +107,8 @@ def _run_layer(lib, name, T, debug=True, path=0):
 
 # the grouped (MFMA) kernels forced at small, ragged batches, every weight format
 GROUPED_SMALL = [("tiny_bf16", 3), ("flint_w4a16", 8), ("flint_bf16", 5), ("inkling_w4a4", 5),
-                 ("inkling_mxfp8", 8), ("mistral_mxfp4", 3), ("mistral_mxfp4_a8", 8)]
+                 ("inkling_mxfp8", 8), ("mistral_mxfp4", 3), ("mistral_mxfp4_a8", 8), ("edge_k16_e16", 3),
+                 ("edge_e1024", 5)]
 
 
 @pytest.mark.parametrize("name,T,path", [(n, t, 0) for n, ts in LAYER_CASES for t in ts] +
@@ -167,7 +171,7 @@ FORWARD_CASES = [("tiny_bf16", 1), ("tiny_bf16", 8), ("flint_w4a16", 1), ("flint
                  ("flint_w4a16", 16), ("flint_bf16", 8), ("inkling_w4a4", 8),
                  ("inkling_mxfp8", 5), ("mistral_mxfp4", 16), ("mistral_mxfp4_a8", 8),
                  ("tiny_softmax_selbias", 8), ("mistral_mxfp4_softmax", 8), ("flint_bf16_selbias", 8),
-                 ("flint_bf16_selbias", 16)]
+                 ("flint_bf16_selbias", 16), ("edge_k1_e5", 7), ("edge_k16_e16", 3), ("edge_e1024", 5)]
 
 
 @pytest.mark.parametrize("name,T", FORWARD_CASES)
