@@ -69,8 +69,8 @@ def read_traffic(kernel: str, workload: str, sha: str):
 
 def requant_bench(args, dev) -> int:
     """Load-time requantization of the Flint-shaped routed gate/up stack (256 experts x
-    [2I = 1536][H = 2048] BF16, 805 MB, seeded N(0, 0.02) drawn on the device) to MXFP4
-    and to NVFP4 (512 tensors: gate and up of each expert). Algorithmic bytes: the BF16
+    [2I = 1536][H = 2048] BF16, 805 MB, seeded N(0, 0.02) drawn on the device) to MXFP4,
+    MXFP8 and NVFP4 (512 tensors: gate and up of each expert). Algorithmic bytes: the BF16
     input read once plus the codes and scales (and tensor scales) written."""
     import torch
 
@@ -84,6 +84,7 @@ def requant_bench(args, dev) -> int:
     n = w.numel()
     runs = {
         "mxfp4": (lambda: moe.requant_mxfp4(w), n * 2 + n // 2 + n // 32),
+        "mxfp8": (lambda: moe.requant_mxfp8(w), n * 2 + n + n // 32),
         "nvfp4": (lambda: moe.requant_nvfp4(w.view(E * 2, I, H)), n * 2 + n // 2 + n // 16 + 4 * E * 2),
     }
     res = {}
@@ -104,7 +105,7 @@ def requant_bench(args, dev) -> int:
     print(json.dumps({"metric": "load-time requantization, achieved HBM GB/s", "unit": "GB/s",
                       "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "data": "synthetic",
                       "config": {"workload": f"BF16 routed gate/up stack E={E} x [{2 * I}][{H}]"},
-                      "dtype": "bf16->fp4", "peak": HBM_PEAK_GBPS, "results": res}))
+                      "dtype": "bf16->fp4/fp8", "peak": HBM_PEAK_GBPS, "results": res}))
     return 0
 
 
@@ -120,7 +121,7 @@ def main() -> int:
     ap.add_argument("--cpu-sample-s", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--requant", action="store_true",
-                    help="time the load-time requantizers instead (BF16 -> MXFP4 / NVFP4)")
+                    help="time the load-time requantizers instead (BF16 -> MXFP4 / MXFP8 / NVFP4)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))

@@ -75,6 +75,7 @@ _SIGNATURES = {
     "quantize_nvfp4_4o6": (_I32, [_P, _I32, _I32, _P, _P, _P, _P, _P]),
     "moe_requant_mxfp4": (_I32, [_P, ctypes.c_int64, _I32, _P, _P, _P]),
     "moe_requant_nvfp4": (_I32, [_P, _I32, ctypes.c_int64, _I32, _P, _P, _P, _P]),
+    "moe_requant_mxfp8": (_I32, [_P, ctypes.c_int64, _I32, _P, _P, _P]),
     "moe_profile_begin": (_I32, []),
     "moe_profile_end": (_I32, [ctypes.POINTER(KernelTimeT), _I32]),
     "moe_last_error": (ctypes.c_char_p, []),
@@ -342,6 +343,17 @@ def requant_mxfp4(w: torch.Tensor):
     codes = _aligned_empty(rows * cols // 2, w.device).view(rows, cols // 2)
     scales = torch.empty((rows, cols // 32), dtype=torch.uint8, device=w.device)
     _check(_lib.moe_requant_mxfp4(w.data_ptr(), rows, cols, codes.data_ptr(), scales.data_ptr(), _stream()))
+    return codes, scales
+
+
+def requant_mxfp8(w: torch.Tensor):
+    """moe_requant_mxfp8 of BF16 rows w [rows, cols]: returns (E4M3 codes [rows, cols],
+    E8M0 scales [rows, cols/32]), the MOE_W_MXFP8 layout."""
+    w = _bits16(w)
+    rows, cols = w.shape
+    codes = _aligned_empty(rows * cols, w.device).view(rows, cols)
+    scales = torch.empty((rows, cols // 32), dtype=torch.uint8, device=w.device)
+    _check(_lib.moe_requant_mxfp8(w.data_ptr(), rows, cols, codes.data_ptr(), scales.data_ptr(), _stream()))
     return codes, scales
 
 

@@ -15,6 +15,8 @@ hipError_t launch_requant_mxfp4(const uint16_t* x, int64_t nblocks, uint8_t* cod
                                 hipStream_t s);
 hipError_t launch_requant_nvfp4(const uint16_t* x, int ntensors, int64_t n, uint8_t* codes, uint8_t* scales,
                                 float* gscale, hipStream_t s);
+hipError_t launch_requant_mxfp8(const uint16_t* x, int64_t nblocks, uint8_t* codes, uint8_t* scales,
+                                hipStream_t s);
 hipError_t launch_quantize_nvfp4(const uint16_t* x, int rows, int cols, uint8_t* codes,
                                  uint8_t* scales, float* g, uint8_t* choice, hipStream_t s);
 hipError_t launch_route(const RouteArgs& a, int n_quant, bool topk, hipStream_t s);
@@ -720,6 +722,23 @@ moe_status_t moe_requant_mxfp4(const uint16_t* w_bf16, int64_t rows, int32_t col
   if (!bad.empty()) return set_err(MOE_EINVAL, bad);
   if (rows == 0) return MOE_OK;
   if (launch_requant_mxfp4(w_bf16, rows * (cols / 32), codes, scales, stream) != hipSuccess)
+    return set_err(MOE_ELAUNCH, "requant kernel launch failed");
+  return MOE_OK;
+}
+
+moe_status_t moe_requant_mxfp8(const uint16_t* w_bf16, int64_t rows, int32_t cols, uint8_t* codes, uint8_t* scales,
+                               hipStream_t stream) {
+  std::string bad;
+  if (rows < 0) bad += "rows must be >= 0; ";
+  if (cols <= 0 || cols % 32) bad += "cols must be a positive multiple of 32; ";
+  if (rows > 0) {
+    if (!w_bf16 || !aligned(w_bf16, 16)) bad += "w_bf16 must be non-NULL and 16-byte aligned; ";
+    if (!codes || !aligned(codes, 16)) bad += "codes must be non-NULL and 16-byte aligned; ";
+    if (!scales) bad += "scales is NULL; ";
+  }
+  if (!bad.empty()) return set_err(MOE_EINVAL, bad);
+  if (rows == 0) return MOE_OK;
+  if (launch_requant_mxfp8(w_bf16, rows * (cols / 32), codes, scales, stream) != hipSuccess)
     return set_err(MOE_ELAUNCH, "requant kernel launch failed");
   return MOE_OK;
 }

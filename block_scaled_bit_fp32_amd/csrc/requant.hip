@@ -1,4 +1,5 @@
-// Load-time weight requantization (off the decode path). MXFP4: BF16 rows to E2M1
+// Load-time weight requantization (off the decode path). MXFP4 (and MXFP8 with E4M3
+// elements, exponent offset 8 and saturation at 448): BF16 rows to E2M1
 // values with one E8M0 scale per 32 (the Mistral Large 4 page's ROCm load path requantizes
 // each expert this way, one layer at a time). The scale follows the OCP MX v1.0 rule:
 // shared exponent floor(log2(block amax)) - 2, clamped to [-127, 127]; elements are the
@@ -84,6 +85,48 @@ hipError_t launch_requant_nvfp4(const uint16_t* x, int ntensors, int64_t n, uint
                                 float* gscale, hipStream_t s) {
   return launch_kernel(K_QUANT, requant_nvfp4_kernel, dim3(ntensors), dim3(kBlock), 0, s, x, n, codes, scales,
                        gscale);
+}
+
+// MXFP8: the same rule with the E4M3 element (largest exponent 8), one thread per
+// 32-element block: 32 code bytes at 32 b, scale byte b.
+__global__ void __launch_bounds__(kBlock) requant_mxfp8_kernel(const uint16_t* x, int64_t nblocks, uint8_t* codes,
+                                                               uint8_t* scales) {
+  const int64_t b = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+  if (b >= nblocks) return;
+  const uint4* src = reinterpret_cast<const uint4*>(x + b * 32);
+  float v[32];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint4 r = src[q];
+    const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[8 * q + 2 * i] = bf16_to_f32(w[i] & 0xFFFFu);
+      v[8 * q + 2 * i + 1] = bf16_to_f32(w[i] >> 16);
+    }
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  int e = amax > 0.0f ? __builtin_amdgcn_frexp_expf(amax) - 9 : -127;
+  e = min(max(e, -127), 127);
+  uint32_t w[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const float y = ldexpf(v[i], -e);
+    w[i >> 2] |= (e4m3_encode_pos(fabsf(y)) | ((__float_as_uint(y) >> 24) & 0x80u)) << (8 * (i & 3));
+  }
+  uint4* dst = reinterpret_cast<uint4*>(codes + 32 * b);
+  dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
+  dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
+  scales[b] = (uint8_t)(e + 127);
+}
+
+hipError_t launch_requant_mxfp8(const uint16_t* x, int64_t nblocks, uint8_t* codes, uint8_t* scales,
+                                hipStream_t s) {
+  const int64_t grid = (nblocks + kBlock - 1) / kBlock;
+  return launch_kernel(K_QUANT, requant_mxfp8_kernel, dim3((unsigned)grid), dim3(kBlock), 0, s, x, nblocks, codes,
+                       scales);
 }
 
 hipError_t launch_requant_mxfp4(const uint16_t* x, int64_t nblocks, uint8_t* codes, uint8_t* scales,

@@ -25,7 +25,7 @@
  *   - Tensor pointers are DEVICE pointers owned by the caller (e.g. a torch tensor's
  *     data_ptr()). The library never allocates, frees or synchronizes inside
  *     moe_route, moe_expert_forward, moe_forward, quantize_nvfp4_4o6,
- *     moe_requant_mxfp4 or moe_requant_nvfp4; they enqueue
+ *     moe_requant_mxfp4, moe_requant_mxfp8 or moe_requant_nvfp4; they enqueue
  *     kernels on `stream` and return.
  *   - Every entry returns a moe_status_t and never throws. Arguments are validated
  *     before anything is launched; on error nothing is enqueued and moe_last_error()
@@ -218,6 +218,16 @@ moe_status_t quantize_nvfp4_4o6(const uint16_t *x_bf16, int32_t rows, int32_t co
  *   rows = 0 enqueues nothing. Asynchronous on stream; caller-owned buffers. A stack
  *   of experts is one call with rows = experts * rows per expert. */
 moe_status_t moe_requant_mxfp4(const uint16_t *w_bf16, int64_t rows, int32_t cols,
+                               uint8_t *codes, uint8_t *scales, hipStream_t stream);
+
+/* Load-time weight requantization to MXFP8 (MOE_W_MXFP8 layout), for MXFP8 expert layers
+ * (Inkling page, mixed-precision MoE: MXFP8 expert layers): the same OCP MX v1.0 rule as
+ * moe_requant_mxfp4 with E4M3 elements, i.e. shared exponent floor(log2(block amax)) - 8,
+ * clamped to [-127, 127], elements E4M3 (nearest-even, saturating at 448, sign kept).
+ *   w_bf16 [rows][cols] BF16, device, 16-byte aligned; cols a positive multiple of 32.
+ *   codes  [rows][cols] E4M3 bytes, 16-byte aligned; scales [rows][cols/32] E8M0 bytes.
+ *   rows = 0 enqueues nothing. */
+moe_status_t moe_requant_mxfp8(const uint16_t *w_bf16, int64_t rows, int32_t cols,
                                uint8_t *codes, uint8_t *scales, hipStream_t stream);
 
 /* Load-time weight requantization to NVFP4 (MOE_W_NVFP4 layout), the load path's other

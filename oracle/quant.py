@@ -17,6 +17,9 @@ Test infrastructure (see oracle/__init__.py).
   E8M0 range [-127, 127]; elements are the block values times 2^-exponent, rounded to
   E2M1 (nearest, ties to even, saturating at 6). An all-zero block takes the smallest
   scale, 2^-127 (byte 0), and zero codes carrying the input signs.
+* quantize_mxfp8 -- the same OCP rule for MXFP8 (the Inkling page's MXFP8 expert layers):
+  shared exponent floor(log2(block amax)) minus 8 (the largest E4M3 exponent), clamped to
+  [-127, 127]; elements rounded to E4M3 (nearest, ties to even, saturating at 448).
 * quantize_nvfp4_weights -- BF16 -> NVFP4 weight requantization (the load path's other
   target format; the pages do not spell its rule out): the two-level NVFP4 recipe, one
   FP32 scale per tensor g = amax / 2688 and, per 16-block, the Four-Over-Six arithmetic
@@ -169,6 +172,22 @@ def quantize_mxfp4(x: np.ndarray):
     y = np.ldexp(xb.astype(np.float64), -shared[:, :, None]).astype(np.float32)   # exact scaling
     codes = e2m1_encode(y).reshape(rows, cols)
     return pack_fp4(codes), (shared + 127).astype(np.uint8)
+
+
+def quantize_mxfp8(x: np.ndarray):
+    """MXFP8 (E4M3) of rows x [rows, cols] (FP32 values, cols % 32 == 0): returns (codes
+    [rows, cols] uint8, E8M0 scale bytes [rows, cols/32])."""
+    x = np.asarray(x, dtype=np.float32)
+    rows, cols = x.shape
+    if cols % MX_BLOCK:
+        raise ValueError("cols must be a multiple of 32")
+    xb = x.reshape(rows, cols // MX_BLOCK, MX_BLOCK)
+    amax = np.abs(xb).max(axis=2).astype(np.float64)
+    _, e = np.frexp(amax)                          # floor(log2(amax)) = e - 1
+    shared = np.where(amax > 0, e - 1 - 8, -127)
+    shared = np.clip(shared, -127, 127).astype(np.int64)
+    y = np.ldexp(xb.astype(np.float64), -shared[:, :, None]).astype(np.float32)   # exact scaling
+    return e4m3_encode_satfinite(y).reshape(rows, cols), (shared + 127).astype(np.uint8)
 
 
 def quantize_nvfp4_weights(x: np.ndarray):

@@ -20,7 +20,7 @@ def _declared_functions():
 def test_header_declares_the_boundary():
     names = _declared_functions()
     for n in ("moe_route", "moe_expert_forward", "moe_forward", "quantize_nvfp4_4o6", "moe_requant_mxfp4",
-              "moe_requant_nvfp4",
+              "moe_requant_nvfp4", "moe_requant_mxfp8",
               "moe_layer_check",
               "moe_workspace_bytes", "moe_workspace_init", "moe_xq_bytes", "moe_last_error",
               "moe_abi_version"):
@@ -123,6 +123,8 @@ def test_calls_validate_before_launching(lib):
     msg = so.moe_last_error().decode()
     assert "w_bf16" in msg and "gscale" in msg
     assert so.moe_requant_nvfp4(None, 0, i64(4), 32, None, None, None, None) == 0
+    assert so.moe_requant_mxfp8(1 << 20, i64(4), 48, 1 << 20, 1 << 20, None) == lib.MOE_EINVAL
+    assert so.moe_requant_mxfp8(None, i64(0), 64, None, None, None) == 0
     # moe_forward: every check of both halves before the first launch
     st = so.moe_forward(ctypes.byref(s), 1 << 20, 1, 1 << 20, 1 << 20, None, None, 1 << 20, 1 << 24, None, None)
     assert st == lib.MOE_EINVAL and "y_bf16" in so.moe_last_error().decode()

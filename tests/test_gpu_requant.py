@@ -157,3 +157,67 @@ def test_nvfp4_requantized_layer_runs_end_to_end(lib):
             ok, max_abs, rel = y_close(bf16_bits_to_f64(y), ref["y"])
             say(f"[requant]   T={T} y max_abs/r={max_abs:.3g} rel_l2={rel:.3g}")
             assert ok, (max_abs, rel)
+
+
+def _check_mx8(lib, xb):
+    say(f"[requant] mxfp8 rows={xb.shape[0]} cols={xb.shape[1]}")
+    codes, scales = lib.requant_mxfp8(torch.from_numpy(xb.view(np.int16)).cuda())
+    torch.cuda.synchronize()
+    x32 = bf16_bits_to_f64(torch.from_numpy(xb.view(np.int16))).astype(np.float32)
+    rc, rs = OQ.quantize_mxfp8(x32)
+    assert np.array_equal(scales.cpu().numpy(), rs)
+    assert np.array_equal(codes.cpu().numpy(), rc)
+
+
+def test_requant_mxfp8_rows(lib):
+    rng = np.random.default_rng(71)
+    _check_mx8(lib, synth.to_bf16_bits(rng.normal(size=(64, 2048)) * np.exp(rng.normal(size=(64, 1)) * 6)))
+    _check_mx8(lib, synth.to_bf16_bits(rng.normal(size=(300, 96)) * 0.02))
+    rows = np.zeros((3, 64))
+    rows[0, :4] = [448.0, 500.0, 0.3, -2.0]
+    rows[1, :32] = 2.0 ** -133
+    rows[2, :32] = 3.0e38
+    xb = synth.to_bf16_bits(rows)
+    xb[0, 10] = 0x8000
+    _check_mx8(lib, xb)
+
+
+def test_requant_mxfp8_all_bf16_values(lib):
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    v = (bits.astype(np.uint32) << 16).view(np.float32)
+    bits = bits[np.isfinite(v)]
+    n = len(bits) // 2048 * 2048
+    _check_mx8(lib, bits[:n].reshape(-1, 2048).copy())
+
+
+def test_mxfp8_requantized_layer_runs_end_to_end(lib):
+    """A Flint-shaped BF16 layer (16 experts, top-4, BF16 shared expert) requantized to
+    MXFP8 on the GPU runs through moe_forward against the oracle on the same codes."""
+    import dataclasses
+    from oracle import layer as OL
+    from parity_util import check_ids, y_close
+    base = dataclasses.replace(synth.CONFIGS["flint_bf16"], name="flint_bf16_e16", E=16, k=4,
+                               router_bias=False)
+    L = synth.make_layer(base)
+    cfg = dataclasses.replace(base, name="flint_mxfp8_requant", wfmt=synth.W_MXFP8)
+    Lq = dict(L, cfg=cfg)
+    for name in ("w13", "w2"):
+        c = L[name]["codes"]
+        say(f"[requant] layer {name} {c.shape} -> mxfp8")
+        codes, scales = lib.requant_mxfp8(torch.from_numpy(c.reshape(-1, c.shape[2]).view(np.int16)).cuda())
+        torch.cuda.synchronize()
+        Lq[name] = {"codes": codes.cpu().numpy().reshape(c.shape),
+                    "scales": scales.cpu().numpy().reshape(c.shape[0], c.shape[1], -1), "gscale": None}
+    dl = lib.DeviceLayer.from_host(Lq)
+    for T in (1, 8):
+        x_np = synth.make_x(base, T)
+        ref = OL.moe_layer(Lq, x_np)
+        ws = lib.Workspace(dl, T)
+        y, ids, w, _ = lib.forward(dl, torch.from_numpy(x_np.view(np.int16)).cuda(), ws)
+        torch.cuda.synchronize()
+        ids_g = ids.cpu().numpy()
+        assert not check_ids(ids_g, ref, cfg.k)
+        if np.array_equal(ids_g, ref["ids"]):
+            ok, max_abs, rel = y_close(bf16_bits_to_f64(y), ref["y"])
+            say(f"[requant]   T={T} y max_abs/r={max_abs:.3g} rel_l2={rel:.3g}")
+            assert ok, (max_abs, rel)

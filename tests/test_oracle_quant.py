@@ -368,3 +368,55 @@ def test_nvfp4_weights_zero_tensor_and_error_bound():
         back = Q.dequant_nvfp4_rows(codes[t], s[t], np.full(8, g[t], np.float32))
         rel = np.linalg.norm(back - x[t]) / np.linalg.norm(x[t])
         assert rel < 0.12, rel
+
+
+# ------------------------------------------------------------------ MXFP8 requant
+def test_mxfp8_worked_block():
+    """amax 500 -> floor(log2 500) = 8 -> exponent 0 (byte 127); 448 stays, 500 saturates
+    to 448, 0.3 rounds to the nearest E4M3 value 0.3125 (0x2A), -2.0 is 0xC0."""
+    x = np.zeros((1, 32), np.float32)
+    x[0, :4] = [448.0, 500.0, 0.3, -2.0]
+    codes, s = Q.quantize_mxfp8(x)
+    assert s.tolist() == [[127]]
+    assert codes[0, :4].tolist() == [0x7E, 0x7E, 0x2A, 0xC0]
+    assert F.e4m3_value(0x2A) == 0.3125
+
+
+def test_mxfp8_round_trip_of_representable_blocks():
+    """Blocks of finite E4M3 values times 2^X whose largest magnitude is 448 * 2^X (so the
+    shared exponent is X) come back bit for bit. A block topped by 240 * 2^X instead takes
+    exponent X - 1, and 240 * 2 saturates to 448: E4M3 has no 1.875 * 2^8."""
+    rng = np.random.default_rng(33)
+    b = rng.integers(0, 254, size=(12, 256))
+    b = b + (b >= 0x7F)                           # skip the NaN bytes 0x7F, 0xFF
+    b[:, ::32] = 0x7E                             # 448 in every block
+    X = rng.integers(-30, 30, size=(12, 8))
+    v = np.ldexp(np.vectorize(F.e4m3_value)(b), np.repeat(X, 32, axis=1)).astype(np.float32)
+    codes, s = Q.quantize_mxfp8(v)
+    back = np.ldexp(np.vectorize(F.e4m3_value)(codes.astype(np.int64)), np.repeat(s.astype(np.int64) - 127, 32, axis=1))
+    assert np.array_equal(back, v.astype(np.float64))
+
+
+def test_mxfp8_scale_and_error_bound():
+    import math
+    rng = np.random.default_rng(34)
+    x = (rng.normal(size=(8, 512)) * np.exp(rng.normal(size=(8, 1)) * 4)).astype(np.float32)
+    codes, s = Q.quantize_mxfp8(x)
+    amax = np.abs(x.reshape(8, -1, 32)).max(axis=2).astype(np.float64)
+    want = np.vectorize(lambda a: min(127, max(-127, math.floor(math.log2(a)) - 8)) + 127)(amax)
+    assert np.array_equal(s, want)
+    X = np.ldexp(1.0, np.repeat(s.astype(np.int64) - 127, 32, axis=1))
+    back = np.vectorize(F.e4m3_value)(codes.astype(np.int64)) * X
+    y = np.abs(x.astype(np.float64)) / X
+    ulp = np.where(y < 2.0 ** -6, 2.0 ** -9, np.exp2(np.floor(np.log2(np.maximum(y, 2.0 ** -6))) - 3))
+    bound = np.maximum(ulp / 2, y - 448.0) * X
+    assert np.all(np.abs(back - x) <= bound * (1 + 1e-12))
+
+
+def test_mxfp8_block_topped_below_256_saturates_its_top():
+    x = np.zeros((1, 32), np.float32)
+    x[0, 0] = 240.0                                # E4M3 0x77, exponent 7
+    x[0, 1] = 1.0
+    codes, s = Q.quantize_mxfp8(x)
+    assert s.tolist() == [[126]]                   # floor(log2 240) - 8 = -1
+    assert codes[0, :2].tolist() == [0x7E, 0x40]   # 480 saturates to 448; 2.0 exact
