@@ -37,9 +37,18 @@ __global__ void __launch_bounds__(kBlock) requant_mxfp4_kernel(const uint16_t* x
   // floor(log2(amax)) = frexp exponent - 1 (amax = m * 2^e, m in [0.5, 1)), then - 2
   int e = amax > 0.0f ? __builtin_amdgcn_frexp_expf(amax) - 3 : -127;
   e = min(max(e, -127), 127);
+  // the hardware convert: two elements over the scale 2^e per instruction
+  const float sc = __builtin_bit_cast(float, (uint32_t)(e + 127) << 23 | (e == -127 ? 0x00400000u : 0u));
   uint32_t w[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-  for (int i = 0; i < 32; ++i) w[i >> 3] |= e2m1_encode(ldexpf(v[i], -e)) << (4 * (i & 7));
+  for (int q = 0; q < 4; ++q) {
+    uint32_t r = 0u;
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[8 * q + 0], v[8 * q + 1], sc, 0);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[8 * q + 2], v[8 * q + 3], sc, 1);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[8 * q + 4], v[8 * q + 5], sc, 2);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[8 * q + 6], v[8 * q + 7], sc, 3);
+    w[q] = r;
+  }
   *reinterpret_cast<uint4*>(codes + 16 * b) = make_uint4(w[0], w[1], w[2], w[3]);
   scales[b] = (uint8_t)(e + 127);
 }
