@@ -746,7 +746,7 @@ moe_status_t moe_requant_mxfp8(const uint16_t* w_bf16, int64_t rows, int32_t col
 moe_status_t moe_requant_nvfp4(const uint16_t* w_bf16, int32_t ntensors, int64_t rows, int32_t cols,
                                uint8_t* codes, uint8_t* scales, float* gscale, hipStream_t stream) {
   std::string bad;
-  if (ntensors < 0) bad += "ntensors must be >= 0; ";
+  if (ntensors < 0 || ntensors > 65535) bad += "ntensors must be in [0, 65535]; ";
   if (rows < 0) bad += "rows must be >= 0; ";
   if (cols <= 0 || cols % 16) bad += "cols must be a positive multiple of 16; ";
   if (rows > 0 && (int64_t)cols * rows / 16 > (int64_t)0x7FFFFFFF) bad += "a tensor may hold at most 2^31 blocks; ";

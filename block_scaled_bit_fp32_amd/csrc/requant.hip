@@ -53,47 +53,96 @@ __global__ void __launch_bounds__(kBlock) requant_mxfp4_kernel(const uint16_t* x
   scales[b] = (uint8_t)(e + 127);
 }
 
-// One workgroup per tensor of n elements (n % 16 == 0): the tensor's amax, then every
-// 16-block with the c = 6 candidate.
-__global__ void __launch_bounds__(kBlock) requant_nvfp4_kernel(const uint16_t* x, int64_t n, uint8_t* codes,
-                                                               uint8_t* scales, float* gscale) {
+// NVFP4 in three launches over tensors of n elements (n % 16 == 0), in stream order, so
+// no launch waits on another inside it:
+//   1. grid (chunks, tensors): each workgroup's maximum |x| over kNvChunk elements, kept
+//      as an FP32 in the tensor's code bytes (which launch 3 overwrites);
+//   2. one workgroup per tensor: amax over those maxima (exact), g = amax / 2688;
+//   3. grid (chunks, tensors): every 16-block of the chunk with the c = 6 candidate.
+constexpr int kNvChunk = 16 * kBlock * 8;   // elements per workgroup (8 blocks of 16 per thread)
+
+__global__ void __launch_bounds__(kBlock) nvfp4_chunk_max_kernel(const uint16_t* x, int64_t n, uint8_t* codes) {
   __shared__ float red[kBlock / kWave];
-  const int64_t t = blockIdx.x, nb = n / 16;
+  const int64_t t = blockIdx.y, c = blockIdx.x;
+  const int64_t b0 = c * (kNvChunk / 16), b1 = min(b0 + kNvChunk / 16, n / 16);
   const Bf16Row row{x + t * n};
   float amax = 0.0f;
-  for (int64_t b = threadIdx.x; b < nb; b += kBlock) {
+  for (int64_t b = b0 + threadIdx.x; b < b1; b += kBlock) {
     float v[16];
     row.load((int)b, v);
 #pragma unroll
     for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(v[i]));
   }
   amax = block_max(amax, red);
-  const float g = amax / 2688.0f;
+  if (threadIdx.x == 0) reinterpret_cast<float*>(codes + t * (n / 2))[c] = amax;
+}
+
+__global__ void __launch_bounds__(kBlock) nvfp4_tensor_scale_kernel(const uint8_t* codes, int64_t n, int nchunks,
+                                                                    float* gscale) {
+  __shared__ float red[kBlock / kWave];
+  const int64_t t = blockIdx.x;
+  const float* part = reinterpret_cast<const float*>(codes + t * (n / 2));
+  float amax = 0.0f;
+  for (int c = threadIdx.x; c < nchunks; c += kBlock) amax = fmaxf(amax, part[c]);
+  amax = block_max(amax, red);
+  if (threadIdx.x == 0) gscale[t] = amax / 2688.0f;
+}
+
+// The c = 6 candidate of one 16-block (the scale and codes of nvfp4_candidate, in the same
+// FP32 operation order, without its error sum).
+__device__ __forceinline__ void nvfp4_block6(const float (&x)[16], float m, float g, uint32_t& sbyte,
+                                             uint32_t (&codes)[2]) {
+#pragma clang fp contract(off)
+  const float u = (m / g) / 6.0f;
+  sbyte = e4m3_encode_pos(u);
+  const float d = e4m3_to_f32(sbyte) * g;
+  codes[0] = codes[1] = 0u;
+  if (d == 0.0f) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) codes[i >> 3] |= ((__float_as_uint(x[i]) >> 28) & 8u) << (4 * (i & 7));
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) codes[i >> 3] |= e2m1_encode(x[i] / d) << (4 * (i & 7));
+  }
+}
+
+__global__ void __launch_bounds__(kBlock) nvfp4_quant_kernel(const uint16_t* x, int64_t n, uint8_t* codes,
+                                                             uint8_t* scales, const float* gscale) {
+  const int64_t t = blockIdx.y, c = blockIdx.x;
+  const int64_t b0 = c * (kNvChunk / 16), b1 = min(b0 + kNvChunk / 16, n / 16);
+  const Bf16Row row{x + t * n};
+  const float g = gscale[t];
   uint8_t* ct = codes + t * (n / 2);
-  uint8_t* st = scales + t * nb;
-  for (int64_t b = threadIdx.x; b < nb; b += kBlock) {
+  uint8_t* st = scales + t * (n / 16);
+  for (int64_t b = b0 + threadIdx.x; b < b1; b += kBlock) {
     float v[16];
     row.load((int)b, v);
-    uint32_t sb = 0, c[2] = {0u, 0u};
-    if (amax == 0.0f) {
+    uint32_t sb = 0, cw[2] = {0u, 0u};
+    if (g == 0.0f) {   // all-zero tensor (amax / 2688 is zero only for amax = 0)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) c[i >> 3] |= ((__float_as_uint(v[i]) >> 28) & 8u) << (4 * (i & 7));
+      for (int i = 0; i < 16; ++i) cw[i >> 3] |= ((__float_as_uint(v[i]) >> 28) & 8u) << (4 * (i & 7));
     } else {
       float m = 0.0f;
 #pragma unroll
       for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(v[i]));
-      nvfp4_candidate(v, m, g, 6.0f, sb, c);
+      nvfp4_block6(v, m, g, sb, cw);
     }
-    *reinterpret_cast<uint2*>(ct + 8 * b) = make_uint2(c[0], c[1]);
+    *reinterpret_cast<uint2*>(ct + 8 * b) = make_uint2(cw[0], cw[1]);
     st[b] = (uint8_t)sb;
   }
-  if (threadIdx.x == 0) gscale[t] = g;
 }
 
 hipError_t launch_requant_nvfp4(const uint16_t* x, int ntensors, int64_t n, uint8_t* codes, uint8_t* scales,
                                 float* gscale, hipStream_t s) {
-  return launch_kernel(K_QUANT, requant_nvfp4_kernel, dim3(ntensors), dim3(kBlock), 0, s, x, n, codes, scales,
-                       gscale);
+  const int64_t nchunks = (n + kNvChunk - 1) / kNvChunk;
+  const dim3 grid((unsigned)nchunks, (unsigned)ntensors);
+  hipError_t err = launch_kernel(K_QUANT, nvfp4_chunk_max_kernel, grid, dim3(kBlock), 0, s, x, n, codes);
+  if (err != hipSuccess) return err;
+  err = launch_kernel(K_QUANT, nvfp4_tensor_scale_kernel, dim3(ntensors), dim3(kBlock), 0, s,
+                      (const uint8_t*)codes, n, (int)nchunks, gscale);
+  if (err != hipSuccess) return err;
+  return launch_kernel(K_QUANT, nvfp4_quant_kernel, grid, dim3(kBlock), 0, s, x, n, codes, scales,
+                       (const float*)gscale);
 }
 
 // MXFP8: the same rule with the E4M3 element (largest exponent 8), one thread per

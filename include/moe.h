@@ -240,7 +240,9 @@ moe_status_t moe_requant_mxfp8(const uint16_t *w_bf16, int64_t rows, int32_t col
  *   w_bf16 [ntensors][rows][cols] BF16, device, 16-byte aligned; cols a positive
  *   multiple of 16. codes [ntensors][rows][cols/2] (element 2i in the low nibble),
  *   8-byte aligned; scales [ntensors][rows][cols/16] E4M3 bytes; gscale [ntensors]
- *   FP32 (outputs). ntensors = 0 or rows = 0 enqueues nothing. One workgroup per tensor. */
+ *   FP32 (outputs). 0 <= ntensors <= 65535; ntensors = 0 or rows = 0 enqueues nothing.
+ *   Three launches in stream order (chunk maxima, kept in the code bytes until the last
+ *   launch overwrites them; tensor scales; quantization). */
 moe_status_t moe_requant_nvfp4(const uint16_t *w_bf16, int32_t ntensors, int64_t rows,
                                int32_t cols, uint8_t *codes, uint8_t *scales,
                                float *gscale, hipStream_t stream);

@@ -123,6 +123,7 @@ def test_calls_validate_before_launching(lib):
     msg = so.moe_last_error().decode()
     assert "w_bf16" in msg and "gscale" in msg
     assert so.moe_requant_nvfp4(None, 0, i64(4), 32, None, None, None, None) == 0
+    assert so.moe_requant_nvfp4(1 << 20, 70000, i64(4), 32, 1 << 20, 1 << 20, 1 << 20, None) == lib.MOE_EINVAL
     assert so.moe_requant_mxfp8(1 << 20, i64(4), 48, 1 << 20, 1 << 20, None) == lib.MOE_EINVAL
     assert so.moe_requant_mxfp8(None, i64(0), 64, None, None, None) == 0
     # moe_forward: every check of both halves before the first launch
