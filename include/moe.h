@@ -155,7 +155,12 @@ size_t moe_xq_bytes(const moe_layer_t *L, int32_t T);
  * that may overlap (different streams). */
 moe_status_t moe_workspace_init(void *ws, size_t ws_bytes, hipStream_t stream);
 
-/* Router: logits = x * router_w^T in FP32, keys = logits + bias; per token the k
+/* Router ("Inkling 2 Small on vLLM: Day-0 Support", accuracy evaluation: the router
+ * runs in FP32; "vLLM Day-0 support for Recursive's Flint", architecture: sigmoid top-6
+ * routing over 256 experts; "Day 0 support for Mistral Large 4 on vLLM", ROCm
+ * implementation details: softmax top-4 router; Inkling page, MoE with fused activation
+ * quantization: tokens quantized to the expert layer's format in the producing kernel).
+ * logits = x * router_w^T in FP32, keys = logits + bias; per token the k
  * largest keys, largest first, ties to the lower expert index; topk_w = the
  * router_score of the selected keys (or bare logits with bias_select_only),
  * renormalized to sum to 1 (FP32). With afmt != MOE_A_BF16 also quantizes every token
@@ -167,13 +172,21 @@ moe_status_t moe_route(const moe_layer_t *L, const uint16_t *x_bf16, int32_t T,
                        int32_t *topk_ids, float *topk_w, void *xq, void *ws,
                        size_t ws_bytes, hipStream_t stream);
 
-/* Experts and combine: for every selected (token, expert) pair, and for the shared
+/* Experts and combine ("vLLM Day-0 support for Recursive's Flint", optimization
+ * strategy: small-batch MoE kernels that read only the selected experts' weights, with
+ * routing and the expert combine fused into the neighbouring GEMVs; Inkling page, MoE
+ * with fused activation quantization: the SwiGLU output is quantized before the down
+ * projection; Flint and Mistral Large 4 architecture sections: one shared expert added
+ * with weight 1). For every selected (token, expert) pair, and for the shared
  * expert, h = silu(Wg x) * (Wu x) (x quantized per afmt for routed experts; the
  * shared expert takes x_bf16), h re-quantized per afmt for routed experts, o = Wd h;
  * y[t] = sum_j topk_w[t][j] * o[t, j] + o_shared[t], FP32 accumulation, BF16 output
  * (round to nearest even). Reads only the experts named in topk_ids.
  *   x_bf16 [T][H]; xq as written by moe_route (ignored for MOE_A_BF16);
- *   topk_ids [T][k] with entries in [0, E); topk_w [T][k]; y_bf16 [T][H] (output).
+ *   topk_ids [T][k]: the k entries of a row must be distinct and in [0, E) (as
+ *   moe_route writes them); for a row that breaks this, that token's y is unspecified
+ *   (every access stays in bounds and the other tokens are unaffected).
+ *   topk_w [T][k]; y_bf16 [T][H] (output).
  *   dbg: NULL or debug outputs. */
 moe_status_t moe_expert_forward(const moe_layer_t *L, const uint16_t *x_bf16,
                                 const void *xq, int32_t T, const int32_t *topk_ids,

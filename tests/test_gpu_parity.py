@@ -2,8 +2,10 @@
 
 Bars: top-k ids, quantized token codes/scales and quantized h codes bit-exact (h codes
 are compared with the oracle's quantizer applied to the GPU's own FP32 h, since FP32 and
-FP64 h legitimately differ in the last bits); combine weights within 2e-6 absolute; the
-layer output within the bar stated in parity_util.
+FP64 h legitimately differ in the last bits); combine weights within 1e-6 relative; the
+layer output within the bar stated in parity_util, against the oracle's own output (for
+layers that re-quantize h, a miss must be explained by the few h codes that FP32 and
+FP64 h round differently, and the output is also checked with the GPU's codes).
 """
 import numpy as np
 import pytest
@@ -16,7 +18,15 @@ from parity_util import (bf16_bits_to_f64, check_ids, device_layer, gpu_hq_rows,
 
 pytestmark = pytest.mark.gpu
 
-W_ATOL = 2e-6
+W_RTOL = 1e-6
+
+
+def check_w(w_gpu: np.ndarray, w_ref: np.ndarray, same: np.ndarray):
+    """Combine weights of the tokens routed like the oracle: within W_RTOL relative."""
+    if not same.any():
+        return
+    d = np.abs(w_gpu[same] - w_ref[same]) / np.abs(w_ref[same])
+    assert d.max() <= W_RTOL, d.max()
 
 
 def _x_dev(x_np):
@@ -35,6 +45,13 @@ def _quant_rows_case():
     z[2, :16] = 1e-30          # tiny blocks: scale underflow paths
     z[2, 100] = 3.0
     rows.append(z)
+    # a block whose 4-vs-6 choice is decided by the summation order of the errors (the
+    # worked case of the oracle's pins: 24, 3, 4 and 2^-24 at 6, 9, 10, with g = 1)
+    f = np.zeros((1, 4096))
+    f[0, 0], f[0, 1], f[0, 2] = 24.0, 3.0, 4.0
+    f[0, [6, 9, 10]] = 2.0 ** -24
+    f[0, 16] = 2688.0
+    rows.append(f)
     return synth.to_bf16_bits(np.concatenate(rows))
 
 
@@ -81,7 +98,7 @@ LAYER_CASES = [
     ("tiny_bf16", [1, 3]),
     ("flint_w4a16", [1, 2, 4, 8]),
     ("flint_bf16", [1, 8]),
-    ("inkling_w4a4", [1, 5, 8]),
+    ("inkling_w4a4", [1, 4, 5, 8]),
     ("inkling_mxfp8", [1, 8]),
     ("mistral_mxfp4", [1, 8]),
     ("mistral_mxfp4_a8", [1, 8]),
@@ -121,7 +138,7 @@ def test_layer_parity(lib, name, T, path):
     bad = check_ids(ids_g, ref, cfg.k)
     assert not bad, f"top-k mismatch on tokens {bad}"
     same = np.all(ids_g == ref["ids"], axis=1)
-    assert np.max(np.abs(w.cpu().numpy()[same] - ref["w"][same]), initial=0) <= W_ATOL
+    check_w(w.cpu().numpy(), ref["w"], same)
     # quantized tokens: bit-exact
     if cfg.afmt != "bf16":
         parts = lib.split_xq(dl, xq, T)
@@ -150,17 +167,43 @@ def test_layer_parity(lib, name, T, path):
             rc, rs = OQ.quantize_fp8_token(h32)
             assert np.array_equal(dbg["hq_codes"].cpu().numpy(), rc)
             assert np.array_equal(dbg["hq_scale"].cpu().numpy().view(np.uint32), rs.view(np.uint32))
-    # layer output (with re-quantized h: the oracle's down path takes the GPU's h codes,
-    # which are checked above)
+    # layer output against the oracle's own y
     if np.array_equal(ids_g, ref["ids"]):
-        if cfg.afmt == "bf16":
-            y_ref = ref["y"]
-        else:
-            hq = gpu_hq_rows(dbg, cfg.afmt, np.arange(T * cfg.k)).reshape(T, cfg.k, cfg.I)
-            y_ref = oracle_y_given_hq(name, x_np, ref["ids"], ref["w"], hq)
-        ok, max_abs, rel = y_close(bf16_bits_to_f64(y), y_ref)
-        say(f"[parity]   y max_abs/r={max_abs:.3g} rel_l2={rel:.3g}")
-        assert ok, (max_abs, rel)
+        check_y_own(name, cfg, T, x_np, ref, bf16_bits_to_f64(y), dbg)
+
+
+def check_y_own(name, cfg, T, x_np, ref, y_gpu, dbg):
+    """y against the oracle's own output. Layers that re-quantize h: the GPU's FP32 h and
+    the oracle's FP64 h can land on opposite sides of a rounding boundary of the h
+    quantizer; such a code moves y by up to one quantization step. A miss of the bar is
+    accepted only if (a) under 0.1 % of the h codes differ between the oracle's quantizer
+    applied to the GPU's h and to its own h, and (b) the output evaluated with the GPU's
+    codes (oracle down projections) meets the bar: the differing codes account for the
+    whole gap."""
+    ok, max_abs, rel = y_close(y_gpu, ref["y"])
+    say(f"[parity]   y vs oracle: max_abs/r={max_abs:.3g} rel_l2={rel:.3g}")
+    if ok:
+        return
+    assert cfg.afmt != "bf16", (max_abs, rel)
+    P = T * cfg.k
+    h_gpu = dbg["h"].cpu().numpy()[:P, :cfg.I]
+    h_own = ref["h"].reshape(P, cfg.I).astype(np.float32)
+    if cfg.afmt == "nvfp4_4o6":
+        c_gpu = OQ.quantize_nvfp4_4o6(h_gpu)[0]
+        c_own = OQ.quantize_nvfp4_4o6(h_own)[0]
+        diff = int(np.sum((c_gpu & 0x0F) != (c_own & 0x0F)) + np.sum((c_gpu >> 4) != (c_own >> 4)))
+    else:
+        c_gpu = OQ.quantize_fp8_token(h_gpu)[0]
+        c_own = OQ.quantize_fp8_token(h_own)[0]
+        diff = int(np.sum(c_gpu != c_own))
+    total = P * cfg.I
+    hq = gpu_hq_rows(dbg, cfg.afmt, np.arange(P)).reshape(T, cfg.k, cfg.I)
+    y_codes = oracle_y_given_hq(name, x_np, ref["ids"], ref["w"], hq)
+    ok2, ma2, rel2 = y_close(y_gpu, y_codes)
+    say(f"[parity]   {diff} of {total} h codes differ (FP32 vs FP64 h); y vs oracle on the GPU's codes: "
+        f"max_abs/r={ma2:.3g} rel_l2={rel2:.3g}")
+    assert diff <= total // 1000, (diff, total)
+    assert ok2, (ma2, rel2)
 
 
 # moe_forward: routing fused into the gate/up kernel (pair mode) or the two launches
@@ -196,10 +239,16 @@ def test_forward_matches_route_and_experts(lib, name, T):
     ids_g = ids2.cpu().numpy()
     bad = check_ids(ids_g, ref, cfg.k)
     assert not bad, f"top-k mismatch on tokens {bad}"
-    if cfg.afmt == "bf16" and np.array_equal(ids_g, ref["ids"]):
-        ok, max_abs, rel = y_close(bf16_bits_to_f64(y2), ref["y"])
-        say(f"[parity]   y max_abs/r={max_abs:.3g} rel_l2={rel:.3g}")
-        assert ok, (max_abs, rel)
+    if np.array_equal(ids_g, ref["ids"]):
+        if cfg.afmt == "bf16":
+            ok, max_abs, rel = y_close(bf16_bits_to_f64(y2), ref["y"])
+            say(f"[parity]   y max_abs/r={max_abs:.3g} rel_l2={rel:.3g}")
+            assert ok, (max_abs, rel)
+        else:   # the same y as expert_forward, which test_layer_parity holds to the oracle
+            y3, dbg = lib.expert_forward(dl, x, xq, ids, w, ws, debug=True)
+            torch.cuda.synchronize()
+            assert np.array_equal(y3.view(torch.int16).cpu().numpy(), y2.view(torch.int16).cpu().numpy())
+            check_y_own(name, cfg, T, x_np, ref, bf16_bits_to_f64(y2), dbg)
 
 
 # Batches past the GEMV sizes (the grouped points of the configurations): routing and the
@@ -226,45 +275,66 @@ def test_layer_parity_large_batch(lib, name, T, path):
     x_np = synth.make_x(name, T)
     x = _x_dev(x_np)
     ids, w, xq = lib.route(dl, x, ws)
-    quant_h = cfg.afmt != "bf16"
-    if quant_h:
-        y, dbg = lib.expert_forward(dl, x, xq, ids, w, ws, debug=True, path=path)
-    else:
-        y = lib.expert_forward(dl, x, xq, ids, w, ws, path=path)
+    y, dbg = lib.expert_forward(dl, x, xq, ids, w, ws, debug=True, path=path)
     torch.cuda.synchronize()
     ref = oracle_route_only(name, x_np)
     ids_g = ids.cpu().numpy()
     bad = check_ids(ids_g, ref, cfg.k)
     assert not bad, f"top-k mismatch on tokens {bad}"
+    check_w(w.cpu().numpy(), ref["w"], np.all(ids_g == ref["ids"], axis=1))
     if cfg.afmt == "nvfp4_4o6":
         rc, rs, rg, _ = OQ.quantize_nvfp4_4o6(synth_bf16_to_f32(x_np))
         parts = lib.split_xq(dl, xq, T)
         assert np.array_equal(parts["codes"].cpu().numpy(), rc)
         assert np.array_equal(parts["scales"].cpu().numpy(), rs)
+        assert np.array_equal(parts["g"].cpu().numpy().view(np.uint32), rg.view(np.uint32))
     elif cfg.afmt == "fp8_token":
         rc, rs = OQ.quantize_fp8_token(synth_bf16_to_f32(x_np))
         parts = lib.split_xq(dl, xq, T)
         assert np.array_equal(parts["codes"].cpu().numpy(), rc)
+        assert np.array_equal(parts["s"].cpu().numpy().view(np.uint32), rs.view(np.uint32))
     sample = sorted({0, T // 3, (2 * T) // 3, T - 1})
     sample = [t for t in sample if np.array_equal(ids_g[t], ref["ids"][t])]
     assert sample, "no sampled token routed like the oracle"
-    if quant_h:
+    own = OL.moe_layer(host_layer(name), x_np[sample])
+    assert np.array_equal(own["ids"], ids_g[sample])
+    pairs = np.array([t * cfg.k + j for t in sample for j in range(cfg.k)])
+    # SwiGLU outputs of the sampled tokens: FP32 vs FP64 (the bar of the small batches)
+    h_g = dbg["h"].cpu().numpy()[pairs, :cfg.I].astype(np.float64)
+    h_r = own["h"].reshape(len(sample) * cfg.k, cfg.I)
+    scale = max(1.0, float(np.sqrt(np.mean(h_r ** 2))))
+    dh = np.max(np.abs(h_g - h_r)) / scale
+    say(f"[parity]   sampled tokens {sample}: h max_abs/r={dh:.3g}")
+    assert dh < 5e-3
+    yg = bf16_bits_to_f64(y)[sample]
+    ok, max_abs, rel = y_close(yg, own["y"])
+    say(f"[parity]   y vs oracle: max_abs/r={max_abs:.3g} rel_l2={rel:.3g}")
+    if cfg.afmt != "bf16":
         # the GPU's h codes of the sampled tokens: bit-exact against the oracle's quantizer
-        # fed the GPU's h; then the rest of the layer against the oracle given those codes
-        pairs = np.array([t * cfg.k + j for t in sample for j in range(cfg.k)])
+        # fed the GPU's h
         h32 = dbg["h"].cpu().numpy()[pairs, :cfg.I]
         if cfg.afmt == "nvfp4_4o6":
             rc, rs, rg, _ = OQ.quantize_nvfp4_4o6(h32)
+            assert np.array_equal(dbg["hq_scales"].cpu().numpy()[pairs], rs)
         else:
             rc, rg = OQ.quantize_fp8_token(h32)
         assert np.array_equal(dbg["hq_codes"].cpu().numpy()[pairs], rc)
-        hq = gpu_hq_rows(dbg, cfg.afmt, pairs).reshape(len(sample), cfg.k, cfg.I)
-        y_ref = oracle_y_given_hq(name, x_np[sample], ref["ids"][sample], ref["w"][sample], hq)
-    else:
-        y_ref = OL.moe_layer(host_layer(name), x_np[sample])["y"]
-    yg = bf16_bits_to_f64(y)[sample]
-    ok, max_abs, rel = y_close(yg, y_ref)
-    say(f"[parity]   sampled tokens {sample}: y max_abs/r={max_abs:.3g} rel_l2={rel:.3g}")
+        assert np.array_equal(dbg["hq_scale"].cpu().numpy()[pairs].view(np.uint32), rg.view(np.uint32))
+        if not ok:   # a miss must be the few codes FP32 and FP64 h round differently
+            h_own = h_r.astype(np.float32)
+            if cfg.afmt == "nvfp4_4o6":
+                c_own = OQ.quantize_nvfp4_4o6(h_own)[0]
+                diff = int(np.sum((rc & 0x0F) != (c_own & 0x0F)) + np.sum((rc >> 4) != (c_own >> 4)))
+            else:
+                diff = int(np.sum(rc != OQ.quantize_fp8_token(h_own)[0]))
+            hq = gpu_hq_rows(dbg, cfg.afmt, pairs).reshape(len(sample), cfg.k, cfg.I)
+            y_codes = oracle_y_given_hq(name, x_np[sample], own["ids"], own["w"], hq)
+            ok2, ma2, rel2 = y_close(yg, y_codes)
+            say(f"[parity]   {diff} of {h32.size} h codes differ; y vs oracle on the GPU's codes: "
+                f"max_abs/r={ma2:.3g} rel_l2={rel2:.3g}")
+            assert diff <= h32.size // 1000, diff
+            assert ok2, (ma2, rel2)
+            return
     assert ok, (max_abs, rel)
 
 

@@ -115,6 +115,19 @@ def test_requant_nvfp4_tensors(lib):
     _check_nv(lib, x)
 
 
+def test_requant_nvfp4_multi_chunk_tensors(lib):
+    """Tensors of 300 x 256 = 76800 elements span three reduction chunks of 32768 (the last
+    one ragged, 11264 elements). Each tensor's maximum sits in a different chunk (the last,
+    the middle, the first), so a tensor scale taken from one chunk only, or one that drops
+    the ragged chunk, changes g and every code."""
+    rng = np.random.default_rng(62)
+    x = rng.normal(size=(3, 300, 256)) * 0.02
+    x[0, 297, 5] = -7.5          # element 76037: chunk 2 (the ragged one)
+    x[1, 150, 200] = 3.25        # element 38600: chunk 1
+    x[2, 3, 9] = 11.0            # element 777: chunk 0
+    _check_nv(lib, x)
+
+
 def test_requant_nvfp4_all_bf16_values(lib):
     bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
     v = (bits.astype(np.uint32) << 16).view(np.float32)
@@ -141,6 +154,12 @@ def test_nvfp4_requantized_layer_runs_end_to_end(lib):
         say(f"[requant] layer {name} {c.shape}")
         codes, scales, g = lib.requant_nvfp4(torch.from_numpy(c.reshape(E * parts, R // parts, K).view(np.int16)).cuda())
         torch.cuda.synchronize()
+        # the whole stack (tensors of 768 x 2048 = 48 chunks each) bit-exact against the oracle
+        rc, rs, rg = OQ.quantize_nvfp4_weights(
+            bf16_bits_to_f64(torch.from_numpy(c.reshape(E * parts, R // parts, K).view(np.int16))).astype(np.float32))
+        assert np.array_equal(g.cpu().numpy().view(np.uint32), rg.view(np.uint32))
+        assert np.array_equal(scales.cpu().numpy(), rs)
+        assert np.array_equal(codes.cpu().numpy(), rc)
         Lq[name] = {"codes": codes.cpu().numpy().reshape(E, R, K // 2),
                     "scales": scales.cpu().numpy().reshape(E, R, K // 16),
                     "gscale": g.cpu().numpy().reshape(E, parts)}

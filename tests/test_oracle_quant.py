@@ -100,6 +100,60 @@ def test_scale_underflow_one_candidate_picks_four():
     assert _decode(codes, sb, g)[0, 0] == 2.0 ** -8
 
 
+# ---------------------------------------------------------------- summation order
+# Four-Over-Six compares two FP32 error sums, so the order of the additions is part of
+# the quantizer (the pairwise tree (i, i+8), then +4, +2, +1). These pins are worked by
+# hand; any other order (sequential, adjacent pairs, reversed) gives different bits.
+T24 = 2.0 ** -24          # half an ulp of 1.0: 1 + T24 rounds to 1.0 (tie, even mantissa)
+
+
+def test_tree_sum16_order_worked_values():
+    # [1, T24 x 15]: level 1 gives 1 + T24 -> 1.0 and seven pairs 2*T24; level 2 gives
+    # 1 + 2*T24 (exact) and 4*T24 x 3; level 3: 1 + 6*T24 and 8*T24; total 1 + 14*T24.
+    # A sequential sum absorbs every T24 into 1.0.
+    e = np.full(16, T24, F32)
+    e[0] = 1.0
+    assert Q.tree_sum16(e) == F32(1.0 + 14 * T24)
+    seq = F32(0.0)
+    for v in e:
+        seq = F32(seq + v)
+    assert seq == F32(1.0) and Q.tree_sum16(e) != seq
+    # the error vectors of the flip block below: 1 at index 1 (target 6) or index 2
+    # (target 4), T24 at indices 6, 9, 10
+    e6 = np.zeros(16, F32); e6[1] = 1.0
+    e4 = np.zeros(16, F32); e4[2] = 1.0
+    for ev in (e6, e4):
+        ev[[6, 9, 10]] = T24
+    # target 6: (1,9) 1+T24 -> 1; (2,10) T24; (6,14) T24 | +4: s[1] = 1, s[2] = 2*T24 |
+    #   +2: s[0] = 2*T24, s[1] = 1 | total 1 + 2*T24 (exact)
+    assert Q.tree_sum16(e6) == F32(1.0 + 2 * T24)
+    # target 4: (1,9) T24; (2,10) 1+T24 -> 1; (6,14) T24 | +4: s[1] = T24, s[2] = 1+T24 -> 1 |
+    #   +2: s[0] = 1, s[1] = T24 | total 1 + T24 -> 1.0
+    assert Q.tree_sum16(e4) == F32(1.0)
+
+
+def test_summation_order_decides_four_over_six():
+    """A block whose exact errors tie (6 would win) but whose tree-ordered FP32 errors pick 4.
+
+    g = 1 (anchor 2688), block max 24: S6 = 4 (d6 = 4), S4 = 6 (d4 = 6), both exact.
+      24: 24/4 = 6 and 24/6 = 4, exact at both targets.
+       3: 3/4 = 0.75 ties 0.5 / 1.0 -> even code (1.0) -> 4, error 1;  3/6 = 0.5 exact.
+       4: 4/4 = 1 exact;  4/6 = 0.667 -> 0.5 -> 3, error 1.
+     T24 at indices 6, 9, 10: zero codes at both targets, error T24 each.
+    Exact sums: both 1 + 3*T24 (a tie, so 6). FP32 sequential: both 1.0 (6). FP32 tree
+    (worked above): err6 = 1 + 2*T24 > err4 = 1.0, so the quantizer keeps 4, with scale
+    byte E4M3(6) = 0x4C and codes 24 -> 4 (code 6), 3 -> 0.5 (code 1), 4 -> 0.5 (code 1).
+    """
+    blk = np.zeros(16, F32)
+    blk[0], blk[1], blk[2] = 24.0, 3.0, 4.0
+    blk[[6, 9, 10]] = T24
+    codes, sb, g, ch = Q.quantize_nvfp4_4o6(_row([blk]))
+    assert g[0] == 1.0
+    assert ch[0, 0] == 4 and sb[0, 0] == 0x4C
+    q = F.unpack_fp4(codes)[0, :16]
+    assert q[0] == 6 and q[1] == 1 and q[2] == 1 and np.all(q[3:] == 0)
+
+
 def _nearest_e4m3(u):
     """Brute-force nearest finite E4M3 (non-negative u), ties to the even byte."""
     grid = F.E4M3_TABLE[:0x7F]
@@ -223,6 +277,15 @@ def test_fp8_token_scale_and_max_code():
     z[0, 2] = -0.0
     codes, s = Q.quantize_fp8_token(z)
     assert s[0] == 0 and codes[0, 2] == 0x80 and codes.sum() == 0x80
+
+
+def test_fp8_token_dequant_worked_values():
+    # 0x38 = 0|0111|000 = 1.0 and 0xC0 = 1|1000|000 = -2.0, times s = 2.5
+    v = Q.dequant_fp8_token(np.array([[0x38, 0xC0]], np.uint8), np.array([2.5], F32))
+    assert np.array_equal(v, [[2.5, -5.0]])
+    # 0x7E = 448 and the smallest subnormal 0x01 = 2^-9, per-row scales 0.125 and 4
+    v = Q.dequant_fp8_token(np.array([[0x7E, 0x81], [0x01, 0x00]], np.uint8), np.array([0.125, 4.0], F32))
+    assert np.array_equal(v, [[56.0, -(2.0 ** -12)], [2.0 ** -7, 0.0]])
 
 
 def test_fp8_token_exhaustive_bf16_sweep():
