@@ -8,6 +8,8 @@ no CPU fallback.
 Names follow include/moe.h:
     route(layer, x, ws)                  -> topk_ids, topk_w, xq
     expert_forward(layer, x, xq, ids, w, ws, debug=False) -> y (BF16) [, debug dict]
+    forward(layer, x, ws)                -> y, topk_ids, topk_w, xq
+    forward_noalloc(layer, x)            -> y, topk_ids, topk_w, xq (library scratch)
     quantize_nvfp4_4o6(x)                -> codes, scales, gscale, choice
 """
 from __future__ import annotations
@@ -72,6 +74,9 @@ _SIGNATURES = {
                                   ctypes.POINTER(DebugT), _P]),
     "moe_forward": (_I32, [ctypes.POINTER(LayerT), _P, _I32, _P, _P, _P, _P, _P, _SZ,
                            ctypes.POINTER(DebugT), _P]),
+    "moe_forward_noalloc": (_I32, [ctypes.POINTER(LayerT), _P, _I32, _P, _P, _P, _P,
+                                   ctypes.POINTER(DebugT), _P]),
+    "moe_noalloc_scratch_bytes": (_SZ, []),
     "quantize_nvfp4_4o6": (_I32, [_P, _I32, _I32, _P, _P, _P, _P, _P]),
     "moe_requant_mxfp4": (_I32, [_P, ctypes.c_int64, _I32, _P, _P, _P]),
     "moe_requant_nvfp4": (_I32, [_P, _I32, ctypes.c_int64, _I32, _P, _P, _P, _P]),
@@ -319,6 +324,31 @@ def forward(layer: DeviceLayer, x: torch.Tensor, ws: Workspace, out=None, path: 
                             _ptr(xq), y.data_ptr(), ws.ptr, ws.nbytes,
                             ctypes.byref(dbg) if dbg is not None else None, _stream()))
     return y, ids, w, xq
+
+
+def forward_noalloc(layer: DeviceLayer, x: torch.Tensor, out=None, path: int = PATH_AUTO):
+    """moe_forward_noalloc: moe_forward on the library's static per-GPU scratch (no
+    workspace argument). Returns (y, topk_ids, topk_w, xq); ``out`` reuses buffers."""
+    x = _bits16(x)
+    T = x.shape[0]
+    cfg = layer.cfg
+    if out is None:
+        y = torch.empty((T, cfg.H), dtype=torch.bfloat16, device=x.device)
+        ids = torch.empty((T, cfg.k), dtype=torch.int32, device=x.device)
+        w = torch.empty((T, cfg.k), dtype=torch.float32, device=x.device)
+        nq = xq_bytes(layer, T)
+        xq = _aligned_empty(nq, x.device) if nq else None
+    else:
+        y, ids, w, xq = out
+    dbg = DebugT(None, None, None, None, path) if path != PATH_AUTO else None
+    _check(_lib.moe_forward_noalloc(ctypes.byref(layer.struct), x.data_ptr(), T, ids.data_ptr(), w.data_ptr(),
+                                    _ptr(xq), y.data_ptr(), ctypes.byref(dbg) if dbg is not None else None,
+                                    _stream()))
+    return y, ids, w, xq
+
+
+def noalloc_scratch_bytes() -> int:
+    return _lib.moe_noalloc_scratch_bytes()
 
 
 def quantize_nvfp4_4o6(x: torch.Tensor, want_choice: bool = True):

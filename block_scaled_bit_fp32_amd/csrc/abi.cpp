@@ -2,9 +2,12 @@
 // dispatch to the gfx950 kernels. Declarations and contracts: include/moe.h.
 #include "moe.h"
 
+#include <hip/hip_runtime.h>
+
 #include <algorithm>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "plan.hpp"
@@ -707,6 +710,68 @@ moe_status_t moe_forward(const moe_layer_t* L, const uint16_t* x_bf16, int32_t T
   if ((st = enqueue_route(L, x_bf16, T, topk_ids, topk_w, xq, ws, ws_bytes, !fused, false, stream)) != MOE_OK)
     return st;
   return enqueue_experts(L, x_bf16, xq, T, topk_ids, topk_w, y_bf16, ws, ws_bytes, dbg, fused, false, stream);
+}
+
+}  // extern "C"
+
+// ------------------------------------------------------------ allocation-free variant
+// moe_forward_noalloc runs moe_forward on a workspace that lives in this library's own
+// device memory: a file-scope array, one copy per GPU, kept until the process ends. Host
+// code never passes the array's name to a kernel (on the host it is only a stand-in): the
+// device address comes from hipGetSymbolAddress, once per device, with that device
+// current.
+namespace {
+
+constexpr size_t kScratchBytes = size_t(16) << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's copy of `scratch`, or NULL with the error set.
+void* scratch_for_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    set_err(MOE_ELAUNCH, "no current HIP device");
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      set_err(MOE_ELAUNCH, std::string("hipGetSymbolAddress(scratch) failed: ") + hipGetErrorString(e));
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
+moe_status_t moe_forward_noalloc(const moe_layer_t* L, const uint16_t* x_bf16, int32_t T, int32_t* topk_ids,
+                                 float* topk_w, void* xq, uint16_t* y_bf16, const moe_debug_t* dbg,
+                                 hipStream_t stream) {
+  moe_status_t st = check_or_fail(L, std::max(1, T));
+  if (st != MOE_OK) return st;
+  if (T < 0) return set_err(MOE_EINVAL, "T must be >= 0");
+  const size_t need = ws_layout(*L, std::max(1, T)).total;
+  if (need > kScratchBytes) {
+    char b[200];
+    snprintf(b, sizeof b, "this call needs %zu bytes of workspace; the library's static scratch holds %zu "
+             "(use moe_forward with a caller workspace)", need, kScratchBytes);
+    return set_err(MOE_EWORKSPACE, b);
+  }
+  if (T == 0) return MOE_OK;
+  void* ws = scratch_for_current_device();
+  if (!ws) return MOE_ELAUNCH;
+  return moe_forward(L, x_bf16, T, topk_ids, topk_w, xq, y_bf16, ws, kScratchBytes, dbg, stream);
 }
 
 moe_status_t moe_requant_mxfp4(const uint16_t* w_bf16, int64_t rows, int32_t cols, uint8_t* codes, uint8_t* scales,

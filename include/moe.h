@@ -206,6 +206,24 @@ moe_status_t moe_forward(const moe_layer_t *L, const uint16_t *x_bf16, int32_t T
                          void *ws, size_t ws_bytes, const moe_debug_t *dbg,
                          hipStream_t stream);
 
+/* moe_forward without a caller workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc). The same arguments, results and checks as moe_forward, minus ws and
+ * ws_bytes: the workspace is a static array inside this library, one copy per GPU of
+ * moe_noalloc_scratch_bytes() bytes (16 MiB), held until the process ends. Its device
+ * address is looked up (hipGetSymbolAddress) on the first call on each device, so make
+ * that first call outside graph capture. The call allocates nothing. A call whose
+ * workspace would exceed the scratch (moe_workspace_bytes(L, T) > 16 MiB, e.g. the
+ * Flint-shaped layer past about 200 tokens) fails with MOE_EWORKSPACE and enqueues
+ * nothing. Every call on one GPU uses the same scratch and leaves the last call's
+ * intermediates in it (nothing in it needs clearing: each call's kernels read only what
+ * earlier kernels of the same call wrote), so calls that may overlap on one GPU (other
+ * streams, other threads) race and must be serialized by the caller. */
+moe_status_t moe_forward_noalloc(const moe_layer_t *L, const uint16_t *x_bf16, int32_t T,
+                                 int32_t *topk_ids, float *topk_w, void *xq, uint16_t *y_bf16,
+                                 const moe_debug_t *dbg, hipStream_t stream);
+size_t moe_noalloc_scratch_bytes(void);
+
 /* Four-Over-Six NVFP4 quantization of rows x[rows][cols] (BF16), cols % 16 == 0
  * ("Inkling 2 Small on vLLM: Day-0 Support", mixed-precision MoE and Four-Over-Six
  * NVFP4): per row g = amax/2688 (FP32); per 16-block with max m and c in {6, 4}:

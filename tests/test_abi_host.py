@@ -146,3 +146,17 @@ def test_xq_bytes_layout(lib):
     assert lib.lib().moe_xq_bytes(ctypes.byref(s), 2) == 2 * 6144 + 256
     s = _fake_layer(lib, "flint_w4a16")
     assert lib.lib().moe_xq_bytes(ctypes.byref(s), 2) == 0
+
+
+def test_noalloc_refuses_calls_past_its_scratch_before_any_device_call(lib):
+    """moe_forward_noalloc checks the workspace a call needs against its static scratch
+    (16 MiB) on the host: the Flint-shaped BF16 layer at 256 tokens needs ~21 MB."""
+    s = _fake_layer(lib, "flint_bf16")
+    T = 256
+    need = lib.lib().moe_workspace_bytes(ctypes.byref(s), T)
+    assert need > lib.lib().moe_noalloc_scratch_bytes() == 16 << 20
+    p = 1 << 20
+    st = lib.lib().moe_forward_noalloc(ctypes.byref(s), p, T, p, p, None, p, None, None)
+    assert st == lib.MOE_EWORKSPACE
+    assert "static scratch" in lib.lib().moe_last_error().decode()
+    assert lib.lib().moe_workspace_bytes(ctypes.byref(s), 8) <= lib.lib().moe_noalloc_scratch_bytes()
