@@ -655,9 +655,25 @@ moe_status_t enqueue_experts(const moe_layer_t* L, const uint16_t* x_bf16, const
                    ? reinterpret_cast<const float*>(base + w.logits) + (size_t)T * L->E : nullptr;
       gu.softmax = L->router_score == MOE_SCORE_SOFTMAX;
     }
-    // token mode: one workgroup per (token, row-step) item; with fewer items than half the
-    // compute units the per-pair walk (and the combine launch) is faster
-    dn.token_mode = pm && p.token && 2 * T * (L->H / p.dn_r.RS) >= ncu ? 1 : 0;
+    // token mode: items of (token, row-step) over all of the token's experts, writing y.
+    // Wide items of G rows, whose experts the four waves split (an item issues two
+    // experts' loads per lane instead of k + 1), while they fit one per resident workgroup
+    // and give at least half a workgroup per compute unit: one or two tokens. Past that,
+    // items of RS rows under the same floor (graph-timed on the Flint W4A16 layer: at
+    // 4 and 8 tokens a workgroup's one burst of k + 1 experts beats wide items streamed
+    // two at a time, 11.3 against 12.3 us and 15.2 against 17.4 us); else the per-pair
+    // walk and the combine launch.
+    {
+      const int full = L->H / p.dn_r.RS, wide = L->H / p.dn_r.G;
+      int tm = 0;
+      if (pm && p.token) {
+        if (T * wide <= dn_grid && 2 * T * wide >= ncu && 4 * p.dn_r.G <= 2 * kWinRows) tm = 2;
+        else if (2 * T * full >= ncu) tm = 1;
+      }
+      dn.token_mode = tm;
+      dn.tok_items = tm == 2 ? wide : full;
+      dn.tok_inv = 1.0f / (float)dn.tok_items;
+    }
     auto q = [](const GemvMap& m, int steps) { return CostQ{m.NG, steps, m.cw, m.ct}; };
     gu.sh_wgs = shared_wgs(*L, T, q(p.gu_s, Ish_ / (p.gu_s.RS / 2)), q(p.gu_r, L->I / (p.gu_r.RS / 2)), gu_grid,
                            ncu, gu.late16, pm);
@@ -670,7 +686,7 @@ moe_status_t enqueue_experts(const moe_layer_t* L, const uint16_t* x_bf16, const
       if (!dn.token_mode)
         split_rounds(dn, T * L->k * p.dn_r.steps, dn_grid - dn.sh_wgs, std::max(0, ncu - dn.sh_wgs));
     }
-    if (dn.token_mode) split_rounds(dn, T * p.dn_r.steps, dn_grid, ncu);
+    if (dn.token_mode) split_rounds(dn, T * dn.tok_items, dn_grid, ncu);
   }
   if (launch_experts(gu, gu_grid, p.gu_lds, dn, dn_grid, p.dn_lds, stream) != hipSuccess)
     return set_err(MOE_ELAUNCH, "expert kernel launch failed");

@@ -1043,25 +1043,31 @@ __device__ __forceinline__ void down_walk(const ExpertArgs& a, const ExpertLds& 
 
 // Token mode of the down projection (pair mode, when the shared expert, if any, has the
 // routed format and size and takes the same FP32 h): a work item is (token t, row-step
-// s), i.e. RS hidden rows of y[t]; its J = k (+1 shared) sub-steps are the token's
-// experts. All J sub-steps' weight loads of an item are issued at once (kTokJMax
-// register sets of kTokPieces pieces: a row-step of the down projection is one batch of
-// at most kTokPieces pieces per lane), so an item costs one memory round trip. Each
-// sub-step's dot products are scaled by its combine weight, global weight scale and
-// activation scale and summed in registers; the item writes the BF16 sum to y: the
-// weighted combine needs no per-pair output. Items split evenly over the workgroups.
-// The J activation rows of the current token sit in LDS (rows j of the tile); the first
-// token's are loaded before the first weight loads, as in walk_class.
-template <int FMT, int AK, int AF>
+// s), i.e. a block of hidden rows of y[t]; its J = k (+1 shared) sub-steps are the
+// token's experts. Each sub-step's dot products are scaled by its combine weight, global
+// weight scale and activation scale and summed in registers; the item writes the BF16
+// sum to y: the weighted combine needs no per-pair output. Items split evenly over the
+// workgroups. The J activation rows of the current token sit in LDS (rows j of the
+// tile); the first token's are loaded before the first weight loads, as in walk_class.
+//   WIDE = false: an item is RS = 4 G rows, each wave G of them over all J sub-steps (all
+//     of an item's weight loads are issued at once: kTokJMax register sets of kTokPieces
+//     pieces, one memory round trip per item).
+//   WIDE = true: an item is G rows and the waves split the sub-steps (wave w takes j = w
+//     and w + 4), so a batch of few tokens still has enough items to fill the GPU; the
+//     four waves' partial sums meet in LDS and are added in wave order.
+template <int FMT, int AK, int AF, bool WIDE>
 __device__ __forceinline__ void walk_tokens(const ExpertArgs& a, const ExpertLds& L, int i0, int i1) {
   constexpr int EPL = elems_per_piece(FMT);
   constexpr int NPT = kTokPieces;
+  constexpr int NJ = WIDE ? kTokJMax / 4 : kTokJMax;   // sub-steps per lane
   if (i1 <= i0) return;
   const GemvMap& m = a.rmap;
-  const int steps = m.steps, J = a.k + a.has_shared, P = a.T * a.k;
-  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-  const int jl = lane & (m.LPR - 1), lrow = wave * m.G + (lane >> m.lg);
+  const int items = a.tok_items, J = a.k + a.has_shared, P = a.T * a.k;
+  const int lane = threadIdx.x & (kWave - 1), wave = uni((int)threadIdx.x / kWave);
+  const int jl = lane & (m.LPR - 1), lrow = (WIDE ? 0 : wave * m.G) + (lane >> m.lg);
+  const int rows_item = WIDE ? m.G : m.RS;
   const int tstride = a.rw.K * m.esize;
+  auto jof = [&](int jj) { return WIDE ? wave + 4 * jj : jj; };
   const DownOps<AF> op{a.h, a.hq_codes, a.hq_scales, a.hq_scale, a.rw.gscale, a.rw.gs_per_expert, a.rw.rows,
                        a.I, m.RS, a.H, a.hs, a.o, L.gs_rt, L.w_tsc, nullptr, 1};
   auto pair_of = [&](int t, int j) { return j < a.k ? t * a.k + j : P + t; };
@@ -1070,12 +1076,12 @@ __device__ __forceinline__ void walk_tokens(const ExpertArgs& a, const ExpertLds
     uint4 w[NPT];
     uint32_t s[NPT];
   };
-  // sub-step j of row-step s of token t, expert e: this lane's NPT pieces of its row
+  // sub-step j of item row-step s of token t, expert e: this lane's NPT pieces of its row
   auto fetch = [&](int s, int j, int e, Regs& R) {
     const bool sh = j >= a.k;
     const uint8_t* codes = sh ? a.sw.codes : a.rw.codes;
     const uint8_t* scales = sh ? a.sw.scales : a.rw.scales;
-    const int64_t row = (int64_t)(sh ? 0 : e) * a.rw.rows + s * m.RS + lrow;
+    const int64_t row = (int64_t)(sh ? 0 : e) * a.rw.rows + s * rows_item + lrow;
     const uint8_t* rp = codes + row * a.rw.code_row_bytes;
     const uint8_t* sp = scales ? scales + row * a.rw.scale_row_bytes : nullptr;
 #pragma unroll
@@ -1098,7 +1104,7 @@ __device__ __forceinline__ void walk_tokens(const ExpertArgs& a, const ExpertLds
     const int p = pair_of(t, j);
     return op.tsc(t, p) * (j < a.k ? a.topk_w[p] : 1.0f);
   };
-  int staged_t = div_by(i0, m.inv_steps);
+  int staged_t = div_by(i0, a.tok_inv);
   auto stage = [&](int t) {
     lds_barrier();
     stage_tile<AK, EPL>(L.tile, m, a.rw.K, J, row_ld(t), [&](uint4 r) { return op.cv(r); });
@@ -1106,13 +1112,14 @@ __device__ __forceinline__ void walk_tokens(const ExpertArgs& a, const ExpertLds
     staged_t = t;
     lds_barrier();
   };
-  Regs R[kTokJMax];
-  int ex[kTokJMax];
-  auto item = [&](int it) {
-    const int t = div_by(it, m.inv_steps), s = it - t * steps;
+  float* red = L.w_gs;   // WIDE: [4][G] partial sums of the waves
+  // one item from the weight registers R (experts ex) of its sub-steps
+  auto item = [&](int it, const Regs (&R)[NJ], const int (&ex)[NJ]) {
+    const int t = div_by(it, a.tok_inv), s = it - t * items;
     float tot = 0.0f;
 #pragma unroll
-    for (int j = 0; j < kTokJMax; ++j) {
+    for (int jj = 0; jj < NJ; ++jj) {
+      const int j = jof(jj);
       if (j < J) {
         float part[1][4];
         part[0][0] = 0.0f;
@@ -1120,23 +1127,51 @@ __device__ __forceinline__ void walk_tokens(const ExpertArgs& a, const ExpertLds
         WeightRegs<1> wr;
 #pragma unroll
         for (int i = 0; i < WeightRegs<1>::NPB; ++i) {
-          wr.w[i][0] = R[j].w[min(i, NPT - 1)];
-          wr.s[i][0] = R[j].s[min(i, NPT - 1)];
+          wr.w[i][0] = R[jj].w[min(i, NPT - 1)];
+          wr.s[i][0] = R[jj].s[min(i, NPT - 1)];
         }
 #pragma unroll
         for (int i = 0; i < NPT; ++i)
           if (i < m.NPB) accumulate_piece<FMT, AK, 1, 1>(wr.w[i], wr.s[i], tile, tstride, m.LPR, i, jl, part);
-        const float g = j < a.k ? L.gs_rt[ex[j] * a.rw.gs_per_expert] : L.gs_sh[0];
+        const float g = j < a.k ? L.gs_rt[ex[jj] * a.rw.gs_per_expert] : L.gs_sh[0];
         tot = fmaf(L.w_tsc[j] * g, part[0][0], tot);
       }
     }
     for (int o = m.LPR / 2; o > 0; o >>= 1) tot += __shfl_xor(tot, o, kWave);
-    if (jl == 0) a.y[(int64_t)t * a.H + s * m.RS + lrow] = (uint16_t)f32_to_bf16_rne(tot);
+    if constexpr (WIDE) {
+      lds_barrier();   // the previous item's partial sums have been read
+      if (jl == 0) red[wave * m.G + lrow] = tot;
+      lds_barrier();
+      if ((int)threadIdx.x < m.G) {
+        const int r = threadIdx.x;
+        const float v = ((red[r] + red[m.G + r]) + red[2 * m.G + r]) + red[3 * m.G + r];
+        a.y[(int64_t)t * a.H + s * rows_item + r] = (uint16_t)f32_to_bf16_rne(v);
+      }
+    } else {
+      if (jl == 0) a.y[(int64_t)t * a.H + s * rows_item + lrow] = (uint16_t)f32_to_bf16_rne(tot);
+    }
   };
+  // the weight loads of item `it` (its experts from the staged topk_ids)
+  auto fetch_item = [&](int it, Regs (&R)[NJ], int (&ex)[NJ]) {
+    const int t = div_by(it, a.tok_inv);
+#pragma unroll
+    for (int jj = 0; jj < NJ; ++jj) {
+      const int j = jof(jj);
+      if (j < J) {
+        ex[jj] = j < a.k ? clamp_e(uni(L.ids[t * a.k + j])) : 0;
+        fetch(it - t * items, j, ex[jj], R[jj]);
+      }
+    }
+  };
+  Regs RA[NJ], RB[NJ];
+  int exA[NJ], exB[NJ];
   // prologue: the first token's experts (scalar loads), rows, factors, global scales and
   // topk_ids, then every sub-step's weight loads of the first item, then LDS
 #pragma unroll
-  for (int j = 0; j < kTokJMax; ++j) ex[j] = j < a.k && j < J ? clamp_e(a.ids[staged_t * a.k + j]) : 0;
+  for (int jj = 0; jj < NJ; ++jj) {
+    const int j = jof(jj);
+    exA[jj] = j < a.k && j < J ? clamp_e(a.ids[staged_t * a.k + j]) : 0;
+  }
   uint4 raw[kPreSlotsTok];
   const SlotMap<AK> smap(m, a.rw.K);
   park_rows<AK, kPreSlotsTok>(smap, J, row_ld(staged_t), raw);
@@ -1151,10 +1186,10 @@ __device__ __forceinline__ void walk_tokens(const ExpertArgs& a, const ExpertLds
   const float gss = ssrc[0];
   const int idv = a.ids[min((int)threadIdx.x, P - 1)];
   {
-    const int s0 = i0 - staged_t * steps;
+    const int s0 = i0 - staged_t * items;
 #pragma unroll
-    for (int j = 0; j < kTokJMax; ++j)
-      if (j < J) fetch(s0, j, ex[j], R[j]);
+    for (int jj = 0; jj < NJ; ++jj)
+      if (jof(jj) < J) fetch(s0, jof(jj), exA[jj], RA[jj]);
   }
   unpark_rows<AK, EPL, kPreSlotsTok>(smap, L.tile, J, [&](uint4 r) { return op.cv(r); }, raw);
   if ((int)threadIdx.x < J) L.w_tsc[threadIdx.x] = fac_r;
@@ -1166,18 +1201,35 @@ __device__ __forceinline__ void walk_tokens(const ExpertArgs& a, const ExpertLds
   if (threadIdx.x == 0) L.gs_sh[0] = a.sw.gscale ? gss : 1.0f;
   if ((int)threadIdx.x < P) L.ids[threadIdx.x] = idv;
   lds_barrier();
-  item(i0);
-  for (int it = i0 + 1; it < i1; ++it) {
-    const int t = div_by(it, m.inv_steps);
-    if (t != staged_t) stage(t);
-#pragma unroll
-    for (int j = 0; j < kTokJMax; ++j) {
-      if (j < J) {
-        ex[j] = j < a.k ? clamp_e(uni(L.ids[t * a.k + j])) : 0;
-        fetch(it - t * steps, j, ex[j], R[j]);
+  if constexpr (WIDE) {
+    // two register sets alternate: the next item's weight loads are in flight while
+    // this item computes (a token change restages the rows after this item)
+    int it = i0;
+    auto step = [&](auto pf, const Regs (&Rc)[NJ], const int (&exc)[NJ], Regs (&Rn)[NJ], int (&exn)[NJ]) {
+      if constexpr (decltype(pf)::value) fetch_item(it + 1, Rn, exn);
+      item(it, Rc, exc);
+      ++it;
+      if constexpr (decltype(pf)::value) {
+        const int t = div_by(it, a.tok_inv);
+        if (t != staged_t) stage(t);
       }
+    };
+    using Yes = std::integral_constant<bool, true>;
+    using No = std::integral_constant<bool, false>;
+    while (true) {
+      if (i1 - it == 1) { step(No{}, RA, exA, RB, exB); break; }
+      step(Yes{}, RA, exA, RB, exB);
+      if (i1 - it == 1) { step(No{}, RB, exB, RA, exA); break; }
+      step(Yes{}, RB, exB, RA, exA);
     }
-    item(it);
+  } else {
+    item(i0, RA, exA);
+    for (int it = i0 + 1; it < i1; ++it) {
+      const int t = div_by(it, a.tok_inv);
+      if (t != staged_t) stage(t);
+      fetch_item(it, RA, exA);
+      item(it, RA, exA);
+    }
   }
 }
 
@@ -1189,7 +1241,10 @@ __global__ void __launch_bounds__(kBlock, 2) __attribute__((amdgpu_waves_per_eu(
     if (a.token_mode) {
       int i0, len;   // items per workgroup: the host's two-round split
       split_at(blockIdx.x, a.pn1, a.pq1, a.pr1, a.pq2, a.pr2, i0, len);
-      walk_tokens<RF, 0, AF>(a, L, i0, i0 + len);
+      if (a.token_mode == 2)
+        walk_tokens<RF, 0, AF, true>(a, L, i0, i0 + len);
+      else
+        walk_tokens<RF, 0, AF, false>(a, L, i0, i0 + len);
       return;
     }
   }

@@ -112,7 +112,10 @@ struct ExpertArgs {
   int grouped;           // run the grouped kernels
   int pair_mode;         // GEMV kernels: one unit per (token, expert) pair
   int token_mode;        // down GEMV: items (token, row-step) over all of a token's
-                         // experts, writing y (no combine launch)
+                         // experts, writing y (no combine launch); 1: an item is RS rows,
+                         // 2 (wide): G rows, the waves splitting the token's experts
+  int tok_items;         // token mode: items per token (H / rows per item)
+  float tok_inv;         // 1 / tok_items
   float inv_k;           // 1 / k
   // pair and token modes, positions of one cost: the class's first n1 workgroups (those
   // dispatched in the first round) take q1 or q1 + 1 (the first r1 of them q1 + 1), the
