@@ -26,9 +26,9 @@ LIB_PATH = os.path.join(_HERE, "libmoe_mi355x.so")
 
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_ELAUNCH = 0, -1, -2, -3, -4
 WFMT = {"bf16": 0, "nvfp4": 1, "mxfp4": 2, "mxfp8": 3}
-AFMT = {"bf16": 0, "nvfp4_4o6": 1, "fp8_token": 2}
+AFMT = {"bf16": 0, "nvfp4_4o6": 1, "fp8_token": 2, "mxfp4": 3, "mxfp8": 4}
 SCORE = {"sigmoid": 0, "softmax": 1}
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 
 class MoeError(RuntimeError):
@@ -269,6 +269,10 @@ def split_xq(layer: DeviceLayer, xq: torch.Tensor, T: int) -> dict:
     if layer.cfg.afmt == "fp8_token":
         a = part(T * H)
         return {"codes": xq[:T * H].view(T, H), "s": xq[a:a + 4 * T].view(torch.float32)}
+    if layer.cfg.afmt in ("mxfp4", "mxfp8"):
+        n = T * H // 2 if layer.cfg.afmt == "mxfp4" else T * H
+        a = part(n)
+        return {"codes": xq[:n].view(T, n // T), "scales": xq[a:a + T * H // 32].view(T, H // 32)}
     return {}
 
 
@@ -297,6 +301,10 @@ def expert_forward(layer: DeviceLayer, x: torch.Tensor, xq, ids: torch.Tensor, w
         elif cfg.afmt == "fp8_token":
             dd["hq_codes"] = _aligned_empty(P * cfg.I, x.device).view(P, cfg.I)
             dd["hq_scale"] = torch.empty(P, dtype=torch.float32, device=x.device)
+        elif cfg.afmt in ("mxfp4", "mxfp8"):
+            n = cfg.I // 2 if cfg.afmt == "mxfp4" else cfg.I
+            dd["hq_codes"] = _aligned_empty(P * n, x.device).view(P, n)
+            dd["hq_scales"] = torch.empty((P, cfg.I // 32), dtype=torch.uint8, device=x.device)
         dbg = DebugT(_ptr(dd.get("h")), _ptr(dd.get("hq_codes")), _ptr(dd.get("hq_scales")),
                      _ptr(dd.get("hq_scale")), path)
     _check(_lib.moe_expert_forward(ctypes.byref(layer.struct), x.data_ptr(), _ptr(xq), T,

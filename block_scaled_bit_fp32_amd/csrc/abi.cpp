@@ -327,9 +327,11 @@ WsLayout ws_layout(const moe_layer_t& L, int maxT) {
   auto take = [&](size_t bytes) { size_t at = off; off = align_up(off + bytes); return at; };
   w.logits = take(8 * (size_t)maxT * L.E);   // logits (keys), then bare logits (selection-only bias)
   w.h = take(4 * Pt * w.hs);
-  const size_t qrow = L.afmt == A_NVFP4_4O6 ? L.I / 2 : (L.afmt == A_FP8_TOKEN ? L.I : 0);
+  const size_t qrow = (L.afmt == A_NVFP4_4O6 || L.afmt == A_MXFP4) ? L.I / 2
+                      : ((L.afmt == A_FP8_TOKEN || L.afmt == A_MXFP8) ? L.I : 0);
   w.hq_codes = take(Pr * qrow);
-  w.hq_scales = take(L.afmt == A_NVFP4_4O6 ? Pr * (L.I / 16) : 0);
+  w.hq_scales = take(L.afmt == A_NVFP4_4O6 ? Pr * (L.I / 16)
+                     : ((L.afmt == A_MXFP4 || L.afmt == A_MXFP8) ? Pr * (L.I / 32) : 0));
   w.hq_scale = take(4 * Pr);
   w.o = take(4 * Pt * L.H);
   w.total = off;
@@ -362,10 +364,12 @@ std::string check_layer(const moe_layer_t* L, int max_tokens) {
   const bool wf_ok = valid_wfmt(L->wfmt), sf_ok = valid_wfmt(L->shared_wfmt);
   if (!wf_ok) { snprintf(b, sizeof b, "unknown wfmt %d", L->wfmt); add(b); }
   if (L->has_shared == 1 && !sf_ok) { snprintf(b, sizeof b, "unknown shared_wfmt %d", L->shared_wfmt); add(b); }
-  if (L->afmt < MOE_A_BF16 || L->afmt > MOE_A_FP8_TOKEN) { snprintf(b, sizeof b, "unknown afmt %d", L->afmt); add(b); }
+  if (L->afmt < MOE_A_BF16 || L->afmt > MOE_A_MXFP8) { snprintf(b, sizeof b, "unknown afmt %d", L->afmt); add(b); }
   if (L->afmt == MOE_A_NVFP4_4O6 && L->wfmt != MOE_W_NVFP4) add("afmt NVFP4_4O6 needs NVFP4 routed weights");
   if (L->afmt == MOE_A_FP8_TOKEN && L->wfmt != MOE_W_MXFP4 && L->wfmt != MOE_W_MXFP8)
     add("afmt FP8_TOKEN needs MXFP4 or MXFP8 routed weights");
+  if ((L->afmt == MOE_A_MXFP4 || L->afmt == MOE_A_MXFP8) && L->wfmt != MOE_W_MXFP4 && L->wfmt != MOE_W_MXFP8)
+    add("afmt MXFP4 / MXFP8 needs MXFP4 or MXFP8 routed weights");
   if (L->has_shared == 1 && wf_ok && sf_ok && L->shared_wfmt != L->wfmt && L->shared_wfmt != MOE_W_BF16)
     add("the shared expert must use the routed format or BF16");
   if (!L->router_w) add("router_w is NULL");
@@ -474,6 +478,8 @@ size_t moe_xq_bytes(const moe_layer_t* L, int32_t T) {
   if (L->afmt == MOE_A_NVFP4_4O6)
     return xq_part((size_t)T * L->H / 2) + xq_part((size_t)T * L->H / 16) + xq_part(4 * (size_t)T);
   if (L->afmt == MOE_A_FP8_TOKEN) return xq_part((size_t)T * L->H) + xq_part(4 * (size_t)T);
+  if (L->afmt == MOE_A_MXFP4) return xq_part((size_t)T * L->H / 2) + xq_part((size_t)T * L->H / 32);
+  if (L->afmt == MOE_A_MXFP8) return xq_part((size_t)T * L->H) + xq_part((size_t)T * L->H / 32);
   return 0;
 }
 
@@ -533,8 +539,10 @@ moe_status_t enqueue_route(const moe_layer_t* L, const uint16_t* x_bf16, int32_t
     if (L->afmt == MOE_A_NVFP4_4O6) {
       a.xq_scales = q + xq_part((size_t)T * L->H / 2);
       a.xq_scale = reinterpret_cast<float*>(a.xq_scales + xq_part((size_t)T * L->H / 16));
-    } else {
+    } else if (L->afmt == MOE_A_FP8_TOKEN) {
       a.xq_scale = reinterpret_cast<float*>(q + xq_part((size_t)T * L->H));
+    } else {   // MX: codes, then E8M0 scales
+      a.xq_scales = q + xq_part((size_t)T * L->H / (L->afmt == MOE_A_MXFP4 ? 2 : 1));
     }
     n_quant = T;
   }
@@ -566,8 +574,10 @@ moe_status_t enqueue_experts(const moe_layer_t* L, const uint16_t* x_bf16, const
   if (!y_bf16) bad += "y_bf16 is NULL; ";
   if (L->afmt != MOE_A_BF16 && (!xq || !aligned(xq, kAlign))) bad += "xq must be non-NULL and 256-byte aligned; ";
   if (dbg && dbg->hq_codes && L->afmt == MOE_A_BF16) bad += "dbg->hq_codes needs a quantized afmt; ";
-  if (dbg && dbg->hq_codes && (!dbg->hq_scale || (L->afmt == MOE_A_NVFP4_4O6 && !dbg->hq_scales)))
-    bad += "dbg->hq_codes needs hq_scale (and hq_scales for NVFP4); ";
+  if (dbg && dbg->hq_codes && L->afmt != MOE_A_BF16 &&
+      (((L->afmt == MOE_A_NVFP4_4O6 || L->afmt == MOE_A_FP8_TOKEN) && !dbg->hq_scale) ||
+       (L->afmt != MOE_A_FP8_TOKEN && !dbg->hq_scales)))
+    bad += "dbg->hq_codes needs hq_scale (NVFP4, FP8 per token) and hq_scales (NVFP4, MX); ";
   if (dbg && dbg->hq_codes && !aligned(dbg->hq_codes, 16)) bad += "dbg->hq_codes must be 16-byte aligned; ";
   if (!bad.empty()) return set_err(MOE_EINVAL, bad);
   WsLayout w;
@@ -592,8 +602,10 @@ moe_status_t enqueue_experts(const moe_layer_t* L, const uint16_t* x_bf16, const
     if (L->afmt == MOE_A_NVFP4_4O6) {
       a.xq_scales = q + xq_part((size_t)T * L->H / 2);
       a.xq_scale = reinterpret_cast<const float*>(a.xq_scales + xq_part((size_t)T * L->H / 16));
-    } else {
+    } else if (L->afmt == MOE_A_FP8_TOKEN) {
       a.xq_scale = reinterpret_cast<const float*>(q + xq_part((size_t)T * L->H));
+    } else {   // MX: codes, then E8M0 scales
+      a.xq_scales = q + xq_part((size_t)T * L->H / (L->afmt == MOE_A_MXFP4 ? 2 : 1));
     }
   }
   a.ids = topk_ids;

@@ -1,8 +1,8 @@
 // Kernels between and after the expert GEMVs:
 //   hquant_kernel   re-quantizes each routed pair's SwiGLU output h (FP32, one row of I)
-//                   per the layer's activation format (Four-Over-Six NVFP4 or FP8 per
-//                   row) -- the quantize-before-down step of the Inkling page's MoE with
-//                   fused activation quantization, done once per pair.
+//                   per the layer's activation format (Four-Over-Six NVFP4, FP8 per row,
+//                   MXFP4 or MXFP8 per 32-block) -- the quantize-before-down step of the
+//                   Inkling page's MoE with fused activation quantization, once per pair.
 //   combine_kernel  y[t][r] = sum_j w[t][j] * o[t*k+j][r] (+ o_shared[t][r]), FP32 in that
 //                   order, rounded to BF16 -- the weighted combine (k <= 16).
 #include "launch.hpp"
@@ -20,9 +20,17 @@ __global__ void __launch_bounds__(kBlock) hquant_kernel(ExpertArgs a) {
     if (a.dbg_codes)
       quant_row_nvfp4(row, a.I, a.dbg_codes + (int64_t)p * (a.I / 2), a.dbg_scales + (int64_t)p * (a.I / 16),
                       a.dbg_scale + p, nullptr, red);
-  } else {
+  } else if (a.afmt == A_FP8_TOKEN) {
     quant_row_fp8(row, a.I, a.hq_codes + (int64_t)p * a.I, a.hq_scale + p, red);
     if (a.dbg_codes) quant_row_fp8(row, a.I, a.dbg_codes + (int64_t)p * a.I, a.dbg_scale + p, red);
+  } else if (a.afmt == A_MXFP4) {
+    quant_row_mx<false>(row, a.I, a.hq_codes + (int64_t)p * (a.I / 2), a.hq_scales + (int64_t)p * (a.I / 32));
+    if (a.dbg_codes)
+      quant_row_mx<false>(row, a.I, a.dbg_codes + (int64_t)p * (a.I / 2), a.dbg_scales + (int64_t)p * (a.I / 32));
+  } else {
+    quant_row_mx<true>(row, a.I, a.hq_codes + (int64_t)p * a.I, a.hq_scales + (int64_t)p * (a.I / 32));
+    if (a.dbg_codes)
+      quant_row_mx<true>(row, a.I, a.dbg_codes + (int64_t)p * a.I, a.dbg_scales + (int64_t)p * (a.I / 32));
   }
 }
 

@@ -264,6 +264,50 @@ __device__ __forceinline__ uint32_t nvfp4_4o6_block(const float (&x)[16], float 
   return four ? 4u : 6u;
 }
 
+// OCP MX v1.0 of one 32-element block (the Mistral Large 4 page's MXFP4 load path and
+// MX activations): shared exponent e = floor(log2(block amax)) - emax, emax the element
+// format's largest exponent (E2M1: 2, E4M3: 8), clamped to [-127, 127] (an all-zero block
+// takes -127); elements are the values times 2^-e (exact), rounded to the element
+// format with ties to even and saturation, sign kept. Returns the E8M0 scale byte e + 127.
+// E2M1: gfx950's scaled FP32 -> FP4 convert does the scaling and rounding, two
+// elements per instruction; codes in w[4] (element 2i in the low nibble).
+__device__ __forceinline__ uint32_t mx_block_fp4(const float (&v)[32], uint32_t (&w)[4]) {
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  // floor(log2(amax)) = frexp exponent - 1 (amax = m * 2^e, m in [0.5, 1)), then - 2
+  int e = amax > 0.0f ? __builtin_amdgcn_frexp_expf(amax) - 3 : -127;
+  e = min(max(e, -127), 127);
+  const float sc = __builtin_bit_cast(float, (uint32_t)(e + 127) << 23 | (e == -127 ? 0x00400000u : 0u));
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    uint32_t r = 0u;
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[8 * q + 0], v[8 * q + 1], sc, 0);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[8 * q + 2], v[8 * q + 3], sc, 1);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[8 * q + 4], v[8 * q + 5], sc, 2);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[8 * q + 6], v[8 * q + 7], sc, 3);
+    w[q] = r;
+  }
+  return (uint32_t)(e + 127);
+}
+
+// The same with E4M3 elements (largest exponent 8, saturation at 448): codes in w[8].
+__device__ __forceinline__ uint32_t mx_block_fp8(const float (&v)[32], uint32_t (&w)[8]) {
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  int e = amax > 0.0f ? __builtin_amdgcn_frexp_expf(amax) - 9 : -127;
+  e = min(max(e, -127), 127);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) w[i] = 0u;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const float y = ldexpf(v[i], -e);
+    w[i >> 2] |= (e4m3_encode_pos(fabsf(y)) | ((__float_as_uint(y) >> 24) & 0x80u)) << (8 * (i & 3));
+  }
+  return (uint32_t)(e + 127);
+}
+
 // FP8-E4M3 of x / s (finite), sign copied from x.
 __device__ __forceinline__ uint32_t fp8_token_code(float x, float s) {
 #pragma clang fp contract(off)

@@ -855,6 +855,28 @@ __device__ __forceinline__ uint4 fp8_cv(uint4 r) {
                     as_u32(fp8x2_to_bf16<false>(r.y, 1.0f)), as_u32(fp8x2_to_bf16<true>(r.y, 1.0f)));
 }
 
+// MXFP4: 8 E2M1 codes (4 bytes) and their block's E8M0 scale; converted to 8 BF16
+// (v * 2^e, exact: E2M1 values times a power of two fit BF16 down to its subnormals).
+__device__ __forceinline__ uint4 mxfp4_ld(const uint8_t* codes, const uint8_t* scales, int el) {
+  return make_uint4(*reinterpret_cast<const uint32_t*>(codes + (el >> 1)), scales[el >> 5], 0u, 0u);
+}
+__device__ __forceinline__ uint4 mxfp4_cv(uint4 r) {
+  const float sc = e8m0_to_f32(r.y);
+  return make_uint4(as_u32(fp4x2_to_bf16<0>(r.x, sc)), as_u32(fp4x2_to_bf16<1>(r.x, sc)),
+                    as_u32(fp4x2_to_bf16<2>(r.x, sc)), as_u32(fp4x2_to_bf16<3>(r.x, sc)));
+}
+// MXFP8: 8 E4M3 codes and their block's E8M0 scale; converted to 8 BF16 (exact but for
+// E4M3 subnormals scaled below BF16's smallest subnormal, 2^-133).
+__device__ __forceinline__ uint4 mxfp8_ld(const uint8_t* codes, const uint8_t* scales, int el) {
+  const uint2 w = *reinterpret_cast<const uint2*>(codes + el);
+  return make_uint4(w.x, w.y, scales[el >> 5], 0u);
+}
+__device__ __forceinline__ uint4 mxfp8_cv(uint4 r) {
+  const float sc = e8m0_to_f32(r.z);
+  return make_uint4(as_u32(fp8x2_to_bf16<false>(r.x, sc)), as_u32(fp8x2_to_bf16<true>(r.x, sc)),
+                    as_u32(fp8x2_to_bf16<false>(r.y, sc)), as_u32(fp8x2_to_bf16<true>(r.y, sc)));
+}
+
 // ================================================================ gate/up kernel
 // Gate/up rows: at row-step s, lane row slot lrow is intermediate index
 // i = s * PS + lrow (PS = 4 * G pairs per step); the lane holds gate row i (q = 0) and
@@ -885,15 +907,21 @@ struct GateupOps {
       return nvfp4_ld(xq_codes + (int64_t)t * (H / 2), xq_scales + (int64_t)t * (H / 16), el);
     else if constexpr (AF == A_FP8_TOKEN)
       return fp8_ld(xq_codes + (int64_t)t * H, el);
+    else if constexpr (AF == A_MXFP4)
+      return mxfp4_ld(xq_codes + (int64_t)t * (H / 2), xq_scales + (int64_t)t * (H / 32), el);
+    else if constexpr (AF == A_MXFP8)
+      return mxfp8_ld(xq_codes + (int64_t)t * H, xq_scales + (int64_t)t * (H / 32), el);
     else
       return ld16(x + (int64_t)t * H + el);
   }
   __device__ __forceinline__ uint4 cv(uint4 r) const {
     if constexpr (AF == A_NVFP4_4O6) return nvfp4_cv(r);
     else if constexpr (AF == A_FP8_TOKEN) return fp8_cv(r);
+    else if constexpr (AF == A_MXFP4) return mxfp4_cv(r);
+    else if constexpr (AF == A_MXFP8) return mxfp8_cv(r);
     else return r;
   }
-  __device__ __forceinline__ float tsc(int t, int) const { return AF == A_BF16 ? 1.0f : xq_scale[t]; }
+  __device__ __forceinline__ float tsc(int t, int) const { return afmt_row_scaled(AF) ? xq_scale[t] : 1.0f; }
   __device__ __forceinline__ float gs(int e, int q) const {
     return gscale ? gscale[(int64_t)e * gs_per_expert + q] : 1.0f;
   }
@@ -1000,6 +1028,10 @@ struct DownOps {
       return nvfp4_ld(hq_codes + (int64_t)p * (Kexp / 2), hq_scales + (int64_t)p * (Kexp / 16), el);
     else if constexpr (AF == A_FP8_TOKEN)
       return fp8_ld(hq_codes + (int64_t)p * Kexp, el);
+    else if constexpr (AF == A_MXFP4)
+      return mxfp4_ld(hq_codes + (int64_t)p * (Kexp / 2), hq_scales + (int64_t)p * (Kexp / 32), el);
+    else if constexpr (AF == A_MXFP8)
+      return mxfp8_ld(hq_codes + (int64_t)p * Kexp, hq_scales + (int64_t)p * (Kexp / 32), el);
     else if (h_bf16)   // BF16 rows at the byte positions of FP32 rows
       return ld16(reinterpret_cast<const uint16_t*>(hf) + (int64_t)p * (2 * hs) + el);
     else
@@ -1008,9 +1040,11 @@ struct DownOps {
   __device__ __forceinline__ uint4 cv(uint4 r) const {
     if constexpr (AF == A_NVFP4_4O6) return nvfp4_cv(r);
     else if constexpr (AF == A_FP8_TOKEN) return fp8_cv(r);
+    else if constexpr (AF == A_MXFP4) return mxfp4_cv(r);
+    else if constexpr (AF == A_MXFP8) return mxfp8_cv(r);
     else return r;
   }
-  __device__ __forceinline__ float tsc(int, int p) const { return AF == A_BF16 ? 1.0f : hq_scale[p]; }
+  __device__ __forceinline__ float tsc(int, int p) const { return afmt_row_scaled(AF) ? hq_scale[p] : 1.0f; }
   __device__ __forceinline__ float gs(int e, int q) const {
     return (q == 0 && gscale) ? gscale[(int64_t)e * gs_per_expert] : 1.0f;
   }
@@ -1306,6 +1340,10 @@ hipError_t launch_experts_t(const ExpertArgs& gu, int gu_grid, size_t gu_lds,
   if constexpr (RF == W_MXFP4 || RF == W_MXFP8) {
     if (gu.afmt == A_FP8_TOKEN)
       return launch_experts_af<RF, SF, A_FP8_TOKEN>(gu, gu_grid, gu_lds, dn, dn_grid, dn_lds, s);
+    if (gu.afmt == A_MXFP4)
+      return launch_experts_af<RF, SF, A_MXFP4>(gu, gu_grid, gu_lds, dn, dn_grid, dn_lds, s);
+    if (gu.afmt == A_MXFP8)
+      return launch_experts_af<RF, SF, A_MXFP8>(gu, gu_grid, gu_lds, dn, dn_grid, dn_lds, s);
   }
   return hipErrorInvalidValue;
 }

@@ -5,7 +5,10 @@
 namespace moe {
 
 enum WFmt : int { W_BF16 = 0, W_NVFP4 = 1, W_MXFP4 = 2, W_MXFP8 = 3 };
-enum AFmt : int { A_BF16 = 0, A_NVFP4_4O6 = 1, A_FP8_TOKEN = 2 };
+enum AFmt : int { A_BF16 = 0, A_NVFP4_4O6 = 1, A_FP8_TOKEN = 2, A_MXFP4 = 3, A_MXFP8 = 4 };
+
+// Activation formats with one FP32 scale per row (the rest carry E8M0 scales per 32).
+inline constexpr bool afmt_row_scaled(int af) { return af == A_NVFP4_4O6 || af == A_FP8_TOKEN; }
 
 // Elements one lane reads per 16-byte weight load.
 inline constexpr int elems_per_piece(int fmt) {

@@ -31,26 +31,10 @@ __global__ void __launch_bounds__(kBlock) requant_mxfp4_kernel(const uint16_t* x
       v[8 * q + 2 * i + 1] = bf16_to_f32(w[i] >> 16);
     }
   }
-  float amax = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
-  // floor(log2(amax)) = frexp exponent - 1 (amax = m * 2^e, m in [0.5, 1)), then - 2
-  int e = amax > 0.0f ? __builtin_amdgcn_frexp_expf(amax) - 3 : -127;
-  e = min(max(e, -127), 127);
-  // the hardware convert: two elements over the scale 2^e per instruction
-  const float sc = __builtin_bit_cast(float, (uint32_t)(e + 127) << 23 | (e == -127 ? 0x00400000u : 0u));
-  uint32_t w[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    uint32_t r = 0u;
-    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[8 * q + 0], v[8 * q + 1], sc, 0);
-    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[8 * q + 2], v[8 * q + 3], sc, 1);
-    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[8 * q + 4], v[8 * q + 5], sc, 2);
-    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[8 * q + 6], v[8 * q + 7], sc, 3);
-    w[q] = r;
-  }
+  uint32_t w[4];
+  const uint32_t sb = mx_block_fp4(v, w);
   *reinterpret_cast<uint4*>(codes + 16 * b) = make_uint4(w[0], w[1], w[2], w[3]);
-  scales[b] = (uint8_t)(e + 127);
+  scales[b] = (uint8_t)sb;
 }
 
 // NVFP4 in three launches over tensors of n elements (n % 16 == 0), in stream order, so
@@ -163,21 +147,12 @@ __global__ void __launch_bounds__(kBlock) requant_mxfp8_kernel(const uint16_t* x
       v[8 * q + 2 * i + 1] = bf16_to_f32(w[i] >> 16);
     }
   }
-  float amax = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
-  int e = amax > 0.0f ? __builtin_amdgcn_frexp_expf(amax) - 9 : -127;
-  e = min(max(e, -127), 127);
-  uint32_t w[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
-#pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    const float y = ldexpf(v[i], -e);
-    w[i >> 2] |= (e4m3_encode_pos(fabsf(y)) | ((__float_as_uint(y) >> 24) & 0x80u)) << (8 * (i & 3));
-  }
+  uint32_t w[8];
+  const uint32_t sb = mx_block_fp8(v, w);
   uint4* dst = reinterpret_cast<uint4*>(codes + 32 * b);
   dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
   dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
-  scales[b] = (uint8_t)(e + 127);
+  scales[b] = (uint8_t)sb;
 }
 
 hipError_t launch_requant_mxfp8(const uint16_t* x, int64_t nblocks, uint8_t* codes, uint8_t* scales,

@@ -23,7 +23,8 @@ quantize_nvfp4_kernel(const uint16_t* x, int cols, uint8_t* codes, uint8_t* scal
 // ======================================================================== route
 // Router GEMV: workgroups tile (tokens x experts); each of the 4 waves reduces a quarter
 // of H, the partial sums meet in LDS in a fixed order. Extra workgroups (one per token)
-// quantize the tokens in the same launch when the layer quantizes x.
+// quantize the tokens in the same launch when the layer quantizes x (Four-Over-Six
+// NVFP4, FP8 per token, MXFP4 or MXFP8).
 template <int ET, int TT>
 __global__ void __launch_bounds__(kBlock) route_gemv_kernel(RouteArgs a) {
   __shared__ float red[(kBlock / kWave) * ET * TT];
@@ -35,8 +36,12 @@ __global__ void __launch_bounds__(kBlock) route_gemv_kernel(RouteArgs a) {
     if (a.afmt == A_NVFP4_4O6) {
       quant_row_nvfp4(row, a.H, a.xq_codes + (int64_t)t * (a.H / 2),
                       a.xq_scales + (int64_t)t * (a.H / 16), a.xq_scale + t, nullptr, red);
-    } else {
+    } else if (a.afmt == A_FP8_TOKEN) {
       quant_row_fp8(row, a.H, a.xq_codes + (int64_t)t * a.H, a.xq_scale + t, red);
+    } else if (a.afmt == A_MXFP4) {
+      quant_row_mx<false>(row, a.H, a.xq_codes + (int64_t)t * (a.H / 2), a.xq_scales + (int64_t)t * (a.H / 32));
+    } else {
+      quant_row_mx<true>(row, a.H, a.xq_codes + (int64_t)t * a.H, a.xq_scales + (int64_t)t * (a.H / 32));
     }
     return;
   }

@@ -90,4 +90,30 @@ __device__ __forceinline__ void quant_row_fp8(const Row& row, int n, uint8_t* co
   if (threadIdx.x == 0) *sout = s;
 }
 
+// OCP MX (MXFP4 or MXFP8) of one row of n elements (n % 32 == 0), whole workgroup: one
+// thread per 32-block (mx_block_fp4 / mx_block_fp8). Codes [n/2] or [n] bytes, E8M0
+// scales [n/32]. Blocks are independent: no row-wide reduction.
+template <bool FP8, class Row>
+__device__ __forceinline__ void quant_row_mx(const Row& row, int n, uint8_t* codes, uint8_t* scales) {
+  const int nb = n >> 5;
+  for (int b = threadIdx.x; b < nb; b += kBlock) {
+    float v[32], lo[16], hi[16];
+    row.load(2 * b, lo);
+    row.load(2 * b + 1, hi);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) { v[i] = lo[i]; v[16 + i] = hi[i]; }
+    if constexpr (FP8) {
+      uint32_t w[8];
+      scales[b] = (uint8_t)mx_block_fp8(v, w);
+      uint4* dst = reinterpret_cast<uint4*>(codes + 32 * b);
+      dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
+      dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
+    } else {
+      uint32_t w[4];
+      scales[b] = (uint8_t)mx_block_fp4(v, w);
+      *reinterpret_cast<uint4*>(codes + 16 * b) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+  }
+}
+
 }  // namespace moe

@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 3
+#define MOE_ABI_VERSION 4
 
 typedef enum {
   MOE_OK = 0,
@@ -69,7 +69,13 @@ typedef enum {
   MOE_A_BF16 = 0,        /* x used as given (BF16); h kept in FP32                      */
   MOE_A_NVFP4_4O6 = 1,   /* NVFP4 with a per-row FP32 global scale amax/2688 and a
                             Four-Over-Six E4M3 scale per 16 elements (NVFP4 weights only) */
-  MOE_A_FP8_TOKEN = 2    /* FP8-E4M3 with one FP32 scale amax/448 per row (MX weights)  */
+  MOE_A_FP8_TOKEN = 2,   /* FP8-E4M3 with one FP32 scale amax/448 per row (MX weights)  */
+  MOE_A_MXFP4 = 3,       /* OCP MXFP4 (a4w4): E2M1 with one E8M0 scale per 32 elements,
+                            shared exponent floor(log2(block amax)) - 2 (MX weights; the
+                            Mistral Large 4 page's ROCm specialized decode runs a4w4)      */
+  MOE_A_MXFP8 = 4        /* OCP MXFP8: E4M3 with one E8M0 scale per 32, exponent
+                            floor(log2(block amax)) - 8 (MX weights; the Inkling page's
+                            MXFP8 layers quantize activations to their own format)       */
 } moe_afmt_t;
 
 /* How the router turns the selected logits into combine weights (the experts are always
@@ -116,6 +122,8 @@ typedef struct {
 /* Layout of the quantized-token buffer `xq` for T tokens (see moe_xq_bytes):
  *   MOE_A_NVFP4_4O6: codes [T][H/2] | scales E4M3 [T][H/16] | g FP32 [T]
  *   MOE_A_FP8_TOKEN: codes E4M3 [T][H] | s FP32 [T]
+ *   MOE_A_MXFP4:     codes E2M1 [T][H/2] (element 2i in the low nibble) | scales E8M0 [T][H/32]
+ *   MOE_A_MXFP8:     codes E4M3 [T][H] | scales E8M0 [T][H/32]
  * Each part starts at a 256-byte boundary from the start of xq. */
 
 /* Optional per-call debug outputs and controls of moe_expert_forward (any pointer may
@@ -124,9 +132,10 @@ typedef struct {
 typedef enum { MOE_PATH_AUTO = 0, MOE_PATH_GEMV = 1, MOE_PATH_GROUPED = 2 } moe_path_t;
 typedef struct {
   float *h;             /* FP32 [T*k + T*has_shared][max(I, I_shared)]: SwiGLU outputs   */
-  uint8_t *hq_codes;    /* quantized routed h: NVFP4 [T*k][I/2] or FP8 [T*k][I]           */
-  uint8_t *hq_scales;   /* NVFP4: E4M3 [T*k][I/16]                                        */
-  float *hq_scale;      /* NVFP4: g [T*k]; FP8: s [T*k]                                   */
+  uint8_t *hq_codes;    /* quantized routed h: NVFP4 / MXFP4 [T*k][I/2], FP8 / MXFP8
+                           [T*k][I]                                                       */
+  uint8_t *hq_scales;   /* NVFP4: E4M3 [T*k][I/16]; MX: E8M0 [T*k][I/32]                  */
+  float *hq_scale;      /* NVFP4: g [T*k]; FP8 per token: s [T*k]; MX: unused             */
   int32_t path;         /* moe_path_t: which expert kernels run. AUTO picks the grouped
                            (MFMA, 32 tokens per unit) kernels from 32 tokens on when units
                            hold many tokens (a shared expert, or T*k >= E), else the GEMV

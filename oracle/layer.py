@@ -10,6 +10,12 @@ What the layer computes, as the pages describe it:
 * "Inkling 2 Small on vLLM: Day-0 Support", MoE with fused activation quantization:
   the token is quantized before the gate/up projection and the SwiGLU output is
   quantized before the down projection (NVFP4 or MXFP8, matching the layer);
+* "Day 0 support for Mistral Large 4 on vLLM", AMD section and ROCm implementation
+  details: MXFP4 experts run with FP8 activations (a8w4) or, in the latency-specialized
+  decode, with MXFP4 activations (a4w4); the Inkling page's MXFP8 expert layers quantize
+  their activations to MXFP8. The MX activation formats follow the OCP MX v1.0 rule of
+  oracle/quant.py (one E8M0 scale per 32 elements, floor(log2(block amax)) minus the
+  element format's largest exponent), applied to each 32-block of a row;
 * a shared expert is added to the routed mix with weight one (Flint and Mistral
   Large 4 architecture sections).
 
@@ -19,8 +25,9 @@ Plain definition, for token t with selected experts e_j and weights w_j:
     MLP(v) = W2 @ Q_h(silu(Wg @ v) * (Wu @ v)),   silu(z) = z / (1 + exp(-z))
 
 W* are the dequantized weights (FP64, exact). xhat and Q_h are identities except with
-NVFP4 Four-Over-Six activations (both projections' inputs quantized per row) and FP8
-per-token activations (likewise). The shared expert always sees the unquantized BF16
+NVFP4 Four-Over-Six activations (both projections' inputs quantized per row), FP8
+per-token activations (likewise), and MXFP4 / MXFP8 activations (both inputs quantized
+per 32-block). The shared expert always sees the unquantized BF16
 token and an unquantized SwiGLU output. "Soft-capped" SwiGLU is named on the Inkling
 page without a constant; no cap is applied.
 """
@@ -30,10 +37,11 @@ import numpy as np
 
 from .formats import bf16_to_f64
 from .quant import (dequant_fp8_token, dequant_nvfp4_rows, dequant_weights,
-                    quantize_fp8_token, quantize_nvfp4_4o6)
+                    quantize_fp8_token, quantize_mxfp4, quantize_mxfp8, quantize_nvfp4_4o6)
 from .router import ambiguous_tokens, route
 
 A_BF16, A_NVFP4_4O6, A_FP8_TOKEN = "bf16", "nvfp4_4o6", "fp8_token"
+A_MXFP4, A_MXFP8 = "mxfp4", "mxfp8"
 
 
 def silu(z: np.ndarray) -> np.ndarray:
@@ -53,6 +61,9 @@ def quantize_rows(afmt: str, v32: np.ndarray):
     if afmt == A_FP8_TOKEN:
         codes, s = quantize_fp8_token(v32)
         return dequant_fp8_token(codes, s), {"codes": codes, "s": s}
+    if afmt in (A_MXFP4, A_MXFP8):
+        codes, sc = (quantize_mxfp4 if afmt == A_MXFP4 else quantize_mxfp8)(v32)
+        return dequant_weights(afmt, codes, sc, None), {"codes": codes, "scales": sc}
     return np.asarray(v32, dtype=np.float64), {}
 
 

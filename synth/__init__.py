@@ -35,6 +35,7 @@ SEED_TAG = 0x4F36
 W_BF16, W_NVFP4, W_MXFP4, W_MXFP8 = "bf16", "nvfp4", "mxfp4", "mxfp8"
 # Formats the routed experts' activations are quantized to before each projection.
 A_BF16, A_NVFP4_4O6, A_FP8_TOKEN = "bf16", "nvfp4_4o6", "fp8_token"
+A_MXFP4, A_MXFP8 = "mxfp4", "mxfp8"
 
 # Expected rms of decode(E2M1 uniform over its 16 codes) * decode(E4M3 scale drawn
 # log-uniform on [2^-8, 2^-2]): E[v^2] = 68.5/8 and E[S^2] = (2^-4 - 2^-16)/(12 ln 2).
@@ -95,6 +96,16 @@ CONFIGS: Dict[str, LayerConfig] = {
     "mistral_mxfp4_a8": LayerConfig("mistral_mxfp4_a8", 6, H=6144, I=2048, E=128, k=4,
                                     has_shared=True, wfmt=W_MXFP4, shared_wfmt=W_BF16,
                                     afmt=A_FP8_TOKEN, batches=(1, 8, 64)),
+    # The Mistral-shaped layer's draws with OCP MXFP4 activations on the routed experts
+    # (a4w4, the ROCm specialized decode of the Mistral Large 4 page).
+    "mistral_mxfp4_a4": LayerConfig("mistral_mxfp4_a4", 4, H=6144, I=2048, E=128, k=4,
+                                    has_shared=True, wfmt=W_MXFP4, shared_wfmt=W_BF16,
+                                    afmt=A_MXFP4, batches=(1, 8, 64)),
+    # Inkling's MXFP8 expert layers with their activations quantized to MXFP8 as well
+    # (the Inkling page: fused activation quantization matching each layer's format).
+    "inkling_mxfp8_a8": LayerConfig("inkling_mxfp8_a8", 5, H=4096, I=1536, E=384, k=8,
+                                    has_shared=False, wfmt=W_MXFP8, shared_wfmt=W_MXFP8,
+                                    afmt=A_MXFP8, batches=(1, 8, 32)),
     # Softmax top-k routing (the router of the Mistral Large 4 page's ROCm decode) on the
     # Mistral-shaped layer: the same draws as mistral_mxfp4.
     "mistral_mxfp4_softmax": LayerConfig("mistral_mxfp4_softmax", 4, H=6144, I=2048, E=128, k=4,

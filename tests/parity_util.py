@@ -105,6 +105,8 @@ def gpu_hq_rows(dbg: dict, afmt: str, pairs) -> np.ndarray:
     if afmt == "nvfp4_4o6":
         return OQ.dequant_nvfp4_rows(codes, dbg["hq_scales"].cpu().numpy()[pairs],
                                      dbg["hq_scale"].cpu().numpy()[pairs])
+    if afmt in ("mxfp4", "mxfp8"):
+        return OQ.dequant_weights(afmt, codes, dbg["hq_scales"].cpu().numpy()[pairs], None)
     return OQ.dequant_fp8_token(codes, dbg["hq_scale"].cpu().numpy()[pairs])
 
 

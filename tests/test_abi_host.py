@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol(lib):
     so = ctypes.CDLL(lib.LIB_PATH)
     for n in _declared_functions():
         assert hasattr(so, n), n
-    assert so.moe_abi_version() == 3
+    assert so.moe_abi_version() == 4
 
 
 def _fake_layer(lib, name, **over):

@@ -10,7 +10,8 @@ from parity_util import device_layer, say
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("name,T", [("flint_w4a16", 4), ("inkling_w4a4", 3), ("mistral_mxfp4_a8", 2)])
+@pytest.mark.parametrize("name,T", [("flint_w4a16", 4), ("inkling_w4a4", 3), ("mistral_mxfp4_a8", 2),
+                                    ("mistral_mxfp4_a4", 3)])
 def test_graph_replays_match_eager(lib, name, T):
     say(f"[graph] {name} T={T}")
     dl = device_layer(name)

@@ -68,6 +68,41 @@ def check_router(name, ws, x_np, ids_g, w_g):
     return float(np.max(gam * S))
 
 
+# the oracle's stored fields of each activation format, and where the GPU keeps them:
+# token fields in lib.split_xq, h fields in the debug outputs
+XQ_FIELDS = {"nvfp4_4o6": {"codes": "codes", "scales": "scales", "g": "g"},
+             "fp8_token": {"codes": "codes", "s": "s"},
+             "mxfp4": {"codes": "codes", "scales": "scales"},
+             "mxfp8": {"codes": "codes", "scales": "scales"}}
+HQ_FIELDS = {"nvfp4_4o6": {"codes": "hq_codes", "scales": "hq_scales", "g": "hq_scale"},
+             "fp8_token": {"codes": "hq_codes", "s": "hq_scale"},
+             "mxfp4": {"codes": "hq_codes", "scales": "hq_scales"},
+             "mxfp8": {"codes": "hq_codes", "scales": "hq_scales"}}
+
+
+def _bits(a: np.ndarray) -> np.ndarray:
+    a = np.ascontiguousarray(a)
+    return a.view(np.uint32) if a.dtype == np.float32 else a
+
+
+def check_fields(afmt: str, v32: np.ndarray, gpu: dict, names: dict, rows=None):
+    """The oracle's quantizer on FP32 rows v32 against the GPU's stored fields, bit for bit."""
+    from oracle import layer as OL
+    ref = OL.quantize_rows(afmt, v32)[1]
+    for key, gkey in names.items():
+        g = gpu[gkey].cpu().numpy()
+        if rows is not None:
+            g = g[rows]
+        assert np.array_equal(_bits(g), _bits(ref[key])), (afmt, key)
+
+
+def code_diffs(afmt: str, a: np.ndarray, b: np.ndarray) -> int:
+    """Elements whose codes differ (nibbles for the 4-bit formats, bytes otherwise)."""
+    if afmt in ("nvfp4_4o6", "mxfp4"):
+        return int(np.sum((a & 0x0F) != (b & 0x0F)) + np.sum((a >> 4) != (b >> 4)))
+    return int(np.sum(a != b))
+
+
 def _x_dev(x_np):
     return torch.from_numpy(x_np.view(np.int16)).cuda()
 
@@ -141,6 +176,8 @@ LAYER_CASES = [
     ("inkling_mxfp8", [1, 8]),
     ("mistral_mxfp4", [1, 8]),
     ("mistral_mxfp4_a8", [1, 8]),
+    ("mistral_mxfp4_a4", [1, 3, 8]),
+    ("inkling_mxfp8_a8", [1, 5, 8]),
     ("tiny_softmax_selbias", [1, 3]),
     ("mistral_mxfp4_softmax", [1, 8]),
     ("flint_bf16_selbias", [1, 8]),
@@ -164,7 +201,7 @@ def _run_layer(lib, name, T, debug=True, path=0):
 # the grouped (MFMA) kernels forced at small, ragged batches, every weight format
 GROUPED_SMALL = [("tiny_bf16", 3), ("flint_w4a16", 8), ("flint_bf16", 5), ("inkling_w4a4", 5),
                  ("inkling_mxfp8", 8), ("mistral_mxfp4", 3), ("mistral_mxfp4_a8", 8), ("edge_k16_e16", 3),
-                 ("edge_e1024", 5)]
+                 ("edge_e1024", 5), ("mistral_mxfp4_a4", 5), ("inkling_mxfp8_a8", 3)]
 
 
 @pytest.mark.parametrize("name,T,path", [(n, t, 0) for n, ts in LAYER_CASES for t in ts] +
@@ -182,13 +219,8 @@ def test_layer_parity(lib, name, T, path):
     # quantized tokens: bit-exact
     if cfg.afmt != "bf16":
         parts = lib.split_xq(dl, xq, T)
-        if cfg.afmt == "nvfp4_4o6":
-            assert np.array_equal(parts["codes"].cpu().numpy(), ref["xq"]["codes"])
-            assert np.array_equal(parts["scales"].cpu().numpy(), ref["xq"]["scales"])
-            assert np.array_equal(parts["g"].cpu().numpy().view(np.uint32), ref["xq"]["g"].view(np.uint32))
-        else:
-            assert np.array_equal(parts["codes"].cpu().numpy(), ref["xq"]["codes"])
-            assert np.array_equal(parts["s"].cpu().numpy().view(np.uint32), ref["xq"]["s"].view(np.uint32))
+        for key, gkey in XQ_FIELDS[cfg.afmt].items():
+            assert np.array_equal(_bits(parts[gkey].cpu().numpy()), _bits(ref["xq"][key])), key
     # SwiGLU outputs: FP32 vs FP64, same routing
     h_g = dbg["h"].cpu().numpy().astype(np.float64)
     if np.array_equal(ids_g, ref["ids"]):
@@ -198,15 +230,7 @@ def test_layer_parity(lib, name, T, path):
     # quantized h: bit-exact when the oracle quantizes the GPU's own h
     if cfg.afmt != "bf16":
         h32 = dbg["h"].cpu().numpy()[:T * cfg.k, :cfg.I]
-        if cfg.afmt == "nvfp4_4o6":
-            rc, rs, rg, _ = OQ.quantize_nvfp4_4o6(h32)
-            assert np.array_equal(dbg["hq_codes"].cpu().numpy(), rc)
-            assert np.array_equal(dbg["hq_scales"].cpu().numpy(), rs)
-            assert np.array_equal(dbg["hq_scale"].cpu().numpy().view(np.uint32), rg.view(np.uint32))
-        else:
-            rc, rs = OQ.quantize_fp8_token(h32)
-            assert np.array_equal(dbg["hq_codes"].cpu().numpy(), rc)
-            assert np.array_equal(dbg["hq_scale"].cpu().numpy().view(np.uint32), rs.view(np.uint32))
+        check_fields(cfg.afmt, h32, dbg, HQ_FIELDS[cfg.afmt])
     # layer output against the oracle's own y
     if np.array_equal(ids_g, ref["ids"]):
         check_y_own(name, cfg, T, x_np, ref, bf16_bits_to_f64(y), dbg)
@@ -225,17 +249,12 @@ def check_y_own(name, cfg, T, x_np, ref, y_gpu, dbg):
     if ok:
         return
     assert cfg.afmt != "bf16", (max_abs, rel)
+    from oracle import layer as OL
     P = T * cfg.k
     h_gpu = dbg["h"].cpu().numpy()[:P, :cfg.I]
     h_own = ref["h"].reshape(P, cfg.I).astype(np.float32)
-    if cfg.afmt == "nvfp4_4o6":
-        c_gpu = OQ.quantize_nvfp4_4o6(h_gpu)[0]
-        c_own = OQ.quantize_nvfp4_4o6(h_own)[0]
-        diff = int(np.sum((c_gpu & 0x0F) != (c_own & 0x0F)) + np.sum((c_gpu >> 4) != (c_own >> 4)))
-    else:
-        c_gpu = OQ.quantize_fp8_token(h_gpu)[0]
-        c_own = OQ.quantize_fp8_token(h_own)[0]
-        diff = int(np.sum(c_gpu != c_own))
+    diff = code_diffs(cfg.afmt, OL.quantize_rows(cfg.afmt, h_gpu)[1]["codes"],
+                      OL.quantize_rows(cfg.afmt, h_own)[1]["codes"])
     total = P * cfg.I
     hq = gpu_hq_rows(dbg, cfg.afmt, np.arange(P)).reshape(T, cfg.k, cfg.I)
     y_codes = oracle_y_given_hq(name, x_np, ref["ids"], ref["w"], hq)
@@ -253,6 +272,7 @@ FORWARD_CASES = [("tiny_bf16", 1), ("tiny_bf16", 8), ("flint_w4a16", 1), ("flint
                  ("flint_w4a16", 3), ("flint_w4a16", 4), ("flint_w4a16", 8), ("flint_w4a16", 10),
                  ("flint_w4a16", 16), ("flint_bf16", 8), ("inkling_w4a4", 8),
                  ("inkling_mxfp8", 5), ("mistral_mxfp4", 16), ("mistral_mxfp4_a8", 8),
+                 ("mistral_mxfp4_a4", 8), ("inkling_mxfp8_a8", 8),
                  ("tiny_softmax_selbias", 8), ("mistral_mxfp4_softmax", 8), ("flint_bf16_selbias", 8),
                  ("flint_bf16_selbias", 16), ("edge_k1_e5", 7), ("edge_k16_e16", 3), ("edge_e1024", 5)]
 
@@ -301,6 +321,8 @@ LARGE_CASES = [
     ("inkling_mxfp8", 32),
     ("mistral_mxfp4", 64),
     ("mistral_mxfp4_a8", 64),
+    ("mistral_mxfp4_a4", 64),
+    ("inkling_mxfp8_a8", 32),
 ]
 
 
@@ -323,17 +345,8 @@ def test_layer_parity_large_batch(lib, name, T, path):
     assert not bad, f"top-k mismatch on tokens {bad}"
     dl_max = check_router(name, ws, x_np, ids_g, w.cpu().numpy())
     check_w(w.cpu().numpy(), ref["w"], np.all(ids_g == ref["ids"], axis=1), W_RTOL + 2 * dl_max)
-    if cfg.afmt == "nvfp4_4o6":
-        rc, rs, rg, _ = OQ.quantize_nvfp4_4o6(synth_bf16_to_f32(x_np))
-        parts = lib.split_xq(dl, xq, T)
-        assert np.array_equal(parts["codes"].cpu().numpy(), rc)
-        assert np.array_equal(parts["scales"].cpu().numpy(), rs)
-        assert np.array_equal(parts["g"].cpu().numpy().view(np.uint32), rg.view(np.uint32))
-    elif cfg.afmt == "fp8_token":
-        rc, rs = OQ.quantize_fp8_token(synth_bf16_to_f32(x_np))
-        parts = lib.split_xq(dl, xq, T)
-        assert np.array_equal(parts["codes"].cpu().numpy(), rc)
-        assert np.array_equal(parts["s"].cpu().numpy().view(np.uint32), rs.view(np.uint32))
+    if cfg.afmt != "bf16":
+        check_fields(cfg.afmt, synth_bf16_to_f32(x_np), lib.split_xq(dl, xq, T), XQ_FIELDS[cfg.afmt])
     sample = sorted({0, T // 3, (2 * T) // 3, T - 1})
     sample = [t for t in sample if np.array_equal(ids_g[t], ref["ids"][t])]
     assert sample, "no sampled token routed like the oracle"
@@ -354,20 +367,10 @@ def test_layer_parity_large_batch(lib, name, T, path):
         # the GPU's h codes of the sampled tokens: bit-exact against the oracle's quantizer
         # fed the GPU's h
         h32 = dbg["h"].cpu().numpy()[pairs, :cfg.I]
-        if cfg.afmt == "nvfp4_4o6":
-            rc, rs, rg, _ = OQ.quantize_nvfp4_4o6(h32)
-            assert np.array_equal(dbg["hq_scales"].cpu().numpy()[pairs], rs)
-        else:
-            rc, rg = OQ.quantize_fp8_token(h32)
-        assert np.array_equal(dbg["hq_codes"].cpu().numpy()[pairs], rc)
-        assert np.array_equal(dbg["hq_scale"].cpu().numpy()[pairs].view(np.uint32), rg.view(np.uint32))
+        check_fields(cfg.afmt, h32, dbg, HQ_FIELDS[cfg.afmt], rows=pairs)
         if not ok:   # a miss must be the few codes FP32 and FP64 h round differently
-            h_own = h_r.astype(np.float32)
-            if cfg.afmt == "nvfp4_4o6":
-                c_own = OQ.quantize_nvfp4_4o6(h_own)[0]
-                diff = int(np.sum((rc & 0x0F) != (c_own & 0x0F)) + np.sum((rc >> 4) != (c_own >> 4)))
-            else:
-                diff = int(np.sum(rc != OQ.quantize_fp8_token(h_own)[0]))
+            diff = code_diffs(cfg.afmt, OL.quantize_rows(cfg.afmt, h32)[1]["codes"],
+                              OL.quantize_rows(cfg.afmt, h_r.astype(np.float32))[1]["codes"])
             hq = gpu_hq_rows(dbg, cfg.afmt, pairs).reshape(len(sample), cfg.k, cfg.I)
             y_codes = oracle_y_given_hq(name, x_np[sample], own["ids"], own["w"], hq)
             ok2, ma2, rel2 = y_close(yg, y_codes)

@@ -145,32 +145,49 @@ def test_single_expert_plus_shared():
         assert np.allclose(out["y"][t], want, rtol=1e-13, atol=1e-15)
 
 
-@pytest.mark.parametrize("afmt", ["nvfp4_4o6", "fp8_token"])
+def _mx_decode(codes, scales, elem):
+    """MX rows by hand: E2M1 nibbles (element 2i low) or E4M3 bytes, times 2^(byte - 127)
+    of each 32-block's E8M0 scale."""
+    from oracle import formats as F
+    if elem == "fp4":
+        q = np.stack([codes & 0x0F, codes >> 4], axis=-1).reshape(codes.shape[0], -1)
+        v = np.array([F.e2m1_value(int(c)) for c in range(16)])[q]
+    else:
+        v = np.array([F.e4m3_value(int(b)) for b in range(256)])[codes]
+    return v * np.repeat(2.0 ** (scales.astype(np.float64) - 127.0), 32, axis=-1)
+
+
+WFMT_OF = {"nvfp4_4o6": "nvfp4", "fp8_token": "mxfp4", "mxfp4": "mxfp4", "mxfp8": "mxfp8"}
+
+
+def _quant_dequant(afmt, v32):
+    if afmt == "nvfp4_4o6":
+        c_, s_, g_, _ = Q.quantize_nvfp4_4o6(v32)
+        return Q.dequant_nvfp4_rows(c_, s_, g_)[0]
+    if afmt == "fp8_token":
+        c_, s_ = Q.quantize_fp8_token(v32)
+        return Q.dequant_fp8_token(c_, s_)[0]
+    c_, s_ = (Q.quantize_mxfp4 if afmt == "mxfp4" else Q.quantize_mxfp8)(v32)
+    return _mx_decode(c_, s_, "fp4" if afmt == "mxfp4" else "fp8")[0]
+
+
+@pytest.mark.parametrize("afmt", ["nvfp4_4o6", "fp8_token", "mxfp4", "mxfp8"])
 def test_quantized_activations_feed_both_projections(afmt):
     """Routed experts see quantize(x) before gate/up and quantize(h) before down; the
-    shared expert sees BF16 x and an unquantized h."""
-    layer, closed, shared = _build("nvfp4" if afmt == "nvfp4_4o6" else "mxfp4", "bf16", afmt, E, E,
-                                   seed=6)
+    shared expert sees BF16 x and an unquantized h. MX formats: MXFP4 activations (a4w4)
+    on MXFP4 experts, MXFP8 activations on MXFP8 experts."""
+    layer, closed, shared = _build(WFMT_OF[afmt], "bf16", afmt, E, E, seed=6)
     x = synth.to_bf16_bits(np.random.default_rng(3).normal(size=(2, H)) * 3)
     out = OL.moe_layer(layer, x)
     xv = bf16_to_f64(x)
     for t in range(2):
         x32 = xv[t:t + 1].astype(np.float32)
-        if afmt == "nvfp4_4o6":
-            c_, s_, g_, _ = Q.quantize_nvfp4_4o6(x32)
-            xhat = Q.dequant_nvfp4_rows(c_, s_, g_)[0]
-        else:
-            c_, s_ = Q.quantize_fp8_token(x32)
-            xhat = Q.dequant_fp8_token(c_, s_)[0]
+        xhat = _quant_dequant(afmt, x32)
+        assert not np.array_equal(xhat, xv[t])            # the quantization is not a no-op
         want = np.zeros(H)
         for c in closed:
             h = _closed_h(c, xhat)[None].astype(np.float32)
-            if afmt == "nvfp4_4o6":
-                hc, hs, hg, _ = Q.quantize_nvfp4_4o6(h)
-                hhat = Q.dequant_nvfp4_rows(hc, hs, hg)[0]
-            else:
-                hc, hs = Q.quantize_fp8_token(h)
-                hhat = Q.dequant_fp8_token(hc, hs)[0]
+            hhat = _quant_dequant(afmt, h)
             want += 0.25 * _closed_down(c, hhat)
         want += _closed_down(shared, _closed_h(shared, xv[t]))
         assert np.allclose(out["y"][t], want, rtol=1e-12, atol=1e-14)
