@@ -129,7 +129,9 @@ constexpr int kGroupTok = 32;         // tokens per unit in the grouped kernels
 // Grouped map of one weight class: rows of K elements, `rows_per_tile` rows (or
 // intermediate indices for gate/up) per row tile of `tile_of` rows, FP32 activations
 // when split. False if the shape does not tile.
-bool plan_group(int fmt, int K, int rows, int rows_per_tile, bool split, GroupMap& g) {
+// mx_bits: 4 or 8 for MX weights on the scaled MFMA with 4- or 8-bit activation codes
+// (staged raw), 0 otherwise.
+bool plan_group(int fmt, int K, int rows, int rows_per_tile, bool split, int mx_bits, GroupMap& g) {
   const int KS = group_ks(fmt);
   if (K % KS || rows % rows_per_tile) return false;
   g.KS = KS;
@@ -141,9 +143,13 @@ bool plan_group(int fmt, int K, int rows, int rows_per_tile, bool split, GroupMa
   g.cw = g.NS * 64;
   g.ct = g.NS * (split ? 4 : 2);
   g.split = split ? 1 : 0;
-  g.tstride = KS * (split ? 4 : 2) + 16;
+  g.scaled = mx_bits ? 1 : 0;
+  g.tstride = mx_bits ? KS * mx_bits / 8 + 16 : KS * (split ? 4 : 2) + 16;
   return true;
 }
+
+// LDS bytes of one staging buffer of a grouped class.
+size_t group_buf_bytes(const GroupMap& g) { return (size_t)kGroupTok * g.tstride + (g.scaled ? 8 * kGroupTok : 0); }
 
 // Weight bytes per element, times 2 (FP4 1, MXFP8 2, BF16 4; block scales ignored).
 int wbytes_x2(int fmt) { return fmt == W_BF16 ? 4 : (fmt == W_MXFP8 ? 2 : 1); }
@@ -231,10 +237,13 @@ bool make_plan(const moe_layer_t& L, int T, int path, Plan& p) {
   // automatic choice: from kGroupedMinT tokens on, when units hold many tokens
   const bool want = path == MOE_PATH_GROUPED ||
                     (path == MOE_PATH_AUTO && T >= kGroupedMinT && (L.has_shared || T * L.k >= L.E));
-  p.grouped = want && plan_group(L.wfmt, L.H, L.I, 64, false, p.gu_rg) &&
-              plan_group(sfmt, L.H, Ish, 64, false, p.gu_sg) &&
-              plan_group(L.wfmt, L.I, L.H, 128, L.afmt == A_BF16, p.dn_rg) &&
-              plan_group(sfmt, Ish, L.H, 128, true, p.dn_sg);
+  // MX routed weights with 8- or 4-bit activations run on the scaled MFMA
+  const bool mx_w = L.wfmt == W_MXFP4 || L.wfmt == W_MXFP8;
+  const int mx_bits = mx_w && (L.afmt == A_FP8_TOKEN || L.afmt == A_MXFP8) ? 8 : (mx_w && L.afmt == A_MXFP4 ? 4 : 0);
+  p.grouped = want && plan_group(L.wfmt, L.H, L.I, 64, false, mx_bits, p.gu_rg) &&
+              plan_group(sfmt, L.H, Ish, 64, false, 0, p.gu_sg) &&
+              plan_group(L.wfmt, L.I, L.H, 128, L.afmt == A_BF16, mx_bits, p.dn_rg) &&
+              plan_group(sfmt, Ish, L.H, 128, true, 0, p.dn_sg);
   if (p.grouped) {
     auto gbound = [&](const GroupMap& g, int units) {
       return (int64_t)units * g.steps * (g.cw + (int64_t)g.ct * g.NG);
@@ -244,7 +253,7 @@ bool make_plan(const moe_layer_t& L, int T, int path, Plan& p) {
   }
   if (p.grouped) {
     auto gtile = [&](const GroupMap& r, const GroupMap& s) {
-      return align_up((size_t)2 * kGroupTok * std::max(r.tstride, L.has_shared ? s.tstride : 0), 16);
+      return align_up(2 * std::max(group_buf_bytes(r), L.has_shared ? group_buf_bytes(s) : 0), 16);
     };
     p.gu_tile = gtile(p.gu_rg, p.gu_sg);
     p.dn_tile = gtile(p.dn_rg, p.dn_sg);
@@ -380,6 +389,9 @@ std::string check_layer(const moe_layer_t* L, int max_tokens) {
     if (fmt != MOE_W_BF16 && !w.scales) { snprintf(b, sizeof b, "%s.scales is NULL", name); add(b); }
     if (fmt == MOE_W_NVFP4 && w.scales && !aligned(w.scales, 2)) {
       snprintf(b, sizeof b, "%s.scales must be 2-byte aligned", name); add(b);
+    }
+    if ((fmt == MOE_W_MXFP4 || fmt == MOE_W_MXFP8) && w.scales && !aligned(w.scales, 4)) {
+      snprintf(b, sizeof b, "%s.scales must be 4-byte aligned", name); add(b);
     }
     if (fmt == MOE_W_NVFP4 && !w.gscale) { snprintf(b, sizeof b, "%s.gscale is NULL", name); add(b); }
   };

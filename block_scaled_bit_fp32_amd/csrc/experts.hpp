@@ -922,6 +922,11 @@ struct GateupOps {
     else return r;
   }
   __device__ __forceinline__ float tsc(int t, int) const { return afmt_row_scaled(AF) ? xq_scale[t] : 1.0f; }
+  // the raw code bytes and E8M0 scales of token t's row (scaled-MFMA staging)
+  __device__ __forceinline__ const uint8_t* codes_row(int t, int) const {
+    return xq_codes + (int64_t)t * (AF == A_MXFP4 ? H / 2 : H);
+  }
+  __device__ __forceinline__ const uint8_t* scales_row(int t, int) const { return xq_scales + (int64_t)t * (H / 32); }
   __device__ __forceinline__ float gs(int e, int q) const {
     return gscale ? gscale[(int64_t)e * gs_per_expert + q] : 1.0f;
   }
@@ -1045,6 +1050,13 @@ struct DownOps {
     else return r;
   }
   __device__ __forceinline__ float tsc(int, int p) const { return afmt_row_scaled(AF) ? hq_scale[p] : 1.0f; }
+  // the raw code bytes and E8M0 scales of pair p's h row (scaled-MFMA staging)
+  __device__ __forceinline__ const uint8_t* codes_row(int, int p) const {
+    return hq_codes + (int64_t)p * (AF == A_MXFP4 ? Kexp / 2 : Kexp);
+  }
+  __device__ __forceinline__ const uint8_t* scales_row(int, int p) const {
+    return hq_scales + (int64_t)p * (Kexp / 32);
+  }
   __device__ __forceinline__ float gs(int e, int q) const {
     return (q == 0 && gscale) ? gscale[(int64_t)e * gs_per_expert] : 1.0f;
   }

@@ -227,6 +227,222 @@ __device__ __forceinline__ void walk_grouped(const WTensor& W, const GroupMap& g
   }
 }
 
+// ------------------------------------------------ MX weights on the scaled MFMA
+// MX weights (MXFP4, MXFP8) with 8- or 4-bit activations (FP8 per token, MXFP4, MXFP8)
+// run on gfx950's v_mfma_scale_f32_32x32x64_f8f6f4: the E2M1 / E4M3 codes go in raw and
+// each operand's E8M0 block scales ride in the instruction, so neither side is decoded.
+// Operand layout of that instruction (checked on the GPU against a host reference for
+// every pairing of FP8 and FP4 operands): lane l holds row (A) or column (B) l % 32 and
+// half h = l / 32 of each 32-element K block: a 4-bit operand holds K [32 h, 32 h + 32)
+// of the instruction's 64, an 8-bit operand holds K [16 h, 16 h + 16) in bytes 0..15 and
+// K [32 + 16 h, 48 + 16 h) in bytes 16..31; the E8M0 scale of K block kb of row r comes
+// from lane r + 32 kb. The walk maps each instruction's two K blocks onto two OCP scale
+// blocks of the stage, the same on both operands:
+//   MXFP4 weights (stage 256): instruction j, K block kb = stage elements 128 kb + 32 j;
+//   MXFP8 weights (stage 128): instruction j, K block kb = stage elements 64 j + 32 kb.
+// FP8-per-token activations take the unit scale (E8M0 127); their FP32 scale is applied
+// in the epilogue. FP4 products are exact; the FP8 x FP8 instruction accumulates with
+// about 1e-5 of the sum of |terms| of internal rounding (measured), far inside the
+// layer's output tolerance.
+template <int FMT, int AF>
+constexpr bool use_scaled_mfma() {
+  return (FMT == W_MXFP4 || FMT == W_MXFP8) && (AF == A_FP8_TOKEN || AF == A_MXFP4 || AF == A_MXFP8);
+}
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+
+// One v_mfma_scale_f32_32x32x64_f8f6f4 (operand formats FA, FB: 4 = E2M1 in 4 registers,
+// 0 = E4M3 in 8). It is issued from inline assembly with its sources as the statement's
+// inputs and 21 wait states after it inside the statement: the compiler's own scheduling
+// of this instruction let later VALU writes land in its A, B and scale registers while
+// the instruction was still reading them (seen in the generated code; a quarter of the
+// outputs came out wrong), so here nothing may reuse the sources, or read the result,
+// until the instruction is done with them.
+template <int FA, int FB>
+struct MfmaOperands {
+  using A = typename std::conditional<FA == 4, i32x4_t, i32x8_t>::type;
+  using B = typename std::conditional<FB == 4, i32x4_t, i32x8_t>::type;
+};
+template <int FA, int FB>
+__device__ __forceinline__ void mfma_scale_32x32x64(f32x16_t& acc, const typename MfmaOperands<FA, FB>::A& a,
+                                                    const typename MfmaOperands<FA, FB>::B& b, int sa, int sb) {
+  asm volatile(
+      "v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[0,0,0] cbsz:%5 blgp:%6\n\t"
+      "s_nop 7\n\ts_nop 7\n\ts_nop 4"
+      : "+v"(acc)
+      : "v"(a), "v"(b), "v"(sa), "v"(sb), "n"(FA), "n"(FB));
+}
+
+struct GStageMx {
+  uint4 w[4];                    // 64 bytes of weight codes
+  uint32_t sc;                   // their 4 E8M0 scale bytes
+  uint4 act[2];                  // staged activation code slots of this thread
+  uint2 asc;                     // a token's activation scale bytes of the stage (MX)
+  float tsc;
+  float gs[2];
+};
+
+template <int FMT, int AF, class Ops, class RowOf, class Sink>
+__device__ __forceinline__ void walk_grouped_mx(const WTensor& W, const GroupMap& gm, const ExpertLds& L,
+                                                const ClassTab& C, const Span& sp, const Ops& op, RowOf row_of,
+                                                Sink sink) {
+  constexpr int KS = group_ks(FMT);                 // 256 (FP4 weights) or 128 (FP8 weights)
+  constexpr bool W4 = FMT == W_MXFP4;
+  constexpr bool A4 = AF == A_MXFP4;
+  constexpr bool AMX = AF == A_MXFP4 || AF == A_MXFP8;
+  constexpr int ABYTES = A4 ? KS / 2 : KS;          // activation code bytes per token and stage
+  constexpr int SPR = ABYTES / 16;                  // 16-byte slots per token and stage
+  constexpr int NSLOT = (kGTok * SPR + kBlock - 1) / kBlock;
+  constexpr int NI = KS / 64;                       // instructions per stage
+  constexpr int SCB = KS / 32;                      // scale blocks per token and stage
+  constexpr int FA = W4 ? 4 : 0, FB = A4 ? 4 : 0;   // operand formats: E2M1 4, E4M3 0
+  static_assert(NSLOT <= 2, "activation slots");
+  if (sp.left <= 0) return;
+  int left = sp.left;
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int half = lane >> 5, lr = lane & 31;
+  const int tstride = gm.tstride;                   // ABYTES + 16
+  const int bufbytes = kGTok * tstride + kGTok * 8;
+  const ClassCost k{gm.NG, gm.steps, gm.cw, gm.ct};
+  auto advance = [&](Cursor& p) {
+    if (++p.b < gm.NS) return;
+    p.b = 0;
+    if (++p.s < k.steps) return;
+    p.s = 0;
+    if (++p.g * k.NG < p.n) return;
+    p.g = 0;
+    if (++p.a < C.A) {
+      p.e = uni(C.ex_id[p.a]);
+      p.n = uni(C.ex_n[p.a]);
+      p.rb = uni(C.ex_row[p.a]);
+    }
+  };
+  auto fetch = [&](const Cursor& p, GStageMx& g) {
+    const int crow = p.rb + p.g * k.NG, n = min(k.NG, p.n - p.g * k.NG);
+#pragma unroll
+    for (int i = 0; i < NSLOT; ++i) {
+      const int u = i * kBlock + threadIdx.x;
+      const int j = u / SPR, c = u % SPR;
+      g.act[i] = make_uint4(0u, 0u, 0u, 0u);
+      if (u < kGTok * SPR && j < n)
+        g.act[i] = ld16(op.codes_row(C.r_tok[crow + j], C.r_pair[crow + j]) + p.b * ABYTES + c * 16);
+    }
+    g.asc = make_uint2(0u, 0u);
+    if constexpr (AMX) {
+      if ((int)threadIdx.x < n) {
+        const uint8_t* sr = op.scales_row(C.r_tok[crow + threadIdx.x], C.r_pair[crow + threadIdx.x]) + p.b * SCB;
+        g.asc = SCB == 8 ? *reinterpret_cast<const uint2*>(sr) : make_uint2(*reinterpret_cast<const uint32_t*>(sr), 0u);
+      }
+    }
+    if (p.b == 0) {
+      g.tsc = lr < n ? op.tsc(C.r_tok[crow + lr], C.r_pair[crow + lr]) : 0.0f;
+      g.gs[0] = op.gs(p.e, 0);
+      g.gs[1] = op.gs(p.e, 1);
+    }
+    const int64_t row = row_of(p.e, p.s, lr);
+    const uint8_t* rp = W.codes + row * W.code_row_bytes;
+    const uint8_t* sp_ = W.scales + row * W.scale_row_bytes;
+    if constexpr (W4) {   // elements [128 h, 128 h + 128) of the stage, contiguous
+      const uint8_t* wp = rp + (p.b * KS + half * (KS / 2)) / 2;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) g.w[i] = load_stream16(wp + 16 * i);
+      g.sc = *reinterpret_cast<const uint32_t*>(sp_ + ((p.b * KS + half * (KS / 2)) >> 5));
+    } else {              // bytes 16 h + 32 q of the stage (q < 4): both halves of each block
+      const uint8_t* wp = rp + p.b * KS + 16 * half;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) g.w[i] = load_stream16(wp + 32 * i);
+      g.sc = *reinterpret_cast<const uint32_t*>(sp_ + ((p.b * KS) >> 5));
+    }
+  };
+  float* s_tsc = L.w_tsc;
+  float* s_gs = L.w_gs;
+  auto store = [&](const Cursor& p, const GStageMx& g, int buf) {
+    uint8_t* tile = L.tile + buf * bufbytes;
+#pragma unroll
+    for (int i = 0; i < NSLOT; ++i) {
+      const int u = i * kBlock + threadIdx.x;
+      if (u < kGTok * SPR) *reinterpret_cast<uint4*>(tile + (u / SPR) * tstride + (u % SPR) * 16) = g.act[i];
+    }
+    if constexpr (AMX) {
+      if ((int)threadIdx.x < kGTok) *reinterpret_cast<uint2*>(tile + kGTok * tstride + threadIdx.x * 8) = g.asc;
+    }
+    if (p.b == 0) {
+      if (wave == 0 && half == 0) s_tsc[lr] = g.tsc;
+      if (threadIdx.x == 0) { s_gs[0] = g.gs[0]; s_gs[1] = g.gs[1]; }
+    }
+  };
+  f32x16_t acc;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+  int buf = 0;
+  auto do_step = [&](auto pf, const Cursor& p, GStageMx& cur, GStageMx& nxt, Cursor& np) {
+    if constexpr (decltype(pf)::value) {
+      np = p;
+      advance(np);
+      fetch(np, nxt);
+    }
+    const uint8_t* tile = L.tile + buf * bufbytes;
+    const uint8_t* arow = tile + lr * tstride;
+    uint2 as2 = make_uint2(0u, 0u);
+    if constexpr (AMX) as2 = *reinterpret_cast<const uint2*>(tile + kGTok * tstride + lr * 8);
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      typename MfmaOperands<FA, FB>::A a;
+      int sa, blk;   // this lane's weight scale; the stage scale block it supplies
+      if constexpr (W4) {
+        a = i32x4_t{(int)cur.w[j].x, (int)cur.w[j].y, (int)cur.w[j].z, (int)cur.w[j].w};
+        sa = (int)((cur.sc >> (8 * j)) & 0xFFu);
+        blk = 4 * half + j;
+      } else {
+        a = i32x8_t{(int)cur.w[2 * j].x, (int)cur.w[2 * j].y, (int)cur.w[2 * j].z, (int)cur.w[2 * j].w,
+                    (int)cur.w[2 * j + 1].x, (int)cur.w[2 * j + 1].y, (int)cur.w[2 * j + 1].z, (int)cur.w[2 * j + 1].w};
+        blk = 2 * j + half;
+        sa = (int)((cur.sc >> (8 * blk)) & 0xFFu);
+      }
+      typename MfmaOperands<FA, FB>::B b;
+      if constexpr (A4) {   // 32 E2M1 of stage elements 32 blk.. (16 bytes)
+        const uint4 v = *reinterpret_cast<const uint4*>(arow + 16 * blk);
+        b = i32x4_t{(int)v.x, (int)v.y, (int)v.z, (int)v.w};
+      } else {              // E4M3: bytes 0..15 from K block 0's half, 16..31 from block 1's
+        const int o0 = W4 ? 32 * j + 16 * half : 64 * j + 16 * half;
+        const int o1 = W4 ? 128 + 32 * j + 16 * half : 64 * j + 32 + 16 * half;
+        const uint4 v0 = *reinterpret_cast<const uint4*>(arow + o0);
+        const uint4 v1 = *reinterpret_cast<const uint4*>(arow + o1);
+        b = i32x8_t{(int)v0.x, (int)v0.y, (int)v0.z, (int)v0.w, (int)v1.x, (int)v1.y, (int)v1.z, (int)v1.w};
+      }
+      int sb = 127;
+      if constexpr (AMX) sb = (int)(((blk < 4 ? as2.x : as2.y) >> (8 * (blk & 3))) & 0xFFu);
+      mfma_scale_32x32x64<FA, FB>(acc, a, b, sa, sb);
+    }
+    if (p.b == gm.NS - 1) {   // row tile done
+      const int crow = p.rb + p.g * k.NG, n = min(k.NG, p.n - p.g * k.NG);
+      sink(UnitCtx{crow, 0, n}, p.s, acc, s_tsc[lr], s_gs[0], s_gs[1]);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+    }
+    if constexpr (decltype(pf)::value) {
+      if (np.b == 0) lds_barrier();   // every wave has read this tile's scales
+      store(np, nxt, buf ^ 1);
+    }
+    lds_barrier();
+    buf ^= 1;
+  };
+  Cursor pa{sp.a0, sp.g0, sp.s0, 0, sp.e0, sp.n0, sp.rb0}, pb = pa;
+  GStageMx A, B;
+  fetch(pa, A);
+  store(pa, A, 0);
+  lds_barrier();
+  using Yes = std::integral_constant<bool, true>;
+  using No = std::integral_constant<bool, false>;
+  while (true) {
+    if (left == 1) { do_step(No{}, pa, A, B, pb); break; }
+    do_step(Yes{}, pa, A, B, pb);
+    if (left == 2) { do_step(No{}, pb, B, A, pa); break; }
+    do_step(Yes{}, pb, B, A, pa);
+    left -= 2;
+  }
+}
+
 // Output row (0..31) of accumulator register r on this lane (32x32 MFMA layout).
 __device__ __forceinline__ int acc_row(int r, int half) { return 8 * (r >> 2) + 4 * half + (r & 3); }
 
@@ -259,7 +475,10 @@ __device__ __forceinline__ void ggateup_walk(const ExpertArgs& a, const ExpertLd
       if (a.dbg_h) a.dbg_h[off + acc_row(r, half)] = hv;
     }
   };
-  walk_grouped<FMT, false>(W, gm, L, C, sp, op, row_of, sink);
+  if constexpr (use_scaled_mfma<FMT, AF>())
+    walk_grouped_mx<FMT, AF>(W, gm, L, C, sp, op, row_of, sink);
+  else
+    walk_grouped<FMT, false>(W, gm, L, C, sp, op, row_of, sink);
 }
 
 template <int RF, int SF, int AF>
@@ -302,7 +521,10 @@ __device__ __forceinline__ void gdown_walk(const ExpertArgs& a, const ExpertLds&
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[acc_row(r, half)] = acc[r] * sc;
   };
-  walk_grouped<FMT, AF == A_BF16>(W, gm, L, C, sp, op, row_of, sink);
+  if constexpr (use_scaled_mfma<FMT, AF>())
+    walk_grouped_mx<FMT, AF>(W, gm, L, C, sp, op, row_of, sink);
+  else
+    walk_grouped<FMT, AF == A_BF16>(W, gm, L, C, sp, op, row_of, sink);
 }
 
 template <int RF, int SF, int AF>

@@ -71,6 +71,8 @@ struct GroupMap {
   int cw, ct;        // cost of one stage of a row tile: cw + ct * tokens
   int split;         // FP32 activations
   int tstride;       // LDS bytes per staged token row (padded)
+  int scaled;        // MX weights on the scaled MFMA: raw activation codes staged, then
+                     // 8 E8M0 bytes per token
 };
 
 struct WTensor {
