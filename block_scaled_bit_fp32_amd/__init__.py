@@ -10,6 +10,7 @@ Names follow include/moe.h:
     expert_forward(layer, x, xq, ids, w, ws, debug=False) -> y (BF16) [, debug dict]
     forward(layer, x, ws)                -> y, topk_ids, topk_w, xq
     forward_noalloc(layer, x)            -> y, topk_ids, topk_w, xq (library scratch)
+    forward_fused(layer, r, gamma, eps, ws) -> r + y, x = RMSNorm(r), topk_ids, topk_w, xq
     quantize_nvfp4_4o6(x)                -> codes, scales, gscale, choice
 """
 from __future__ import annotations
@@ -58,6 +59,10 @@ class DebugT(ctypes.Structure):
 PATH_AUTO, PATH_GEMV, PATH_GROUPED = 0, 1, 2
 
 
+class NormT(ctypes.Structure):
+    _fields_ = [("gamma", ctypes.c_void_p), ("eps", ctypes.c_float)]
+
+
 class KernelTimeT(ctypes.Structure):
     _fields_ = [("name", ctypes.c_char_p), ("launches", ctypes.c_int32), ("total_ms", ctypes.c_double)]
 
@@ -74,6 +79,8 @@ _SIGNATURES = {
                                   ctypes.POINTER(DebugT), _P]),
     "moe_forward": (_I32, [ctypes.POINTER(LayerT), _P, _I32, _P, _P, _P, _P, _P, _SZ,
                            ctypes.POINTER(DebugT), _P]),
+    "moe_forward_fused": (_I32, [ctypes.POINTER(LayerT), ctypes.POINTER(NormT), _P, _I32, _P, _P, _P, _P, _P, _P,
+                                 _SZ, ctypes.POINTER(DebugT), _P]),
     "moe_forward_noalloc": (_I32, [ctypes.POINTER(LayerT), _P, _I32, _P, _P, _P, _P,
                                    ctypes.POINTER(DebugT), _P]),
     "moe_noalloc_scratch_bytes": (_SZ, []),
@@ -332,6 +339,33 @@ def forward(layer: DeviceLayer, x: torch.Tensor, ws: Workspace, out=None, path: 
                             _ptr(xq), y.data_ptr(), ws.ptr, ws.nbytes,
                             ctypes.byref(dbg) if dbg is not None else None, _stream()))
     return y, ids, w, xq
+
+
+def forward_fused(layer: DeviceLayer, resid: torch.Tensor, gamma: torch.Tensor, eps: float, ws: Workspace,
+                  out=None, resid_out: Optional[torch.Tensor] = None, path: int = PATH_AUTO):
+    """moe_forward_fused: x = RMSNorm(resid) * gamma (BF16), the layer on x, and the residual
+    stream resid + y. Returns (resid_out, x, topk_ids, topk_w, xq); ``out`` = (x, ids, w,
+    xq) reuses buffers; ``resid_out`` may be ``resid`` itself (in place)."""
+    resid = _bits16(resid)
+    gamma = _bits16(gamma)
+    T = resid.shape[0]
+    cfg = layer.cfg
+    if out is None:
+        x = torch.empty((T, cfg.H), dtype=torch.bfloat16, device=resid.device)
+        ids = torch.empty((T, cfg.k), dtype=torch.int32, device=resid.device)
+        w = torch.empty((T, cfg.k), dtype=torch.float32, device=resid.device)
+        nq = xq_bytes(layer, T)
+        xq = _aligned_empty(nq, resid.device) if nq else None
+    else:
+        x, ids, w, xq = out
+    if resid_out is None:
+        resid_out = torch.empty((T, cfg.H), dtype=torch.bfloat16, device=resid.device)
+    norm = NormT(gamma.data_ptr(), float(eps))
+    dbg = DebugT(None, None, None, None, path) if path != PATH_AUTO else None
+    _check(_lib.moe_forward_fused(ctypes.byref(layer.struct), ctypes.byref(norm), resid.data_ptr(), T, x.data_ptr(),
+                                  ids.data_ptr(), w.data_ptr(), _ptr(xq), resid_out.data_ptr(), ws.ptr, ws.nbytes,
+                                  ctypes.byref(dbg) if dbg is not None else None, _stream()))
+    return resid_out, x, ids, w, xq
 
 
 def forward_noalloc(layer: DeviceLayer, x: torch.Tensor, out=None, path: int = PATH_AUTO):

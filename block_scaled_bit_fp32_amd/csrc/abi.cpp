@@ -508,9 +508,17 @@ namespace {
 
 // Router GEMV (+ token quantization) and, if `topk`, the top-k launch.
 // dry: check the arguments only.
+// RMSNorm before the layer (moe_forward_fused): resid / gamma / eps, x written to x_out.
+struct NormIn {
+  const uint16_t* resid = nullptr;
+  const uint16_t* gamma = nullptr;
+  float eps = 0.0f;
+  uint16_t* x_out = nullptr;
+};
+
 moe_status_t enqueue_route(const moe_layer_t* L, const uint16_t* x_bf16, int32_t T, int32_t* topk_ids,
                            float* topk_w, void* xq, void* ws, size_t ws_bytes, bool topk, bool dry,
-                           hipStream_t stream) {
+                           hipStream_t stream, const NormIn& nin = NormIn{}) {
   moe_status_t st = check_or_fail(L, std::max(1, T));
   if (st != MOE_OK) return st;
   if (T < 0) return set_err(MOE_EINVAL, "T must be >= 0");
@@ -558,6 +566,13 @@ moe_status_t enqueue_route(const moe_layer_t* L, const uint16_t* x_bf16, int32_t
     }
     n_quant = T;
   }
+  if (nin.resid) {   // the per-token workgroups also write the normalized tokens
+    a.resid = nin.resid;
+    a.gamma = nin.gamma;
+    a.eps = nin.eps;
+    a.x_out = nin.x_out;
+    n_quant = T;
+  }
   if (launch_route(a, n_quant, topk, stream) != hipSuccess) return set_err(MOE_ELAUNCH, "route kernel launch failed");
   return MOE_OK;
 }
@@ -574,7 +589,7 @@ bool pair_mode_plan(const moe_layer_t& L, int T, int path) {
 moe_status_t enqueue_experts(const moe_layer_t* L, const uint16_t* x_bf16, const void* xq, int32_t T,
                              const int32_t* topk_ids, const float* topk_w, uint16_t* y_bf16, void* ws,
                              size_t ws_bytes, const moe_debug_t* dbg, bool fused_topk, bool dry,
-                             hipStream_t stream) {
+                             hipStream_t stream, const uint16_t* resid = nullptr) {
   moe_status_t st = check_or_fail(L, std::max(1, T));
   if (st != MOE_OK) return st;
   if (T < 0) return set_err(MOE_EINVAL, "T must be >= 0");
@@ -633,6 +648,7 @@ moe_status_t enqueue_experts(const moe_layer_t* L, const uint16_t* x_bf16, const
   a.hq_scale = reinterpret_cast<float*>(base + w.hq_scale);
   a.o = reinterpret_cast<float*>(base + w.o);
   a.y = y_bf16;
+  a.resid = resid;
   if (dbg) {
     a.dbg_h = dbg->h;
     a.dbg_codes = dbg->hq_codes;
@@ -750,6 +766,44 @@ moe_status_t moe_forward(const moe_layer_t* L, const uint16_t* x_bf16, int32_t T
   if ((st = enqueue_route(L, x_bf16, T, topk_ids, topk_w, xq, ws, ws_bytes, !fused, false, stream)) != MOE_OK)
     return st;
   return enqueue_experts(L, x_bf16, xq, T, topk_ids, topk_w, y_bf16, ws, ws_bytes, dbg, fused, false, stream);
+}
+
+moe_status_t moe_forward_fused(const moe_layer_t* L, const moe_norm_t* norm, const uint16_t* resid_in, int32_t T,
+                               uint16_t* x_out, int32_t* topk_ids, float* topk_w, void* xq, uint16_t* resid_out,
+                               void* ws, size_t ws_bytes, const moe_debug_t* dbg, hipStream_t stream) {
+  moe_status_t st = check_or_fail(L, std::max(1, T));
+  if (st != MOE_OK) return st;
+  if (T < 0) return set_err(MOE_EINVAL, "T must be >= 0");
+  std::string bad;
+  if (!norm) bad += "norm is NULL; ";
+  else {
+    if (!norm->gamma || !aligned(norm->gamma, 16)) bad += "norm->gamma must be non-NULL and 16-byte aligned; ";
+    if (!(norm->eps >= 0.0f) || !(norm->eps < 3.4e38f)) bad += "norm->eps must be finite and >= 0; ";
+  }
+  if (T > 0) {
+    if (!resid_in || !aligned(resid_in, 16)) bad += "resid_in must be non-NULL and 16-byte aligned; ";
+    if (!x_out || !aligned(x_out, 16)) bad += "x_out must be non-NULL and 16-byte aligned; ";
+    if (!resid_out) bad += "resid_out is NULL; ";
+    // x_out is written while the router reads resid_in, in the same launch
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(resid_in), x0 = reinterpret_cast<uintptr_t>(x_out);
+    const uintptr_t n = (uintptr_t)T * L->H * 2;
+    if (resid_in && x_out && a0 < x0 + n && x0 < a0 + n) bad += "x_out must not overlap resid_in; ";
+  }
+  if (!bad.empty()) return set_err(MOE_EINVAL, bad);
+  if (T == 0) return MOE_OK;
+  const int path = dbg ? dbg->path : MOE_PATH_AUTO;
+  if (path < MOE_PATH_AUTO || path > MOE_PATH_GROUPED) return set_err(MOE_EINVAL, "dbg->path is not a moe_path_t");
+  const bool fused = pair_mode_plan(*L, T, path);
+  const NormIn nin{resid_in, norm->gamma, norm->eps, x_out};
+  // every check of both halves before the first launch
+  if ((st = enqueue_route(L, x_out, T, topk_ids, topk_w, xq, ws, ws_bytes, !fused, true, stream, nin)) != MOE_OK ||
+      (st = enqueue_experts(L, x_out, xq, T, topk_ids, topk_w, resid_out, ws, ws_bytes, dbg, fused, true, stream,
+                            resid_in)) != MOE_OK)
+    return st;
+  if ((st = enqueue_route(L, x_out, T, topk_ids, topk_w, xq, ws, ws_bytes, !fused, false, stream, nin)) != MOE_OK)
+    return st;
+  return enqueue_experts(L, x_out, xq, T, topk_ids, topk_w, resid_out, ws, ws_bytes, dbg, fused, false, stream,
+                         resid_in);
 }
 
 }  // extern "C"

@@ -3,8 +3,9 @@
 //                   per the layer's activation format (Four-Over-Six NVFP4, FP8 per row,
 //                   MXFP4 or MXFP8 per 32-block) -- the quantize-before-down step of the
 //                   Inkling page's MoE with fused activation quantization, once per pair.
-//   combine_kernel  y[t][r] = sum_j w[t][j] * o[t*k+j][r] (+ o_shared[t][r]), FP32 in that
-//                   order, rounded to BF16 -- the weighted combine (k <= 16).
+//   combine_kernel  y[t][r] = sum_j w[t][j] * o[t*k+j][r] (+ o_shared[t][r]) (+ the residual
+//                   stream's r[t][r]), FP32 in that order, rounded to BF16 -- the weighted
+//                   combine (k <= 16).
 #include "launch.hpp"
 #include "rows.hpp"
 
@@ -54,6 +55,7 @@ __global__ void __launch_bounds__(kBlock) combine_kernel(ExpertArgs a) {
   for (int j = 0; j < KM; ++j)
     if (j < a.k) s = fmaf(wv[j], ov[j], s);
   if (a.has_shared) s += osh;
+  if (a.resid) s += bf16_to_f32(a.resid[(int64_t)t * a.H + r]);   // the residual add
   a.y[(int64_t)t * a.H + r] = (uint16_t)f32_to_bf16_rne(s);
 }
 

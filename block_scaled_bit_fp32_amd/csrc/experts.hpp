@@ -1190,11 +1190,17 @@ __device__ __forceinline__ void walk_tokens(const ExpertArgs& a, const ExpertLds
       lds_barrier();
       if ((int)threadIdx.x < m.G) {
         const int r = threadIdx.x;
-        const float v = ((red[r] + red[m.G + r]) + red[2 * m.G + r]) + red[3 * m.G + r];
-        a.y[(int64_t)t * a.H + s * rows_item + r] = (uint16_t)f32_to_bf16_rne(v);
+        const int64_t yi = (int64_t)t * a.H + s * rows_item + r;
+        float v = ((red[r] + red[m.G + r]) + red[2 * m.G + r]) + red[3 * m.G + r];
+        if (a.resid) v += bf16_to_f32(a.resid[yi]);   // the residual add, then one rounding
+        a.y[yi] = (uint16_t)f32_to_bf16_rne(v);
       }
     } else {
-      if (jl == 0) a.y[(int64_t)t * a.H + s * rows_item + lrow] = (uint16_t)f32_to_bf16_rne(tot);
+      if (jl == 0) {
+        const int64_t yi = (int64_t)t * a.H + s * rows_item + lrow;
+        if (a.resid) tot += bf16_to_f32(a.resid[yi]);
+        a.y[yi] = (uint16_t)f32_to_bf16_rne(tot);
+      }
     }
   };
   // the weight loads of item `it` (its experts from the staged topk_ids)

@@ -102,6 +102,12 @@ struct RouteArgs {
   int softmax;              // combine weights: softmax (1) or sigmoid (0) of the selected
   float* raw;               // [T][E] bare logits (bias for selection only: logits hold
                             // logit + bias, the weights take these), or NULL
+  // RMSNorm before the layer (resid != NULL): x = RMSNorm(resid) * gamma in BF16 is the
+  // layer's input; the router computes it on the fly, the per-token workgroups write it
+  const uint16_t* resid;    // [T][H] residual stream, or NULL (x taken as given)
+  const uint16_t* gamma;    // [H] BF16
+  float eps;
+  uint16_t* x_out;          // [T][H] the normalized tokens
 };
 
 struct ExpertArgs {
@@ -150,6 +156,7 @@ struct ExpertArgs {
   float* dbg_scale;
   int lds_list_bytes;    // offset of the activation tile in dynamic LDS
   int lds_act_bytes;     // size of the activation tile
+  const uint16_t* resid; // [T][H] residual stream added to y before its rounding, or NULL
 };
 
 }  // namespace moe

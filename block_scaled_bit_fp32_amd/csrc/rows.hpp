@@ -32,6 +32,58 @@ struct F32Row {
   }
 };
 
+// ----------------------------------------------------------------- RMSNorm
+// The MoE sublayer's input as the RMSNorm of the residual stream ("Day 0 support for
+// Mistral Large 4 on vLLM", decode-round fusions: residual add and RMSNorm in one kernel;
+// "Inkling 2 Small on vLLM: Day-0 Support", kernel fusion of the memory-bound steps
+// between sublayers): x = r / sqrt(mean(r^2) + eps) * gamma, rounded to BF16. In FP32 in a
+// fixed order, so every workgroup that needs a token's x computes the same bits: thread i
+// sums the squares of elements i, i + kBlock, ...; the wave sums them in an xor tree, and
+// the four waves' sums are added in wave order.
+__device__ __forceinline__ float block_sum_fixed(float v, float* red) {
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  __syncthreads();
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  return ((red[0] + red[1]) + red[2]) + red[3];
+}
+__device__ __forceinline__ float row_rstd(const uint16_t* r, int H, float eps, float* red) {
+#pragma clang fp contract(off)
+  float ss = 0.0f;
+  for (int h = threadIdx.x; h < H; h += kBlock) {
+    const float v = bf16_to_f32(r[h]);
+    ss = ss + v * v;
+  }
+  ss = block_sum_fixed(ss, red);
+  return 1.0f / sqrtf(ss / (float)H + eps);
+}
+// One normalized element, rounded to BF16 (returned as its FP32 value).
+__device__ __forceinline__ float norm_x(float r, float rstd, float g) {
+#pragma clang fp contract(off)
+  const float v = (r * rstd) * g;
+  return bf16_to_f32(f32_to_bf16_rne(v));
+}
+// Rows of normalized tokens for the quantizers: 16 elements at a time.
+struct NormRow {
+  const uint16_t* r;
+  const uint16_t* g;
+  float rstd;
+  __device__ __forceinline__ void load(int b, float (&v)[16]) const {
+    const uint4* q = reinterpret_cast<const uint4*>(r + 16 * b);
+    const uint4* w = reinterpret_cast<const uint4*>(g + 16 * b);
+    const uint4 a = q[0], c = q[1], ga = w[0], gc = w[1];
+    const uint32_t x[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
+    const uint32_t y[8] = {ga.x, ga.y, ga.z, ga.w, gc.x, gc.y, gc.z, gc.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      v[2 * i] = norm_x(bf16_to_f32(x[i] & 0xFFFFu), rstd, bf16_to_f32(y[i] & 0xFFFFu));
+      v[2 * i + 1] = norm_x(bf16_to_f32(x[i] >> 16), rstd, bf16_to_f32(y[i] >> 16));
+    }
+  }
+};
+
 // Four-Over-Six NVFP4 of one row of n elements (n % 16 == 0), whole workgroup.
 template <class Row>
 __device__ __forceinline__ void quant_row_nvfp4(const Row& row, int n, uint8_t* codes, uint8_t* scales,

@@ -216,6 +216,30 @@ moe_status_t moe_forward(const moe_layer_t *L, const uint16_t *x_bf16, int32_t T
                          void *ws, size_t ws_bytes, const moe_debug_t *dbg,
                          hipStream_t stream);
 
+/* RMSNorm of the residual stream before the layer (weight gamma, BF16 [H]; eps >= 0). */
+typedef struct {
+  const uint16_t *gamma;
+  float eps;
+} moe_norm_t;
+
+/* The layer with its neighbouring steps of a pre-norm transformer block fused in ("Day 0
+ * support for Mistral Large 4 on vLLM", fusions of the decode round: the residual add
+ * and the RMSNorm run in one kernel with the all-reduce; "Inkling 2 Small on vLLM: Day-0
+ * Support", kernel fusion: the memory-bound steps between sublayers are folded into
+ * neighbouring kernels). With r = resid_in [T][H] (BF16):
+ *   x_out     = RMSNorm(r) = r / sqrt(mean_h r^2 + eps) * gamma, in FP32 (the squares
+ *               summed in a fixed order), rounded to BF16; the router launch computes it
+ *   topk_ids, topk_w, xq, and y = the layer on x_out, exactly as moe_forward;
+ *   resid_out = r + y, summed in FP32 and rounded once to BF16 (y is not rounded first);
+ *               the kernel that writes y writes this instead.
+ * No launch is added to moe_forward's. resid_out may be resid_in (updated in place);
+ * x_out must not overlap resid_in. resid_in, x_out and gamma 16-byte aligned. Other
+ * arguments, checks and errors as moe_forward. */
+moe_status_t moe_forward_fused(const moe_layer_t *L, const moe_norm_t *norm, const uint16_t *resid_in,
+                               int32_t T, uint16_t *x_out, int32_t *topk_ids, float *topk_w, void *xq,
+                               uint16_t *resid_out, void *ws, size_t ws_bytes, const moe_debug_t *dbg,
+                               hipStream_t stream);
+
 /* moe_forward without a caller workspace, for callers that cannot allocate device
  * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
  * hipMalloc). The same arguments, results and checks as moe_forward, minus ws and

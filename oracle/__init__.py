@@ -11,10 +11,11 @@ Modules:
              weight dequantization
   router  -- FP64 router logits, sigmoid top-k, renormalised combine weights
   layer   -- expert MLPs (SwiGLU), activation re-quantization, weighted combine
+  norm    -- RMSNorm of the residual stream before the layer, residual add after it
 
 Every function is pinned by tests under tests/ (hand-worked tables, brute force on
 small inputs, closed forms, exact rational arithmetic). The full-layer composition
 has no printed worked example on the pages: it is pinned only through its parts and
 the closed-form layers in tests/test_oracle_layer.py.
 """
-from . import formats, quant, router, layer  # noqa: F401
+from . import formats, quant, router, layer, norm  # noqa: F401

@@ -160,3 +160,19 @@ def test_noalloc_refuses_calls_past_its_scratch_before_any_device_call(lib):
     assert st == lib.MOE_EWORKSPACE
     assert "static scratch" in lib.lib().moe_last_error().decode()
     assert lib.lib().moe_workspace_bytes(ctypes.byref(s), 8) <= lib.lib().moe_noalloc_scratch_bytes()
+
+
+def test_fused_entry_checks_its_arguments_before_any_launch(lib):
+    """moe_forward_fused refuses a NULL norm, a misaligned gamma, a negative eps and an
+    x_out that overlaps resid_in, on the host."""
+    s = _fake_layer(lib, "flint_w4a16")
+    p = 1 << 20
+    st = lib.lib().moe_forward_fused(ctypes.byref(s), None, p, 2, p + (1 << 16), p, p, None, p, p, 1 << 30,
+                                     None, None)
+    assert st == lib.MOE_EINVAL and "norm is NULL" in lib.lib().moe_last_error().decode()
+    norm = lib.NormT(p + 2, -1.0)
+    st = lib.lib().moe_forward_fused(ctypes.byref(s), ctypes.byref(norm), p, 2, p + 64, p, p, None, p, p, 1 << 30,
+                                     None, None)
+    why = lib.lib().moe_last_error().decode()
+    assert st == lib.MOE_EINVAL
+    assert "gamma" in why and "eps" in why and "overlap" in why
