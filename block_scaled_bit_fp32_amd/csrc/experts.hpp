@@ -748,13 +748,18 @@ __device__ __forceinline__ void walk_class(const WTensor& W, const GemvMap& m, c
   // fused routing (fr, pair mode) the router logits of the span's tokens are loaded first
   // and the experts are selected while the other prologue loads are in flight.
   const int nrows0 = r1 - r0;
-  float lv[kFusedTopkSlots];
+  TopkRt lv;
   int t_lo = 0, t_hi = -1;
+  const int fnk = topk_rt_slots(fr.E);
+  auto route_load = [&](int t) {
+    const int64_t off = (int64_t)min(t, t_hi) * fr.E;
+    topk_rt_load(fr.logits + off, fr.raw ? fr.raw + off : nullptr, fr.E, fnk, lv);
+  };
   if constexpr (VW == VW_PAIR) {
     if (fr.logits) {
       t_lo = div_by(sp.a0, fr.inv_k);
       t_hi = div_by(sp.row_limit - 1, fr.inv_k);
-      wave_topk_load<kFusedTopkSlots>(fr.logits + (int64_t)min(t_lo + wave, t_hi) * fr.E, fr.E, lv);
+      route_load(t_lo + wave);
     }
   }
   uint4 raw[NS];
@@ -777,14 +782,10 @@ __device__ __forceinline__ void walk_class(const WTensor& W, const GemvMap& m, c
     if (fr.logits) {   // one token per wave (more rounds for longer spans), then the first expert
       for (int tb = t_lo; tb <= t_hi; tb += kBlock / kWave) {
         const int t = tb + wave;
-        if (tb != t_lo) wave_topk_load<kFusedTopkSlots>(fr.logits + (int64_t)min(t, t_hi) * fr.E, fr.E, lv);
+        if (tb != t_lo) route_load(t);
         int e;
         float w;
-        if (fr.raw)
-          wave_topk_select<kFusedTopkSlots, true>(lv, fr.E, fr.k, fr.raw + (int64_t)min(t, t_hi) * fr.E, fr.softmax,
-                                                  e, w);
-        else
-          wave_topk_select<kFusedTopkSlots, false>(lv, fr.E, fr.k, nullptr, fr.softmax, e, w);
+        topk_rt_select(lv, fr.raw != nullptr, fr.E, fr.k, fr.softmax, fnk, e, w);
         if (t <= t_hi && lane < fr.k) {
           L.ids[t * fr.k + lane] = e;
           fr.ids_out[t * fr.k + lane] = e;

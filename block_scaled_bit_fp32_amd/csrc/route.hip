@@ -192,6 +192,7 @@ hipError_t launch_route(const RouteArgs& a, int n_quant, bool topk, hipStream_t 
   if (a.E <= 64) return launch_kernel(K_TOPK, topk_kernel<1>, tg, dim3(kBlock), 0, s, a);
   if (a.E <= 128) return launch_kernel(K_TOPK, topk_kernel<2>, tg, dim3(kBlock), 0, s, a);
   if (a.E <= 256) return launch_kernel(K_TOPK, topk_kernel<4>, tg, dim3(kBlock), 0, s, a);
+  if (a.E <= 384) return launch_kernel(K_TOPK, topk_kernel<6>, tg, dim3(kBlock), 0, s, a);
   if (a.E <= 512) return launch_kernel(K_TOPK, topk_kernel<8>, tg, dim3(kBlock), 0, s, a);
   return launch_kernel(K_TOPK, topk_kernel<16>, tg, dim3(kBlock), 0, s, a);
 }

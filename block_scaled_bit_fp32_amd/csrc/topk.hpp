@@ -1,100 +1,253 @@
-// Sigmoid top-k of one token by one wave, shared by the top-k kernel and the gate/up
-// kernel's fused routing (both take the same steps, so they select the same experts and
-// compute the same weights bit for bit).
+// Sigmoid / softmax top-k of one token by one wave, shared by the top-k kernel and the
+// gate/up kernel's fused routing (both take the same steps, so they select the same
+// experts and compute the same weights bit for bit).
 #pragma once
+#include <utility>
+
 #include "device.hpp"
 
 namespace moe {
 
 // The k largest of lg[0..E), largest first, ties to the lower expert index; weights are
 // the sigmoids (softmax = 0) or the exponentials (softmax = 1) of the selected values,
-// renormalized over the selection in selection order (FP32). The values are the
-// selected entries of lg, or, when raw is given (a router bias that only selects: lg
-// holds logit + bias, raw the bare logits), the selected entries of raw. Expert e
-// sits in lane e % 64, slot e / 64 (E <= 64 * NK); keys are the logits' order-preserving
-// bits (0 marks an empty or taken slot; a valid key is at least 1). Each lane keeps its
-// best slot (the lowest slot among equal keys, i.e. the lowest index); a round takes the
-// wave maximum of those, the lane holding it (the lowest index if several do), and only
-// that lane rescans its slots. Lane j < k returns the j-th expert and its weight.
-// Whole-wave call (uniform arguments).
-// The loads (one logit per slot) and the selection are separate steps, so that a caller
-// can issue the loads early: wave_topk_load then wave_topk_select (wave_topk does both).
-template <int NK>
-__device__ __forceinline__ void wave_topk_load(const float* lg, int E, float (&lv)[NK]) {
-  const int lane = threadIdx.x & (kWave - 1);
-#pragma unroll
-  for (int i = 0; i < NK; ++i) lv[i] = lg[min(lane + kWave * i, E - 1)];
-}
-// RAW: the weights take raw[] (a load per selected expert). A compile-time choice: a
-// load behind a run-time branch would make the wait for its value drain every load the
-// caller has in flight.
+// renormalized over the selection (FP32). The values are the selected entries of lg, or,
+// when raw is given (a router bias that only selects: lg holds logit + bias, raw the bare
+// logits), the selected entries of raw.
+//
+// Layout: expert e sits in lane e / NK, slot e % NK (E <= 64 * NK), so lane order is
+// expert order. Keys are the logits' order-preserving bits (0 marks an empty slot, a
+// valid key is at least 1). Each lane first sorts its NK (key, slot) pairs, largest key
+// first and the lower slot first among equal keys (a sorting network on 64-bit (key,
+// ~slot) composites). A round then takes the wave maximum m of the lanes' heads (DPP),
+// picks the lowest lane whose head equals m (its head is then the lowest expert index
+// holding m, since lanes and slots are both in expert order) and pops that lane's list.
+// k rounds select the k experts in order. A wave instruction costs the same whether the
+// lanes need it or not, so the rounds are kept short: one fused DPP maximum per level,
+// a ballot and a find-first for the winner, a register shift for the pop.
+// Lane j < k returns the j-th expert and its weight. Whole-wave call (uniform arguments).
+//
+// The loads (one logit, and with RAW one bare logit, per slot) and the selection are
+// separate steps, so that a caller can issue the loads early.
 template <int NK, bool RAW>
-__device__ __forceinline__ void wave_topk_select(const float (&lv)[NK], int E, int k, const float* raw, bool softmax,
-                                                 int& mye, float& myw) {
+struct TopkIn {
+  float v[NK];
+  float r[RAW ? NK : 1];
+};
+
+template <int NK, bool RAW>
+__device__ __forceinline__ void wave_topk_load(const float* lg, const float* raw, int E, TopkIn<NK, RAW>& in) {
   const int lane = threadIdx.x & (kWave - 1);
-  uint32_t key[NK];
 #pragma unroll
   for (int i = 0; i < NK; ++i) {
-    const int e = lane + kWave * i;
-    const uint32_t o = float_order_key(lv[i]);
-    key[i] = e < E ? (o > 1u ? o : 1u) : 0u;
+    const int e = min(NK * lane + i, E - 1);
+    in.v[i] = lg[e];
+    if constexpr (RAW) in.r[i] = raw[e];
   }
-  uint32_t lb = 0;
-  int li = 0;
-  auto rescan = [&]() {
-    lb = key[0];
-    li = 0;
+}
+
+// Comparator lists that sort NK values with the larger one first: optimal networks for
+// 2, 4, 6 and 8 inputs, Batcher's bitonic network for 16.
+template <int NK>
+struct SortNet;
+template <>
+struct SortNet<1> {
+  static constexpr int n = 0;
+  static constexpr int8_t ab[1][2] = {{0, 0}};
+};
+template <>
+struct SortNet<2> {
+  static constexpr int n = 1;
+  static constexpr int8_t ab[1][2] = {{0, 1}};
+};
+template <>
+struct SortNet<4> {
+  static constexpr int n = 5;
+  static constexpr int8_t ab[5][2] = {{0, 1}, {2, 3}, {0, 2}, {1, 3}, {1, 2}};
+};
+template <>
+struct SortNet<6> {
+  static constexpr int n = 12;
+  static constexpr int8_t ab[12][2] = {{0, 5}, {1, 3}, {2, 4}, {1, 2}, {3, 4}, {0, 3},
+                                       {2, 5}, {0, 1}, {2, 3}, {4, 5}, {1, 2}, {3, 4}};
+};
+template <>
+struct SortNet<8> {
+  static constexpr int n = 19;
+  static constexpr int8_t ab[19][2] = {{0, 1}, {2, 3}, {4, 5}, {6, 7}, {0, 2}, {1, 3}, {4, 6},
+                                       {5, 7}, {1, 2}, {5, 6}, {0, 4}, {1, 5}, {2, 6}, {3, 7},
+                                       {2, 4}, {3, 5}, {1, 2}, {3, 4}, {5, 6}};
+};
+template <>
+struct SortNet<16> {
+  static constexpr int n = 80;
+  // bitonic: blocks of size 2, 4, 8, 16; a block's direction alternates with bit `size`
+  static constexpr int8_t ab[80][2] = {
+      {0, 1},  {3, 2},   {4, 5},   {7, 6},   {8, 9},   {11, 10}, {12, 13}, {15, 14},   // size 2
+      {0, 2},  {1, 3},   {6, 4},   {7, 5},   {8, 10},  {9, 11},  {14, 12}, {15, 13},   // size 4
+      {0, 1},  {2, 3},   {5, 4},   {7, 6},   {8, 9},   {10, 11}, {13, 12}, {15, 14},
+      {0, 4},  {1, 5},   {2, 6},   {3, 7},   {12, 8},  {13, 9},  {14, 10}, {15, 11},   // size 8
+      {0, 2},  {1, 3},   {4, 6},   {5, 7},   {10, 8},  {11, 9},  {14, 12}, {15, 13},
+      {0, 1},  {2, 3},   {4, 5},   {6, 7},   {9, 8},   {11, 10}, {13, 12}, {15, 14},
+      {0, 8},  {1, 9},   {2, 10},  {3, 11},  {4, 12},  {5, 13},  {6, 14},  {7, 15},    // size 16
+      {0, 4},  {1, 5},   {2, 6},   {3, 7},   {8, 12},  {9, 13},  {10, 14}, {11, 15},
+      {0, 2},  {1, 3},   {4, 6},   {5, 7},   {8, 10},  {9, 11},  {12, 14}, {13, 15},
+      {0, 1},  {2, 3},   {4, 5},   {6, 7},   {8, 9},   {10, 11}, {12, 13}, {14, 15}};
+};
+
+// Wave maximum of a 32-bit value, as a scalar: four DPP levels within each row of 16
+// lanes, then row_bcast:15 and row_bcast:31 carry the row maxima up to lane 63.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint32_t dpp_max_step(uint32_t v) {
+  const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROWS, 0xF, false);
+  return o > v ? o : v;
+}
+__device__ __forceinline__ uint32_t wave_max_dpp(uint32_t v) {
+  v = dpp_max_step<0xB1, 0xF>(v);    // quad_perm [1,0,3,2]
+  v = dpp_max_step<0x4E, 0xF>(v);    // quad_perm [2,3,0,1]
+  v = dpp_max_step<0x124, 0xF>(v);   // row_ror:4
+  v = dpp_max_step<0x128, 0xF>(v);   // row_ror:8
+  v = dpp_max_step<0x142, 0xA>(v);   // row_bcast:15 into rows 1 and 3
+  v = dpp_max_step<0x143, 0xC>(v);   // row_bcast:31 into rows 2 and 3
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+// Sum (or maximum) of lanes 0..15, as a scalar: xor 1 and xor 2 within quads, then the
+// rotations by 4 and 8; lane 0's value is ((q0 + q1) + (q2 + q3)) over the quad values q.
+template <bool MAX>
+__device__ __forceinline__ float row0_reduce(float v) {
+  auto op = [](float a, float b) { return MAX ? fmaxf(a, b) : a + b; };
+  v = op(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false)));
+  v = op(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false)));
+  v = op(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xF, 0xF, false)));
+  v = op(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, false)));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+}
+
+// The lists live in vector registers typed as vectors, so that every access has a constant
+// index and the pop is one vector select (an array here can be turned into an indexed
+// stack object by the optimizer, which costs a compare chain per element).
+template <int NK>
+using U64v = uint64_t __attribute__((ext_vector_type(NK)));
+template <int NK>
+using F32v = float __attribute__((ext_vector_type(NK)));
+template <class V, size_t... I>
+__device__ __forceinline__ V shift_down(V c, std::index_sequence<I...>) {
+  return __builtin_shufflevector(c, V{}, (int)(I + 1)...);   // c[1..NK) then one zero
+}
+
+template <int NK, bool RAW>
+__device__ __forceinline__ void wave_topk_select(const TopkIn<NK, RAW>& in, int E, int k, bool softmax, int& mye,
+                                                 float& myw) {
+  const int lane = threadIdx.x & (kWave - 1);
+  U64v<NK> c;   // (key << 32) | ~slot
+  F32v<NK> rv;
 #pragma unroll
-    for (int i = 1; i < NK; ++i)
-      if (key[i] > lb) { lb = key[i]; li = i; }
-  };
-  rescan();
+  for (int i = 0; i < NK; ++i) {
+    const uint32_t o = float_order_key(in.v[i]);
+    const uint32_t key = NK * lane + i < E ? (o > 1u ? o : 1u) : 0u;
+    c[i] = ((uint64_t)key << 32) | (uint32_t)~(uint32_t)i;
+    rv[i] = RAW ? in.r[RAW ? i : 0] : 0.0f;
+  }
+#pragma unroll
+  for (int q = 0; q < SortNet<NK>::n; ++q) {
+    const int a = SortNet<NK>::ab[q][0], b = SortNet<NK>::ab[q][1];
+    const bool sw = c[b] > c[a];
+    const uint64_t ca = c[a], cb = c[b];
+    c[a] = sw ? cb : ca;
+    c[b] = sw ? ca : cb;
+    if constexpr (RAW) {
+      const float ra = rv[a], rb = rv[b];
+      rv[a] = sw ? rb : ra;
+      rv[b] = sw ? ra : rb;
+    }
+  }
   float myv = 0.0f;
   mye = 0;
   for (int j = 0; j < k; ++j) {
-    const uint32_t m = wave_ext_u32<true>(lb);
-    const uint64_t tied = __ballot(lb == m);
-    int be;
-    if (__popcll(tied) == 1) {
-      const int wl = __ffsll((long long)tied) - 1;
-      be = wl + kWave * __builtin_amdgcn_readlane(li, wl);
-    } else {   // equal keys in several lanes: the lowest index among them
-      be = (int)wave_ext_u32<false>(lb == m ? (uint32_t)(lane + kWave * li) : 0xFFFFFFFFu);
-    }
-    if (lane == (be & (kWave - 1))) {
-      const int taken = be / kWave;
-#pragma unroll
-      for (int i = 0; i < NK; ++i)
-        if (i == taken) key[i] = 0u;
-      rescan();
-    }
+    const uint64_t h = c[0];
+    const uint32_t head = (uint32_t)(h >> 32);
+    const uint32_t m = wave_max_dpp(head);
+    const int wl = __ffsll((long long)__ballot(head == m)) - 1;   // the lowest lane holding m
+    const int slot = (int)~(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)h, wl);
+    const float bv = RAW ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int((float)rv[0]), wl))
+                         : float_from_order_key(m);
+    const bool me = lane == wl;
+    c = me ? shift_down(c, std::make_index_sequence<NK>{}) : c;
+    if constexpr (RAW) rv = me ? shift_down(rv, std::make_index_sequence<NK>{}) : rv;
     if (lane == j) {
-      myv = float_from_order_key(m);
-      mye = be;
+      mye = NK * wl + slot;
+      myv = bv;
     }
   }
-  if constexpr (RAW) myv = raw[lane < k ? mye : 0];   // one load per selected expert
   float s;
   if (softmax) {   // exp(v - max v): with a selection bias the largest value need not come first
-    float mx = -INFINITY;
-    for (int j = 0; j < k; ++j) mx = fmaxf(mx, __int_as_float(__builtin_amdgcn_readlane(__float_as_int(myv), j)));
+    const float mx = RAW ? row0_reduce<true>(lane < k ? myv : -INFINITY)
+                         : __int_as_float(__builtin_amdgcn_readlane(__float_as_int(myv), 0));
     s = lane < k ? expf(myv - mx) : 0.0f;
   } else {
     s = lane < k ? 1.0f / (1.0f + expf(-myv)) : 0.0f;
   }
-  float tot = 0.0f;
-  for (int j = 0; j < k; ++j) tot += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s), j));
+  const float tot = row0_reduce<false>(s);   // k <= 16: the selection sits in lanes 0..15
   myw = lane < k ? s / tot : 0.0f;
 }
+
 template <int NK>
 __device__ __forceinline__ void wave_topk(const float* lg, int E, int k, const float* raw, bool softmax, int& mye,
                                           float& myw) {
-  float lv[NK];
-  wave_topk_load<NK>(lg, E, lv);
-  if (raw)
-    wave_topk_select<NK, true>(lv, E, k, raw, softmax, mye, myw);
-  else
-    wave_topk_select<NK, false>(lv, E, k, nullptr, softmax, mye, myw);
+  if (raw) {
+    TopkIn<NK, true> in;
+    wave_topk_load<NK, true>(lg, raw, E, in);
+    wave_topk_select<NK, true>(in, E, k, softmax, mye, myw);
+  } else {
+    TopkIn<NK, false> in;
+    wave_topk_load<NK, false>(lg, nullptr, E, in);
+    wave_topk_select<NK, false>(in, E, k, softmax, mye, myw);
+  }
+}
+
+// Routing fused into another kernel's prologue: the slot count follows E at run time
+// (1, 2, 4, 6 or 8 slots, E <= 512). Every load is issued whatever the count (unused
+// slots repeat a clamped index; without raw the raw loads repeat the logits), so the
+// caller's later waits for other loads never depend on a branch.
+constexpr int kTopkRtSlots = 8;
+__device__ __forceinline__ int topk_rt_slots(int E) {
+  return E <= 64 ? 1 : E <= 128 ? 2 : E <= 256 ? 4 : E <= 384 ? 6 : 8;
+}
+struct TopkRt {
+  float v[kTopkRtSlots];
+  float r[kTopkRtSlots];
+};
+__device__ __forceinline__ void topk_rt_load(const float* lg, const float* raw, int E, int nk, TopkRt& in) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const float* rs = raw ? raw : lg;
+#pragma unroll
+  for (int i = 0; i < kTopkRtSlots; ++i) {
+    const int e = min(nk * lane + i, E - 1);
+    in.v[i] = lg[e];
+    in.r[i] = rs[e];
+  }
+}
+template <int NK, bool RAW>
+__device__ __forceinline__ void topk_rt_select_n(const TopkRt& in, int E, int k, bool softmax, int& e, float& w) {
+  TopkIn<NK, RAW> t;
+#pragma unroll
+  for (int i = 0; i < NK; ++i) {
+    t.v[i] = in.v[i];
+    if constexpr (RAW) t.r[i] = in.r[i];
+  }
+  wave_topk_select<NK, RAW>(t, E, k, softmax, e, w);
+}
+__device__ __forceinline__ void topk_rt_select(const TopkRt& in, bool raw, int E, int k, bool softmax, int nk, int& e,
+                                               float& w) {
+  auto go = [&](auto nkc) {
+    constexpr int N = decltype(nkc)::value;
+    if (raw) topk_rt_select_n<N, true>(in, E, k, softmax, e, w);
+    else topk_rt_select_n<N, false>(in, E, k, softmax, e, w);
+  };
+  if (nk == 1) go(std::integral_constant<int, 1>{});
+  else if (nk == 2) go(std::integral_constant<int, 2>{});
+  else if (nk == 4) go(std::integral_constant<int, 4>{});
+  else if (nk == 6) go(std::integral_constant<int, 6>{});
+  else go(std::integral_constant<int, 8>{});
 }
 
 }  // namespace moe
