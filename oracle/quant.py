@@ -20,6 +20,13 @@ Test infrastructure (see oracle/__init__.py).
 * quantize_mxfp8 -- the same OCP rule for MXFP8 (the Inkling page's MXFP8 expert layers):
   shared exponent floor(log2(block amax)) minus 8 (the largest E4M3 exponent), clamped to
   [-127, 127]; elements rounded to E4M3 (nearest, ties to even, saturating at 448).
+* dequant_fp8_block -- the same page's load path starts from a block-scaled FP8
+  checkpoint: E4M3 expert weights with their block scales, each expert dequantized to
+  BF16 before the MXFP4 requantization. Readings: one FP32 scale per block_rows x
+  block_cols block of a [rows, cols] matrix (scales [ceil(rows/br), ceil(cols/bc)], the
+  edge blocks ragged); a value is E4M3(code) times its block's scale, one FP32 product
+  (rounded to nearest even), then rounded to BF16 (nearest even). NaN codes are outside
+  the domain.
 * quantize_nvfp4_weights -- BF16 -> NVFP4 weight requantization (the load path's other
   target format; the pages do not spell its rule out): the two-level NVFP4 recipe, one
   FP32 scale per tensor g = amax / 2688 and, per 16-block, the Four-Over-Six arithmetic
@@ -36,6 +43,7 @@ import numpy as np
 
 from .formats import (E2M1_TABLE, E4M3_TABLE, E8M0_TABLE, bf16_to_f64, e2m1_encode,
                       e4m3_encode_satfinite, pack_fp4, unpack_fp4)
+from .norm import to_bf16_bits
 
 F32 = np.float32
 NVFP4_BLOCK = 16
@@ -188,6 +196,34 @@ def quantize_mxfp8(x: np.ndarray):
     shared = np.clip(shared, -127, 127).astype(np.int64)
     y = np.ldexp(xb.astype(np.float64), -shared[:, :, None]).astype(np.float32)   # exact scaling
     return e4m3_encode_satfinite(y).reshape(rows, cols), (shared + 127).astype(np.uint8)
+
+
+def dequant_fp8_block(codes: np.ndarray, scales: np.ndarray, block_rows: int, block_cols: int) -> np.ndarray:
+    """Block-scaled FP8 weights to BF16 bit patterns: codes [rows, cols] E4M3 bytes, scales
+    [ceil(rows/block_rows), ceil(cols/block_cols)] FP32. Element (r, c) takes the scale of
+    block (r // block_rows, c // block_cols); its value is the FP32 product E4M3(code) *
+    scale (E4M3 values are exact in FP32; numpy's float32 product is correctly rounded),
+    then rounded once more, to BF16 with ties to even. Returns uint16 [rows, cols]."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    rows, cols = codes.shape
+    s = np.asarray(scales, dtype=np.float32)
+    if s.shape != (-(-rows // block_rows), -(-cols // block_cols)):
+        raise ValueError("scales must be [ceil(rows / block_rows), ceil(cols / block_cols)]")
+    vals = E4M3_TABLE[codes]
+    if not np.all(np.isfinite(vals)):
+        raise ValueError("dequant_fp8_block: NaN codes")
+    per = s[(np.arange(rows) // block_rows)[:, None], (np.arange(cols) // block_cols)[None, :]]
+    prod = vals.astype(np.float32) * per                       # one FP32 rounding
+    if not np.all(np.isfinite(prod)):
+        raise ValueError("dequant_fp8_block: product outside FP32")
+    return to_bf16_bits(prod.astype(np.float64))              # then BF16
+
+
+def requant_fp8_block_mxfp4(codes: np.ndarray, scales: np.ndarray, block_rows: int, block_cols: int):
+    """The load path from a block-scaled FP8 checkpoint: dequant_fp8_block, then
+    quantize_mxfp4 of those BF16 values. Returns (packed E2M1 codes, E8M0 scale bytes)."""
+    bits = dequant_fp8_block(codes, scales, block_rows, block_cols)
+    return quantize_mxfp4(bf16_to_f64(bits).astype(np.float32))
 
 
 def quantize_nvfp4_weights(x: np.ndarray):

@@ -483,3 +483,60 @@ def test_mxfp8_block_topped_below_256_saturates_its_top():
     codes, s = Q.quantize_mxfp8(x)
     assert s.tolist() == [[126]]                   # floor(log2 240) - 8 = -1
     assert codes[0, :2].tolist() == [0x7E, 0x40]   # 480 saturates to 448; 2.0 exact
+
+
+# ---------------------------------------------------------------- block-scaled FP8 input
+# "Day 0 support for Mistral Large 4 on vLLM", ROCm implementation details: the loader
+# reads block-FP8 expert weights with their block scales and dequantizes each expert to
+# BF16 before requantizing it to MXFP4.
+
+def test_fp8_block_worked_values():
+    # E4M3 0x38 = 1.0, 0x40 = 2.0, 0xC0 = -2.0, 0x3C = 1.5, 0x01 = 2^-9 (smallest subnormal)
+    codes = np.array([[0x38, 0x40, 0xC0, 0x3C, 0x01]], np.uint8)
+    bits = Q.dequant_fp8_block(codes, np.array([[0.5]], F32), 128, 128)
+    assert [int(b) for b in bits[0]] == [0x3F00, 0x3F80, 0xBF80, 0x3F40, 0x3A80]   # 0.5, 1, -1, 0.75, 2^-10
+
+
+def test_fp8_block_indexing_against_exact_products():
+    # a 5 x 7 matrix in 2 x 3 blocks (ragged last row and column of blocks); power-of-two
+    # scales keep every product exact, so each element must equal code value * its own
+    # block's scale, worked out here with rationals in explicit loops
+    rng = np.random.default_rng(3)
+    codes = rng.integers(0, 0x7F, size=(5, 7)).astype(np.uint8)   # non-negative, no NaN
+    codes[codes == 0x7F] = 0x7E
+    scales = np.ldexp(1.0, rng.integers(-6, 7, size=(3, 3))).astype(F32)
+    got = F.bf16_to_f64(Q.dequant_fp8_block(codes, scales, 2, 3))
+    for r in range(5):
+        for c in range(7):
+            want = Fraction(F.e4m3_value(int(codes[r, c]))) * Fraction(float(scales[r // 2, c // 3]))
+            assert Fraction(float(got[r, c])) == want, (r, c)
+
+
+def test_fp8_block_rounds_to_fp32_before_bf16():
+    # code 0x31 = 0.5625 and the FP32 scale with bits 0x3FB238E4: the exact product lies
+    # just above the BF16 midpoint 0.783203125 (between 0x3F48 = 0.78125 and 0x3F49 =
+    # 0.78515625); its FP32 rounding is that midpoint itself, which BF16 rounds to even
+    # (0x3F48). Rounding the exact product straight to BF16 would give 0x3F49 instead.
+    s = np.array([[0x3FB238E4]], np.uint32).view(F32)
+    exact = Fraction(F.e4m3_value(0x31)) * Fraction(float(s[0, 0]))
+    mid = Fraction(0.78125) + Fraction(1, 512)
+    assert exact > mid
+    assert Fraction(float(F32(float(exact)))) == mid
+    bits = Q.dequant_fp8_block(np.array([[0x31]], np.uint8), s, 1, 1)
+    assert int(bits[0, 0]) == 0x3F48
+
+
+def test_fp8_block_to_mxfp4_worked_block():
+    # one 32-block of E4M3 3.0 (0x44) with scale 2: BF16 6.0 everywhere, amax 6 ->
+    # exponent floor(log2 6) - 2 = 0 (byte 127), elements 6 -> E2M1 code 7
+    codes = np.full((1, 32), 0x44, np.uint8)
+    packed, sb = Q.requant_fp8_block_mxfp4(codes, np.array([[2.0]], F32), 128, 128)
+    assert sb.tolist() == [[127]]
+    assert packed.tolist() == [[0x77] * 16]
+
+
+def test_fp8_block_rejects_bad_scale_shape_and_nan():
+    with pytest.raises(ValueError):
+        Q.dequant_fp8_block(np.zeros((4, 4), np.uint8), np.ones((1, 1), F32), 2, 2)
+    with pytest.raises(ValueError):
+        Q.dequant_fp8_block(np.full((1, 1), 0x7F, np.uint8), np.ones((1, 1), F32), 1, 1)
