@@ -85,6 +85,24 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// Brings every 64-byte line of a kernel's argument block (an Args struct passed by value)
+// into the scalar cache at the kernel's start. The compiler loads the argument fields it
+// needs in several batches (it keeps few in scalar registers and reloads them), each batch
+// waiting for all of its loads; a batch that touches a line not cached yet waits a memory
+// round trip, and several such batches in a row delay the prologue. One plain load per
+// line, consumed together, joins the first batch, so later batches hit the cache.
+// Offsets stay inside the struct.
+template <class Args>
+__device__ __forceinline__ void warm_args() {
+  constexpr int S = (int)sizeof(Args);
+  static_assert(S >= 4 && S <= 64 * 12, "argument block of at most 12 lines");
+  const auto* p = (const __attribute__((address_space(4))) uint32_t*)__builtin_amdgcn_kernarg_segment_ptr();
+  auto at = [&](int i) { return p[(64 * i < S - 4 ? 64 * i : S - 4) / 4]; };
+  // one statement consumes every value, so the loads go out in one batch
+  asm volatile("" ::"s"(at(0)), "s"(at(1)), "s"(at(2)), "s"(at(3)), "s"(at(4)), "s"(at(5)), "s"(at(6)),
+               "s"(at(7)), "s"(at(8)), "s"(at(9)), "s"(at(10)), "s"(at(11)), "s"(p[S / 4 - 1]));
+}
+
 // ---------------------------------------------------------------- reductions
 // Wave-wide maximum of a 64-bit key, returned to every lane. Within each row of 16
 // lanes DPP moves (xor 1, xor 2, rotate 4, rotate 8) spread the row maximum to all its

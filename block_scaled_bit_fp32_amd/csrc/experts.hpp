@@ -980,6 +980,7 @@ __device__ __forceinline__ void gateup_walk(const ExpertArgs& a, const ExpertLds
 template <int RF, int SF, int AF>
 __global__ void __launch_bounds__(kBlock, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) gateup_kernel(ExpertArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
+  warm_args<ExpertArgs>();
   ExpertLds L = carve(a, smem);
   const bool shared = (int)blockIdx.x < a.sh_wgs;
   if (shared) {
@@ -1221,9 +1222,10 @@ __device__ __forceinline__ void walk_tokens(const ExpertArgs& a, const ExpertLds
   // prologue: the first token's experts (scalar loads), rows, factors, global scales and
   // topk_ids, then every sub-step's weight loads of the first item, then LDS
 #pragma unroll
-  for (int jj = 0; jj < NJ; ++jj) {
+  for (int jj = 0; jj < NJ; ++jj) {   // every load issued (clamped index), so they go out as one batch
     const int j = jof(jj);
-    exA[jj] = j < a.k && j < J ? clamp_e(a.ids[staged_t * a.k + j]) : 0;
+    const int v = a.ids[staged_t * a.k + min(j, a.k - 1)];
+    exA[jj] = j < a.k && j < J ? clamp_e(v) : 0;
   }
   uint4 raw[kPreSlotsTok];
   const SlotMap<AK> smap(m, a.rw.K);
@@ -1289,6 +1291,7 @@ __device__ __forceinline__ void walk_tokens(const ExpertArgs& a, const ExpertLds
 template <int RF, int SF, int AF>
 __global__ void __launch_bounds__(kBlock, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) down_kernel(ExpertArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
+  warm_args<ExpertArgs>();
   ExpertLds L = carve(a, smem);
   if constexpr (SF == RF) {
     if (a.token_mode) {

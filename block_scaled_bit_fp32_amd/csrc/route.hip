@@ -47,6 +47,7 @@ __device__ __forceinline__ void quant_token(const RouteArgs& a, const Row& row, 
 // code in the same order) and quantize them.
 template <int ET, int TT, bool NORM>
 __global__ void __launch_bounds__(kBlock) route_gemv_kernel(RouteArgs a) {
+  warm_args<RouteArgs>();
   __shared__ float red[(kBlock / kWave) * ET * TT];
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int n_router = a.n_tt * a.n_et;
