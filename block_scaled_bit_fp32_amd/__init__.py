@@ -29,7 +29,7 @@ MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_ELAUNCH = 0, -1, -2, -
 WFMT = {"bf16": 0, "nvfp4": 1, "mxfp4": 2, "mxfp8": 3}
 AFMT = {"bf16": 0, "nvfp4_4o6": 1, "fp8_token": 2, "mxfp4": 3, "mxfp8": 4}
 SCORE = {"sigmoid": 0, "softmax": 1}
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 
 class MoeError(RuntimeError):
@@ -88,6 +88,7 @@ _SIGNATURES = {
     "moe_requant_mxfp4": (_I32, [_P, ctypes.c_int64, _I32, _P, _P, _P]),
     "moe_requant_nvfp4": (_I32, [_P, _I32, ctypes.c_int64, _I32, _P, _P, _P, _P]),
     "moe_requant_mxfp8": (_I32, [_P, ctypes.c_int64, _I32, _P, _P, _P]),
+    "moe_requant_fp8_block_mxfp4": (_I32, [_P, _P, ctypes.c_int64, _I32, _I32, _I32, _P, _P, _P]),
     "moe_profile_begin": (_I32, []),
     "moe_profile_end": (_I32, [ctypes.POINTER(KernelTimeT), _I32]),
     "moe_last_error": (ctypes.c_char_p, []),
@@ -426,6 +427,22 @@ def requant_mxfp8(w: torch.Tensor):
     codes = _aligned_empty(rows * cols, w.device).view(rows, cols)
     scales = torch.empty((rows, cols // 32), dtype=torch.uint8, device=w.device)
     _check(_lib.moe_requant_mxfp8(w.data_ptr(), rows, cols, codes.data_ptr(), scales.data_ptr(), _stream()))
+    return codes, scales
+
+
+def requant_fp8_block_mxfp4(w: torch.Tensor, block_scales: torch.Tensor, block_rows: int, block_cols: int):
+    """moe_requant_fp8_block_mxfp4 of E4M3 bytes w [rows, cols] (uint8) with FP32 block
+    scales [ceil(rows/block_rows), ceil(cols/block_cols)]: returns (codes [rows, cols/2],
+    E8M0 scales [rows, cols/32]), the MOE_W_MXFP4 layout."""
+    if w.dtype != torch.uint8 or w.dim() != 2 or block_scales.dtype != torch.float32:
+        raise TypeError("w must be uint8 [rows, cols] and block_scales float32")
+    w = w.contiguous()
+    block_scales = block_scales.contiguous()
+    rows, cols = w.shape
+    codes = _aligned_empty(rows * cols // 2, w.device).view(rows, cols // 2)
+    scales = torch.empty((rows, cols // 32), dtype=torch.uint8, device=w.device)
+    _check(_lib.moe_requant_fp8_block_mxfp4(w.data_ptr(), block_scales.data_ptr(), rows, cols, block_rows, block_cols,
+                                            codes.data_ptr(), scales.data_ptr(), _stream()))
     return codes, scales
 
 

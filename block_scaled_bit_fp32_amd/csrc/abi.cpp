@@ -18,6 +18,8 @@ hipError_t launch_requant_mxfp4(const uint16_t* x, int64_t nblocks, uint8_t* cod
                                 hipStream_t s);
 hipError_t launch_requant_nvfp4(const uint16_t* x, int ntensors, int64_t n, uint8_t* codes, uint8_t* scales,
                                 float* gscale, hipStream_t s);
+hipError_t launch_requant_fp8b_mxfp4(const uint8_t* w, const float* bscale, int64_t rows, int cols, int block_rows,
+                                     int block_cols, uint8_t* codes, uint8_t* scales, hipStream_t s);
 hipError_t launch_requant_mxfp8(const uint16_t* x, int64_t nblocks, uint8_t* codes, uint8_t* scales,
                                 hipStream_t s);
 hipError_t launch_quantize_nvfp4(const uint16_t* x, int rows, int cols, uint8_t* codes,
@@ -881,6 +883,28 @@ moe_status_t moe_requant_mxfp4(const uint16_t* w_bf16, int64_t rows, int32_t col
   if (!bad.empty()) return set_err(MOE_EINVAL, bad);
   if (rows == 0) return MOE_OK;
   if (launch_requant_mxfp4(w_bf16, rows * (cols / 32), codes, scales, stream) != hipSuccess)
+    return set_err(MOE_ELAUNCH, "requant kernel launch failed");
+  return MOE_OK;
+}
+
+moe_status_t moe_requant_fp8_block_mxfp4(const uint8_t* w_fp8, const float* block_scales, int64_t rows, int32_t cols,
+                                         int32_t block_rows, int32_t block_cols, uint8_t* codes, uint8_t* scales,
+                                         hipStream_t stream) {
+  std::string bad;
+  if (rows < 0) bad += "rows must be >= 0; ";
+  if (cols <= 0 || cols % 32) bad += "cols must be a positive multiple of 32; ";
+  if (block_rows <= 0 || block_cols <= 0) bad += "block_rows and block_cols must be positive; ";
+  if (rows > 0 && cols > 0 && rows > (int64_t)0x7FFFFFFF * 32 / cols) bad += "at most 2^31 blocks of 32 per call; ";
+  if (rows > 0) {
+    if (!w_fp8 || !aligned(w_fp8, 16)) bad += "w_fp8 must be non-NULL and 16-byte aligned; ";
+    if (!block_scales) bad += "block_scales is NULL; ";
+    if (!codes || !aligned(codes, 16)) bad += "codes must be non-NULL and 16-byte aligned; ";
+    if (!scales) bad += "scales is NULL; ";
+  }
+  if (!bad.empty()) return set_err(MOE_EINVAL, bad);
+  if (rows == 0) return MOE_OK;
+  if (launch_requant_fp8b_mxfp4(w_fp8, block_scales, rows, cols, block_rows, block_cols, codes, scales, stream) !=
+      hipSuccess)
     return set_err(MOE_ELAUNCH, "requant kernel launch failed");
   return MOE_OK;
 }

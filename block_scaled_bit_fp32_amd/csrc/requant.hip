@@ -155,6 +155,54 @@ __global__ void __launch_bounds__(kBlock) requant_mxfp8_kernel(const uint16_t* x
   scales[b] = (uint8_t)sb;
 }
 
+// Block-scaled FP8 input (the checkpoint the Mistral Large 4 page's loader reads: E4M3
+// expert weights with one FP32 scale per block_rows x block_cols block): each value is
+// decoded, multiplied by its block's scale (one FP32 product) and rounded to BF16, the
+// expert's BF16 form; its 32-blocks then take the MXFP4 rule above. One thread per
+// 32-block of a row: block b holds row r = b / (cols / 32), columns c0 .. c0 + 31, whose
+// scales sit in row r / block_rows of the scale grid, from column c0 / block_cols on.
+__global__ void __launch_bounds__(kBlock) requant_fp8b_mxfp4_kernel(const uint8_t* w, const float* bscale,
+                                                                    int64_t nblocks, int cols, int block_rows,
+                                                                    int block_cols, int scale_cols, uint8_t* codes,
+                                                                    uint8_t* scales) {
+  const int64_t b = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+  if (b >= nblocks) return;
+  const int per_row = cols / 32;
+  const int64_t r = b / per_row;
+  const int c0 = (int)(b - r * per_row) * 32;
+  const float* srow = bscale + (r / block_rows) * scale_cols;
+  const uint4* src = reinterpret_cast<const uint4*>(w + b * 32);
+  const uint4 q0 = src[0], q1 = src[1];
+  const uint32_t wd[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+  int sc = c0 / block_cols;
+  int next = (sc + 1) * block_cols;   // first column of the next scale block
+  float s = srow[sc];
+  float v[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    if (c0 + i == next) {
+      ++sc;
+      next += block_cols;
+      s = srow[sc];
+    }
+    const float p = e4m3_to_f32((wd[i >> 2] >> (8 * (i & 3))) & 0xFFu) * s;
+    v[i] = bf16_to_f32(f32_to_bf16_rne(p));
+  }
+  uint32_t q[4];
+  const uint32_t sb = mx_block_fp4(v, q);
+  *reinterpret_cast<uint4*>(codes + 16 * b) = make_uint4(q[0], q[1], q[2], q[3]);
+  scales[b] = (uint8_t)sb;
+}
+
+hipError_t launch_requant_fp8b_mxfp4(const uint8_t* w, const float* bscale, int64_t rows, int cols, int block_rows,
+                                     int block_cols, uint8_t* codes, uint8_t* scales, hipStream_t s) {
+  const int64_t nblocks = rows * (cols / 32);
+  const int64_t grid = (nblocks + kBlock - 1) / kBlock;
+  const int scale_cols = (cols + block_cols - 1) / block_cols;
+  return launch_kernel(K_QUANT, requant_fp8b_mxfp4_kernel, dim3((unsigned)grid), dim3(kBlock), 0, s, w, bscale,
+                       nblocks, cols, block_rows, block_cols, scale_cols, codes, scales);
+}
+
 hipError_t launch_requant_mxfp8(const uint16_t* x, int64_t nblocks, uint8_t* codes, uint8_t* scales,
                                 hipStream_t s) {
   const int64_t grid = (nblocks + kBlock - 1) / kBlock;

@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 4
+#define MOE_ABI_VERSION 5
 
 typedef enum {
   MOE_OK = 0,
@@ -284,6 +284,28 @@ moe_status_t quantize_nvfp4_4o6(const uint16_t *x_bf16, int32_t rows, int32_t co
  *   of experts is one call with rows = experts * rows per expert. */
 moe_status_t moe_requant_mxfp4(const uint16_t *w_bf16, int64_t rows, int32_t cols,
                                uint8_t *codes, uint8_t *scales, hipStream_t stream);
+
+/* Load-time requantization of block-scaled FP8 weights to MXFP4 (MOE_W_MXFP4 layout): the
+ * checkpoint the Mistral Large 4 page's loader reads (ROCm implementation details: block-FP8
+ * expert weights with their block scales, each expert dequantized to BF16 and requantized
+ * to MXFP4). Element (r, c) is E4M3(w_fp8[r][c]) times block_scales[r / block_rows]
+ * [c / block_cols], one FP32 product rounded to nearest even, then rounded to BF16 (nearest
+ * even); the BF16 rows then take the moe_requant_mxfp4 rule, bit for bit.
+ *   w_fp8 [rows][cols] E4M3 bytes (OCP), device, 16-byte aligned; cols a positive
+ *   multiple of 32; NaN codes (0x7F, 0xFF) and products beyond BF16's range are outside
+ *   the contract (their blocks' outputs are unspecified).
+ *   block_scales [ceil(rows / block_rows)][ceil(cols / block_cols)] FP32, device; the
+ *   edge blocks may be ragged; block_rows, block_cols >= 1 (128 x 128 in common
+ *   checkpoints; block_cols need not be a multiple of 32).
+ *   codes [rows][cols/2] (element 2i in the low nibble), 16-byte aligned; scales
+ *   [rows][cols/32] E8M0 bytes (outputs). rows = 0 enqueues nothing; at most 2^31
+ *   32-blocks per call. A stack of experts is one call when the rows per expert are a
+ *   multiple of block_rows (the scale grid then stacks the same way), else one call per
+ *   expert. Asynchronous on stream; caller-owned buffers. */
+moe_status_t moe_requant_fp8_block_mxfp4(const uint8_t *w_fp8, const float *block_scales,
+                                         int64_t rows, int32_t cols, int32_t block_rows,
+                                         int32_t block_cols, uint8_t *codes, uint8_t *scales,
+                                         hipStream_t stream);
 
 /* Load-time weight requantization to MXFP8 (MOE_W_MXFP8 layout), for MXFP8 expert layers
  * (Inkling page, mixed-precision MoE: MXFP8 expert layers): the same OCP MX v1.0 rule as

@@ -20,7 +20,7 @@ def _declared_functions():
 def test_header_declares_the_boundary():
     names = _declared_functions()
     for n in ("moe_route", "moe_expert_forward", "moe_forward", "quantize_nvfp4_4o6", "moe_requant_mxfp4",
-              "moe_requant_nvfp4", "moe_requant_mxfp8",
+              "moe_requant_nvfp4", "moe_requant_mxfp8", "moe_requant_fp8_block_mxfp4",
               "moe_layer_check",
               "moe_workspace_bytes", "moe_workspace_init", "moe_xq_bytes", "moe_last_error",
               "moe_abi_version"):
@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol(lib):
     so = ctypes.CDLL(lib.LIB_PATH)
     for n in _declared_functions():
         assert hasattr(so, n), n
-    assert so.moe_abi_version() == 4
+    assert so.moe_abi_version() == 5
 
 
 def _fake_layer(lib, name, **over):
@@ -126,6 +126,17 @@ def test_calls_validate_before_launching(lib):
     assert so.moe_requant_nvfp4(1 << 20, 70000, i64(4), 32, 1 << 20, 1 << 20, 1 << 20, None) == lib.MOE_EINVAL
     assert so.moe_requant_mxfp8(1 << 20, i64(4), 48, 1 << 20, 1 << 20, None) == lib.MOE_EINVAL
     assert so.moe_requant_mxfp8(None, i64(0), 64, None, None, None) == 0
+    # block-scaled FP8 input: the same conventions, plus the block shape
+    fb = so.moe_requant_fp8_block_mxfp4
+    assert fb(1 << 20, 1 << 20, i64(4), 48, 128, 128, 1 << 20, 1 << 20, None) == lib.MOE_EINVAL
+    assert "multiple of 32" in so.moe_last_error().decode()
+    assert fb(1 << 20, 1 << 20, i64(4), 64, 0, 128, 1 << 20, 1 << 20, None) == lib.MOE_EINVAL
+    assert "block_rows" in so.moe_last_error().decode()
+    assert fb(None, None, i64(1), 64, 128, 128, (1 << 20) + 8, None, None) == lib.MOE_EINVAL
+    msg = so.moe_last_error().decode()
+    assert "w_fp8" in msg and "block_scales" in msg and "codes" in msg and "scales is NULL" in msg
+    assert fb(1 << 20, 1 << 20, i64(-1), 64, 128, 128, 1 << 20, 1 << 20, None) == lib.MOE_EINVAL
+    assert fb(None, None, i64(0), 64, 128, 128, None, None, None) == 0
     # moe_forward: every check of both halves before the first launch
     st = so.moe_forward(ctypes.byref(s), 1 << 20, 1, 1 << 20, 1 << 20, None, None, 1 << 20, 1 << 24, None, None)
     assert st == lib.MOE_EINVAL and "y_bf16" in so.moe_last_error().decode()

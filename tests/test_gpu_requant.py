@@ -240,3 +240,94 @@ def test_mxfp8_requantized_layer_runs_end_to_end(lib):
             ok, max_abs, rel = y_close(bf16_bits_to_f64(y), ref["y"])
             say(f"[requant]   T={T} y max_abs/r={max_abs:.3g} rel_l2={rel:.3g}")
             assert ok, (max_abs, rel)
+
+
+# ---------------------------------------------------------------- block-scaled FP8 input
+def _check_fp8b(lib, codes, bscale, br, bc):
+    rows, cols = codes.shape
+    say(f"[requant] fp8-block -> mxfp4 rows={rows} cols={cols} block={br}x{bc}")
+    gc, gs = lib.requant_fp8_block_mxfp4(torch.from_numpy(codes).cuda(), torch.from_numpy(bscale).cuda(), br, bc)
+    torch.cuda.synchronize()
+    rc, rs = OQ.requant_fp8_block_mxfp4(codes, bscale, br, bc)
+    assert np.array_equal(gs.cpu().numpy(), rs)
+    assert np.array_equal(gc.cpu().numpy(), rc)
+
+
+def _fp8_codes(rng, shape):
+    c = rng.integers(0, 256, size=shape).astype(np.uint8)
+    c[(c & 0x7F) == 0x7F] ^= 0x01          # no NaN codes
+    return c
+
+
+def test_requant_fp8_block_128x128(lib):
+    rng = np.random.default_rng(51)
+    codes = _fp8_codes(rng, (256, 512))
+    bscale = np.exp(rng.normal(size=(2, 4)) * 3).astype(np.float32) * 1e-3
+    _check_fp8b(lib, codes, bscale, 128, 128)
+
+
+def test_requant_fp8_block_ragged_and_straddling_blocks(lib):
+    """300 x 96 in 128 x 128 blocks (ragged edge blocks), then 45 x 160 in 7 x 48 blocks:
+    a 32-block of a row straddles two scale blocks."""
+    rng = np.random.default_rng(52)
+    codes = _fp8_codes(rng, (300, 96))
+    _check_fp8b(lib, codes, (rng.random((3, 1)) + 0.5).astype(np.float32), 128, 128)
+    codes = _fp8_codes(rng, (45, 160))
+    _check_fp8b(lib, codes, np.exp(rng.normal(size=(7, 4)) * 2).astype(np.float32), 7, 48)
+
+
+def test_requant_fp8_block_every_code_and_double_rounding(lib):
+    """Every finite E4M3 code in every column position, under scales that include the one
+    whose products round to FP32 exactly on a BF16 tie (bits 0x3FB238E4)."""
+    finite = np.array([c for c in range(256) if (c & 0x7F) != 0x7F] + [0x00, 0x80], np.uint8)   # 256
+    codes = np.stack([np.roll(finite, 37 * i) for i in range(32)])                              # [32][256]
+    sbits = np.array([0x3FB238E4, 0x3F800000, 0x3B800000, 0x42F00000], np.uint32)
+    bscale = np.resize(sbits, (32, 8)).view(np.float32).copy()
+    _check_fp8b(lib, codes, bscale, 1, 32)
+
+
+def test_fp8_block_requantized_layer_runs_end_to_end(lib):
+    """The load path from a block-FP8 checkpoint: a 16-expert Flint-shaped layer whose BF16
+    expert weights are turned into FP8 with 128 x 128 block scales (amax / 448 per block),
+    requantized to MXFP4 on the GPU (codes bit-exact against the oracle), loaded as an
+    MXFP4 layer, and run: ids and y against the oracle on those codes."""
+    import dataclasses
+    from oracle import formats as OF
+    from oracle import layer as OL
+    from parity_util import check_ids, y_close
+    base = dataclasses.replace(synth.CONFIGS["flint_bf16"], name="flint_bf16_e16", E=16, k=4,
+                               router_bias=False)
+    L = synth.make_layer(base)
+    cfg = dataclasses.replace(base, name="flint_mxfp4_from_fp8", wfmt=synth.W_MXFP4)
+    Lq = dict(L, cfg=cfg)
+    for name in ("w13", "w2"):
+        w = bf16_bits_to_f64(torch.from_numpy(L[name]["codes"].view(np.int16)))     # [E][rows][K]
+        E, rows, K = w.shape
+        w2 = w.reshape(E * rows, K)
+        br, bc = 128, 128
+        nb_r, nb_c = -(-E * rows // br), -(-K // bc)
+        pad = np.zeros((nb_r * br, nb_c * bc))
+        pad[:E * rows, :K] = np.abs(w2)
+        amax = pad.reshape(nb_r, br, nb_c, bc).max(axis=(1, 3))
+        bscale = np.where(amax > 0, amax / 448.0, 1.0).astype(np.float32)
+        per = bscale[(np.arange(E * rows) // br)[:, None], (np.arange(K) // bc)[None, :]].astype(np.float64)
+        fp8 = OF.e4m3_encode_satfinite((w2 / per).astype(np.float32))
+        _check_fp8b(lib, fp8, bscale, br, bc)
+        codes, scales = lib.requant_fp8_block_mxfp4(torch.from_numpy(fp8).cuda(), torch.from_numpy(bscale).cuda(),
+                                                    br, bc)
+        torch.cuda.synchronize()
+        Lq[name] = {"codes": codes.cpu().numpy().reshape(E, rows, -1),
+                    "scales": scales.cpu().numpy().reshape(E, rows, -1), "gscale": None}
+    dl = lib.DeviceLayer.from_host(Lq)
+    for T in (1, 8):
+        x_np = synth.make_x(base, T)
+        ref = OL.moe_layer(Lq, x_np)
+        ws = lib.Workspace(dl, T)
+        y, ids, w, _ = lib.forward(dl, torch.from_numpy(x_np.view(np.int16)).cuda(), ws)
+        torch.cuda.synchronize()
+        ids_g = ids.cpu().numpy()
+        assert not check_ids(ids_g, ref, cfg.k)
+        if np.array_equal(ids_g, ref["ids"]):
+            ok, max_abs, rel = y_close(bf16_bits_to_f64(y), ref["y"])
+            say(f"[requant]   T={T} y max_abs/r={max_abs:.3g} rel_l2={rel:.3g}")
+            assert ok, (max_abs, rel)
