@@ -129,11 +129,11 @@ constexpr int kLateDown16 = 14;       // in 16ths (timestamps: they end ~15% / ~
 constexpr int kGroupTok = 32;         // tokens per unit in the grouped kernels
 
 // Grouped map of one weight class: rows of K elements, `rows_per_tile` rows (or
-// intermediate indices for gate/up) per row tile of `tile_of` rows, FP32 activations
-// when split. False if the shape does not tile.
+// intermediate indices for gate/up) per row tile, BF16 activations staged. False if the
+// shape does not tile.
 // mx_bits: 4 or 8 for MX weights on the scaled MFMA with 4- or 8-bit activation codes
 // (staged raw), 0 otherwise.
-bool plan_group(int fmt, int K, int rows, int rows_per_tile, bool split, int mx_bits, GroupMap& g) {
+bool plan_group(int fmt, int K, int rows, int rows_per_tile, int mx_bits, GroupMap& g) {
   const int KS = group_ks(fmt);
   if (K % KS || rows % rows_per_tile) return false;
   g.KS = KS;
@@ -143,10 +143,9 @@ bool plan_group(int fmt, int K, int rows, int rows_per_tile, bool split, int mx_
   // a row tile moves NS stages of 4 waves x 64 bytes x 64 lanes of weights (cw: 256-byte
   // units); each token adds a share of MFMA and staging work
   g.cw = g.NS * 64;
-  g.ct = g.NS * (split ? 4 : 2);
-  g.split = split ? 1 : 0;
+  g.ct = g.NS * 2;
   g.scaled = mx_bits ? 1 : 0;
-  g.tstride = mx_bits ? KS * mx_bits / 8 + 16 : KS * (split ? 4 : 2) + 16;
+  g.tstride = mx_bits ? KS * mx_bits / 8 + 16 : KS * 2 + 16;
   return true;
 }
 
@@ -242,10 +241,10 @@ bool make_plan(const moe_layer_t& L, int T, int path, Plan& p) {
   // MX routed weights with 8- or 4-bit activations run on the scaled MFMA
   const bool mx_w = L.wfmt == W_MXFP4 || L.wfmt == W_MXFP8;
   const int mx_bits = mx_w && (L.afmt == A_FP8_TOKEN || L.afmt == A_MXFP8) ? 8 : (mx_w && L.afmt == A_MXFP4 ? 4 : 0);
-  p.grouped = want && plan_group(L.wfmt, L.H, L.I, 64, false, mx_bits, p.gu_rg) &&
-              plan_group(sfmt, L.H, Ish, 64, false, 0, p.gu_sg) &&
-              plan_group(L.wfmt, L.I, L.H, 128, L.afmt == A_BF16, mx_bits, p.dn_rg) &&
-              plan_group(sfmt, Ish, L.H, 128, true, 0, p.dn_sg);
+  p.grouped = want && plan_group(L.wfmt, L.H, L.I, 64, mx_bits, p.gu_rg) &&
+              plan_group(sfmt, L.H, Ish, 64, 0, p.gu_sg) &&
+              plan_group(L.wfmt, L.I, L.H, 128, mx_bits, p.dn_rg) &&
+              plan_group(sfmt, Ish, L.H, 128, 0, p.dn_sg);
   if (p.grouped) {
     auto gbound = [&](const GroupMap& g, int units) {
       return (int64_t)units * g.steps * (g.cw + (int64_t)g.ct * g.NG);
@@ -254,13 +253,22 @@ bool make_plan(const moe_layer_t& L, int T, int path, Plan& p) {
       p.grouped = false;
   }
   if (p.grouped) {
+    const size_t gemv_tiles[4] = {p.gu_tile, p.dn_tile, p.gu_lds, p.dn_lds};
     auto gtile = [&](const GroupMap& r, const GroupMap& s) {
-      return align_up(2 * std::max(group_buf_bytes(r), L.has_shared ? group_buf_bytes(s) : 0), 16);
+      return align_up(2 * std::max(group_buf_bytes(r), L.has_shared ? group_buf_bytes(s) : 0), 16) + kGWeightLds;
     };
     p.gu_tile = gtile(p.gu_rg, p.gu_sg);
     p.dn_tile = gtile(p.dn_rg, p.dn_sg);
     p.gu_lds = p.list_bytes + p.gu_tile;
     p.dn_lds = p.list_bytes + p.dn_tile;
+    // two workgroups per compute unit, or the GEMV kernels (their LDS stays within 64 KB)
+    if (std::max(p.gu_lds, p.dn_lds) > (size_t)kGroupedLdsMax) {
+      p.grouped = false;
+      p.gu_tile = gemv_tiles[0];
+      p.dn_tile = gemv_tiles[1];
+      p.gu_lds = gemv_tiles[2];
+      p.dn_lds = gemv_tiles[3];
+    }
   }
   return true;
 }

@@ -7,15 +7,19 @@
 // the unit's (up to) 32 tokens with v_mfma_f32_32x32x16_bf16:
 //   A (32 rows x 16 K): weights, decoded exactly to BF16 in registers (E2M1 and E4M3
 //     values times their block scale have at most 6 significant bits);
-//   B (16 K x 32 tokens): activations, staged per K stage in LDS as BF16 (exact for
-//     BF16 tokens and for decoded NVFP4 / FP8 activations), or as FP32 for the down
-//     projection of FP32 h, fed as three BF16 parts hi + mid + lo that sum to h exactly;
+//   B (16 K x 32 tokens): activations, staged per K stage in LDS as BF16 (BF16 tokens,
+//     decoded NVFP4 / FP8 activations, and h, which the gate/up kernel stores as BF16
+//     where it is not re-quantized, as the GEMV kernels do);
 //   accumulation in FP32. Lane l holds row l % 32 of A and token l % 32 of B and takes
 //   its K elements from half l / 32 of the stage; A and B use the same K order, which
 //   is all the dot products need.
-// A lane holds 64 bytes of weights per stage, loaded one stage ahead (two register
-// sets alternate), and the next stage's activations and scales are loaded before those
-// weights and stored to the other LDS buffer after the current stage's MFMAs.
+// Weights: a stage is 128 bytes of each of the workgroup's 128 rows. They are loaded
+// coalesced (each load covers 8 rows x 128 contiguous bytes), one stage ahead in
+// registers, and written to an LDS tile after the current stage's MFMAs; each lane then
+// reads its 64 bytes in the MFMA layout from there. Loading the MFMA layout directly
+// (a lane reads 64 bytes of one row, a wave 32 rows) reads far slower on this chip. The
+// next stage's activations and scales are loaded before those weights and stored to the
+// other LDS buffer after the current stage's MFMAs.
 #pragma once
 #include "experts.hpp"
 
@@ -84,11 +88,11 @@ __device__ __forceinline__ bf16x8_t weight_frag(const GStage& g, int s) {
 // this wave's row r (0..31) of row tile `tile` of expert e; `op` is the class's
 // GateupOps / DownOps (activation loads and scales); `sink(cx, tile, acc, tsc, gs)`
 // consumes a finished row tile (lane token l % 32, rows per the MFMA layout).
-template <int FMT, bool SPLIT, class Ops, class RowOf, class Sink>
+template <int FMT, class Ops, class RowOf, class Sink>
 __device__ __forceinline__ void walk_grouped(const WTensor& W, const GroupMap& gm, const ExpertLds& L,
                                              const ClassTab& C, const Span& sp, const Ops& op, RowOf row_of,
                                              Sink sink) {
-  constexpr int PER = SPLIT ? 4 : 8;      // staged elements per 16-byte slot
+  constexpr int PER = 8;                  // staged BF16 elements per 16-byte slot
   constexpr int KS = group_ks(FMT);
   constexpr int SPR = KS / PER;           // slots per staged token row
   constexpr int NSTEP = KS / 16;          // MFMA steps per stage
@@ -127,11 +131,17 @@ __device__ __forceinline__ void walk_grouped(const WTensor& W, const GroupMap& g
       g.gs[0] = op.gs(p.e, 0);
       g.gs[1] = op.gs(p.e, 1);
     }
+    // weights: load q covers rows 8q .. 8q + 7 of the wave's 32, 128 contiguous bytes each
+    // (the stage's part of the row); lane l takes 16-byte chunk (l % 8) ^ (row % 8) of row
+    // 8q + l / 8, which is where it lands in the LDS tile (see store)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int r = 8 * q + (lane >> 3);
+      const int64_t wr = row_of(p.e, p.s, r);
+      g.w[q] = load_stream16(W.codes + wr * W.code_row_bytes + elem_byte<FMT>(p.b * KS) + 16 * ((lane ^ r) & 7));
+    }
     const int64_t row = row_of(p.e, p.s, lr);
     const int k0 = p.b * KS + half * (KS / 2);
-    const uint8_t* wp = W.codes + row * W.code_row_bytes + elem_byte<FMT>(k0);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) g.w[i] = load_stream16(wp + 16 * i);
     if constexpr (FMT == W_NVFP4) {
       g.sc = *reinterpret_cast<const uint2*>(W.scales + row * W.scale_row_bytes + (k0 >> 4));
     } else if constexpr (FMT == W_MXFP4) {
@@ -145,7 +155,14 @@ __device__ __forceinline__ void walk_grouped(const WTensor& W, const GroupMap& g
   // stores of one position's staged data into LDS buffer `buf`
   float* s_tsc = L.w_tsc;       // [32] token scales of the current row tile
   float* s_gs = L.w_gs;         // [2] its expert's global scales
+  // weight tile: [wave][32 rows][128 bytes], 16-byte chunk c of row r at slot c ^ (r % 8),
+  // so that the 8 lanes of a read phase hit 8 different bank groups
+  uint8_t* wlds = L.tile + 2 * (kGTok * gm.tstride);
   auto store = [&](const Cursor& p, const GStage& g, int buf) {
+    uint8_t* wt = wlds + wave * (kGWeightStage / 4);
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      *reinterpret_cast<uint4*>(wt + (8 * q + (lane >> 3)) * 128 + 16 * (lane & 7)) = g.w[q];
     uint8_t* tile = L.tile + buf * (kGTok * gm.tstride);
 #pragma unroll
     for (int i = 0; i < kGActSlots; ++i) {
@@ -169,34 +186,19 @@ __device__ __forceinline__ void walk_grouped(const WTensor& W, const GroupMap& g
       fetch(np, nxt);
     }
     const uint8_t* tile = L.tile + buf * (kGTok * gm.tstride) + lr * gm.tstride;
+    GStage wc;   // this lane's 64 bytes of the stage (chunks 4 half .. 4 half + 3 of row lr)
+    {
+      const uint8_t* wt = wlds + wave * (kGWeightStage / 4) + lr * 128;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) wc.w[j] = *reinterpret_cast<const uint4*>(wt + 16 * ((4 * half + j) ^ (lr & 7)));
+      wc.sc = cur.sc;
+    }
 #pragma unroll
     for (int s = 0; s < NSTEP; ++s) {
-      const bf16x8_t a = weight_frag<FMT>(cur, s);
+      const bf16x8_t a = weight_frag<FMT>(wc, s);
       const int kk = half * (KS / 2) + 8 * s;   // K offset of this lane's B fragment
-      if constexpr (SPLIT) {
-        const float4 b0 = *reinterpret_cast<const float4*>(tile + kk * 4);
-        const float4 b1 = *reinterpret_cast<const float4*>(tile + kk * 4 + 16);
-        const float v[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
-        uint32_t hi[4], mi[4], lo[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float x0 = v[2 * q], x1 = v[2 * q + 1];
-          const float h0 = __uint_as_float(__float_as_uint(x0) & 0xFFFF0000u);
-          const float h1 = __uint_as_float(__float_as_uint(x1) & 0xFFFF0000u);
-          const float r0 = x0 - h0, r1 = x1 - h1;
-          const float m0 = __uint_as_float(__float_as_uint(r0) & 0xFFFF0000u);
-          const float m1 = __uint_as_float(__float_as_uint(r1) & 0xFFFF0000u);
-          hi[q] = trunc_pair(h0, h1);
-          mi[q] = trunc_pair(m0, m1);
-          lo[q] = trunc_pair(r0 - m0, r1 - m1);
-        }
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pack_bf16x8(hi[0], hi[1], hi[2], hi[3]), acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pack_bf16x8(mi[0], mi[1], mi[2], mi[3]), acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pack_bf16x8(lo[0], lo[1], lo[2], lo[3]), acc, 0, 0, 0);
-      } else {
-        const bf16x8_t b = as_bf16x8(*reinterpret_cast<const uint4*>(tile + kk * 2));
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
-      }
+      const bf16x8_t b = as_bf16x8(*reinterpret_cast<const uint4*>(tile + kk * 2));
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
     }
     if (p.b == gm.NS - 1) {   // row tile done
       const int crow = p.rb + p.g * k.NG, n = min(k.NG, p.n - p.g * k.NG);
@@ -339,24 +341,29 @@ __device__ __forceinline__ void walk_grouped_mx(const WTensor& W, const GroupMap
       g.gs[0] = op.gs(p.e, 0);
       g.gs[1] = op.gs(p.e, 1);
     }
+    // weights coalesced as in walk_grouped: 128 bytes of the stage per row, through LDS
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int r = 8 * q + (lane >> 3);
+      const int64_t wr = row_of(p.e, p.s, r);
+      g.w[q] = load_stream16(W.codes + wr * W.code_row_bytes + (W4 ? p.b * KS / 2 : p.b * KS) + 16 * ((lane ^ r) & 7));
+    }
     const int64_t row = row_of(p.e, p.s, lr);
-    const uint8_t* rp = W.codes + row * W.code_row_bytes;
     const uint8_t* sp_ = W.scales + row * W.scale_row_bytes;
-    if constexpr (W4) {   // elements [128 h, 128 h + 128) of the stage, contiguous
-      const uint8_t* wp = rp + (p.b * KS + half * (KS / 2)) / 2;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) g.w[i] = load_stream16(wp + 16 * i);
+    if constexpr (W4) {   // this lane's elements [128 h, 128 h + 128) of the stage
       g.sc = *reinterpret_cast<const uint32_t*>(sp_ + ((p.b * KS + half * (KS / 2)) >> 5));
-    } else {              // bytes 16 h + 32 q of the stage (q < 4): both halves of each block
-      const uint8_t* wp = rp + p.b * KS + 16 * half;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) g.w[i] = load_stream16(wp + 32 * i);
+    } else {              // its bytes 16 h + 32 q of the stage (q < 4): both halves of each block
       g.sc = *reinterpret_cast<const uint32_t*>(sp_ + ((p.b * KS) >> 5));
     }
   };
   float* s_tsc = L.w_tsc;
   float* s_gs = L.w_gs;
+  uint8_t* wlds = L.tile + 2 * bufbytes;   // weight tiles, laid out as in walk_grouped
   auto store = [&](const Cursor& p, const GStageMx& g, int buf) {
+    uint8_t* wt = wlds + wave * (kGWeightStage / 4);
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      *reinterpret_cast<uint4*>(wt + (8 * q + (lane >> 3)) * 128 + 16 * (lane & 7)) = g.w[q];
     uint8_t* tile = L.tile + buf * bufbytes;
 #pragma unroll
     for (int i = 0; i < NSLOT; ++i) {
@@ -385,19 +392,29 @@ __device__ __forceinline__ void walk_grouped_mx(const WTensor& W, const GroupMap
     const uint8_t* arow = tile + lr * tstride;
     uint2 as2 = make_uint2(0u, 0u);
     if constexpr (AMX) as2 = *reinterpret_cast<const uint2*>(tile + kGTok * tstride + lr * 8);
+    GStageMx wc;   // this lane's 64 bytes: chunks 4 h + j (FP4) or 2 j + h (FP8) of row lr
+    {
+      const uint8_t* wt = wlds + wave * (kGWeightStage / 4) + lr * 128;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int c = W4 ? 4 * half + j : 2 * j + half;
+        wc.w[j] = *reinterpret_cast<const uint4*>(wt + 16 * (c ^ (lr & 7)));
+      }
+      wc.sc = cur.sc;
+    }
 #pragma unroll
     for (int j = 0; j < NI; ++j) {
       typename MfmaOperands<FA, FB>::A a;
       int sa, blk;   // this lane's weight scale; the stage scale block it supplies
       if constexpr (W4) {
-        a = i32x4_t{(int)cur.w[j].x, (int)cur.w[j].y, (int)cur.w[j].z, (int)cur.w[j].w};
-        sa = (int)((cur.sc >> (8 * j)) & 0xFFu);
+        a = i32x4_t{(int)wc.w[j].x, (int)wc.w[j].y, (int)wc.w[j].z, (int)wc.w[j].w};
+        sa = (int)((wc.sc >> (8 * j)) & 0xFFu);
         blk = 4 * half + j;
       } else {
-        a = i32x8_t{(int)cur.w[2 * j].x, (int)cur.w[2 * j].y, (int)cur.w[2 * j].z, (int)cur.w[2 * j].w,
-                    (int)cur.w[2 * j + 1].x, (int)cur.w[2 * j + 1].y, (int)cur.w[2 * j + 1].z, (int)cur.w[2 * j + 1].w};
+        a = i32x8_t{(int)wc.w[2 * j].x, (int)wc.w[2 * j].y, (int)wc.w[2 * j].z, (int)wc.w[2 * j].w,
+                    (int)wc.w[2 * j + 1].x, (int)wc.w[2 * j + 1].y, (int)wc.w[2 * j + 1].z, (int)wc.w[2 * j + 1].w};
         blk = 2 * j + half;
-        sa = (int)((cur.sc >> (8 * blk)) & 0xFFu);
+        sa = (int)((wc.sc >> (8 * blk)) & 0xFFu);
       }
       typename MfmaOperands<FA, FB>::B b;
       if constexpr (A4) {   // 32 E2M1 of stage elements 32 blk.. (16 bytes)
@@ -471,14 +488,20 @@ __device__ __forceinline__ void ggateup_walk(const ExpertArgs& a, const ExpertLd
     for (int r = 0; r < 8; ++r) {
       const float gv = acc[r] * gsg * ts, uv = acc[r + 8] * gsu * ts;
       const float hv = gv / (1.0f + expf(-gv)) * uv;
-      a.h[off + acc_row(r, half)] = hv;
+      // an h that is not re-quantized is stored as BF16 at the byte position of its FP32
+      // row, as the GEMV kernels store it (16-bit-activation layers, every shared expert)
+      if constexpr (AF == A_BF16)
+        reinterpret_cast<uint16_t*>(a.h)[off + (int64_t)C.r_pair[cx.crow + lr] * a.hs + acc_row(r, half)] =
+            (uint16_t)f32_to_bf16_rne(hv);
+      else
+        a.h[off + acc_row(r, half)] = hv;
       if (a.dbg_h) a.dbg_h[off + acc_row(r, half)] = hv;
     }
   };
   if constexpr (use_scaled_mfma<FMT, AF>())
     walk_grouped_mx<FMT, AF>(W, gm, L, C, sp, op, row_of, sink);
   else
-    walk_grouped<FMT, false>(W, gm, L, C, sp, op, row_of, sink);
+    walk_grouped<FMT>(W, gm, L, C, sp, op, row_of, sink);
 }
 
 template <int RF, int SF, int AF>
@@ -511,7 +534,7 @@ __device__ __forceinline__ void gdown_walk(const ExpertArgs& a, const ExpertLds&
   const GemvMap& m = routed ? a.rmap : a.smap;
   const GroupMap& gm = routed ? a.rgm : a.sgm;
   const DownOps<AF> op{a.h, a.hq_codes, a.hq_scales, a.hq_scale, W.gscale, W.gs_per_expert, W.rows,
-                       routed ? a.I : a.Ish, m.RS, a.H, a.hs, a.o, L.w_gs, L.w_tsc, C.r_pair};
+                       routed ? a.I : a.Ish, m.RS, a.H, a.hs, a.o, L.w_gs, L.w_tsc, C.r_pair, 1};
   const int wave = threadIdx.x / kWave, half = (threadIdx.x & (kWave - 1)) >> 5, lr = threadIdx.x & 31;
   auto row_of = [&](int e, int t, int r) -> int64_t { return (int64_t)e * W.rows + 128 * t + 32 * wave + r; };
   auto sink = [&](const UnitCtx& cx, int t, const f32x16_t& acc, float ts, float g, float) {
@@ -524,7 +547,7 @@ __device__ __forceinline__ void gdown_walk(const ExpertArgs& a, const ExpertLds&
   if constexpr (use_scaled_mfma<FMT, AF>())
     walk_grouped_mx<FMT, AF>(W, gm, L, C, sp, op, row_of, sink);
   else
-    walk_grouped<FMT, AF == A_BF16>(W, gm, L, C, sp, op, row_of, sink);
+    walk_grouped<FMT>(W, gm, L, C, sp, op, row_of, sink);   // h as BF16 (or its decoded codes)
 }
 
 template <int RF, int SF, int AF>

@@ -58,18 +58,25 @@ inline int expert_lds_list_bytes(int E, int T, int k) {
 // row tile (gate/up: 16 gate rows and the 16 matching up rows; down: 32 hidden rows),
 // a unit is an expert with up to NG = 32 of its tokens, and the K dimension is walked in
 // stages of KS elements (each lane holds 64 bytes of weights per stage: FP4 256, FP8
-// 128, BF16 64 elements per stage). Activations of a stage sit in LDS as BF16 (FP32
-// when split: the down projection of FP32 h, taken as three exact BF16 parts).
+// 128, BF16 64 elements per stage). Activations of a stage sit in LDS as BF16 (or as
+// raw MX codes with their scales on the scaled MFMA).
 // K elements per stage of the grouped kernels: 64 bytes of weights per lane, both
 // halves of the wave.
 inline constexpr int group_ks(int fmt) { return fmt == W_BF16 ? 64 : (fmt == W_MXFP8 ? 128 : 256); }
+// Grouped kernels: each stage's weights (4 waves x 32 rows x 128 bytes) pass through LDS
+// after the activation buffers. One buffer: a wave reads only its own rows, and it writes
+// the next stage's rows after its reads of the current stage's (LDS operations of one
+// wave complete in order).
+constexpr int kGWeightStage = 4 * 32 * 128;
+constexpr int kGWeightLds = kGWeightStage;
+// LDS of a grouped launch that keeps two workgroups on a compute unit (160 KB on gfx950)
+constexpr int kGroupedLdsMax = 80 * 1024;
 
 struct GroupMap {
   int KS, NS;        // K elements per stage, stages per row tile
   int steps;         // row tiles per expert
   int NG;            // tokens per unit
   int cw, ct;        // cost of one stage of a row tile: cw + ct * tokens
-  int split;         // FP32 activations
   int tstride;       // LDS bytes per staged token row (padded)
   int scaled;        // MX weights on the scaled MFMA: raw activation codes staged, then
                      // 8 E8M0 bytes per token
