@@ -121,7 +121,9 @@ struct Plan {
   GroupMap gu_rg, gu_sg, dn_rg, dn_sg;
 };
 
-constexpr int kGroupedMinT = 32;      // the grouped (MFMA) kernels from this batch on
+constexpr int kGroupedMinT = 32;      // the grouped (MFMA) kernels from this batch on (4-bit weights)
+constexpr int kGroupedMinTSharedBf16 = 8;   // ... with a BF16 shared expert
+constexpr int kGroupedMinTWide = 24;        // ... with BF16 or MXFP8 routed weights
 constexpr int kTokPctGateup = 200;    // GEMV cost model: token-term scale (see set_costs)
 constexpr int kTokPctDown = 100;
 constexpr int kLateGateup16 = 13;     // GEMV kernels: weight of a second-round workgroup,
@@ -235,9 +237,18 @@ bool make_plan(const moe_layer_t& L, int T, int path, Plan& p) {
   consts(p.dn_r, L.I, L.H / p.dn_r.RS, p.dn_tile, 12);
   consts(p.dn_s, Ish, L.H / p.dn_s.RS, p.dn_tile, 12);
   // grouped kernels: gate/up tiles of 64 intermediate indices, down tiles of 128 rows
-  // automatic choice: from kGroupedMinT tokens on, when units hold many tokens
-  const bool want = path == MOE_PATH_GROUPED ||
-                    (path == MOE_PATH_AUTO && T >= kGroupedMinT && (L.has_shared || T * L.k >= L.E));
+  // automatic choice (graph-timed crossovers of both kernel pairs on the synthetic layers):
+  // a BF16 shared expert is read once per 32 tokens instead of once per 4, which pays from
+  // 8 tokens on (Flint BF16 T = 8: 95 against 111 us; Mistral a8w4: 182 against 236 us);
+  // BF16 or MXFP8 routed weights, whose GEMV decode is the dearest, from 24 (Inkling MXFP8:
+  // even at 16, grouped ahead from 32); 4-bit weights from 32 tokens when units hold many
+  // tokens (a shared expert, or T*k >= E).
+  const bool bf16_shared = L.has_shared && L.shared_wfmt == MOE_W_BF16;
+  const bool wide_w = L.wfmt == W_BF16 || L.wfmt == W_MXFP8;
+  const bool auto_grouped = bf16_shared ? T >= kGroupedMinTSharedBf16
+                            : wide_w    ? T >= kGroupedMinTWide
+                                        : T >= kGroupedMinT && (L.has_shared || T * L.k >= L.E);
+  const bool want = path == MOE_PATH_GROUPED || (path == MOE_PATH_AUTO && auto_grouped);
   // MX routed weights with 8- or 4-bit activations run on the scaled MFMA
   const bool mx_w = L.wfmt == W_MXFP4 || L.wfmt == W_MXFP8;
   const int mx_bits = mx_w && (L.afmt == A_FP8_TOKEN || L.afmt == A_MXFP8) ? 8 : (mx_w && L.afmt == A_MXFP4 ? 4 : 0);
