@@ -134,9 +134,10 @@ def cpu_info() -> dict:
 
 
 # Decode points of the other configurations, timed after the headline sweep (the
-# quantized-activation layers run the in-kernel token and h quantizers).
-EXTRA_CONFIGS = [("inkling_w4a4", (1, 4, 8)), ("mistral_mxfp4_a8", (1, 8)), ("mistral_mxfp4_a4", (1, 8)),
-                 ("mistral_mxfp4", (1, 8)), ("inkling_mxfp8_a8", (1, 8)), ("flint_bf16", (1, 8))]
+# quantized-activation layers run the in-kernel token and h quantizers; Mistral a8w4 at
+# 64 tokens and Flint BF16 at 256 run the grouped MFMA kernels).
+EXTRA_CONFIGS = [("inkling_w4a4", (1, 4, 8)), ("mistral_mxfp4_a8", (1, 8, 64)), ("mistral_mxfp4_a4", (1, 8)),
+                 ("mistral_mxfp4", (1, 8)), ("inkling_mxfp8_a8", (1, 8)), ("flint_bf16", (1, 8, 256))]
 
 
 def main() -> int:
