@@ -636,7 +636,9 @@ moe_status_t enqueue_experts(const moe_layer_t* L, const uint16_t* x_bf16, const
   Plan p;
   if (!make_plan(*L, T, path, p)) return set_err(MOE_EUNSUPPORTED, "no launch plan");
   if (path == MOE_PATH_GROUPED && !p.grouped)
-    return set_err(MOE_EUNSUPPORTED, "grouped kernels need K and rows that tile (H, I multiples of the stage and tile sizes)");
+    return set_err(MOE_EUNSUPPORTED,
+                   "grouped kernels need K and rows that tile (H, I multiples of the stage and tile sizes) and at "
+                   "most 80 KB of LDS per workgroup (the expert tables grow with T * k and E)");
   if (fused_topk && (p.grouped || T * L->k > kPairMax)) return set_err(MOE_EINVAL, "fused routing needs pair mode");
   if (dry) return MOE_OK;
   uint8_t* base = static_cast<uint8_t*>(ws);

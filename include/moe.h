@@ -138,10 +138,13 @@ typedef struct {
   uint8_t *hq_scales;   /* NVFP4: E4M3 [T*k][I/16]; MX: E8M0 [T*k][I/32]                  */
   float *hq_scale;      /* NVFP4: g [T*k]; FP8 per token: s [T*k]; MX: unused             */
   int32_t path;         /* moe_path_t: which expert kernels run. AUTO picks the grouped
-                           (MFMA, 32 tokens per unit) kernels from 32 tokens on when units
-                           hold many tokens (a shared expert, or T*k >= E), else the GEMV
-                           kernels (4 tokens per unit); GROUPED is refused where the
-                           shapes do not tile (see moe_layer_check)                       */
+                           (MFMA, 32 tokens per unit) kernels from 8 tokens on with a BF16
+                           shared expert, from 24 with BF16 or MXFP8 routed weights, and
+                           from 32 with 4-bit weights when units hold many tokens (a
+                           shared expert, or T*k >= E); else the GEMV kernels (4 tokens
+                           per unit). GROUPED is refused where the shapes do not tile or
+                           a workgroup would need more than 80 KB of LDS (the expert
+                           tables grow with T*k and E); AUTO then runs the GEMV kernels  */
 } moe_debug_t;
 
 /* Host only; no device access. Checks every constraint the kernels rely on for a
