@@ -317,6 +317,7 @@ def test_forward_matches_route_and_experts(lib, name, T):
 LARGE_CASES = [
     ("flint_bf16", 64),
     ("flint_bf16", 256),
+    ("flint_w4a16", 64),
     ("inkling_w4a4", 32),
     ("inkling_mxfp8", 32),
     ("mistral_mxfp4", 64),
@@ -324,9 +325,22 @@ LARGE_CASES = [
     ("mistral_mxfp4_a4", 64),
     ("inkling_mxfp8_a8", 32),
 ]
+# The largest batch the boundary takes (256 tokens), with the kernels the host picks: the
+# largest routing tables in LDS (384 experts, top-8: 2048 pairs) and, where the grouped
+# kernels' LDS would pass 80 KB, the GEMV kernels with one workgroup per compute unit.
+MAX_CASES = [
+    ("inkling_w4a4", 256, 0),
+    ("inkling_mxfp8_a8", 256, 0),
+    ("mistral_mxfp4_a8", 256, 0),
+    ("mistral_mxfp4_a8", 256, 1),
+]
 
 
-@pytest.mark.parametrize("name,T,path", [(n, t, p) for n, t in LARGE_CASES for p in (1, 2)])
+# (each layer's maximum cases right after its other cases: the drawn layers are cached)
+LARGE_PARAMS = [c for n, t in LARGE_CASES for c in [(n, t, 1), (n, t, 2)] + [m for m in MAX_CASES if m[0] == n]]
+
+
+@pytest.mark.parametrize("name,T,path", LARGE_PARAMS)
 def test_layer_parity_large_batch(lib, name, T, path):
     from oracle import layer as OL
     from parity_util import oracle_route_only
