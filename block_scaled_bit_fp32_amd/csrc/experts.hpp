@@ -975,9 +975,15 @@ __device__ __forceinline__ void gateup_walk(const ExpertArgs& a, const ExpertLds
                             gs_tab, (routed ? a.E : 1) * W.gs_per_expert, ids, fr);
 }
 
+// How a GEMV launch walks the routed experts (the same for every workgroup of a launch,
+// so each is a kernel of its own: a kernel's registers are sized for the largest path it
+// holds, and the table builds need far more than the pair and token walks).
+enum { RW_PAIR = 0, RW_TABLE = 1, RW_TOKEN = 2 };
+
 // Workgroups [0, sh_wgs) walk the shared expert (BF16 activations, no dependency on the
-// routing), the others split the selected experts.
-template <int RF, int SF, int AF>
+// routing), the others split the selected experts: pairs (MODE = RW_PAIR, a.pair_mode)
+// or the tables' units (RW_TABLE).
+template <int RF, int SF, int AF, int MODE>
 __global__ void __launch_bounds__(kBlock, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) gateup_kernel(ExpertArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
   warm_args<ExpertArgs>();
@@ -987,7 +993,7 @@ __global__ void __launch_bounds__(kBlock, 2) __attribute__((amdgpu_waves_per_eu(
     const Span sp = shared_span(a.T, gateup_cost(a, false), a.smap.NB, blockIdx.x, a.sh_wgs,
                                 ShareW{0, a.ncu, a.late16});
     gateup_walk<SF, A_BF16, VW_SHARED>(a, L, sp, nullptr);
-  } else if (a.pair_mode) {
+  } else if constexpr (MODE == RW_PAIR) {
     Span sp = pair_span(a, gateup_cost(a, true), a.rmap.inv_steps, a.rmap.NB, blockIdx.x - a.sh_wgs,
                         gridDim.x - a.sh_wgs);
     if (!a.fuse_topk && sp.a0 < a.T * a.k) {
@@ -1288,28 +1294,30 @@ __device__ __forceinline__ void walk_tokens(const ExpertArgs& a, const ExpertLds
   }
 }
 
-template <int RF, int SF, int AF>
+// MODE: RW_TOKEN (a.token_mode: token items over all of a token's experts, writing y;
+// the shared expert, if any, has the routed format), else the shared expert's workgroups
+// and the routed pairs (RW_PAIR) or tables' units (RW_TABLE), as in gate/up.
+template <int RF, int SF, int AF, int MODE>
 __global__ void __launch_bounds__(kBlock, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) down_kernel(ExpertArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
   warm_args<ExpertArgs>();
   ExpertLds L = carve(a, smem);
-  if constexpr (SF == RF) {
-    if (a.token_mode) {
-      int i0, len;   // items per workgroup: the host's two-round split
-      split_at(blockIdx.x, a.pn1, a.pq1, a.pr1, a.pq2, a.pr2, i0, len);
-      if (a.token_mode == 2)
-        walk_tokens<RF, 0, AF, true>(a, L, i0, i0 + len);
-      else
-        walk_tokens<RF, 0, AF, false>(a, L, i0, i0 + len);
-      return;
-    }
+  if constexpr (MODE == RW_TOKEN) {
+    static_assert(SF == RF, "token mode reads the shared expert as a routed one");
+    int i0, len;   // items per workgroup: the host's two-round split
+    split_at(blockIdx.x, a.pn1, a.pq1, a.pr1, a.pq2, a.pr2, i0, len);
+    if (a.token_mode == 2)
+      walk_tokens<RF, 0, AF, true>(a, L, i0, i0 + len);
+    else
+      walk_tokens<RF, 0, AF, false>(a, L, i0, i0 + len);
+    return;
   }
   const bool shared = (int)blockIdx.x < a.sh_wgs;
   if (shared) {
     const Span sp = shared_span(a.T, down_cost(a, false), a.smap.NB, blockIdx.x, a.sh_wgs,
                                 ShareW{0, a.ncu, a.late16});
     down_walk<SF, A_BF16, VW_SHARED>(a, L, sp);
-  } else if (a.pair_mode) {
+  } else if constexpr (MODE == RW_PAIR) {
     Span sp = pair_span(a, down_cost(a, true), a.rmap.inv_steps, a.rmap.NB, blockIdx.x - a.sh_wgs,
                         gridDim.x - a.sh_wgs);
     if (sp.a0 < a.T * a.k) {
@@ -1337,14 +1345,23 @@ __global__ void gdown_kernel(ExpertArgs a);
 template <int RF, int SF, int AF>
 hipError_t launch_experts_af(const ExpertArgs& gu, int gu_grid, size_t gu_lds,
                              const ExpertArgs& dn, int dn_grid, size_t dn_lds, hipStream_t s) {
-  hipError_t err = gu.grouped
-      ? launch_kernel(K_GATEUP, ggateup_kernel<RF, SF, AF>, dim3(gu_grid), dim3(kBlock), gu_lds, s, gu)
-      : launch_kernel(K_GATEUP, gateup_kernel<RF, SF, AF>, dim3(gu_grid), dim3(kBlock), gu_lds, s, gu);
+  auto go = [&](int kind, auto kern, int grid, size_t lds, const ExpertArgs& a) {
+    return launch_kernel(kind, kern, dim3(grid), dim3(kBlock), lds, s, a);
+  };
+  hipError_t err = gu.grouped     ? go(K_GATEUP, ggateup_kernel<RF, SF, AF>, gu_grid, gu_lds, gu)
+                   : gu.pair_mode ? go(K_GATEUP, gateup_kernel<RF, SF, AF, RW_PAIR>, gu_grid, gu_lds, gu)
+                                  : go(K_GATEUP, gateup_kernel<RF, SF, AF, RW_TABLE>, gu_grid, gu_lds, gu);
   if (err != hipSuccess) return err;
   if (AF != A_BF16 && (err = launch_hquant(gu, s)) != hipSuccess) return err;
-  err = dn.grouped
-      ? launch_kernel(K_DOWN, gdown_kernel<RF, SF, AF>, dim3(dn_grid), dim3(kBlock), dn_lds, s, dn)
-      : launch_kernel(K_DOWN, down_kernel<RF, SF, AF>, dim3(dn_grid), dim3(kBlock), dn_lds, s, dn);
+  if (dn.grouped) {
+    err = go(K_DOWN, gdown_kernel<RF, SF, AF>, dn_grid, dn_lds, dn);
+  } else if (dn.token_mode) {
+    if constexpr (SF == RF) err = go(K_DOWN, down_kernel<RF, SF, AF, RW_TOKEN>, dn_grid, dn_lds, dn);
+    else return hipErrorInvalidValue;   // the plan never picks token mode for a shared expert of another format
+  } else {
+    err = dn.pair_mode ? go(K_DOWN, down_kernel<RF, SF, AF, RW_PAIR>, dn_grid, dn_lds, dn)
+                       : go(K_DOWN, down_kernel<RF, SF, AF, RW_TABLE>, dn_grid, dn_lds, dn);
+  }
   if (err != hipSuccess) return err;
   return dn.token_mode ? hipSuccess : launch_combine(dn, s);
 }
