@@ -642,7 +642,7 @@ struct FusedRoute {
 // the next one, so the compiler waits for one step's loads while the next step's are in
 // flight. Later windows are staged when a unit does not fit; only LDS barriers are used,
 // so weight loads stream across them.
-template <int FMT, int AK, int RPL, int VW, class Ops>
+template <int FMT, int AK, int RPL, int VW, int NKF, class Ops>
 __device__ __forceinline__ void walk_class(const WTensor& W, const GemvMap& m, const ExpertLds& L,
                                            int lds_tile_bytes, const ClassView<VW>& V, const ClassCost& k,
                                            const Span& sp, const Ops& op, float* gs_tab, int ngs,
@@ -745,22 +745,25 @@ __device__ __forceinline__ void walk_class(const WTensor& W, const GemvMap& m, c
     }
   };
   // prologue: loads that need no expert id, then the first weight loads, then LDS. With
-  // fused routing (fr, pair mode) the router logits of the span's tokens are loaded first
-  // and the experts are selected while the other prologue loads are in flight.
+  // fused routing (NKF > 0 slots per lane, pair mode) the router logits of the span's
+  // tokens are loaded first and the experts are selected while the other prologue loads
+  // are in flight.
+  constexpr bool FUSED = VW == VW_PAIR && NKF > 0;
+  constexpr int NKL = NKF > 0 ? NKF : 1;
   const int nrows0 = r1 - r0;
-  TopkRt lv;
+  struct NoTopk {};
+  std::conditional_t<FUSED, TopkIn<NKL, true>, NoTopk> lv;   // (nothing without fused routing)
   int t_lo = 0, t_hi = -1;
-  const int fnk = topk_rt_slots(fr.E);
   auto route_load = [&](int t) {
-    const int64_t off = (int64_t)min(t, t_hi) * fr.E;
-    topk_rt_load(fr.logits + off, fr.raw ? fr.raw + off : nullptr, fr.E, fnk, lv);
-  };
-  if constexpr (VW == VW_PAIR) {
-    if (fr.logits) {
-      t_lo = div_by(sp.a0, fr.inv_k);
-      t_hi = div_by(sp.row_limit - 1, fr.inv_k);
-      route_load(t_lo + wave);
+    if constexpr (FUSED) {
+      const int64_t off = (int64_t)min(t, t_hi) * fr.E;
+      topk_fused_load<NKL>(fr.logits + off, fr.raw ? fr.raw + off : nullptr, fr.E, lv);
     }
+  };
+  if constexpr (FUSED) {
+    t_lo = div_by(sp.a0, fr.inv_k);
+    t_hi = div_by(sp.row_limit - 1, fr.inv_k);
+    route_load(t_lo + wave);
   }
   uint4 raw[NS];
   const SlotMap<AK> smap(m, W.K);
@@ -778,24 +781,22 @@ __device__ __forceinline__ void walk_class(const WTensor& W, const GemvMap& m, c
     if (ids) idv = ids[min((int)threadIdx.x, V.P - 1)];
   }
   Cursor pa{sp.a0, sp.g0, sp.s0, 0, sp.e0, sp.n0, sp.rb0}, pb = pa;
-  if constexpr (VW == VW_PAIR) {
-    if (fr.logits) {   // one token per wave (more rounds for longer spans), then the first expert
-      for (int tb = t_lo; tb <= t_hi; tb += kBlock / kWave) {
-        const int t = tb + wave;
-        if (tb != t_lo) route_load(t);
-        int e;
-        float w;
-        topk_rt_select(lv, fr.raw != nullptr, fr.E, fr.k, fr.softmax, fnk, e, w);
-        if (t <= t_hi && lane < fr.k) {
-          L.ids[t * fr.k + lane] = e;
-          fr.ids_out[t * fr.k + lane] = e;
-          fr.w_out[t * fr.k + lane] = w;
-        }
+  if constexpr (FUSED) {   // one token per wave (more rounds for longer spans), then the first expert
+    for (int tb = t_lo; tb <= t_hi; tb += kBlock / kWave) {
+      const int t = tb + wave;
+      if (tb != t_lo) route_load(t);
+      int e;
+      float w;
+      topk_fused_select<NKL>(lv, fr.E, fr.k, fr.softmax, e, w);
+      if (t <= t_hi && lane < fr.k) {
+        L.ids[t * fr.k + lane] = e;
+        fr.ids_out[t * fr.k + lane] = e;
+        fr.w_out[t * fr.k + lane] = w;
       }
-      lds_barrier();
-      const int e0 = uni(L.ids[sp.a0]);
-      pa.e = (unsigned)e0 < (unsigned)fr.E ? e0 : 0;
     }
+    lds_barrier();
+    const int e0 = uni(L.ids[sp.a0]);
+    pa.e = (unsigned)e0 < (unsigned)fr.E ? e0 : 0;
   }
   WeightRegs<RPL> A_, B_;
   {
@@ -961,7 +962,7 @@ __device__ __forceinline__ ClassView<VW> class_view(const ExpertArgs& a, const E
   return ClassView<VW>{&L.rt, L.ids, a.k, a.E, a.T, a.T * a.k, a.inv_k};
 }
 
-template <int FMT, int AF, int VW>
+template <int FMT, int AF, int VW, int NKF = 0>
 __device__ __forceinline__ void gateup_walk(const ExpertArgs& a, const ExpertLds& L, const Span& sp,
                                             const int32_t* ids, const FusedRoute fr = FusedRoute{}) {
   constexpr bool routed = VW != VW_SHARED;
@@ -971,8 +972,8 @@ __device__ __forceinline__ void gateup_walk(const ExpertArgs& a, const ExpertLds
   float* gs_tab = routed ? L.gs_rt : L.gs_sh;
   const GateupOps<AF> op{a.x, a.xq_codes, a.xq_scales, a.xq_scale, W.gscale, W.gs_per_expert, W.rows, Iexp,
                          4 * m.G, a.H, a.hs, a.h, a.dbg_h, gs_tab, L.w_tsc, nullptr, AF == A_BF16};
-  walk_class<FMT, 0, 2, VW>(W, m, L, a.lds_act_bytes, class_view<VW>(a, L), gateup_cost(a, routed), sp, op,
-                            gs_tab, (routed ? a.E : 1) * W.gs_per_expert, ids, fr);
+  walk_class<FMT, 0, 2, VW, NKF>(W, m, L, a.lds_act_bytes, class_view<VW>(a, L), gateup_cost(a, routed), sp, op,
+                                 gs_tab, (routed ? a.E : 1) * W.gs_per_expert, ids, fr);
 }
 
 // How a GEMV launch walks the routed experts (the same for every workgroup of a launch,
@@ -982,8 +983,9 @@ enum { RW_PAIR = 0, RW_TABLE = 1, RW_TOKEN = 2 };
 
 // Workgroups [0, sh_wgs) walk the shared expert (BF16 activations, no dependency on the
 // routing), the others split the selected experts: pairs (MODE = RW_PAIR, a.pair_mode)
-// or the tables' units (RW_TABLE).
-template <int RF, int SF, int AF, int MODE>
+// or the tables' units (RW_TABLE). NKF > 0 (pair mode, a.fuse_topk): the walk's prologue
+// selects the experts from the router logits, NKF = fused_topk_slots(E) slots per lane.
+template <int RF, int SF, int AF, int MODE, int NKF>
 __global__ void __launch_bounds__(kBlock, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) gateup_kernel(ExpertArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
   warm_args<ExpertArgs>();
@@ -996,16 +998,16 @@ __global__ void __launch_bounds__(kBlock, 2) __attribute__((amdgpu_waves_per_eu(
   } else if constexpr (MODE == RW_PAIR) {
     Span sp = pair_span(a, gateup_cost(a, true), a.rmap.inv_steps, a.rmap.NB, blockIdx.x - a.sh_wgs,
                         gridDim.x - a.sh_wgs);
-    if (!a.fuse_topk && sp.a0 < a.T * a.k) {
-      const int e = a.ids[sp.a0];
-      sp.e0 = (unsigned)e < (unsigned)a.E ? e : 0;
+    if constexpr (NKF > 0) {   // (a workgroup with an empty span selects nothing)
+      const FusedRoute fr{a.logits, a.ids_out, a.w_out, a.E, a.k, a.inv_k, a.raw, a.softmax};
+      gateup_walk<RF, AF, VW_PAIR, NKF>(a, L, sp, nullptr, fr);
+    } else {
+      if (sp.a0 < a.T * a.k) {
+        const int e = a.ids[sp.a0];
+        sp.e0 = (unsigned)e < (unsigned)a.E ? e : 0;
+      }
+      gateup_walk<RF, AF, VW_PAIR>(a, L, sp, a.ids);
     }
-    // fused routing: the walk's prologue selects the experts (a workgroup with an empty
-    // span selects nothing)
-    const FusedRoute fr =
-        a.fuse_topk ? FusedRoute{a.logits, a.ids_out, a.w_out, a.E, a.k, a.inv_k, a.raw, a.softmax}
-                    : FusedRoute{};
-    gateup_walk<RF, AF, VW_PAIR>(a, L, sp, a.fuse_topk ? nullptr : a.ids, fr);
   } else {
     build_routed(a, L, L.rt, gateup_cost(a, true), a.rmap.NB, blockIdx.x - a.sh_wgs, gridDim.x - a.sh_wgs);
     build_rows(a, L, L.rt);
@@ -1090,7 +1092,7 @@ __device__ __forceinline__ void down_walk(const ExpertArgs& a, const ExpertLds& 
   float* gs_tab = routed ? L.gs_rt : L.gs_sh;
   const DownOps<AF> op{a.h, a.hq_codes, a.hq_scales, a.hq_scale, W.gscale, W.gs_per_expert, W.rows,
                        routed ? a.I : a.Ish, m.RS, a.H, a.hs, a.o, gs_tab, L.w_tsc, nullptr, 1};
-  walk_class<FMT, 0, 1, VW>(W, m, L, a.lds_act_bytes, class_view<VW>(a, L),
+  walk_class<FMT, 0, 1, VW, 0>(W, m, L, a.lds_act_bytes, class_view<VW>(a, L),
                                                down_cost(a, routed), sp, op, gs_tab,
                                                (routed ? a.E : 1) * W.gs_per_expert, a.ids);
 }
@@ -1348,9 +1350,13 @@ hipError_t launch_experts_af(const ExpertArgs& gu, int gu_grid, size_t gu_lds,
   auto go = [&](int kind, auto kern, int grid, size_t lds, const ExpertArgs& a) {
     return launch_kernel(kind, kern, dim3(grid), dim3(kBlock), lds, s, a);
   };
+  const int nkf = gu.fuse_topk ? fused_topk_slots(gu.E) : 0;
   hipError_t err = gu.grouped     ? go(K_GATEUP, ggateup_kernel<RF, SF, AF>, gu_grid, gu_lds, gu)
-                   : gu.pair_mode ? go(K_GATEUP, gateup_kernel<RF, SF, AF, RW_PAIR>, gu_grid, gu_lds, gu)
-                                  : go(K_GATEUP, gateup_kernel<RF, SF, AF, RW_TABLE>, gu_grid, gu_lds, gu);
+                   : !gu.pair_mode ? go(K_GATEUP, gateup_kernel<RF, SF, AF, RW_TABLE, 0>, gu_grid, gu_lds, gu)
+                   : nkf == 0     ? go(K_GATEUP, gateup_kernel<RF, SF, AF, RW_PAIR, 0>, gu_grid, gu_lds, gu)
+                   : nkf == 2     ? go(K_GATEUP, gateup_kernel<RF, SF, AF, RW_PAIR, 2>, gu_grid, gu_lds, gu)
+                   : nkf == 4     ? go(K_GATEUP, gateup_kernel<RF, SF, AF, RW_PAIR, 4>, gu_grid, gu_lds, gu)
+                                  : go(K_GATEUP, gateup_kernel<RF, SF, AF, RW_PAIR, 8>, gu_grid, gu_lds, gu);
   if (err != hipSuccess) return err;
   if (AF != A_BF16 && (err = launch_hquant(gu, s)) != hipSuccess) return err;
   if (dn.grouped) {

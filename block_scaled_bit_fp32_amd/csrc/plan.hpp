@@ -38,6 +38,9 @@ struct GemvMap {
 constexpr int kWinRows = 64;   // most token rows one staged window of units holds
 constexpr int kPairMax = 64;   // GEMV kernels: one unit per (token, expert) pair up to this many pairs
 constexpr int kFusedTopkSlots = 8;          // routing fused into gate/up: E <= 64 * this
+// Slots per lane of the routing fused into the gate/up GEMV (a kernel per count): E <= 128
+// in 2, E <= 256 in 4, E <= 512 in 8.
+inline constexpr int fused_topk_slots(int E) { return E <= 128 ? 2 : (E <= 256 ? 4 : 8); }
 constexpr int kTokParkBytes = 8 * 256 * 16;   // activation bytes the token walk's prologue holds in registers
 constexpr int kTokJMax = 8;     // token mode of the down GEMV: experts per token (k + shared)
 constexpr int kTokPieces = 3;   // and pieces per lane of a row-step (NP, one batch)

@@ -204,50 +204,20 @@ __device__ __forceinline__ void wave_topk(const float* lg, int E, int k, const f
   }
 }
 
-// Routing fused into another kernel's prologue: the slot count follows E at run time
-// (1, 2, 4, 6 or 8 slots, E <= 512). Every load is issued whatever the count (unused
-// slots repeat a clamped index; without raw the raw loads repeat the logits), so the
-// caller's later waits for other loads never depend on a branch.
-constexpr int kTopkRtSlots = 8;
-__device__ __forceinline__ int topk_rt_slots(int E) {
-  return E <= 64 ? 1 : E <= 128 ? 2 : E <= 256 ? 4 : E <= 384 ? 6 : 8;
+// Routing fused into another kernel's prologue, NK slots per lane (the kernel is built
+// per slot count: fused_topk_slots(E) of plan.hpp). It always takes the bare-logit path:
+// without bare logits (raw == NULL) it reads the logits in their place, and the selection
+// and weights come out the same (the weights then take the selected logits, which the
+// other path recovers from the keys, and the softmax maximum over the selection is its
+// first value), so one code path serves both kinds of layer.
+template <int NK>
+__device__ __forceinline__ void topk_fused_load(const float* lg, const float* raw, int E, TopkIn<NK, true>& in) {
+  wave_topk_load<NK, true>(lg, raw ? raw : lg, E, in);
 }
-struct TopkRt {
-  float v[kTopkRtSlots];
-  float r[kTopkRtSlots];
-};
-__device__ __forceinline__ void topk_rt_load(const float* lg, const float* raw, int E, int nk, TopkRt& in) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const float* rs = raw ? raw : lg;
-#pragma unroll
-  for (int i = 0; i < kTopkRtSlots; ++i) {
-    const int e = min(nk * lane + i, E - 1);
-    in.v[i] = lg[e];
-    in.r[i] = rs[e];
-  }
-}
-template <int NK, bool RAW>
-__device__ __forceinline__ void topk_rt_select_n(const TopkRt& in, int E, int k, bool softmax, int& e, float& w) {
-  TopkIn<NK, RAW> t;
-#pragma unroll
-  for (int i = 0; i < NK; ++i) {
-    t.v[i] = in.v[i];
-    if constexpr (RAW) t.r[i] = in.r[i];
-  }
-  wave_topk_select<NK, RAW>(t, E, k, softmax, e, w);
-}
-__device__ __forceinline__ void topk_rt_select(const TopkRt& in, bool raw, int E, int k, bool softmax, int nk, int& e,
-                                               float& w) {
-  auto go = [&](auto nkc) {
-    constexpr int N = decltype(nkc)::value;
-    if (raw) topk_rt_select_n<N, true>(in, E, k, softmax, e, w);
-    else topk_rt_select_n<N, false>(in, E, k, softmax, e, w);
-  };
-  if (nk == 1) go(std::integral_constant<int, 1>{});
-  else if (nk == 2) go(std::integral_constant<int, 2>{});
-  else if (nk == 4) go(std::integral_constant<int, 4>{});
-  else if (nk == 6) go(std::integral_constant<int, 6>{});
-  else go(std::integral_constant<int, 8>{});
+template <int NK>
+__device__ __forceinline__ void topk_fused_select(const TopkIn<NK, true>& in, int E, int k, bool softmax, int& e,
+                                                  float& w) {
+  wave_topk_select<NK, true>(in, E, k, softmax, e, w);
 }
 
 }  // namespace moe
