@@ -979,7 +979,7 @@ __device__ __forceinline__ void gateup_walk(const ExpertArgs& a, const ExpertLds
 // How a GEMV launch walks the routed experts (the same for every workgroup of a launch,
 // so each is a kernel of its own: a kernel's registers are sized for the largest path it
 // holds, and the table builds need far more than the pair and token walks).
-enum { RW_PAIR = 0, RW_TABLE = 1, RW_TOKEN = 2 };
+enum { RW_PAIR = 0, RW_TABLE = 1, RW_TOKEN = 2, RW_TOKEN_WIDE = 3 };
 
 // Workgroups [0, sh_wgs) walk the shared expert (BF16 activations, no dependency on the
 // routing), the others split the selected experts: pairs (MODE = RW_PAIR, a.pair_mode)
@@ -1296,22 +1296,20 @@ __device__ __forceinline__ void walk_tokens(const ExpertArgs& a, const ExpertLds
   }
 }
 
-// MODE: RW_TOKEN (a.token_mode: token items over all of a token's experts, writing y;
-// the shared expert, if any, has the routed format), else the shared expert's workgroups
-// and the routed pairs (RW_PAIR) or tables' units (RW_TABLE), as in gate/up.
+// MODE: RW_TOKEN or RW_TOKEN_WIDE (a.token_mode 1 or 2: token items over all of a
+// token's experts, writing y; the shared expert, if any, has the routed format), else the
+// shared expert's workgroups and the routed pairs (RW_PAIR) or tables' units (RW_TABLE),
+// as in gate/up.
 template <int RF, int SF, int AF, int MODE>
 __global__ void __launch_bounds__(kBlock, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) down_kernel(ExpertArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
   warm_args<ExpertArgs>();
   ExpertLds L = carve(a, smem);
-  if constexpr (MODE == RW_TOKEN) {
+  if constexpr (MODE == RW_TOKEN || MODE == RW_TOKEN_WIDE) {
     static_assert(SF == RF, "token mode reads the shared expert as a routed one");
     int i0, len;   // items per workgroup: the host's two-round split
     split_at(blockIdx.x, a.pn1, a.pq1, a.pr1, a.pq2, a.pr2, i0, len);
-    if (a.token_mode == 2)
-      walk_tokens<RF, 0, AF, true>(a, L, i0, i0 + len);
-    else
-      walk_tokens<RF, 0, AF, false>(a, L, i0, i0 + len);
+    walk_tokens<RF, 0, AF, MODE == RW_TOKEN_WIDE>(a, L, i0, i0 + len);
     return;
   }
   const bool shared = (int)blockIdx.x < a.sh_wgs;
@@ -1362,8 +1360,12 @@ hipError_t launch_experts_af(const ExpertArgs& gu, int gu_grid, size_t gu_lds,
   if (dn.grouped) {
     err = go(K_DOWN, gdown_kernel<RF, SF, AF>, dn_grid, dn_lds, dn);
   } else if (dn.token_mode) {
-    if constexpr (SF == RF) err = go(K_DOWN, down_kernel<RF, SF, AF, RW_TOKEN>, dn_grid, dn_lds, dn);
-    else return hipErrorInvalidValue;   // the plan never picks token mode for a shared expert of another format
+    if constexpr (SF == RF) {
+      err = dn.token_mode == 2 ? go(K_DOWN, down_kernel<RF, SF, AF, RW_TOKEN_WIDE>, dn_grid, dn_lds, dn)
+                               : go(K_DOWN, down_kernel<RF, SF, AF, RW_TOKEN>, dn_grid, dn_lds, dn);
+    } else {
+      return hipErrorInvalidValue;   // the plan never picks token mode for a shared expert of another format
+    }
   } else {
     err = dn.pair_mode ? go(K_DOWN, down_kernel<RF, SF, AF, RW_PAIR>, dn_grid, dn_lds, dn)
                        : go(K_DOWN, down_kernel<RF, SF, AF, RW_TABLE>, dn_grid, dn_lds, dn);
