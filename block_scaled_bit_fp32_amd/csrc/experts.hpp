@@ -711,7 +711,7 @@ __device__ __forceinline__ void walk_class(const WTensor& W, const GemvMap& m, c
       fetch_batch<FMT, RPL>(W, m, nr, np.b, jl, nxt);
     }
     const uint8_t* tile = L.tile + cx.wrow * tstride;
-    const int n = cx.n;
+    const int n = VW == VW_PAIR ? 1 : cx.n;   // a pair is one token
 #pragma unroll
     for (int i = 0; i < WeightRegs<RPL>::NPB; ++i) {
       if (i < m.NPB) {
