@@ -220,8 +220,13 @@ bool make_plan(const moe_layer_t& L, int T, int path, Plan& p) {
               jb <= (size_t)kTokParkBytes && jb <= room;
     if (p.token) p.dn_tile = std::max(p.dn_tile, align_up(jb, 16));
   }
-  p.gu_lds = p.list_bytes + p.gu_tile;
-  p.dn_lds = p.list_bytes + p.dn_tile;
+  // NVFP4 walks stage each row-step's block scales in 1 KB of LDS per wave after the tile
+  // (a row's pieces must then fit one batch)
+  const bool nv_r = L.wfmt == W_NVFP4, nv_s = sfmt == W_NVFP4;
+  if ((nv_r && (p.gu_r.NB != 1 || p.dn_r.NB != 1)) || (nv_s && (p.gu_s.NB != 1 || p.dn_s.NB != 1))) return false;
+  const size_t stage = nv_r || nv_s ? (size_t)kScaleStageBytes : 0;
+  p.gu_lds = p.list_bytes + p.gu_tile + stage;
+  p.dn_lds = p.list_bytes + p.dn_tile + stage;
   // the kernels' launch constants (so that their prologues divide nothing): steps per
   // unit, rows the tile holds, rows the first window's register slots hold (4 slots per
   // thread for gate/up, 12 for down, 16-byte slots)
@@ -408,8 +413,8 @@ std::string check_layer(const moe_layer_t* L, int max_tokens) {
     if (!w.codes) { snprintf(b, sizeof b, "%s.codes is NULL", name); add(b); }
     else if (!aligned(w.codes, 16)) { snprintf(b, sizeof b, "%s.codes must be 16-byte aligned", name); add(b); }
     if (fmt != MOE_W_BF16 && !w.scales) { snprintf(b, sizeof b, "%s.scales is NULL", name); add(b); }
-    if (fmt == MOE_W_NVFP4 && w.scales && !aligned(w.scales, 2)) {
-      snprintf(b, sizeof b, "%s.scales must be 2-byte aligned", name); add(b);
+    if (fmt == MOE_W_NVFP4 && w.scales && !aligned(w.scales, 16)) {
+      snprintf(b, sizeof b, "%s.scales must be 16-byte aligned", name); add(b);
     }
     if ((fmt == MOE_W_MXFP4 || fmt == MOE_W_MXFP8) && w.scales && !aligned(w.scales, 4)) {
       snprintf(b, sizeof b, "%s.scales must be 4-byte aligned", name); add(b);

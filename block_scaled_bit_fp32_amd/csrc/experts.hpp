@@ -340,7 +340,28 @@ struct WeightRegs {
   static constexpr int NPB = 4;
   uint4 w[NPB][RPL];
   uint32_t s[NPB][RPL];
+  uint4 sc;   // NVFP4: 16 bytes of the wave's block-scale rows (see ScaleChunk)
 };
+
+// NVFP4 block scales of a row-step, one 16-byte load per lane instead of one 2-byte load
+// per piece and row: the wave's RPL x G rows are contiguous per q (RPL x G x K/16 bytes,
+// at most 1 KB since a row's pieces fit one batch), lane c loads chunk c of them and
+// writes it to the wave's own 1 KB of LDS, where each lane then reads its pieces' scales
+// (a wave's LDS operations complete in order: no barrier). ScaleChunk is the lane's
+// constant part of the address: which q, the row relative to its own, the byte offset.
+struct ScaleChunk {
+  int q, drow, coff;
+  int qbytes;   // bytes of one q's rows (G x K/16)
+};
+template <int RPL>
+__device__ __forceinline__ ScaleChunk scale_chunk(const GemvMap& m, int64_t scale_row_bytes) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int cpr = (int)scale_row_bytes >> 4, cpq = m.G * cpr;
+  const int c = min(lane, RPL * cpq - 1);
+  const int q = RPL == 2 && c >= cpq ? 1 : 0;
+  const int rem = c - q * cpq, crow = rem / cpr;
+  return ScaleChunk{q, crow - (lane >> m.lg), (rem - crow * cpr) * 16, cpq * 16};
+}
 
 // Loads batch b (pieces b*NPB .. b*NPB + NPB - 1) of the lane's rows. Always issues
 // exactly NPB_max x RPL weight loads and as many scale loads (slots beyond the batch
@@ -349,7 +370,7 @@ struct WeightRegs {
 // retire in issue order).
 template <int FMT, int RPL>
 __device__ __forceinline__ void fetch_batch(const WTensor& W, const GemvMap& m, const int64_t (&rows)[RPL],
-                                            int b, int jl, WeightRegs<RPL>& R) {
+                                            int b, int jl, const ScaleChunk& sk, WeightRegs<RPL>& R) {
   constexpr int EPL = elems_per_piece(FMT);
 #pragma unroll
   for (int q = 0; q < RPL; ++q) {
@@ -361,12 +382,16 @@ __device__ __forceinline__ void fetch_batch(const WTensor& W, const GemvMap& m, 
       const int el = ((b * m.NPB + ii) * m.LPR + jl) * EPL;
       R.w[i][q] = load_stream16(rp + elem_byte<FMT>(el));
       if constexpr (FMT == W_NVFP4)
-        R.s[i][q] = *reinterpret_cast<const uint16_t*>(sp + (el >> 4));
+        R.s[i][q] = 0u;   // (from the staged chunk)
       else if constexpr (FMT == W_MXFP4 || FMT == W_MXFP8)
         R.s[i][q] = sp[el >> 5];
       else
         R.s[i][q] = 0u;
     }
+  }
+  if constexpr (FMT == W_NVFP4) {
+    const int64_t r = (sk.q ? rows[RPL - 1] : rows[0]) + sk.drow;
+    R.sc = load_stream16(W.scales + r * W.scale_row_bytes + sk.coff);
   }
 }
 
@@ -656,6 +681,10 @@ __device__ __forceinline__ void walk_class(const WTensor& W, const GemvMap& m, c
   const int tstride = W.K * m.esize;
   const int cap = m.cap;
   const int A = V.count();
+  // NVFP4: the wave's staged block scales (1 KB of LDS per wave after the tile)
+  const ScaleChunk sk = FMT == W_NVFP4 ? scale_chunk<RPL>(m, W.scale_row_bytes) : ScaleChunk{0, 0, 0, 0};
+  const int scale_rb = (int)W.scale_row_bytes;
+  uint8_t* const sca = L.tile + lds_tile_bytes + wave * kScaleStageWave;
   auto advance = [&](Cursor& p) {
     if (++p.b < m.NB) return;
     p.b = 0;
@@ -708,25 +737,35 @@ __device__ __forceinline__ void walk_class(const WTensor& W, const GemvMap& m, c
       advance(np);
       int64_t nr[RPL];
       op.rows(np.e, np.s, lrow, nr);
-      fetch_batch<FMT, RPL>(W, m, nr, np.b, jl, nxt);
+      fetch_batch<FMT, RPL>(W, m, nr, np.b, jl, sk, nxt);
     }
     const uint8_t* tile = L.tile + cx.wrow * tstride;
     const int n = VW == VW_PAIR ? 1 : cx.n;   // a pair is one token
+    if constexpr (FMT == W_NVFP4) *reinterpret_cast<uint4*>(sca + lane * 16) = cur.sc;   // (the step's scales)
 #pragma unroll
     for (int i = 0; i < WeightRegs<RPL>::NPB; ++i) {
       if (i < m.NPB) {
         const int pc = p.b * m.NPB + i;
+        uint32_t sv[RPL];
+#pragma unroll
+        for (int q = 0; q < RPL; ++q) {
+          if constexpr (FMT == W_NVFP4)
+            sv[q] = *reinterpret_cast<const uint16_t*>(sca + q * sk.qbytes + (lane >> m.lg) * scale_rb +
+                                                        (((pc * m.LPR + jl) * EPL) >> 4));
+          else
+            sv[q] = cur.s[i][q];
+        }
         // the empty asm statements keep the three variants real (scalar) branches: with
         // nothing but arithmetic in them the compiler would run all three and select
         if (n == 1) {
           asm volatile("");
-          accumulate_piece<FMT, AK, 1, RPL>(cur.w[i], cur.s[i], tile, tstride, m.LPR, pc, jl, acc);
+          accumulate_piece<FMT, AK, 1, RPL>(cur.w[i], sv, tile, tstride, m.LPR, pc, jl, acc);
         } else if (AK == 1 || n == 2) {
           asm volatile("");
-          accumulate_piece<FMT, AK, 2, RPL>(cur.w[i], cur.s[i], tile, tstride, m.LPR, pc, jl, acc);
+          accumulate_piece<FMT, AK, 2, RPL>(cur.w[i], sv, tile, tstride, m.LPR, pc, jl, acc);
         } else {
           asm volatile("");
-          accumulate_piece<FMT, AK, 4, RPL>(cur.w[i], cur.s[i], tile, tstride, m.LPR, pc, jl, acc);
+          accumulate_piece<FMT, AK, 4, RPL>(cur.w[i], sv, tile, tstride, m.LPR, pc, jl, acc);
         }
       }
     }
@@ -802,7 +841,7 @@ __device__ __forceinline__ void walk_class(const WTensor& W, const GemvMap& m, c
   {
     int64_t rr[RPL];
     op.rows(pa.e, pa.s, lrow, rr);
-    fetch_batch<FMT, RPL>(W, m, rr, 0, jl, A_);
+    fetch_batch<FMT, RPL>(W, m, rr, 0, jl, sk, A_);
   }
   unpark_rows<AK, EPL, NS>(smap, L.tile, nrows0, [&](uint4 r) { return op.cv(r); }, raw);
   if ((int)threadIdx.x < nrows0) L.w_tsc[threadIdx.x] = ts_r;

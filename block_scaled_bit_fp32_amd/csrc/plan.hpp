@@ -36,6 +36,10 @@ struct GemvMap {
 };
 
 constexpr int kWinRows = 64;   // most token rows one staged window of units holds
+// GEMV walks with NVFP4 weights: LDS per wave for the row-step's block scales (after the
+// activation tile; RPL x G rows x K/16 bytes <= 1 KB when a row's pieces fit one batch)
+constexpr int kScaleStageWave = 1024;
+constexpr int kScaleStageBytes = 4 * kScaleStageWave;
 constexpr int kPairMax = 64;   // GEMV kernels: one unit per (token, expert) pair up to this many pairs
 constexpr int kFusedTopkSlots = 8;          // routing fused into gate/up: E <= 64 * this
 // Slots per lane of the routing fused into the gate/up GEMV (a kernel per count): E <= 128

@@ -92,7 +92,7 @@ typedef enum { MOE_SCORE_SIGMOID = 0, MOE_SCORE_SOFTMAX = 1 } moe_score_t;
  * codes + e * rows * (bytes per row); scales and gscale likewise. */
 typedef struct {
   const void *codes;       /* see moe_wfmt_t; 16-byte aligned                           */
-  const uint8_t *scales;   /* NVFP4 / MX: see moe_wfmt_t (NVFP4 2-byte, MX 4-byte
+  const uint8_t *scales;   /* NVFP4 / MX: see moe_wfmt_t (NVFP4 16-byte, MX 4-byte
                               aligned); BF16: NULL                                       */
   const float *gscale;     /* NVFP4 only: FP32 [n][2] for w13 (gate, up), [n][1] for w2 */
 } moe_weights_t;
