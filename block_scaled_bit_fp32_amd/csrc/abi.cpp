@@ -220,10 +220,13 @@ bool make_plan(const moe_layer_t& L, int T, int path, Plan& p) {
               jb <= (size_t)kTokParkBytes && jb <= room;
     if (p.token) p.dn_tile = std::max(p.dn_tile, align_up(jb, 16));
   }
-  // NVFP4 walks stage each row-step's block scales in 1 KB of LDS per wave after the tile
-  // (a row's pieces must then fit one batch)
+  // NVFP4 walks stage each batch's block scales in 1 KB of LDS per wave after the tile,
+  // 16-byte chunks of the wave's rows: with several batches per row, a row's scales of one
+  // batch (NPB x LPR x 2 bytes) must be a multiple of 16 (true for K a multiple of 256)
   const bool nv_r = L.wfmt == W_NVFP4, nv_s = sfmt == W_NVFP4;
-  if ((nv_r && (p.gu_r.NB != 1 || p.dn_r.NB != 1)) || (nv_s && (p.gu_s.NB != 1 || p.dn_s.NB != 1))) return false;
+  auto chunked = [](const GemvMap& m) { return m.NB == 1 || (m.NPB * m.LPR * 2) % 16 == 0; };
+  if (nv_r && !(chunked(p.gu_r) && chunked(p.dn_r))) return false;
+  if (nv_s && !(chunked(p.gu_s) && chunked(p.dn_s))) return false;
   const size_t stage = nv_r || nv_s ? (size_t)kScaleStageBytes : 0;
   p.gu_lds = p.list_bytes + p.gu_tile + stage;
   p.dn_lds = p.list_bytes + p.dn_tile + stage;

@@ -340,34 +340,47 @@ struct WeightRegs {
   static constexpr int NPB = 4;
   uint4 w[NPB][RPL];
   uint32_t s[NPB][RPL];
-  uint4 sc;   // NVFP4: 16 bytes of the wave's block-scale rows (see ScaleChunk)
+  uint4 sc;   // NVFP4: 16 bytes of the batch's scales of the wave's rows (ScaleChunk)
 };
 
-// NVFP4 block scales of a row-step, one 16-byte load per lane instead of one 2-byte load
-// per piece and row: the wave's RPL x G rows are contiguous per q (RPL x G x K/16 bytes,
-// at most 1 KB since a row's pieces fit one batch), lane c loads chunk c of them and
-// writes it to the wave's own 1 KB of LDS, where each lane then reads its pieces' scales
-// (a wave's LDS operations complete in order: no barrier). ScaleChunk is the lane's
-// constant part of the address: which q, the row relative to its own, the byte offset.
+// NVFP4 block scales of a batch (E4M3, one per 16 elements), one 16-byte load per lane
+// instead of one 2-byte load per piece and row (MX scales, one byte per piece, stay
+// per-piece loads). The batch's pieces of a row are one contiguous run of its scale row,
+// bb = NPB x LPR x 2 bytes at b x bb; the wave's G rows of one q hold G x bb = 128 x NPB
+// bytes, RPL x that is at most 1 KB. Lane c loads chunk c of them (clamped to the last)
+// and writes it to the wave's own 1 KB of LDS, where each lane then reads its pieces'
+// scales (a wave's LDS operations complete in order: no barrier). With one batch per row
+// the G rows are contiguous and a chunk may span rows; with several, bb is a multiple of
+// 16 (the host checks) and a chunk lies in one row. ScaleChunk is the lane's constant
+// part of the address: which q, the wave's first row relative to the lane's own, the
+// offset from that row's start.
 struct ScaleChunk {
-  int q, drow, coff;
-  int qbytes;   // bytes of one q's rows (G x K/16)
+  int q, drow, off;
+  int bb;       // bytes of a row's scales per batch
+  int qbytes;   // bytes of one q's staged rows (G x bb)
 };
-template <int RPL>
+template <int FMT, int RPL>
 __device__ __forceinline__ ScaleChunk scale_chunk(const GemvMap& m, int64_t scale_row_bytes) {
+  constexpr int EPL = elems_per_piece(FMT);
   const int lane = threadIdx.x & (kWave - 1);
-  const int cpr = (int)scale_row_bytes >> 4, cpq = m.G * cpr;
+  const int bb = (m.NPB * m.LPR * EPL) >> 4;
+  const int qbytes = m.G * bb, cpq = qbytes >> 4;
   const int c = min(lane, RPL * cpq - 1);
   const int q = RPL == 2 && c >= cpq ? 1 : 0;
-  const int rem = c - q * cpq, crow = rem / cpr;
-  return ScaleChunk{q, crow - (lane >> m.lg), (rem - crow * cpr) * 16, cpq * 16};
+  const int cc = c - q * cpq;
+  int off = cc * 16;
+  if (m.NB > 1) {
+    const int cpr = bb >> 4, crow = cc / cpr;
+    off = crow * (int)scale_row_bytes + (cc - crow * cpr) * 16;
+  }
+  return ScaleChunk{q, -(lane >> m.lg), off, bb, qbytes};
 }
 
 // Loads batch b (pieces b*NPB .. b*NPB + NPB - 1) of the lane's rows. Always issues
-// exactly NPB_max x RPL weight loads and as many scale loads (slots beyond the batch
-// reload its first piece): a step-independent count lets the compiler wait for one
-// step's loads while the next step's are still in flight (vector-memory counters
-// retire in issue order).
+// exactly NPB_max x RPL weight loads (slots beyond the batch reload its first piece) and,
+// for NVFP4, one scale chunk: a step-independent count lets the compiler
+// wait for one step's loads while the next step's are still in flight (vector-memory
+// counters retire in issue order).
 template <int FMT, int RPL>
 __device__ __forceinline__ void fetch_batch(const WTensor& W, const GemvMap& m, const int64_t (&rows)[RPL],
                                             int b, int jl, const ScaleChunk& sk, WeightRegs<RPL>& R) {
@@ -381,17 +394,15 @@ __device__ __forceinline__ void fetch_batch(const WTensor& W, const GemvMap& m, 
       const int ii = i < m.NPB ? i : 0;
       const int el = ((b * m.NPB + ii) * m.LPR + jl) * EPL;
       R.w[i][q] = load_stream16(rp + elem_byte<FMT>(el));
-      if constexpr (FMT == W_NVFP4)
-        R.s[i][q] = 0u;   // (from the staged chunk)
-      else if constexpr (FMT == W_MXFP4 || FMT == W_MXFP8)
+      if constexpr (FMT == W_MXFP4 || FMT == W_MXFP8)
         R.s[i][q] = sp[el >> 5];
       else
-        R.s[i][q] = 0u;
+        R.s[i][q] = 0u;   // (NVFP4: from the staged chunk)
     }
   }
   if constexpr (FMT == W_NVFP4) {
     const int64_t r = (sk.q ? rows[RPL - 1] : rows[0]) + sk.drow;
-    R.sc = load_stream16(W.scales + r * W.scale_row_bytes + sk.coff);
+    R.sc = load_stream16(W.scales + r * W.scale_row_bytes + sk.off + b * sk.bb);
   }
 }
 
@@ -681,9 +692,8 @@ __device__ __forceinline__ void walk_class(const WTensor& W, const GemvMap& m, c
   const int tstride = W.K * m.esize;
   const int cap = m.cap;
   const int A = V.count();
-  // NVFP4: the wave's staged block scales (1 KB of LDS per wave after the tile)
-  const ScaleChunk sk = FMT == W_NVFP4 ? scale_chunk<RPL>(m, W.scale_row_bytes) : ScaleChunk{0, 0, 0, 0};
-  const int scale_rb = (int)W.scale_row_bytes;
+  // NVFP4: the wave's staged scales (1 KB of LDS per wave after the tile)
+  const ScaleChunk sk = FMT == W_NVFP4 ? scale_chunk<FMT, RPL>(m, W.scale_row_bytes) : ScaleChunk{0, 0, 0, 0, 0};
   uint8_t* const sca = L.tile + lds_tile_bytes + wave * kScaleStageWave;
   auto advance = [&](Cursor& p) {
     if (++p.b < m.NB) return;
@@ -741,7 +751,7 @@ __device__ __forceinline__ void walk_class(const WTensor& W, const GemvMap& m, c
     }
     const uint8_t* tile = L.tile + cx.wrow * tstride;
     const int n = VW == VW_PAIR ? 1 : cx.n;   // a pair is one token
-    if constexpr (FMT == W_NVFP4) *reinterpret_cast<uint4*>(sca + lane * 16) = cur.sc;   // (the step's scales)
+    if constexpr (FMT == W_NVFP4) *reinterpret_cast<uint4*>(sca + lane * 16) = cur.sc;   // (the batch's scales)
 #pragma unroll
     for (int i = 0; i < WeightRegs<RPL>::NPB; ++i) {
       if (i < m.NPB) {
@@ -750,8 +760,8 @@ __device__ __forceinline__ void walk_class(const WTensor& W, const GemvMap& m, c
 #pragma unroll
         for (int q = 0; q < RPL; ++q) {
           if constexpr (FMT == W_NVFP4)
-            sv[q] = *reinterpret_cast<const uint16_t*>(sca + q * sk.qbytes + (lane >> m.lg) * scale_rb +
-                                                        (((pc * m.LPR + jl) * EPL) >> 4));
+            sv[q] = *reinterpret_cast<const uint16_t*>(sca + q * sk.qbytes + (lane >> m.lg) * sk.bb +
+                                                       (((i * m.LPR + jl) * EPL) >> 4));
           else
             sv[q] = cur.s[i][q];
         }

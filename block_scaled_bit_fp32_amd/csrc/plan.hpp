@@ -36,8 +36,8 @@ struct GemvMap {
 };
 
 constexpr int kWinRows = 64;   // most token rows one staged window of units holds
-// GEMV walks with NVFP4 weights: LDS per wave for the row-step's block scales (after the
-// activation tile; RPL x G rows x K/16 bytes <= 1 KB when a row's pieces fit one batch)
+// GEMV walks with NVFP4 weights: LDS per wave for a batch's block scales (after the
+// activation tile; RPL x G rows x NPB x LPR x 2 bytes <= 1 KB)
 constexpr int kScaleStageWave = 1024;
 constexpr int kScaleStageBytes = 4 * kScaleStageWave;
 constexpr int kPairMax = 64;   // GEMV kernels: one unit per (token, expert) pair up to this many pairs

@@ -97,6 +97,10 @@ typedef struct {
   const float *gscale;     /* NVFP4 only: FP32 [n][2] for w13 (gate, up), [n][1] for w2 */
 } moe_weights_t;
 
+/* Sizes: H, I and I_shared multiples of 32. With NVFP4 weights the GEMV walks also need
+ * each K (H for gate/up, I or I_shared for down) to be a multiple of 256, or small enough
+ * that a row's pieces form one batch of the walk; other sizes are refused
+ * (MOE_EUNSUPPORTED, reported by moe_layer_check). */
 typedef struct {
   int32_t H;            /* hidden size (K of gate/up, rows of down); multiple of 32      */
   int32_t I;            /* routed expert intermediate size; multiple of 32               */

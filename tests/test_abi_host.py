@@ -85,6 +85,21 @@ def test_default_deny_lists_every_reason(lib):
     assert lib.lib().moe_workspace_bytes(ctypes.byref(s), 8) == 0
 
 
+def test_nvfp4_row_lengths(lib):
+    # NVFP4 walks stage a batch's block scales in 16-byte chunks: K a multiple of 256 plans
+    # at any length (H = 7168: 7 batches per row), K = 1408 (11 batches of 8 scale bytes)
+    # is refused; MX weights load their scales per piece and take any multiple of 32.
+    for H in (7168, 5120, 1792):
+        st, why = _check(lib, _fake_layer(lib, "flint_w4a16", H=H), 8)
+        assert st == 0, (H, why)
+    st, why = _check(lib, _fake_layer(lib, "flint_w4a16", H=1408), 8)
+    assert st == lib.MOE_EUNSUPPORTED and "no workgroup row mapping" in why
+    st, why = _check(lib, _fake_layer(lib, "flint_w4a16", I=1408), 8)
+    assert st == lib.MOE_EUNSUPPORTED and "no workgroup row mapping" in why
+    st, why = _check(lib, _fake_layer(lib, "mistral_mxfp4", H=1408, I=1408), 8)
+    assert st == 0, why
+
+
 def test_misaligned_and_null_weights_are_refused(lib):
     s = _fake_layer(lib, "flint_w4a16")
     s.w13 = lib.WeightsT((1 << 20) + 4, 0, 0)

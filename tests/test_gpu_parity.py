@@ -184,6 +184,7 @@ LAYER_CASES = [
     ("edge_k1_e5", [1, 7]),
     ("edge_k16_e16", [1, 3]),
     ("edge_e1024", [1, 5]),
+    ("edge_nvfp4_batches", [1, 4]),
 ]
 
 
