@@ -746,11 +746,25 @@ moe_status_t enqueue_experts(const moe_layer_t* L, const uint16_t* x_bf16, const
       dn.tok_inv = 1.0f / (float)dn.tok_items;
     }
     auto q = [](const GemvMap& m, int steps) { return CostQ{m.NG, steps, m.cw, m.ct}; };
-    gu.sh_wgs = shared_wgs(*L, T, q(p.gu_s, Ish_ / (p.gu_s.RS / 2)), q(p.gu_r, L->I / (p.gu_r.RS / 2)), gu_grid,
-                           ncu, gu.late16, pm);
+    // The shared expert's token groups each walk all of its rows. With groups of equal
+    // size and a multiple of 8 x groups shared workgroups (all in the first round), group
+    // g's workgroup b + g x (count / groups) walks the same rows as workgroup b of group 0,
+    // at the same time and on the same XCD (blocks go round-robin over the 8 XCDs), so
+    // the later groups' reads hit that XCD's L2 instead of memory.
+    auto xcd_align = [&](int g, const GemvMap& m, int grid) {
+      const int groups = (T + m.NG - 1) / m.NG, step = 8 * groups;
+      if (groups < 2 || T % m.NG || g < step) return g;
+      int r = (g + step / 2) / step * step;
+      while (r > std::min(grid, ncu) - 1) r -= step;
+      return r >= step ? r : g;
+    };
+    gu.sh_wgs = xcd_align(shared_wgs(*L, T, q(p.gu_s, Ish_ / (p.gu_s.RS / 2)), q(p.gu_r, L->I / (p.gu_r.RS / 2)),
+                                     gu_grid, ncu, gu.late16, pm),
+                          p.gu_s, gu_grid);
     dn.sh_wgs = dn.token_mode ? 0
-                              : shared_wgs(*L, T, q(p.dn_s, L->H / p.dn_s.RS), q(p.dn_r, L->H / p.dn_r.RS),
-                                           dn_grid, ncu, dn.late16, pm);
+                              : xcd_align(shared_wgs(*L, T, q(p.dn_s, L->H / p.dn_s.RS), q(p.dn_r, L->H / p.dn_r.RS),
+                                                     dn_grid, ncu, dn.late16, pm),
+                                          p.dn_s, dn_grid);
     // pair and token modes: every position of the class costs the same
     if (pm) {
       split_rounds(gu, T * L->k * p.gu_r.steps, gu_grid - gu.sh_wgs, std::max(0, ncu - gu.sh_wgs));
