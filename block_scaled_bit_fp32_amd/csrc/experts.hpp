@@ -1180,10 +1180,20 @@ __device__ __forceinline__ void walk_tokens(const ExpertArgs& a, const ExpertLds
   struct Regs {
     uint4 w[NPT];
     uint32_t s[NPT];
+    float g;   // WIDE, routed sub-steps: the expert's global weight scale (1 without one)
   };
-  // sub-step j of item row-step s of token t, expert e: this lane's NPT pieces of its row
+  // sub-step j of item row-step s of token t, expert e: this lane's NPT pieces of its row.
+  // WIDE (two sub-steps per lane) also loads a routed expert's global scale as a scalar
+  // load (e is wave-uniform) instead of staging every expert's scales; with the narrow
+  // items' eight sub-steps per lane those scalars would spill.
   auto fetch = [&](int s, int j, int e, Regs& R) {
     const bool sh = j >= a.k;
+    if constexpr (WIDE) {
+      const float* gp = a.rw.gscale ? a.rw.gscale + (int64_t)e * a.rw.gs_per_expert
+                                    : reinterpret_cast<const float*>(a.rw.codes);
+      const float gv = *(const __attribute__((address_space(4))) float*)(uintptr_t)gp;
+      R.g = a.rw.gscale ? gv : 1.0f;
+    }
     const uint8_t* codes = sh ? a.sw.codes : a.rw.codes;
     const uint8_t* scales = sh ? a.sw.scales : a.rw.scales;
     const int64_t row = (int64_t)(sh ? 0 : e) * a.rw.rows + s * rows_item + lrow;
@@ -1238,7 +1248,7 @@ __device__ __forceinline__ void walk_tokens(const ExpertArgs& a, const ExpertLds
 #pragma unroll
         for (int i = 0; i < NPT; ++i)
           if (i < m.NPB) accumulate_piece<FMT, AK, 1, 1>(wr.w[i], wr.s[i], tile, tstride, m.LPR, i, jl, part);
-        const float g = j < a.k ? L.gs_rt[ex[jj] * a.rw.gs_per_expert] : L.gs_sh[0];
+        const float g = j >= a.k ? L.gs_sh[0] : (WIDE ? R[jj].g : L.gs_rt[ex[jj] * a.rw.gs_per_expert]);
         tot = fmaf(L.w_tsc[j] * g, part[0][0], tot);
       }
     }
@@ -1276,8 +1286,9 @@ __device__ __forceinline__ void walk_tokens(const ExpertArgs& a, const ExpertLds
   };
   Regs RA[NJ], RB[NJ];
   int exA[NJ], exB[NJ];
-  // prologue: the first token's experts (scalar loads), rows, factors, global scales and
-  // topk_ids, then every sub-step's weight loads of the first item, then LDS
+  // prologue: the first token's experts (scalar loads), rows, factors, global scales
+  // (narrow: every routed expert's; wide: the shared expert's) and topk_ids, then every
+  // sub-step's weight loads (wide: and routed global scales) of the first item, then LDS
 #pragma unroll
   for (int jj = 0; jj < NJ; ++jj) {   // every load issued (clamped index), so they go out as one batch
     const int j = jof(jj);
@@ -1288,12 +1299,16 @@ __device__ __forceinline__ void walk_tokens(const ExpertArgs& a, const ExpertLds
   const SlotMap<AK> smap(m, a.rw.K);
   park_rows<AK, kPreSlotsTok>(smap, J, row_ld(staged_t), raw);
   const float fac_r = row_fac(staged_t, min((int)threadIdx.x, J - 1));
+  // narrow items: every routed expert's global scale, staged in LDS
+  constexpr int NGS = WIDE ? 1 : kGsPer;
   const int ngs = a.E * a.rw.gs_per_expert;
   const float* gsrc = a.rw.gscale ? a.rw.gscale : reinterpret_cast<const float*>(a.rw.codes);
   const int gmax = a.rw.gscale ? ngs - 1 : 0;
-  float gsv[kGsPer];
+  float gsv[NGS];
+  if constexpr (!WIDE) {
 #pragma unroll
-  for (int j = 0; j < kGsPer; ++j) gsv[j] = gsrc[min((int)threadIdx.x + j * kBlock, gmax)];
+    for (int j = 0; j < NGS; ++j) gsv[j] = gsrc[min((int)threadIdx.x + j * kBlock, gmax)];
+  }
   const float* ssrc = a.sw.gscale ? a.sw.gscale : reinterpret_cast<const float*>(a.sw.codes);
   const float gss = ssrc[0];
   const int idv = a.ids[min((int)threadIdx.x, P - 1)];
@@ -1305,10 +1320,12 @@ __device__ __forceinline__ void walk_tokens(const ExpertArgs& a, const ExpertLds
   }
   unpark_rows<AK, EPL, kPreSlotsTok>(smap, L.tile, J, [&](uint4 r) { return op.cv(r); }, raw);
   if ((int)threadIdx.x < J) L.w_tsc[threadIdx.x] = fac_r;
+  if constexpr (!WIDE) {
 #pragma unroll
-  for (int j = 0; j < kGsPer; ++j) {
-    const int i = threadIdx.x + j * kBlock;
-    if (i < ngs) L.gs_rt[i] = a.rw.gscale ? gsv[j] : 1.0f;
+    for (int j = 0; j < NGS; ++j) {
+      const int i = threadIdx.x + j * kBlock;
+      if (i < ngs) L.gs_rt[i] = a.rw.gscale ? gsv[j] : 1.0f;
+    }
   }
   if (threadIdx.x == 0) L.gs_sh[0] = a.sw.gscale ? gss : 1.0f;
   if ((int)threadIdx.x < P) L.ids[threadIdx.x] = idv;
