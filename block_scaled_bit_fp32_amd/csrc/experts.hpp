@@ -53,8 +53,8 @@ struct ExpertLds {
   ClassTab rt, sh;
   float* w_gs;      // [2 * kWinRows] global weight scales of the staged rows' experts
   float* w_tsc;     // [kWinRows] activation scales of the staged rows
-  float* gs_rt;     // [2 * E] global weight scales of the routed experts (GEMV kernels)
-  float* gs_sh;     // [2] those of the shared expert
+  float* gs_rt;     // [2 * E] global weight scales of the routed experts (narrow token items)
+  float* gs_sh;     // [2] those of the shared expert (token items)
   uint8_t* tile;    // activations of the staged rows, K * esize bytes each
 };
 
@@ -604,6 +604,7 @@ __device__ __forceinline__ void build_rows(const ExpertArgs& a, const ExpertLds&
 struct UnitCtx {
   int crow, wrow, n, e;
   int pr[4];
+  float g[2];   // GEMV walks: the expert's global weight scales (gate/up: gate, up; down: [0])
 };
 
 // How a walk reads its class: units (expert, token count, first row), the unit count, and
@@ -646,7 +647,7 @@ struct ClassView {
   }
 };
 
-constexpr int kGsPer = 8;   // global weight scales staged per thread: 2 * E <= 8 * kBlock
+constexpr int kGsPer = 8;   // narrow token items: global weight scales staged per thread (2 E <= 8 kBlock)
 
 // Routing fused into the gate/up walk (pair mode): where the router logits are and where
 // the selection goes (logits == nullptr: not fused).
@@ -665,13 +666,13 @@ struct FusedRoute {
 //   op.ld(tok, pair, el) -> uint4  raw bytes behind 16 staged bytes of a row at element el
 //   op.cv(uint4) -> uint4          those 16 staged bytes
 //   op.tsc(tok, pair) -> float     a row's activation scale
-//   op.sink(ctx, s, lrow, acc)     results, on the lanes with jl == 0 (global weight
-//                                  scales from the class's table in LDS, gs_tab)
+//   op.sink(ctx, s, lrow, acc)     results, on the lanes with jl == 0 (the unit's global
+//                                  weight scales in ctx.g: scalar loads at each unit
+//                                  change, whose latency the step's weight wait hides)
 // Ops is a plain struct per (projection, activation format), so the shared and routed
 // classes run the same code whenever their formats agree.
 // Prologue: the first staged window (rows of the first units, which the span alone
-// names), the class's global weight scales (ngs of them, from gscale or 1) and, in pair
-// mode, topk_ids are loaded into registers; then the first weight loads are issued (they
+// names) and, in pair mode, topk_ids are loaded into registers; then the first weight loads are issued (they
 // need only the first unit's expert, sp.e0); then everything goes to LDS. So the weights
 // are in flight one memory round trip after launch. Two register sets alternate (no
 // loop-carried copy); every step but the last issues the same number of weight loads for
@@ -681,8 +682,8 @@ struct FusedRoute {
 template <int FMT, int AK, int RPL, int VW, int NKF, class Ops>
 __device__ __forceinline__ void walk_class(const WTensor& W, const GemvMap& m, const ExpertLds& L,
                                            int lds_tile_bytes, const ClassView<VW>& V, const ClassCost& k,
-                                           const Span& sp, const Ops& op, float* gs_tab, int ngs,
-                                           const int32_t* ids, const FusedRoute fr = FusedRoute{}) {
+                                           const Span& sp, const Ops& op, const int32_t* ids,
+                                           const FusedRoute fr = FusedRoute{}) {
   constexpr int EPL = elems_per_piece(FMT);
   constexpr int PER = AK == 0 ? 8 : 4;
   if (sp.left <= 0) return;
@@ -721,7 +722,7 @@ __device__ __forceinline__ void walk_class(const WTensor& W, const GemvMap& m, c
   };
   float acc[RPL][4];
   int cur_a = -1, cur_g = -1;
-  UnitCtx cx{0, 0, 0, 0, {0, 0, 0, 0}};
+  UnitCtx cx{0, 0, 0, 0, {0, 0, 0, 0}, {1.0f, 1.0f}};
   auto do_step = [&](auto pf, const Cursor& p, WeightRegs<RPL>& cur, WeightRegs<RPL>& nxt, Cursor& np) {
     if (p.a != cur_a || p.g != cur_g) {   // next unit
       cur_a = p.a;
@@ -735,6 +736,13 @@ __device__ __forceinline__ void walk_class(const WTensor& W, const GemvMap& m, c
       cx.e = p.e;
 #pragma unroll
       for (int t = 0; t < 4; ++t) cx.pr[t] = t < nt ? V.pair(ur + t) : 0;
+      // (every load issues: without gscale it reads the first codes and takes 1)
+      const float* gp = W.gscale ? W.gscale + (int64_t)p.e * W.gs_per_expert : reinterpret_cast<const float*>(W.codes);
+#pragma unroll
+      for (int q = 0; q < RPL; ++q) {
+        const float gv = reinterpret_cast<const __attribute__((address_space(4))) float*>((uintptr_t)gp)[W.gscale ? q : 0];
+        cx.g[q] = W.gscale ? gv : 1.0f;
+      }
     }
     if (p.b == 0) {
 #pragma unroll
@@ -819,12 +827,6 @@ __device__ __forceinline__ void walk_class(const WTensor& W, const GemvMap& m, c
   park_rows<AK, NS>(smap, nrows0, row_ld(r0), raw);
   float ts_r = 0.0f;
   if ((int)threadIdx.x < nrows0) ts_r = op.tsc(V.tok(r0 + threadIdx.x), V.pair(r0 + threadIdx.x));
-  // (every load issues, at a clamped index; without gscale it reads the first codes)
-  const float* gsrc = W.gscale ? W.gscale : reinterpret_cast<const float*>(W.codes);
-  const int gmax = W.gscale ? ngs - 1 : 0;
-  float gsv[kGsPer];
-#pragma unroll
-  for (int j = 0; j < kGsPer; ++j) gsv[j] = gsrc[min((int)threadIdx.x + j * kBlock, gmax)];
   int idv = 0;
   if constexpr (VW == VW_PAIR) {
     if (ids) idv = ids[min((int)threadIdx.x, V.P - 1)];
@@ -855,11 +857,6 @@ __device__ __forceinline__ void walk_class(const WTensor& W, const GemvMap& m, c
   }
   unpark_rows<AK, EPL, NS>(smap, L.tile, nrows0, [&](uint4 r) { return op.cv(r); }, raw);
   if ((int)threadIdx.x < nrows0) L.w_tsc[threadIdx.x] = ts_r;
-#pragma unroll
-  for (int j = 0; j < kGsPer; ++j) {
-    const int i = threadIdx.x + j * kBlock;
-    if (i < ngs) gs_tab[i] = W.gscale ? gsv[j] : 1.0f;
-  }
   if constexpr (VW == VW_PAIR) {
     if (ids && (int)threadIdx.x < V.P) L.ids[threadIdx.x] = idv;
   }
@@ -942,7 +939,6 @@ struct GateupOps {
   int gs_per_expert, wrows, Iexp, PS, H, hs;
   float* h;
   float* dbg_h;
-  const float* w_gs;
   const float* w_tsc;
   const int* r_pair;
   int h_bf16;            // GEMV kernels: store h as BF16 (RNE) for the down GEMV
@@ -983,7 +979,7 @@ struct GateupOps {
   }
   __device__ __forceinline__ void sink(const UnitCtx& cx, int st, int lrow, const float (&acc)[2][4]) const {
     const int i = st * PS + lrow;
-    const float gsg = w_gs[cx.e * gs_per_expert], gsu = w_gs[cx.e * gs_per_expert + 1];
+    const float gsg = cx.g[0], gsu = cx.g[1];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       if (t < cx.n) {
@@ -1018,11 +1014,10 @@ __device__ __forceinline__ void gateup_walk(const ExpertArgs& a, const ExpertLds
   const WTensor& W = routed ? a.rw : a.sw;
   const GemvMap& m = routed ? a.rmap : a.smap;
   const int Iexp = routed ? a.I : a.Ish;
-  float* gs_tab = routed ? L.gs_rt : L.gs_sh;
   const GateupOps<AF> op{a.x, a.xq_codes, a.xq_scales, a.xq_scale, W.gscale, W.gs_per_expert, W.rows, Iexp,
-                         4 * m.G, a.H, a.hs, a.h, a.dbg_h, gs_tab, L.w_tsc, nullptr, AF == A_BF16};
+                         4 * m.G, a.H, a.hs, a.h, a.dbg_h, L.w_tsc, nullptr, AF == A_BF16};
   walk_class<FMT, 0, 2, VW, NKF>(W, m, L, a.lds_act_bytes, class_view<VW>(a, L), gateup_cost(a, routed), sp, op,
-                                 gs_tab, (routed ? a.E : 1) * W.gs_per_expert, ids, fr);
+                                 ids, fr);
 }
 
 // How a GEMV launch walks the routed experts (the same for every workgroup of a launch,
@@ -1079,7 +1074,6 @@ struct DownOps {
   const float* gscale;
   int gs_per_expert, wrows, Kexp, RS, H, hs;
   float* o;
-  const float* w_gs;
   const float* w_tsc;
   const int* r_pair;
   int h_bf16;            // h stored as BF16 (GEMV kernels)
@@ -1120,7 +1114,7 @@ struct DownOps {
     return (q == 0 && gscale) ? gscale[(int64_t)e * gs_per_expert] : 1.0f;
   }
   __device__ __forceinline__ void sink(const UnitCtx& cx, int st, int lrow, const float (&acc)[1][4]) const {
-    const float g = w_gs[cx.e * gs_per_expert];
+    const float g = cx.g[0];
     const int row = st * RS + lrow;
 #pragma unroll
     for (int t = 0; t < 4; ++t)
@@ -1138,12 +1132,10 @@ __device__ __forceinline__ void down_walk(const ExpertArgs& a, const ExpertLds& 
   constexpr bool routed = VW != VW_SHARED;
   const WTensor& W = routed ? a.rw : a.sw;
   const GemvMap& m = routed ? a.rmap : a.smap;
-  float* gs_tab = routed ? L.gs_rt : L.gs_sh;
   const DownOps<AF> op{a.h, a.hq_codes, a.hq_scales, a.hq_scale, W.gscale, W.gs_per_expert, W.rows,
-                       routed ? a.I : a.Ish, m.RS, a.H, a.hs, a.o, gs_tab, L.w_tsc, nullptr, 1};
-  walk_class<FMT, 0, 1, VW, 0>(W, m, L, a.lds_act_bytes, class_view<VW>(a, L),
-                                               down_cost(a, routed), sp, op, gs_tab,
-                                               (routed ? a.E : 1) * W.gs_per_expert, a.ids);
+                       routed ? a.I : a.Ish, m.RS, a.H, a.hs, a.o, L.w_tsc, nullptr, 1};
+  walk_class<FMT, 0, 1, VW, 0>(W, m, L, a.lds_act_bytes, class_view<VW>(a, L), down_cost(a, routed), sp, op,
+                               a.ids);
 }
 
 // Token mode of the down projection (pair mode, when the shared expert, if any, has the
@@ -1174,7 +1166,7 @@ __device__ __forceinline__ void walk_tokens(const ExpertArgs& a, const ExpertLds
   const int tstride = a.rw.K * m.esize;
   auto jof = [&](int jj) { return WIDE ? wave + 4 * jj : jj; };
   const DownOps<AF> op{a.h, a.hq_codes, a.hq_scales, a.hq_scale, a.rw.gscale, a.rw.gs_per_expert, a.rw.rows,
-                       a.I, m.RS, a.H, a.hs, a.o, L.gs_rt, L.w_tsc, nullptr, 1};
+                       a.I, m.RS, a.H, a.hs, a.o, L.w_tsc, nullptr, 1};
   auto pair_of = [&](int t, int j) { return j < a.k ? t * a.k + j : P + t; };
   auto clamp_e = [&](int v) { return (unsigned)v < (unsigned)a.E ? v : 0; };
   struct Regs {

@@ -475,7 +475,7 @@ __device__ __forceinline__ void ggateup_walk(const ExpertArgs& a, const ExpertLd
   const GroupMap& gm = routed ? a.rgm : a.sgm;
   const int Iexp = routed ? a.I : a.Ish;
   const GateupOps<AF> op{a.x, a.xq_codes, a.xq_scales, a.xq_scale, W.gscale, W.gs_per_expert, W.rows, Iexp,
-                         4 * m.G, a.H, a.hs, a.h, a.dbg_h, L.w_gs, L.w_tsc, C.r_pair};
+                         4 * m.G, a.H, a.hs, a.h, a.dbg_h, L.w_tsc, C.r_pair};
   const int wave = threadIdx.x / kWave, half = (threadIdx.x & (kWave - 1)) >> 5, lr = threadIdx.x & 31;
   auto row_of = [&](int e, int t, int r) -> int64_t {
     const int i = 64 * t + 16 * wave + (r & 15);
@@ -534,7 +534,7 @@ __device__ __forceinline__ void gdown_walk(const ExpertArgs& a, const ExpertLds&
   const GemvMap& m = routed ? a.rmap : a.smap;
   const GroupMap& gm = routed ? a.rgm : a.sgm;
   const DownOps<AF> op{a.h, a.hq_codes, a.hq_scales, a.hq_scale, W.gscale, W.gs_per_expert, W.rows,
-                       routed ? a.I : a.Ish, m.RS, a.H, a.hs, a.o, L.w_gs, L.w_tsc, C.r_pair, 1};
+                       routed ? a.I : a.Ish, m.RS, a.H, a.hs, a.o, L.w_tsc, C.r_pair, 1};
   const int wave = threadIdx.x / kWave, half = (threadIdx.x & (kWave - 1)) >> 5, lr = threadIdx.x & 31;
   auto row_of = [&](int e, int t, int r) -> int64_t { return (int64_t)e * W.rows + 128 * t + 32 * wave + r; };
   auto sink = [&](const UnitCtx& cx, int t, const f32x16_t& acc, float ts, float g, float) {
