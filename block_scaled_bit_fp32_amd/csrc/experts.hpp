@@ -679,7 +679,7 @@ struct FusedRoute {
 // the next one, so the compiler waits for one step's loads while the next step's are in
 // flight. Later windows are staged when a unit does not fit; only LDS barriers are used,
 // so weight loads stream across them.
-template <int FMT, int AK, int RPL, int VW, int NKF, class Ops>
+template <int FMT, int AK, int RPL, int VW, int NKF, bool FRAW, class Ops>
 __device__ __forceinline__ void walk_class(const WTensor& W, const GemvMap& m, const ExpertLds& L,
                                            int lds_tile_bytes, const ClassView<VW>& V, const ClassCost& k,
                                            const Span& sp, const Ops& op, const int32_t* ids,
@@ -809,12 +809,12 @@ __device__ __forceinline__ void walk_class(const WTensor& W, const GemvMap& m, c
   constexpr int NKL = NKF > 0 ? NKF : 1;
   const int nrows0 = r1 - r0;
   struct NoTopk {};
-  std::conditional_t<FUSED, TopkIn<NKL, true>, NoTopk> lv;   // (nothing without fused routing)
+  std::conditional_t<FUSED, TopkIn<NKL, FRAW>, NoTopk> lv;   // (nothing without fused routing)
   int t_lo = 0, t_hi = -1;
   auto route_load = [&](int t) {
     if constexpr (FUSED) {
       const int64_t off = (int64_t)min(t, t_hi) * fr.E;
-      topk_fused_load<NKL>(fr.logits + off, fr.raw ? fr.raw + off : nullptr, fr.E, lv);
+      wave_topk_load<NKL, FRAW>(fr.logits + off, FRAW ? fr.raw + off : nullptr, fr.E, lv);
     }
   };
   if constexpr (FUSED) {
@@ -838,7 +838,7 @@ __device__ __forceinline__ void walk_class(const WTensor& W, const GemvMap& m, c
       if (tb != t_lo) route_load(t);
       int e;
       float w;
-      topk_fused_select<NKL>(lv, fr.E, fr.k, fr.softmax, e, w);
+      wave_topk_select<NKL, FRAW>(lv, fr.E, fr.k, fr.softmax, e, w);
       if (t <= t_hi && lane < fr.k) {
         L.ids[t * fr.k + lane] = e;
         fr.ids_out[t * fr.k + lane] = e;
@@ -1007,7 +1007,7 @@ __device__ __forceinline__ ClassView<VW> class_view(const ExpertArgs& a, const E
   return ClassView<VW>{&L.rt, L.ids, a.k, a.E, a.T, a.T * a.k, a.inv_k};
 }
 
-template <int FMT, int AF, int VW, int NKF = 0>
+template <int FMT, int AF, int VW, int NKF = 0, bool FRAW = false>
 __device__ __forceinline__ void gateup_walk(const ExpertArgs& a, const ExpertLds& L, const Span& sp,
                                             const int32_t* ids, const FusedRoute fr = FusedRoute{}) {
   constexpr bool routed = VW != VW_SHARED;
@@ -1016,7 +1016,7 @@ __device__ __forceinline__ void gateup_walk(const ExpertArgs& a, const ExpertLds
   const int Iexp = routed ? a.I : a.Ish;
   const GateupOps<AF> op{a.x, a.xq_codes, a.xq_scales, a.xq_scale, W.gscale, W.gs_per_expert, W.rows, Iexp,
                          4 * m.G, a.H, a.hs, a.h, a.dbg_h, L.w_tsc, nullptr, AF == A_BF16};
-  walk_class<FMT, 0, 2, VW, NKF>(W, m, L, a.lds_act_bytes, class_view<VW>(a, L), gateup_cost(a, routed), sp, op,
+  walk_class<FMT, 0, 2, VW, NKF, FRAW>(W, m, L, a.lds_act_bytes, class_view<VW>(a, L), gateup_cost(a, routed), sp, op,
                                  ids, fr);
 }
 
@@ -1028,8 +1028,9 @@ enum { RW_PAIR = 0, RW_TABLE = 1, RW_TOKEN = 2, RW_TOKEN_WIDE = 3 };
 // Workgroups [0, sh_wgs) walk the shared expert (BF16 activations, no dependency on the
 // routing), the others split the selected experts: pairs (MODE = RW_PAIR, a.pair_mode)
 // or the tables' units (RW_TABLE). NKF > 0 (pair mode, a.fuse_topk): the walk's prologue
-// selects the experts from the router logits, NKF = fused_topk_slots(E) slots per lane.
-template <int RF, int SF, int AF, int MODE, int NKF>
+// selects the experts from the router logits, NKF = fused_topk_slots(E) slots per lane;
+// FRAW: with bare logits (a router bias that only selects, a.raw != NULL).
+template <int RF, int SF, int AF, int MODE, int NKF, bool FRAW = false>
 __global__ void __launch_bounds__(kBlock, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) gateup_kernel(ExpertArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
   warm_args<ExpertArgs>();
@@ -1044,7 +1045,7 @@ __global__ void __launch_bounds__(kBlock, 2) __attribute__((amdgpu_waves_per_eu(
                         gridDim.x - a.sh_wgs);
     if constexpr (NKF > 0) {   // (a workgroup with an empty span selects nothing)
       const FusedRoute fr{a.logits, a.ids_out, a.w_out, a.E, a.k, a.inv_k, a.raw, a.softmax};
-      gateup_walk<RF, AF, VW_PAIR, NKF>(a, L, sp, nullptr, fr);
+      gateup_walk<RF, AF, VW_PAIR, NKF, FRAW>(a, L, sp, nullptr, fr);
     } else {
       if (sp.a0 < a.T * a.k) {
         const int e = a.ids[sp.a0];
@@ -1134,7 +1135,7 @@ __device__ __forceinline__ void down_walk(const ExpertArgs& a, const ExpertLds& 
   const GemvMap& m = routed ? a.rmap : a.smap;
   const DownOps<AF> op{a.h, a.hq_codes, a.hq_scales, a.hq_scale, W.gscale, W.gs_per_expert, W.rows,
                        routed ? a.I : a.Ish, m.RS, a.H, a.hs, a.o, L.w_tsc, nullptr, 1};
-  walk_class<FMT, 0, 1, VW, 0>(W, m, L, a.lds_act_bytes, class_view<VW>(a, L), down_cost(a, routed), sp, op,
+  walk_class<FMT, 0, 1, VW, 0, false>(W, m, L, a.lds_act_bytes, class_view<VW>(a, L), down_cost(a, routed), sp, op,
                                a.ids);
 }
 
@@ -1407,12 +1408,16 @@ hipError_t launch_experts_af(const ExpertArgs& gu, int gu_grid, size_t gu_lds,
     return launch_kernel(kind, kern, dim3(grid), dim3(kBlock), lds, s, a);
   };
   const int nkf = gu.fuse_topk ? fused_topk_slots(gu.E) : 0;
+  const bool fraw = gu.raw != nullptr;
   hipError_t err = gu.grouped     ? go(K_GATEUP, ggateup_kernel<RF, SF, AF>, gu_grid, gu_lds, gu)
                    : !gu.pair_mode ? go(K_GATEUP, gateup_kernel<RF, SF, AF, RW_TABLE, 0>, gu_grid, gu_lds, gu)
                    : nkf == 0     ? go(K_GATEUP, gateup_kernel<RF, SF, AF, RW_PAIR, 0>, gu_grid, gu_lds, gu)
-                   : nkf == 2     ? go(K_GATEUP, gateup_kernel<RF, SF, AF, RW_PAIR, 2>, gu_grid, gu_lds, gu)
-                   : nkf == 4     ? go(K_GATEUP, gateup_kernel<RF, SF, AF, RW_PAIR, 4>, gu_grid, gu_lds, gu)
-                                  : go(K_GATEUP, gateup_kernel<RF, SF, AF, RW_PAIR, 8>, gu_grid, gu_lds, gu);
+                   : nkf == 2 ? (fraw ? go(K_GATEUP, gateup_kernel<RF, SF, AF, RW_PAIR, 2, true>, gu_grid, gu_lds, gu)
+                                      : go(K_GATEUP, gateup_kernel<RF, SF, AF, RW_PAIR, 2>, gu_grid, gu_lds, gu))
+                   : nkf == 4 ? (fraw ? go(K_GATEUP, gateup_kernel<RF, SF, AF, RW_PAIR, 4, true>, gu_grid, gu_lds, gu)
+                                      : go(K_GATEUP, gateup_kernel<RF, SF, AF, RW_PAIR, 4>, gu_grid, gu_lds, gu))
+                   : fraw ? go(K_GATEUP, gateup_kernel<RF, SF, AF, RW_PAIR, 8, true>, gu_grid, gu_lds, gu)
+                          : go(K_GATEUP, gateup_kernel<RF, SF, AF, RW_PAIR, 8>, gu_grid, gu_lds, gu);
   if (err != hipSuccess) return err;
   if (AF != A_BF16 && (err = launch_hquant(gu, s)) != hipSuccess) return err;
   if (dn.grouped) {

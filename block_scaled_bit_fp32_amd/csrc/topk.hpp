@@ -204,20 +204,9 @@ __device__ __forceinline__ void wave_topk(const float* lg, int E, int k, const f
   }
 }
 
-// Routing fused into another kernel's prologue, NK slots per lane (the kernel is built
-// per slot count: fused_topk_slots(E) of plan.hpp). It always takes the bare-logit path:
-// without bare logits (raw == NULL) it reads the logits in their place, and the selection
-// and weights come out the same (the weights then take the selected logits, which the
-// other path recovers from the keys, and the softmax maximum over the selection is its
-// first value), so one code path serves both kinds of layer.
-template <int NK>
-__device__ __forceinline__ void topk_fused_load(const float* lg, const float* raw, int E, TopkIn<NK, true>& in) {
-  wave_topk_load<NK, true>(lg, raw ? raw : lg, E, in);
-}
-template <int NK>
-__device__ __forceinline__ void topk_fused_select(const TopkIn<NK, true>& in, int E, int k, bool softmax, int& e,
-                                                  float& w) {
-  wave_topk_select<NK, true>(in, E, k, softmax, e, w);
-}
+// Routing fused into another kernel's prologue calls wave_topk_load and wave_topk_select
+// itself, built per slot count (fused_topk_slots(E) of plan.hpp) and per presence of bare
+// logits: it takes the same steps as the top-k kernel for that kind of layer, so both
+// select the same experts and compute the same weights bit for bit.
 
 }  // namespace moe

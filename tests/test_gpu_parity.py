@@ -274,7 +274,8 @@ FORWARD_CASES = [("tiny_bf16", 1), ("tiny_bf16", 8), ("flint_w4a16", 1), ("flint
                  ("flint_w4a16", 16), ("flint_bf16", 8), ("inkling_w4a4", 8),
                  ("inkling_mxfp8", 5), ("mistral_mxfp4", 16), ("mistral_mxfp4_a8", 8),
                  ("mistral_mxfp4_a4", 8), ("inkling_mxfp8_a8", 8),
-                 ("tiny_softmax_selbias", 8), ("mistral_mxfp4_softmax", 8), ("flint_bf16_selbias", 8),
+                 ("tiny_softmax_selbias", 3), ("tiny_softmax_selbias", 8), ("mistral_mxfp4_softmax", 8),
+                 ("flint_bf16_selbias", 4), ("flint_bf16_selbias", 8),
                  ("flint_bf16_selbias", 16), ("edge_k1_e5", 7), ("edge_k16_e16", 3), ("edge_e1024", 5)]
 
 
