@@ -88,9 +88,12 @@ bool plan_class(int fmt, int K, int ntok, int esize, bool paired, GemvMap& m) {
   if (K <= 0 || K % EPL) return false;
   const int units = K / EPL;
   // lanes per row: the largest power of two giving every lane >= 3 pieces of the row
+  // (gate/up: >= 6; fewer lanes per row put more rows on a wave, so each activation piece
+  // read from LDS serves more rows, and the row-sum takes one shuffle step less)
   int LPR = 1;
+  const int min_pieces = paired ? 6 : 3;
   for (int l = 64; l >= 1; l >>= 1)
-    if (units % l == 0 && units / l >= 3) { LPR = l; break; }
+    if (units % l == 0 && units / l >= min_pieces) { LPR = l; break; }
   const int NP = units / LPR;
   int NPB = 1;
   for (int d = 4; d >= 1; --d)
