@@ -88,16 +88,22 @@ bool plan_class(int fmt, int K, int ntok, int esize, bool paired, GemvMap& m) {
   if (K <= 0 || K % EPL) return false;
   const int units = K / EPL;
   // lanes per row: the largest power of two giving every lane >= 3 pieces of the row
-  // (gate/up: >= 6; fewer lanes per row put more rows on a wave, so each activation piece
-  // read from LDS serves more rows, and the row-sum takes one shuffle step less)
-  int LPR = 1;
-  const int min_pieces = paired ? 6 : 3;
-  for (int l = 64; l >= 1; l >>= 1)
-    if (units % l == 0 && units / l >= min_pieces) { LPR = l; break; }
-  const int NP = units / LPR;
-  int NPB = 1;
-  for (int d = 4; d >= 1; --d)
-    if (NP % d == 0) { NPB = d; break; }
+  // (gate/up: >= 6 first; fewer lanes per row put more rows on a wave, so each activation
+  // piece read from LDS serves more rows, and the row-sum takes one shuffle step less).
+  // pieces per batch: the largest divisor of NP up to 4. A gate/up mapping whose NVFP4
+  // block scales could not be staged (several batches of a row with a batch's scales not
+  // a multiple of 16 bytes) falls back to >= 3.
+  int LPR = 1, NP = units, NPB = 1;
+  for (int min_pieces : {paired ? 6 : 3, 3}) {
+    LPR = 1;
+    for (int l = 64; l >= 1; l >>= 1)
+      if (units % l == 0 && units / l >= min_pieces) { LPR = l; break; }
+    NP = units / LPR;
+    NPB = 1;
+    for (int d = 4; d >= 1; --d)
+      if (NP % d == 0) { NPB = d; break; }
+    if (fmt != W_NVFP4 || NP == NPB || (NPB * LPR * 2) % 16 == 0) break;
+  }
   m.LPR = LPR;
   m.G = 64 / LPR;
   m.NP = NP;

@@ -87,9 +87,11 @@ def test_default_deny_lists_every_reason(lib):
 
 def test_nvfp4_row_lengths(lib):
     # NVFP4 walks stage a batch's block scales in 16-byte chunks: K a multiple of 256 plans
-    # at any length (H = 7168: 7 batches per row), K = 1408 (11 batches of 8 scale bytes)
-    # is refused; MX weights load their scales per piece and take any multiple of 32.
-    for H in (7168, 5120, 1792):
+    # at any length (H = 7168: 7 batches per row; H = 256, where gate/up's preferred 8
+    # pieces per lane would take two batches of 8 scale bytes, falls back to 4 pieces),
+    # K = 1408 (11 batches of 8 scale bytes) is refused; MX weights load their scales per
+    # piece and take any multiple of 32.
+    for H in (7168, 5120, 1792, 512, 256):
         st, why = _check(lib, _fake_layer(lib, "flint_w4a16", H=H), 8)
         assert st == 0, (H, why)
     st, why = _check(lib, _fake_layer(lib, "flint_w4a16", H=1408), 8)
