@@ -82,19 +82,20 @@ int64_t scale_row_bytes(int fmt, int K) {
 }
 
 // Row mapping of one weight class (see GemvMap) for rows of length K, activations of
-// `esize` bytes per element, up to ntok tokens per expert; paired = gate/up.
-bool plan_class(int fmt, int K, int ntok, int esize, bool paired, GemvMap& m) {
+// `esize` bytes per element, up to ntok tokens per expert; paired = gate/up; pref = the
+// pieces per lane to aim for (6, or 3 for the down rows of token-mode items).
+bool plan_class(int fmt, int K, int ntok, int esize, bool paired, GemvMap& m, int pref = 6) {
   const int EPL = elems_per_piece(fmt);
   if (K <= 0 || K % EPL) return false;
   const int units = K / EPL;
-  // lanes per row: the largest power of two giving every lane >= 3 pieces of the row
-  // (gate/up: >= 6 first; fewer lanes per row put more rows on a wave, so each activation
-  // piece read from LDS serves more rows, and the row-sum takes one shuffle step less).
-  // pieces per batch: the largest divisor of NP up to 4. A gate/up mapping whose NVFP4
-  // block scales could not be staged (several batches of a row with a batch's scales not
-  // a multiple of 16 bytes) falls back to >= 3.
+  // lanes per row: the largest power of two giving every lane >= pref pieces of the row
+  // (fewer lanes per row put more rows on a wave, so each activation piece read from LDS
+  // serves more rows, and the row-sum takes one shuffle step less), else >= 3. Pieces per
+  // batch: the largest divisor of NP up to 4. A mapping whose NVFP4 block scales could not
+  // be staged (several batches of a row with a batch's scales not a multiple of 16 bytes)
+  // falls back to >= 3.
   int LPR = 1, NP = units, NPB = 1;
-  for (int min_pieces : {paired ? 6 : 3, 3}) {
+  for (int min_pieces : {pref, 3}) {
     LPR = 1;
     for (int l = 64; l >= 1; l >>= 1)
       if (units % l == 0 && units / l >= min_pieces) { LPR = l; break; }
@@ -187,9 +188,21 @@ bool make_plan(const moe_layer_t& L, int T, int path, Plan& p) {
   if (!plan_class(L.wfmt, L.H, nt, 2, true, p.gu_r) || !plan_class(sfmt, L.H, nt, 2, true, p.gu_s))
     return false;
   if (L.I % (p.gu_r.RS / 2) || Ish % (p.gu_s.RS / 2)) return false;
-  // the down GEMV stages BF16: h stored as BF16, or decoded from its FP4 / FP8 codes
-  if (!plan_class(L.wfmt, L.I, nt, 2, false, p.dn_r) || !plan_class(sfmt, Ish, nt, 2, false, p.dn_s))
+  // the down GEMV stages BF16: h stored as BF16, or decoded from its FP4 / FP8 codes.
+  // Token-mode items (decided below) need 3 pieces per lane in one batch; where the
+  // layer's shape rules them out, the down rows aim for 6 pieces per lane like gate/up.
+  if (!plan_class(L.wfmt, L.I, nt, 2, false, p.dn_r, 3) || !plan_class(sfmt, Ish, nt, 2, false, p.dn_s, 3))
     return false;
+  {
+    const int J = L.k + (L.has_shared ? 1 : 0);
+    const size_t lb = (size_t)expert_lds_list_bytes(L.E, nt, L.k);
+    const size_t jb = (size_t)J * L.I * p.dn_r.esize, room = 64 * 1024 > lb ? 64 * 1024 - lb : 0;
+    const bool tok = nt * L.k <= kPairMax && J <= kTokJMax && p.dn_r.NP == kTokPieces && p.dn_r.NB == 1 &&
+                     (!L.has_shared || (sfmt == L.wfmt && Ish == L.I && L.afmt == A_BF16)) &&
+                     jb <= (size_t)kTokParkBytes && jb <= room;
+    if (!tok && (!plan_class(L.wfmt, L.I, nt, 2, false, p.dn_r) || !plan_class(sfmt, Ish, nt, 2, false, p.dn_s)))
+      return false;
+  }
   if (L.H % p.dn_r.RS || L.H % p.dn_s.RS) return false;
   set_costs(p.gu_r, L.wfmt, L.H, kTokPctGateup);
   set_costs(p.gu_s, sfmt, L.H, kTokPctGateup);
