@@ -83,8 +83,8 @@ int64_t scale_row_bytes(int fmt, int K) {
 
 // Row mapping of one weight class (see GemvMap) for rows of length K, activations of
 // `esize` bytes per element, up to ntok tokens per expert; paired = gate/up; pref = the
-// pieces per lane to aim for (6, or 3 for the down rows of token-mode items).
-bool plan_class(int fmt, int K, int ntok, int esize, bool paired, GemvMap& m, int pref = 6) {
+// pieces per lane to aim for (8, or 3 for the down rows of token-mode items).
+bool plan_class(int fmt, int K, int ntok, int esize, bool paired, GemvMap& m, int pref = 8) {
   const int EPL = elems_per_piece(fmt);
   if (K <= 0 || K % EPL) return false;
   const int units = K / EPL;
@@ -190,7 +190,7 @@ bool make_plan(const moe_layer_t& L, int T, int path, Plan& p) {
   if (L.I % (p.gu_r.RS / 2) || Ish % (p.gu_s.RS / 2)) return false;
   // the down GEMV stages BF16: h stored as BF16, or decoded from its FP4 / FP8 codes.
   // Token-mode items (decided below) need 3 pieces per lane in one batch; where the
-  // layer's shape rules them out, the down rows aim for 6 pieces per lane like gate/up.
+  // layer's shape rules them out, the down rows aim for 8 pieces per lane like gate/up.
   if (!plan_class(L.wfmt, L.I, nt, 2, false, p.dn_r, 3) || !plan_class(sfmt, Ish, nt, 2, false, p.dn_s, 3))
     return false;
   {
