@@ -126,8 +126,8 @@ CONFIGS: Dict[str, LayerConfig] = {
                                 wfmt=W_NVFP4, shared_wfmt=W_NVFP4, afmt=A_BF16, batches=(1, 3)),
     "edge_e1024": LayerConfig("edge_e1024", 10, H=512, I=256, E=1024, k=8, has_shared=False,
                               wfmt=W_MXFP4, shared_wfmt=W_MXFP4, afmt=A_BF16, batches=(1, 5)),
-    # NVFP4 with rows longer than one batch of the GEMV walks (H = 1792: 7 batches of one
-    # piece per lane; I = 1280: 5), at a small expert count.
+    # NVFP4 with rows longer than one batch of the GEMV walks (H = 1792: 7 batches per row;
+    # I = 1280: 5), at a small expert count.
     "edge_nvfp4_batches": LayerConfig("edge_nvfp4_batches", 11, H=1792, I=1280, E=16, k=4,
                                       has_shared=True, wfmt=W_NVFP4, shared_wfmt=W_NVFP4,
                                       afmt=A_BF16, batches=(1, 4)),
